@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the swizzled GEMM on one MI355X.
+
+A step is one call of the hot path on one batch of synthetic input that is
+already resident in HBM.  The default workload is the dense 8192^3 bf16 GEMM
+D = A*B + C (A and B K-major, C bf16, bf16 output, fp32 accumulation); the
+other workloads (--workload) are the grouped 16 x 4096^2 GEMM, the MXFP8
+8192^3 GEMM, the 1024^3 and the 128x128x32 single-tile GEMMs.
+
+Prints ONE JSON line on stdout (everything else goes to stderr):
+  value          whole-job TFLOP/s = 2*M*N*K / (measured seconds per step)
+  roofline       the dominant kernel against MI355X's published dense MFMA
+                 peak for its dtype (bf16/fp16 2516.6, fp8 5033.2 TFLOP/s);
+                 achieved = algorithmic FLOP per launch / mean launch time
+                 from HIP events recorded on the launch stream
+  cpu_baseline   the CPU oracle (fp64 triple loop, all host cores) timed on a
+                 bounded row sample of the same workload, in TFLOP/s
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2}
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_workload(name: str, dev):
+    """Returns (run callable, flops per step, dtype, config dict, oracle
+    sample callable(rows) -> seconds, rows_total)."""
+    import torch
+
+    import dense_gemm_swizzled_amd as sg
+    import synth_inputs as si
+
+    if name in ("dense_8192", "dense_1024", "single_tile"):
+        case = {"dense_8192": si.dense_8192, "dense_1024": si.dense_1024,
+                "single_tile": si.single_tile}[name]()
+        A, B = case.A.to(dev), case.B.to(dev)
+        C = case.C.to(dev) if case.C is not None else None
+        dt = {"f32": torch.float32, "bf16": torch.bfloat16}[case.d_dtype]
+        D = torch.empty(case.M, case.N, dtype=dt, device=dev)
+
+        def run():
+            sg.gemm(A, B, a_major=case.a_major, b_major=case.b_major, C=C, out=D)
+
+        flops = 2.0 * case.M * case.N * case.K
+        cfg = {"workload": case.name, "M": case.M, "N": case.N, "K": case.K,
+               "a_major": case.a_major, "b_major": case.b_major,
+               "ab_dtype": case.ab_dtype, "c": case.c_dtype, "d_dtype": case.d_dtype}
+
+        def oracle_sample(rows):
+            import oracle
+            a = case.A[:rows] if case.a_major == "k" else case.A[:, :rows].contiguous()
+            c = case.C[:rows] if case.C is not None else None
+            t0 = time.perf_counter()
+            oracle.gemm(rows, case.N, case.K, a, case.a_major, case.B, case.b_major,
+                        case.ab_dtype, c, case.c_dtype, with_bound=False)
+            return time.perf_counter() - t0, 2.0 * rows * case.N * case.K
+
+        return run, flops, case.ab_dtype, cfg, oracle_sample, case.M
+
+    if name == "grouped":
+        case = si.grouped()
+        A, B = case.A.to(dev), case.B.to(dev)
+        D = torch.empty(case.A.shape[0], case.N, dtype=torch.bfloat16, device=dev)
+
+        def run():
+            sg.grouped_gemm(A, B, case.m_offsets, out=D)
+
+        flops = 2.0 * case.m_offsets[-1] * case.N * case.K
+        cfg = {"workload": case.name, "G": case.G, "m_sizes": case.m_sizes,
+               "N": case.N, "K": case.K, "ab_dtype": "bf16", "d_dtype": "bf16"}
+
+        def oracle_sample(rows):
+            import oracle
+            Bn = case.B.reshape(case.G, case.N, case.K)
+            t0 = time.perf_counter()
+            oracle.gemm(rows, case.N, case.K, case.A[:rows], "k", Bn[0], "k", "bf16",
+                        with_bound=False)
+            return time.perf_counter() - t0, 2.0 * rows * case.N * case.K
+
+        return run, flops, "bf16", cfg, oracle_sample, case.m_sizes[0]
+
+    if name == "mxfp8":
+        case = si.mxfp8()
+        A, SFA, B, SFB = (t.to(dev) for t in (case.A, case.SFA, case.B, case.SFB))
+        D = torch.empty(case.M, case.N, dtype=torch.bfloat16, device=dev)
+
+        def run():
+            sg.mx_gemm(A, SFA, B, SFB, out=D)
+
+        flops = 2.0 * case.M * case.N * case.K
+        cfg = {"workload": case.name, "M": case.M, "N": case.N, "K": case.K,
+               "block": 32, "ab_dtype": "e4m3", "scale": "e8m0", "d_dtype": "bf16"}
+
+        def oracle_sample(rows):
+            import oracle
+            t0 = time.perf_counter()
+            oracle.mx_gemm(rows, case.N, case.K, case.A[:rows], case.SFA[:rows], case.B,
+                           case.SFB, with_bound=False)
+            return time.perf_counter() - t0, 2.0 * rows * case.N * case.K
+
+        return run, flops, "e4m3", cfg, oracle_sample, case.M
+
+    raise SystemExit(f"unknown workload {name}")
+
+
+def cpu_baseline(oracle_sample, rows_total, target_s=12.0):
+    """Times the oracle on a row sample sized for about target_s seconds."""
+    import oracle
+    cores = oracle.default_threads()
+    rows = min(32, rows_total)
+    t, fl = oracle_sample(rows)
+    rows2 = int(min(rows_total, max(rows, rows * target_s / max(t, 1e-3))))
+    rows2 = max(cores, rows2 - rows2 % cores) if rows_total >= cores else rows2
+    if rows2 > rows:
+        t, fl = oracle_sample(rows2)
+        rows = rows2
+    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {rows} of {rows_total} output rows (all columns, full K), "
+                      f"{t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dense_8192",
+                    choices=["dense_8192", "grouped", "mxfp8", "dense_1024", "single_tile"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {args.workload}: generating inputs")
+    run, flops, dtype, cfg, oracle_sample, rows_total = build_workload(args.workload, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+
+    # HIP events bracket the timed steps on the launch stream (the library
+    # launches on torch's current stream); per-launch events give the kernel
+    # time, the wall clock around the region gives the step time.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        run()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    mean_ms = sum(per_launch_ms) / len(per_launch_ms)
+    sorted_ms = sorted(per_launch_ms)
+    median_ms = sorted_ms[len(sorted_ms) // 2]
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    log(f"[bench] {cfg['workload']}: {ms_per_step:.4f} ms/step wall, kernel mean "
+        f"{mean_ms:.4f} ms median {median_ms:.4f} ms -> {achieved:.1f} TFLOP/s "
+        f"({100 * achieved / peak:.1f}% of {peak} TFLOP/s)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a row sample")
+        cpu = cpu_baseline(oracle_sample, rows_total)
+        log(f"[bench] cpu oracle: {cpu}")
+
+    out = {
+        "metric": "GEMM TFLOP/s and % of bf16 MFMA peak at 8192^3 on 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": cfg,
+        "pct_of_bf16_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None, "kernel_ms_mean": round(mean_ms, 5),
+                     "kernel_ms_median": round(median_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

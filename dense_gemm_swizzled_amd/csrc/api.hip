@@ -1,0 +1,286 @@
+// api.hip -- the C ABI of libswizzled_gemm.so: argument validation, the
+// variant plan (tile shape, grid, raster) and the launch on the caller's
+// stream.  Every check runs before any HIP call, so each error path is
+// reachable on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/swizzled_gemm.h"
+#include "launch.h"
+#include "lds_layout.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SG_OK;
+}
+
+int elem_bytes(int dt) {
+  switch (dt) {
+    case SG_F16:
+    case SG_BF16:
+      return 2;
+    case SG_F32:
+      return 4;
+    case SG_E4M3:
+    case SG_E8M0:
+      return 1;
+    default:
+      return 0;
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_out_dtype(int dt) { return dt == SG_F32 || dt == SG_BF16 || dt == SG_F16; }
+
+constexpr int64_t kMaxExtent = (int64_t)1 << 31;  // buffer offsets are 32-bit
+constexpr int kCUs = 256;                          // MI355X compute units
+constexpr int kGroupM = 8;
+
+// Largest byte extent one workgroup addresses through a buffer resource.
+int64_t panel_extent(int major, int64_t rows, int64_t K, int64_t tile_rows, int eb) {
+  return major == SG_K_MAJOR ? (rows < tile_rows ? rows : tile_rows) * K * eb
+                             : rows * K * eb;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+sg::TileShape pick_tile(int64_t tiles256) {
+  return tiles256 >= kCUs ? sg::kTile256 : sg::kTile128;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gemm_last_error(void) { return g_last_error.c_str(); }
+
+const char* gemm_version(void) {
+  return "swizzled_gemm 0.1 (gfx950; 16-bit MFMA 32x32x16, MXFP8 scaled MFMA "
+         "32x32x64; LDS XOR swizzle over 256-byte bank lines)";
+}
+
+int gemm_run(int64_t M, int64_t N, int64_t K, const void* A, int a_major,
+             const void* B, int b_major, int ab_dtype, const void* C, int c_dtype,
+             void* D, int d_dtype, void* stream) {
+  if (M < 0 || N < 0 || K < 0)
+    return fail(SG_ERR_SHAPE, "gemm_run: negative size M=%lld N=%lld K=%lld",
+                (long long)M, (long long)N, (long long)K);
+  if (ab_dtype != SG_F16 && ab_dtype != SG_BF16)
+    return fail(SG_ERR_DTYPE, "gemm_run: ab_dtype %d is not SG_F16/SG_BF16", ab_dtype);
+  if (!is_out_dtype(d_dtype))
+    return fail(SG_ERR_DTYPE, "gemm_run: d_dtype %d is not SG_F32/SG_BF16/SG_F16", d_dtype);
+  if (C && !is_out_dtype(c_dtype))
+    return fail(SG_ERR_DTYPE, "gemm_run: c_dtype %d is not SG_F32/SG_BF16/SG_F16", c_dtype);
+  if (C && C == D && c_dtype != d_dtype)
+    return fail(SG_ERR_DTYPE, "gemm_run: in-place C == D needs c_dtype == d_dtype");
+  if ((a_major != SG_K_MAJOR && a_major != SG_MN_MAJOR) ||
+      (b_major != SG_K_MAJOR && b_major != SG_MN_MAJOR))
+    return fail(SG_ERR_MAJOR, "gemm_run: majorness must be SG_K_MAJOR or SG_MN_MAJOR");
+  if (M == 0 || N == 0) return ok();
+  if (!D) return fail(SG_ERR_NULL, "gemm_run: D is NULL");
+  if (K > 0 && (!A || !B)) return fail(SG_ERR_NULL, "gemm_run: A or B is NULL");
+  const int eb = 2, db = elem_bytes(d_dtype), cb = C ? elem_bytes(c_dtype) : 0;
+  if ((K > 0 && (!aligned16(A) || !aligned16(B))) || !aligned16(D) || (C && !aligned16(C)))
+    return fail(SG_ERR_ALIGN, "gemm_run: every pointer must be 16-byte aligned");
+  const int64_t a_pitch = (a_major == SG_K_MAJOR ? K : M) * eb;
+  const int64_t b_pitch = (b_major == SG_K_MAJOR ? K : N) * eb;
+  if ((K > 0 && (a_pitch % 16 || b_pitch % 16)) || (N * db) % 16 || (C && (N * cb) % 16))
+    return fail(SG_ERR_ALIGN,
+                "gemm_run: row pitches must be multiples of 16 bytes (A %lld, B %lld, "
+                "D %lld bytes)", (long long)a_pitch, (long long)b_pitch,
+                (long long)(N * db));
+  const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256);
+  const sg::TileShape tile = pick_tile(tiles256);
+  const int64_t T = tile == sg::kTile256 ? 256 : 128;
+  if (panel_extent(a_major, M, K, T, eb) >= kMaxExtent ||
+      panel_extent(b_major, N, K, T, eb) >= kMaxExtent)
+    return fail(SG_ERR_SHAPE, "gemm_run: an operand panel spans 2^31 bytes or more");
+  const int64_t tiles_m = cdiv(M, T), tiles_n = cdiv(N, T);
+  if (tiles_m * tiles_n >= kMaxExtent || tiles_m * tiles_n > 0x7fffffffLL)
+    return fail(SG_ERR_SHAPE, "gemm_run: too many tiles");
+
+  sg::DenseParams p;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.c_dtype = C ? c_dtype : SG_NONE;
+  p.d_dtype = d_dtype;
+  p.tiles_m = (int)tiles_m;
+  p.tiles_n = (int)tiles_n;
+  p.group_m = kGroupM;
+  hipError_t e = sg::launch_dense(tile, ab_dtype == SG_BF16, a_major == SG_MN_MAJOR,
+                                  b_major == SG_MN_MAJOR, sg::kSwzDefault, p,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemm_run launch");
+  return ok();
+}
+
+int grouped_gemm_run(int G, const int64_t* m_offsets, int64_t N, int64_t K,
+                     const void* A, int a_major, const void* B, int b_major,
+                     int ab_dtype, void* D, int d_dtype, void* stream) {
+  if (G < 1 || G > SG_MAX_GROUPS)
+    return fail(SG_ERR_GROUPS, "grouped_gemm_run: G=%d outside [1, %d]", G, SG_MAX_GROUPS);
+  if (!m_offsets) return fail(SG_ERR_NULL, "grouped_gemm_run: m_offsets is NULL");
+  if (m_offsets[0] != 0)
+    return fail(SG_ERR_GROUPS, "grouped_gemm_run: m_offsets[0] must be 0");
+  for (int g = 0; g < G; ++g)
+    if (m_offsets[g + 1] < m_offsets[g])
+      return fail(SG_ERR_GROUPS, "grouped_gemm_run: m_offsets decrease at group %d", g);
+  if (N < 0 || K < 0)
+    return fail(SG_ERR_SHAPE, "grouped_gemm_run: negative size N=%lld K=%lld",
+                (long long)N, (long long)K);
+  if (ab_dtype != SG_F16 && ab_dtype != SG_BF16)
+    return fail(SG_ERR_DTYPE, "grouped_gemm_run: ab_dtype %d is not SG_F16/SG_BF16", ab_dtype);
+  if (!is_out_dtype(d_dtype))
+    return fail(SG_ERR_DTYPE, "grouped_gemm_run: d_dtype %d unsupported", d_dtype);
+  if (a_major != SG_K_MAJOR || b_major != SG_K_MAJOR)
+    return fail(SG_ERR_MAJOR, "grouped_gemm_run: A and B must be SG_K_MAJOR");
+  const int64_t total = m_offsets[G];
+  if (total == 0 || N == 0) return ok();
+  if (!D) return fail(SG_ERR_NULL, "grouped_gemm_run: D is NULL");
+  if (K > 0 && (!A || !B)) return fail(SG_ERR_NULL, "grouped_gemm_run: A or B is NULL");
+  const int eb = 2, db = elem_bytes(d_dtype);
+  if ((K > 0 && (!aligned16(A) || !aligned16(B))) || !aligned16(D))
+    return fail(SG_ERR_ALIGN, "grouped_gemm_run: every pointer must be 16-byte aligned");
+  if ((K * eb) % 16 || (N * db) % 16)
+    return fail(SG_ERR_ALIGN, "grouped_gemm_run: row pitches must be multiples of 16 bytes");
+  int64_t tiles256 = 0;
+  for (int g = 0; g < G; ++g) tiles256 += cdiv(m_offsets[g + 1] - m_offsets[g], 256);
+  tiles256 *= cdiv(N, 256);
+  const sg::TileShape tile = pick_tile(tiles256);
+  const int64_t T = tile == sg::kTile256 ? 256 : 128;
+  if (T * K * eb >= kMaxExtent)
+    return fail(SG_ERR_SHAPE, "grouped_gemm_run: an operand panel spans 2^31 bytes or more");
+  sg::GroupedParams p;
+  p.A = A;
+  p.B = B;
+  p.D = D;
+  p.N = N;
+  p.K = K;
+  p.d_dtype = d_dtype;
+  p.G = G;
+  p.tiles_n = (int)cdiv(N, T);
+  p.group_m = kGroupM;
+  int64_t acc = 0;
+  for (int g = 0; g <= G; ++g) {
+    p.m_off[g] = m_offsets[g];
+    p.tile_start[g] = (int32_t)acc;
+    if (g < G) acc += cdiv(m_offsets[g + 1] - m_offsets[g], T) * p.tiles_n;
+    if (acc > 0x7fffffffLL) return fail(SG_ERR_SHAPE, "grouped_gemm_run: too many tiles");
+  }
+  for (int g = G + 1; g <= SG_MAX_GROUPS; ++g) {
+    p.m_off[g] = m_offsets[G];
+    p.tile_start[g] = (int32_t)acc;
+  }
+  if (acc == 0) return ok();
+  hipError_t e = sg::launch_grouped(tile, ab_dtype == SG_BF16, sg::kSwzDefault, p,
+                                    (int)acc, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "grouped_gemm_run launch");
+  return ok();
+}
+
+int mx_gemm_run(int64_t M, int64_t N, int64_t K, const void* A, const void* SFA,
+                const void* B, const void* SFB, void* D, int d_dtype, void* stream) {
+  if (M < 0 || N < 0 || K < 0)
+    return fail(SG_ERR_SHAPE, "mx_gemm_run: negative size");
+  if (K % 128)
+    return fail(SG_ERR_SHAPE, "mx_gemm_run: K=%lld is not a multiple of 128", (long long)K);
+  if (d_dtype != SG_F32 && d_dtype != SG_BF16)
+    return fail(SG_ERR_DTYPE, "mx_gemm_run: d_dtype %d is not SG_F32/SG_BF16", d_dtype);
+  if (M == 0 || N == 0) return ok();
+  if (!D) return fail(SG_ERR_NULL, "mx_gemm_run: D is NULL");
+  if (K > 0 && (!A || !B || !SFA || !SFB))
+    return fail(SG_ERR_NULL, "mx_gemm_run: A, B, SFA or SFB is NULL");
+  const int db = elem_bytes(d_dtype);
+  if ((K > 0 && (!aligned16(A) || !aligned16(B))) || !aligned16(D) ||
+      (K > 0 && ((reinterpret_cast<uintptr_t>(SFA) | reinterpret_cast<uintptr_t>(SFB)) & 3u)))
+    return fail(SG_ERR_ALIGN,
+                "mx_gemm_run: A, B, D must be 16-byte aligned, SFA and SFB 4-byte aligned");
+  if ((N * db) % 16)
+    return fail(SG_ERR_ALIGN, "mx_gemm_run: D row pitch must be a multiple of 16 bytes");
+  const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256);
+  const sg::TileShape tile = pick_tile(tiles256);
+  const int64_t T = tile == sg::kTile256 ? 256 : 128;
+  if (T * K >= kMaxExtent)
+    return fail(SG_ERR_SHAPE, "mx_gemm_run: an operand panel spans 2^31 bytes or more");
+  const int64_t tiles_m = cdiv(M, T), tiles_n = cdiv(N, T);
+  if (tiles_m * tiles_n > 0x7fffffffLL) return fail(SG_ERR_SHAPE, "mx_gemm_run: too many tiles");
+  sg::MxParams p;
+  p.A = A;
+  p.SFA = SFA;
+  p.B = B;
+  p.SFB = SFB;
+  p.D = D;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.d_dtype = d_dtype;
+  p.tiles_m = (int)tiles_m;
+  p.tiles_n = (int)tiles_n;
+  p.group_m = kGroupM;
+  hipError_t e = sg::launch_mx(tile, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mx_gemm_run launch");
+  return ok();
+}
+
+int gemm_lds_layout(int rows, int row_bytes, int32_t* out) {
+  if (!out) return fail(SG_ERR_NULL, "gemm_lds_layout: out is NULL");
+  if (rows <= 0 || rows % 8 || (row_bytes != 64 && row_bytes != 128 && row_bytes != 256))
+    return fail(SG_ERR_SHAPE, "gemm_lds_layout: rows must be a positive multiple of 8 "
+                              "and row_bytes 64, 128 or 256");
+  const int chunks = row_bytes / 16;
+  for (int r = 0; r < rows; ++r)
+    for (int c = 0; c < chunks; ++c)
+      out[r * chunks + c] = (int32_t)sg::lds_offset_rt(row_bytes, sg::kSwzDefault, r, c);
+  return ok();
+}
+
+int gemm_lds_image(const void* X, int64_t rows_total, int64_t K, int elem_bytes_,
+                   int64_t row0, int64_t k0, int tile_rows, void* out, void* stream) {
+  if (!X || !out) return fail(SG_ERR_NULL, "gemm_lds_image: X or out is NULL");
+  if (elem_bytes_ != 1 && elem_bytes_ != 2)
+    return fail(SG_ERR_DTYPE, "gemm_lds_image: elem_bytes must be 1 or 2");
+  if (tile_rows != 128 && tile_rows != 256)
+    return fail(SG_ERR_SHAPE, "gemm_lds_image: tile_rows must be 128 or 256");
+  if (rows_total < 0 || K <= 0 || row0 < 0 || row0 >= rows_total || k0 < 0 || k0 >= K ||
+      (k0 * elem_bytes_) % 128)
+    return fail(SG_ERR_SHAPE, "gemm_lds_image: tile origin out of range or not on a "
+                              "128-byte K boundary");
+  if (!aligned16(X) || !aligned16(out) || (K * elem_bytes_) % 16)
+    return fail(SG_ERR_ALIGN, "gemm_lds_image: 16-byte alignment required");
+  if ((int64_t)tile_rows * K * elem_bytes_ >= kMaxExtent)
+    return fail(SG_ERR_SHAPE, "gemm_lds_image: panel spans 2^31 bytes or more");
+  hipError_t e = sg::launch_lds_image(X, rows_total, K, elem_bytes_, row0, k0, tile_rows,
+                                      out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemm_lds_image launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,188 @@
+// gemm_device.h -- device building blocks of the swizzled GEMM kernels
+// (gfx950 / CDNA4): vector types, the LDS swizzle, buffer loads with
+// hardware out-of-range zero fill, the operand-tile loaders and the MFMA
+// wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lds_layout.h"
+
+namespace sg {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWaveSize = 64;
+constexpr int kThreads = 256;  // 4 waves per workgroup
+
+// Byte offset past every extent the library accepts: a buffer load there
+// returns zeros (raw buffer range check), which is how ragged M/N/K edges
+// and K tails are filled.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// gfx9 buffer descriptor word 3: 32-bit data format, raw (stride 0) access.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r,
+                                               uint32_t off) {
+  return __builtin_bit_cast(u32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r,
+                                                 uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// LDS access in 16-byte units (the swizzle never splits a 16-byte atom).
+__device__ __forceinline__ u32x4 lds_read16(const char* lds, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(lds + off);
+}
+__device__ __forceinline__ void lds_write16(char* lds, uint32_t off, u32x4 v) {
+  *reinterpret_cast<u32x4*>(lds + off) = v;
+}
+
+// ---------------------------------------------------------------------------
+// Operand tile loaders.  A tile is `Rows` operand rows (M rows of A or N rows
+// of B) by 128 bytes of K (64 fp16/bf16 or 128 fp8 elements), stored in LDS
+// K-major as Rows x 128 B under lds_offset<128, Swz>.  Global reads are 16
+// bytes per lane; consecutive lanes read consecutive 16-byte chunks of one
+// row (coalesced); the swizzle permutes only the LDS destination.
+// ---------------------------------------------------------------------------
+
+// K-major source [rows][K]: chunk (row, c) lives at row*pitch + kbyte0 + 16c.
+// Thread t, step i: row = i*32 + t/8, chunk = t%8.
+template <int Rows>
+struct KMajorLoader {
+  static constexpr int kSteps = Rows * 8 / kThreads;  // 16-byte loads per thread
+  u32x4 v[kSteps];
+
+  // row_pitch: bytes per source row; rows_valid: rows of this tile that
+  // exist; kbytes_total: bytes of K per row that exist (K * elem size).
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int tid,
+                                       uint32_t row_pitch, int rows_valid,
+                                       uint32_t kbyte0, uint32_t kbytes_total) {
+    const int c = tid & 7;
+    const uint32_t kb = kbyte0 + 16u * c;
+    const bool k_ok = kb < kbytes_total;
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+      const int row = i * 32 + (tid >> 3);
+      const bool ok = k_ok && row < rows_valid;
+      v[i] = buffer_load16(r, ok ? row * row_pitch + kb : kOutOfRange);
+    }
+  }
+
+  template <int Swz>
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+    const int c = tid & 7;
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+      const int row = i * 32 + (tid >> 3);
+      lds_write16(lds, lds_offset<128, Swz>(row, c), v[i]);
+    }
+  }
+};
+
+// MN-major source [K][rows] (rows contiguous, 16-bit elements): the tile is
+// 64 k-rows x Rows.  Thread t owns the 8x8 block (k-chunk kc = t%8, row
+// chunk rc = t/8): it reads 8 k-rows of 16 bytes, transposes the 8x8 block
+// of 16-bit values in registers, and writes 8 K-major LDS rows.
+template <int Rows>
+struct MNMajorLoader {
+  static constexpr int kActive = Rows / 8 * 8;  // threads that own a block
+  u32x4 v[8];
+
+  // row_pitch: bytes per k-row of the source (= total rows * 2);
+  // cols_valid: tile rows that exist; k0: first k of the tile; K: total k.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int tid,
+                                       uint32_t row_pitch, int cols_valid,
+                                       int k0, int K) {
+    const int kc = tid & 7, rc = tid >> 3;
+    const bool c_ok = tid < kActive && rc * 8 < cols_valid;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + kc * 8 + j;
+      const bool ok = c_ok && k < K;
+      v[j] = buffer_load16(r, ok ? (uint32_t)k * row_pitch + 16u * rc
+                                 : kOutOfRange);
+    }
+  }
+
+  template <int Swz>
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+    if (tid >= kActive) return;
+    const int kc = tid & 7, rc = tid >> 3;
+    // v[j] holds k-row j, columns 0..7 of the block as 4 dwords of 2 values
+    // (even column in the low half).  Output row c needs column c of every
+    // k-row: dword q of row c = { v[2q] col c, v[2q+1] col c }.
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = __builtin_amdgcn_perm(v[2 * q + 1][c >> 1], v[2 * q][c >> 1], sel);
+      lds_write16(lds, lds_offset<128, Swz>(rc * 8 + c, kc), o);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers (v_mfma_f32_32x32x16_{bf16,f16}, v_mfma_scale_f32_32x32x64_
+// f8f6f4).  Operand lane layout used throughout: lane l supplies row l%32 of
+// its operand and the 16-byte K chunk l/32 of the current K step; A and B use
+// the same K assignment, so the product is independent of how the hardware
+// orders K inside the instruction.
+// ---------------------------------------------------------------------------
+template <bool IsBF16>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (IsBF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(
+        __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue element conversions (round to nearest even).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  // RNE to bfloat16 of finite values; NaN stays NaN (quiet bit forced).
+  auto cvt = [](float f) -> uint32_t {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu))
+      return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  };
+  return cvt(lo) | (cvt(hi) << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) {
+  return __builtin_bit_cast(float, h << 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+}  // namespace sg

@@ -1,0 +1,329 @@
+// gemm_kernels.h -- the dense / grouped swizzled GEMM kernel template and
+// its launch parameters (included by the per-dtype translation units).
+//
+// Structure of one workgroup (256 threads = 4 wave64s, one output tile):
+//   1. tile schedule: workgroup id -> (group, tile row, tile column), with an
+//      XCD-aware remap and GROUP_M-style rasterisation (the Triton matmul
+//      listing in "Tensor Cores, layouts, and swizzling" groups tile rows
+//      for cache reuse; here each of the 8 XCDs, which have private L2s, is
+//      given a contiguous range of that order);
+//   2. global -> LDS: each lane moves 16 bytes per load, consecutive lanes
+//      consecutive chunks of a row (the cooperative loader of "LBO, SBO and
+//      SWZ for a tcgen05 tile", section 2); the global order stays logical
+//      and only the LDS destination is swizzled (same page, section 3);
+//   3. a two-stage LDS ring: the loads for K tile k+1 are in flight while
+//      tile k is consumed; one barrier per K tile keeps a stage from being
+//      overwritten before every wave has read it (the rule of the Hopper
+//      mainloop in "Tensor Cores, layouts, and swizzling");
+//   4. MFMA: each wave owns a (BM/2) x (BN/2) block of 32x32 fp32
+//      accumulators, fed by ds_read_b128 of swizzled 16-byte chunks; the
+//      first K step starts from zero (the accumulate-flag rule of "06
+//      Blackwell Tensor Core", section "How tcgen05.mma Executes");
+//   5. epilogue: registers -> global with optional C, no LDS staging (the
+//      output-tile swizzle "does practically nothing" per the Results of
+//      "Swizzling explained properly").
+#pragma once
+
+#include <type_traits>
+
+#include "gemm_device.h"
+#include "../../include/swizzled_gemm.h"
+
+namespace sg {
+
+struct DenseParams {
+  const void* A;
+  const void* B;
+  const void* C;
+  void* D;
+  int64_t M, N, K;
+  int c_dtype, d_dtype;
+  int tiles_m, tiles_n;
+  int group_m;
+};
+
+struct GroupedParams {
+  const void* A;
+  const void* B;
+  void* D;
+  int64_t N, K;
+  int d_dtype;
+  int G;
+  int tiles_n;
+  int group_m;
+  int64_t m_off[SG_MAX_GROUPS + 1];      // row offsets of the groups
+  int32_t tile_start[SG_MAX_GROUPS + 1]; // first tile id of each group
+};
+
+// Spread workgroups so that each XCD (workgroups are dealt to the 8 XCDs
+// round robin) receives a contiguous range of tile ids.
+__device__ __forceinline__ int xcd_remap(int wg, int total) {
+  const int per = total >> 3, rem = total & 7;
+  const int x = wg & 7, idx = wg >> 3;
+  return x * per + (x < rem ? x : rem) + idx;
+}
+
+// Tile id -> (tile row, tile column): columns of group_m tile rows.
+__device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n,
+                                       int group_m, int& tm, int& tn) {
+  const int width = group_m * tiles_n;
+  const int g = t / width;
+  const int first = g * group_m;
+  const int gm = min(tiles_m - first, group_m);
+  const int local = t - g * width;
+  tm = first + local % gm;
+  tn = local / gm;
+}
+
+// Where one workgroup's operand panels and output tile live.
+struct TileJob {
+  const char* a;        // A panel base (see loaders for the addressing)
+  uint32_t a_bytes;     // bytes readable from a
+  uint32_t a_pitch;     // bytes per source row of A
+  int m_valid;          // rows of this tile that exist (<= BM)
+  const char* b;
+  uint32_t b_bytes;
+  uint32_t b_pitch;
+  int n_valid;
+  int64_t d_row0;       // first output row (absolute)
+  int64_t n0;           // first output column
+};
+
+template <int BM, int BN, bool IsBF16, bool AMn, bool BMn, int Swz>
+struct GemmTile {
+  static constexpr int kBK = 64;            // K elements per stage
+  static constexpr int kRowBytes = 128;     // kBK * 2 bytes
+  static constexpr int kATileBytes = BM * kRowBytes;
+  static constexpr int kBTileBytes = BN * kRowBytes;
+  static constexpr int kStageBytes = kATileBytes + kBTileBytes;
+  static constexpr int kLdsBytes = 2 * kStageBytes;
+  static constexpr int kWM = BM / 2, kWN = BN / 2;  // per-wave block
+  static constexpr int kFM = kWM / 32, kFN = kWN / 32;
+  static_assert(kStageBytes % 4096 == 0, "stage bases must keep the swizzle phase");
+
+  using ALoader = typename std::conditional<AMn, MNMajorLoader<BM>, KMajorLoader<BM>>::type;
+  using BLoader = typename std::conditional<BMn, MNMajorLoader<BN>, KMajorLoader<BN>>::type;
+
+  __device__ __forceinline__ static void load(ALoader& la, BLoader& lb,
+                                              const TileJob& j,
+                                              __amdgpu_buffer_rsrc_t ra,
+                                              __amdgpu_buffer_rsrc_t rb, int tid,
+                                              int k0, int K) {
+    if constexpr (AMn)
+      la.load(ra, tid, j.a_pitch, j.m_valid, k0, K);
+    else
+      la.load(ra, tid, j.a_pitch, j.m_valid, (uint32_t)k0 * 2u, (uint32_t)K * 2u);
+    if constexpr (BMn)
+      lb.load(rb, tid, j.b_pitch, j.n_valid, k0, K);
+    else
+      lb.load(rb, tid, j.b_pitch, j.n_valid, (uint32_t)k0 * 2u, (uint32_t)K * 2u);
+  }
+
+  // Runs the mainloop over K and the epilogue for one tile.
+  __device__ __forceinline__ static void run(char* smem, const TileJob& j,
+                                             int64_t K, const void* C,
+                                             int c_dtype, void* D, int d_dtype,
+                                             int64_t ldd) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(j.a, j.a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(j.b, j.b_bytes);
+
+    f32x16 acc[kFM][kFN];
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int k = 0; k < kFN; ++k) acc[i][k] = f32x16{};
+
+    const int kt_total = (int)((K + kBK - 1) / kBK);
+    ALoader la;
+    BLoader lb;
+    if (kt_total > 0) {
+      load(la, lb, j, ra, rb, tid, 0, (int)K);
+      la.template store<Swz>(smem, tid);
+      lb.template store<Swz>(smem + kATileBytes, tid);
+    }
+    __syncthreads();
+
+    // Per-lane LDS read offsets: row (l%32) of each 32-row fragment, K
+    // chunk 2*kk + l/32.  Fragments 32 rows apart share the XOR key (the
+    // key depends on the line index modulo 16 = row/2 modulo 16), so they
+    // differ by a constant 4096 bytes.
+    const int lrow = lane & 31, lhalf = lane >> 5;
+
+    for (int kt = 0; kt < kt_total; ++kt) {
+      const int stage = kt & 1;
+      const bool more = kt + 1 < kt_total;
+      if (more) load(la, lb, j, ra, rb, tid, (kt + 1) * kBK, (int)K);
+
+      const char* As = smem + stage * kStageBytes;
+      const char* Bs = As + kATileBytes;
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        u32x4 af[kFM], bfr[kFN];
+#pragma unroll
+        for (int fm = 0; fm < kFM; ++fm)
+          af[fm] = lds_read16(As, lds_offset<kRowBytes, Swz>(
+                                      wm * kWM + fm * 32 + lrow, 2 * kk + lhalf));
+#pragma unroll
+        for (int fn = 0; fn < kFN; ++fn)
+          bfr[fn] = lds_read16(Bs, lds_offset<kRowBytes, Swz>(
+                                       wn * kWN + fn * 32 + lrow, 2 * kk + lhalf));
+        // MFMA rows take B rows (n), columns take A rows (m): each lane then
+        // ends up holding 4 consecutive n of one m (wide epilogue stores).
+#pragma unroll
+        for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < kFN; ++fn)
+            acc[fm][fn] = mfma32x32x16<IsBF16>(bfr[fn], af[fm], acc[fm][fn]);
+      }
+
+      if (more) {
+        char* nxt = smem + (stage ^ 1) * kStageBytes;
+        la.template store<Swz>(nxt, tid);
+        lb.template store<Swz>(nxt + kATileBytes, tid);
+      }
+      __syncthreads();
+    }
+
+    epilogue(acc, j, C, c_dtype, D, d_dtype, ldd, lane, wm, wn);
+  }
+
+  // Accumulator layout of v_mfma_f32_32x32x*: lane l, register r holds MFMA
+  // row 8*(r/4) + 4*(l/32) + r%4 and column l%32; with the operand swap
+  // above that is n = 8q + 4*(l/32) + {0..3} (q = r/4) and m = l%32.
+  __device__ __forceinline__ static void epilogue(const f32x16 (&acc)[kFM][kFN],
+                                                  const TileJob& j, const void* C,
+                                                  int c_dtype, void* D, int d_dtype,
+                                                  int64_t ldd, int lane, int wm,
+                                                  int wn) {
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm) {
+      const int ml = wm * kWM + fm * 32 + (lane & 31);
+      if (ml >= j.m_valid) continue;
+      const int64_t row = j.d_row0 + ml;
+#pragma unroll
+      for (int fn = 0; fn < kFN; ++fn) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wn * kWN + fn * 32 + 8 * q + 4 * (lane >> 5);
+          if (nl >= j.n_valid) continue;
+          const int64_t idx = row * ldd + j.n0 + nl;
+          f32x4 v = {acc[fm][fn][4 * q + 0], acc[fm][fn][4 * q + 1],
+                     acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
+          if (C) {
+            if (c_dtype == SG_F32) {
+              v += *reinterpret_cast<const f32x4*>(static_cast<const float*>(C) + idx);
+            } else {
+              const u32x2 c2 = *reinterpret_cast<const u32x2*>(
+                  static_cast<const uint16_t*>(C) + idx);
+              if (c_dtype == SG_BF16) {
+                v[0] += bf16_to_f32(c2[0] & 0xffffu);
+                v[1] += bf16_to_f32(c2[0] >> 16);
+                v[2] += bf16_to_f32(c2[1] & 0xffffu);
+                v[3] += bf16_to_f32(c2[1] >> 16);
+              } else {
+                v[0] += f16_to_f32(c2[0] & 0xffffu);
+                v[1] += f16_to_f32(c2[0] >> 16);
+                v[2] += f16_to_f32(c2[1] & 0xffffu);
+                v[3] += f16_to_f32(c2[1] >> 16);
+              }
+            }
+          }
+          if (d_dtype == SG_F32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(D) + idx) = v;
+          } else {
+            u32x2 o;
+            if (d_dtype == SG_BF16) {
+              o[0] = pack_bf16x2(v[0], v[1]);
+              o[1] = pack_bf16x2(v[2], v[3]);
+            } else {
+              o[0] = pack_f16x2(v[0], v[1]);
+              o[1] = pack_f16x2(v[2], v[3]);
+            }
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(D) + idx) = o;
+          }
+        }
+      }
+    }
+  }
+};
+
+template <int BM, int BN, bool IsBF16, bool AMn, bool BMn, int Swz>
+__global__ void __launch_bounds__(kThreads, 1)
+    dense_gemm_kernel(const DenseParams p) {
+  using Tile = GemmTile<BM, BN, IsBF16, AMn, BMn, Swz>;
+  __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+
+  const int total = p.tiles_m * p.tiles_n;
+  const int t = xcd_remap(blockIdx.x, total);
+  int tm, tn;
+  raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  TileJob j;
+  const int64_t es = 2;
+  j.m_valid = (int)min<int64_t>(BM, p.M - m0);
+  j.n_valid = (int)min<int64_t>(BN, p.N - n0);
+  if constexpr (AMn) {  // A stored [K][M]
+    j.a = static_cast<const char*>(p.A) + m0 * es;
+    j.a_pitch = (uint32_t)(p.M * es);
+    j.a_bytes = (uint32_t)(p.K * p.M * es - m0 * es);
+  } else {              // A stored [M][K]
+    j.a = static_cast<const char*>(p.A) + m0 * p.K * es;
+    j.a_pitch = (uint32_t)(p.K * es);
+    j.a_bytes = (uint32_t)(j.m_valid * p.K * es);
+  }
+  if constexpr (BMn) {  // B stored [K][N]
+    j.b = static_cast<const char*>(p.B) + n0 * es;
+    j.b_pitch = (uint32_t)(p.N * es);
+    j.b_bytes = (uint32_t)(p.K * p.N * es - n0 * es);
+  } else {              // B stored [N][K]
+    j.b = static_cast<const char*>(p.B) + n0 * p.K * es;
+    j.b_pitch = (uint32_t)(p.K * es);
+    j.b_bytes = (uint32_t)(j.n_valid * p.K * es);
+  }
+  j.d_row0 = m0;
+  j.n0 = n0;
+  Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.N);
+}
+
+template <int BM, int BN, bool IsBF16, int Swz>
+__global__ void __launch_bounds__(kThreads, 1)
+    grouped_gemm_kernel(const GroupedParams p) {
+  using Tile = GemmTile<BM, BN, IsBF16, false, false, Swz>;
+  __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+
+  const int total = p.tile_start[p.G];
+  const int t = xcd_remap(blockIdx.x, total);
+  // Group of tile t: the last g with tile_start[g] <= t (binary search).
+  int lo = 0, hi = p.G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.tile_start[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int g = lo;
+  const int64_t Mg = p.m_off[g + 1] - p.m_off[g];
+  const int tiles_m = (int)((Mg + BM - 1) / BM);
+  int tm, tn;
+  raster(t - p.tile_start[g], tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  TileJob j;
+  const int64_t es = 2;
+  j.m_valid = (int)min<int64_t>(BM, Mg - m0);
+  j.n_valid = (int)min<int64_t>(BN, p.N - n0);
+  j.a = static_cast<const char*>(p.A) + (p.m_off[g] + m0) * p.K * es;
+  j.a_pitch = (uint32_t)(p.K * es);
+  j.a_bytes = (uint32_t)(j.m_valid * p.K * es);
+  j.b = static_cast<const char*>(p.B) + ((int64_t)g * p.N + n0) * p.K * es;
+  j.b_pitch = (uint32_t)(p.K * es);
+  j.b_bytes = (uint32_t)(j.n_valid * p.K * es);
+  j.d_row0 = p.m_off[g] + m0;
+  j.n0 = n0;
+  Tile::run(smem, j, p.K, nullptr, SG_NONE, p.D, p.d_dtype, p.N);
+}
+
+}  // namespace sg

@@ -1,0 +1,25 @@
+// launch.h -- host-side launchers of the kernel variants (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gemm_kernels.h"
+#include "mx_kernels.h"
+
+namespace sg {
+
+// Tile shapes the planner chooses between.
+enum TileShape { kTile256 = 0, kTile128 = 1 };
+
+// Launches the dense kernel for (tile, dtype, majorness); swz selects the
+// LDS layout (0, 8 or 16 units per line).  Returns the launch status.
+hipError_t launch_dense(TileShape tile, bool bf16, bool a_mn, bool b_mn,
+                        int swz, const DenseParams& p, hipStream_t s);
+hipError_t launch_grouped(TileShape tile, bool bf16, int swz,
+                          const GroupedParams& p, int grid, hipStream_t s);
+hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s);
+hipError_t launch_lds_image(const void* X, int64_t rows_total, int64_t K,
+                            int elem_bytes, int64_t row0, int64_t k0,
+                            int tile_rows, void* out, hipStream_t s);
+
+}  // namespace sg

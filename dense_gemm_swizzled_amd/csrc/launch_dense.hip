@@ -1,0 +1,68 @@
+// launch_dense.hip -- instantiations and launchers of the 16-bit dense and
+// grouped kernels.
+#include "launch.h"
+
+namespace sg {
+
+namespace {
+
+template <int BM, int BN, bool BF, bool AMn, bool BMn, int Swz>
+hipError_t go_dense(const DenseParams& p, hipStream_t s) {
+  const int grid = p.tiles_m * p.tiles_n;
+  hipLaunchKernelGGL((dense_gemm_kernel<BM, BN, BF, AMn, BMn, Swz>), dim3(grid),
+                     dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, bool BF, int Swz>
+hipError_t dense_by_major(bool a_mn, bool b_mn, const DenseParams& p, hipStream_t s) {
+  if (!a_mn && !b_mn) return go_dense<BM, BN, BF, false, false, Swz>(p, s);
+  if (!a_mn && b_mn) return go_dense<BM, BN, BF, false, true, Swz>(p, s);
+  if (a_mn && !b_mn) return go_dense<BM, BN, BF, true, false, Swz>(p, s);
+  return go_dense<BM, BN, BF, true, true, Swz>(p, s);
+}
+
+template <int BM, int BN, int Swz>
+hipError_t dense_by_dtype(bool bf16, bool a_mn, bool b_mn, const DenseParams& p,
+                          hipStream_t s) {
+  return bf16 ? dense_by_major<BM, BN, true, Swz>(a_mn, b_mn, p, s)
+              : dense_by_major<BM, BN, false, Swz>(a_mn, b_mn, p, s);
+}
+
+}  // namespace
+
+hipError_t launch_dense(TileShape tile, bool bf16, bool a_mn, bool b_mn, int swz,
+                        const DenseParams& p, hipStream_t s) {
+  if (swz == 16) {
+    return tile == kTile256 ? dense_by_dtype<256, 256, 16>(bf16, a_mn, b_mn, p, s)
+                            : dense_by_dtype<128, 128, 16>(bf16, a_mn, b_mn, p, s);
+  }
+  // Layout ablation variants: bf16, K-major operands, 256x256 tiles only.
+  if (tile != kTile256 || !bf16 || a_mn || b_mn) return hipErrorInvalidValue;
+  if (swz == 8) return go_dense<256, 256, true, false, false, 8>(p, s);
+  if (swz == 0) return go_dense<256, 256, true, false, false, 0>(p, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_grouped(TileShape tile, bool bf16, int swz, const GroupedParams& p,
+                          int grid, hipStream_t s) {
+  if (swz != 16) return hipErrorInvalidValue;
+  if (tile == kTile256) {
+    if (bf16)
+      hipLaunchKernelGGL((grouped_gemm_kernel<256, 256, true, 16>), dim3(grid),
+                         dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((grouped_gemm_kernel<256, 256, false, 16>), dim3(grid),
+                         dim3(kThreads), 0, s, p);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL((grouped_gemm_kernel<128, 128, true, 16>), dim3(grid),
+                         dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((grouped_gemm_kernel<128, 128, false, 16>), dim3(grid),
+                         dim3(kThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sg

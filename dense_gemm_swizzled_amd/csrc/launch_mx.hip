@@ -1,0 +1,53 @@
+// launch_mx.hip -- MXFP8 kernel launchers and the LDS-image debug kernel.
+#include "launch.h"
+
+namespace sg {
+
+hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s) {
+  const int grid = p.tiles_m * p.tiles_n;
+  if (tile == kTile256)
+    hipLaunchKernelGGL((mx_gemm_kernel<256, 256, kSwzDefault>), dim3(grid),
+                       dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((mx_gemm_kernel<128, 128, kSwzDefault>), dim3(grid),
+                       dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+// Runs the K-major tile loader once (rows [row0, row0 + Rows), bytes
+// [k0*eb, k0*eb + 128) of each row) into LDS under the kernels' swizzle and
+// copies the LDS stage out linearly.
+template <int Rows>
+__global__ void __launch_bounds__(kThreads, 1)
+    lds_image_kernel(const char* X, uint32_t x_bytes, uint32_t pitch, int rows_valid,
+                     uint32_t kbyte0, uint32_t kbytes_total, char* out) {
+  __shared__ __attribute__((aligned(4096))) char smem[Rows * 128];
+  const int tid = threadIdx.x;
+  KMajorLoader<Rows> ld;
+  ld.load(make_rsrc(X, x_bytes), tid, pitch, rows_valid, kbyte0, kbytes_total);
+  ld.template store<kSwzDefault>(smem, tid);
+  __syncthreads();
+  for (int i = tid; i < Rows * 128 / 16; i += kThreads)
+    reinterpret_cast<u32x4*>(out)[i] = reinterpret_cast<const u32x4*>(smem)[i];
+}
+
+hipError_t launch_lds_image(const void* X, int64_t rows_total, int64_t K, int eb,
+                            int64_t row0, int64_t k0, int tile_rows, void* out,
+                            hipStream_t s) {
+  const char* base = static_cast<const char*>(X) + row0 * K * eb;
+  const int64_t rv = rows_total - row0;
+  const int rows_valid = (int)(rv < tile_rows ? (rv > 0 ? rv : 0) : tile_rows);
+  const uint32_t pitch = (uint32_t)(K * eb);
+  const uint32_t bytes = (uint32_t)((int64_t)rows_valid * K * eb);
+  if (tile_rows == 256)
+    hipLaunchKernelGGL((lds_image_kernel<256>), dim3(1), dim3(kThreads), 0, s, base,
+                       bytes, pitch, rows_valid, (uint32_t)(k0 * eb), pitch,
+                       static_cast<char*>(out));
+  else
+    hipLaunchKernelGGL((lds_image_kernel<128>), dim3(1), dim3(kThreads), 0, s, base,
+                       bytes, pitch, rows_valid, (uint32_t)(k0 * eb), pitch,
+                       static_cast<char*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace sg

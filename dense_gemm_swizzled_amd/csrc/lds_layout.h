@@ -1,0 +1,57 @@
+// lds_layout.h -- the LDS byte map of a K-major operand tile (host + device).
+//
+// The swizzle is f(r, c) = (r, c XOR r) of "Swizzling explained properly"
+// (section "What does swizzling do?") taken on the grid whose rows are LDS
+// bank lines and whose columns are the 16-byte units of a line.  In that
+// page's byte-offset notation (section "CUTLASS swizzling notation") it is
+// Swizzle(bits = u, base = 4, shift = u) with 2^u units per line: the low 4
+// bits (one 16-byte atom -- the same atom as the "core matrix" rows of "LBO,
+// SBO and SWZ for a tcgen05 tile", section 1) never move, and the unit index
+// inside a line is XORed with the line index modulo 2^u.
+//
+// gfx950's LDS serves ds_read_b128 from 64 banks of 4 bytes, a 256-byte line
+// (measured with the LDS probe: two lanes 256 bytes apart conflict, 128
+// bytes apart do not), so the kernels use u = 4 (Swz = 16 units).  Swz = 8
+// is the same construction for 128-byte lines (the tcgen05/TMA 128-byte mode)
+// and Swz = 0 the unswizzled layout; both stay selectable for the layout
+// ablation.  Stage bases are multiples of the 4 KiB swizzle period, so the
+// map's phase is the same in every stage (the matrix-base-offset issue of
+// "LBO, SBO and SWZ for a tcgen05 tile", section 3, cannot arise).
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define SG_HD __host__ __device__ __forceinline__
+#else
+#define SG_HD inline
+#endif
+
+namespace sg {
+
+constexpr int kSwzDefault = 16;
+
+// Byte offset, within one stage, of logical 16-byte chunk `chunk` of tile
+// row `row`, for rows of RowBytes bytes and a line of Swz 16-byte units.
+template <int RowBytes, int Swz>
+SG_HD constexpr uint32_t lds_offset(uint32_t row, uint32_t chunk) {
+  static_assert(Swz == 0 || Swz == 8 || Swz == 16, "unsupported swizzle");
+  const uint32_t off = row * RowBytes + chunk * 16u;
+  if constexpr (Swz == 0) {
+    return off;
+  } else {
+    constexpr uint32_t line_shift = Swz == 8 ? 7 : 8;  // log2(line bytes)
+    return off ^ (((off >> line_shift) & (uint32_t)(Swz - 1)) << 4);
+  }
+}
+
+// Runtime-dispatched form for host tools.
+SG_HD uint32_t lds_offset_rt(int row_bytes, int swz, uint32_t row,
+                             uint32_t chunk) {
+  const uint32_t off = row * (uint32_t)row_bytes + chunk * 16u;
+  if (swz == 0) return off;
+  const uint32_t line_shift = swz == 8 ? 7 : 8;
+  return off ^ (((off >> line_shift) & (uint32_t)(swz - 1)) << 4);
+}
+
+}  // namespace sg

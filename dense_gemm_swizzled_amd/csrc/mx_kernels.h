@@ -1,0 +1,206 @@
+// mx_kernels.h -- block-scaled (MXFP8) GEMM kernel template.
+//
+// D[m][n] = sum_blk 2^(SFA[m][blk]-127) 2^(SFB[n][blk]-127)
+//           * sum_{k in blk} A[m][k] B[n][k]            (32-element blocks)
+// -- output (m, n) takes SFA for row m and SFB for column n of the block
+// ("06 Blackwell Tensor Core - tcgen05 MMA", section "Block-Scaled MMA").
+//
+// Same tile machinery as the 16-bit kernels: e4m3 operands staged K-major in
+// LDS, 128 bytes (= 128 elements = 4 scale blocks) of K per stage, under the
+// same swizzle.  Operand and scale layout of v_mfma_scale_f32_32x32x64_
+// f8f6f4 (checked on the GPU with one-hot operands): lane l supplies row l%32
+// and, of the 64-wide K step, K values [16h, 16h+16) in its low 16 bytes and
+// [32+16h, 32+16h+16) in its high 16 bytes (h = l/32); the e8m0 byte of lane
+// l scales 32-element block h of the step for row l%32 -- so block 0 is the
+// low halves of both lane halves and block 1 the high halves.  The scales are
+// not staged: each lane loads the 4 scale bytes of its row for the current
+// stage straight into a VGPR.
+#pragma once
+
+#include "gemm_device.h"
+#include "gemm_kernels.h"
+
+namespace sg {
+
+struct MxParams {
+  const void* A;    // e4m3 [M][K]
+  const void* SFA;  // e8m0 [M][K/32]
+  const void* B;    // e4m3 [N][K]
+  const void* SFB;  // e8m0 [N][K/32]
+  void* D;
+  int64_t M, N, K;
+  int d_dtype;
+  int tiles_m, tiles_n;
+  int group_m;
+};
+
+__device__ __forceinline__ f32x16 mfma_scale_f8(const u32x4 (&a)[2],
+                                                const u32x4 (&b)[2], f32x16 c,
+                                                uint32_t sa, uint32_t sb,
+                                                int kk) {
+  const i32x8 av = {(int)a[0][0], (int)a[0][1], (int)a[0][2], (int)a[0][3],
+                    (int)a[1][0], (int)a[1][1], (int)a[1][2], (int)a[1][3]};
+  const i32x8 bv = {(int)b[0][0], (int)b[0][1], (int)b[0][2], (int)b[0][3],
+                    (int)b[1][0], (int)b[1][1], (int)b[1][2], (int)b[1][3]};
+  // Format codes 0/0: both operands OCP fp8 E4M3.  The op-select immediate
+  // picks byte 2*kk of the scale register (see the caller's pre-shift).
+  if (kk == 0)
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0,
+                                                           (int)sa, 0, (int)sb);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 2,
+                                                         (int)sa, 2, (int)sb);
+}
+
+template <int BM, int BN, int Swz>
+struct MxTile {
+  static constexpr int kBK = 128;           // fp8 elements (= bytes) per stage
+  static constexpr int kRowBytes = 128;
+  static constexpr int kATileBytes = BM * kRowBytes;
+  static constexpr int kBTileBytes = BN * kRowBytes;
+  static constexpr int kStageBytes = kATileBytes + kBTileBytes;
+  static constexpr int kLdsBytes = 2 * kStageBytes;
+  static constexpr int kWM = BM / 2, kWN = BN / 2;
+  static constexpr int kFM = kWM / 32, kFN = kWN / 32;
+  static_assert(kStageBytes % 4096 == 0, "stage bases must keep the swizzle phase");
+
+  struct Scales {
+    uint32_t a[kFM], b[kFN];
+  };
+
+  // One dword = the 4 scale bytes of K blocks [4kt, 4kt+4) of a row; the
+  // lane then shifts its own block (l/32) into the even byte positions so
+  // that op-select 2*kk addresses block 4kt + 2kk + l/32.
+  __device__ __forceinline__ static void load_scales(
+      Scales& s, __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb,
+      uint32_t sf_pitch, int kt, int lane, int wm, int wn, int m_valid,
+      int n_valid) {
+    const int lrow = lane & 31;
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm) {
+      const int r = wm * kWM + fm * 32 + lrow;
+      s.a[fm] = buffer_load4(rsa, r < m_valid ? r * sf_pitch + 4u * kt : kOutOfRange);
+    }
+#pragma unroll
+    for (int fn = 0; fn < kFN; ++fn) {
+      const int r = wn * kWN + fn * 32 + lrow;
+      s.b[fn] = buffer_load4(rsb, r < n_valid ? r * sf_pitch + 4u * kt : kOutOfRange);
+    }
+  }
+
+  __device__ __forceinline__ static void run(char* smem, const TileJob& j,
+                                             const char* sfa, const char* sfb,
+                                             int64_t K, void* D, int d_dtype,
+                                             int64_t ldd) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(j.a, j.a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(j.b, j.b_bytes);
+    const uint32_t sf_pitch = (uint32_t)(K / 32);
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sfa, (uint32_t)j.m_valid * sf_pitch);
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sfb, (uint32_t)j.n_valid * sf_pitch);
+
+    f32x16 acc[kFM][kFN];
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int k = 0; k < kFN; ++k) acc[i][k] = f32x16{};
+
+    const int kt_total = (int)(K / kBK);
+    KMajorLoader<BM> la;
+    KMajorLoader<BN> lb;
+    Scales sc, sc_next;
+    if (kt_total > 0) {
+      la.load(ra, tid, j.a_pitch, j.m_valid, 0, (uint32_t)K);
+      lb.load(rb, tid, j.b_pitch, j.n_valid, 0, (uint32_t)K);
+      load_scales(sc, rsa, rsb, sf_pitch, 0, lane, wm, wn, j.m_valid, j.n_valid);
+      la.template store<Swz>(smem, tid);
+      lb.template store<Swz>(smem + kATileBytes, tid);
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < kt_total; ++kt) {
+      const int stage = kt & 1;
+      const bool more = kt + 1 < kt_total;
+      if (more) {
+        la.load(ra, tid, j.a_pitch, j.m_valid, (uint32_t)(kt + 1) * kBK, (uint32_t)K);
+        lb.load(rb, tid, j.b_pitch, j.n_valid, (uint32_t)(kt + 1) * kBK, (uint32_t)K);
+        load_scales(sc_next, rsa, rsb, sf_pitch, kt + 1, lane, wm, wn, j.m_valid,
+                    j.n_valid);
+      }
+      uint32_t sa[kFM], sb[kFN];
+#pragma unroll
+      for (int fm = 0; fm < kFM; ++fm) sa[fm] = sc.a[fm] >> (8 * lhalf);
+#pragma unroll
+      for (int fn = 0; fn < kFN; ++fn) sb[fn] = sc.b[fn] >> (8 * lhalf);
+
+      const char* As = smem + stage * kStageBytes;
+      const char* Bs = As + kATileBytes;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        // Lane half h = l/32 supplies 16-byte chunk 4*kk + h (block 2*kk)
+        // then chunk 4*kk + 2 + h (block 2*kk + 1).
+        u32x4 af[kFM][2], bfr[kFN][2];
+#pragma unroll
+        for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            af[fm][h] = lds_read16(As, lds_offset<kRowBytes, Swz>(
+                                           wm * kWM + fm * 32 + lrow, 4 * kk + 2 * h + lhalf));
+#pragma unroll
+        for (int fn = 0; fn < kFN; ++fn)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            bfr[fn][h] = lds_read16(Bs, lds_offset<kRowBytes, Swz>(
+                                            wn * kWN + fn * 32 + lrow, 4 * kk + 2 * h + lhalf));
+#pragma unroll
+        for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < kFN; ++fn)
+            acc[fm][fn] = mfma_scale_f8(bfr[fn], af[fm], acc[fm][fn], sb[fn], sa[fm], kk);
+      }
+
+      if (more) {
+        char* nxt = smem + (stage ^ 1) * kStageBytes;
+        la.template store<Swz>(nxt, tid);
+        lb.template store<Swz>(nxt + kATileBytes, tid);
+        sc = sc_next;
+      }
+      __syncthreads();
+    }
+
+    GemmTile<BM, BN, true, false, false, Swz>::epilogue(acc, j, nullptr, SG_NONE, D,
+                                                        d_dtype, ldd, lane, wm, wn);
+  }
+};
+
+template <int BM, int BN, int Swz>
+__global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(const MxParams p) {
+  using Tile = MxTile<BM, BN, Swz>;
+  __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+
+  const int total = p.tiles_m * p.tiles_n;
+  const int t = xcd_remap(blockIdx.x, total);
+  int tm, tn;
+  raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  TileJob j;
+  j.m_valid = (int)min<int64_t>(BM, p.M - m0);
+  j.n_valid = (int)min<int64_t>(BN, p.N - n0);
+  j.a = static_cast<const char*>(p.A) + m0 * p.K;
+  j.a_pitch = (uint32_t)p.K;
+  j.a_bytes = (uint32_t)(j.m_valid * p.K);
+  j.b = static_cast<const char*>(p.B) + n0 * p.K;
+  j.b_pitch = (uint32_t)p.K;
+  j.b_bytes = (uint32_t)(j.n_valid * p.K);
+  j.d_row0 = m0;
+  j.n0 = n0;
+  const char* sfa = static_cast<const char*>(p.SFA) + m0 * (p.K / 32);
+  const char* sfb = static_cast<const char*>(p.SFB) + n0 * (p.K / 32);
+  Tile::run(smem, j, sfa, sfb, p.K, p.D, p.d_dtype, p.N);
+}
+
+}  // namespace sg

@@ -1,0 +1,166 @@
+/*
+ * swizzled_gemm.h -- C ABI of libswizzled_gemm.so, an MI355X (gfx950) GEMM
+ * whose operand tiles are staged in LDS under an XOR swizzle.
+ *
+ * Operation.  D = A*B (+C): a tiled matrix multiply-accumulate with 16-bit
+ * inputs and fp32 accumulation -- the tensor-core operation D = A*B + C of
+ * "Tensor Cores, layouts, and swizzling" (opening section), computed by the
+ * sample tiled matmul of "Swizzling explained properly" (section "Sample
+ * swizzled matmul") with tiles staged in on-chip memory under the swizzle
+ * f(r, c) = (r, c XOR r) of that page (section "What does swizzling do?").
+ * Passing C = NULL computes D = A*B, the "enable-input-d = false" form of
+ * "06 Blackwell Tensor Core - tcgen05 MMA" (operand table); a non-NULL C is
+ * the accumulate form D = A*B + C.
+ *
+ * Conventions shared by every entry point:
+ *  - All pointers named A, B, C, D, SFA, SFB are DEVICE pointers of the
+ *    current HIP device; m_offsets is a HOST pointer.  The caller owns every
+ *    buffer; the library never allocates, frees or synchronises.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  A
+ *    call enqueues its kernels on that stream and returns at once; results
+ *    are visible after the stream is synchronised.
+ *  - Matrices are dense and row-major with no padding: a "K-major" operand
+ *    is stored [rows][K] (K contiguous), an "MN-major" one [K][rows].
+ *    A: K-major [M][K] or MN-major [K][M].  B: K-major [N][K] (B transposed)
+ *    or MN-major [K][N].  C and D: [M][N].
+ *  - Every pointer must be 16-byte aligned and every row pitch (contiguous
+ *    extent x element size) a multiple of 16 bytes, the 16-byte atom rule of
+ *    both swizzle pages ("LBO, SBO and SWZ", section 1; "Swizzling explained
+ *    properly", section "What about base?") and of the TMA stride rule in
+ *    "Tensor Cores, layouts, and swizzling".  Violations return
+ *    SG_ERR_ALIGN.  M, N and K themselves may be ragged (not multiples of
+ *    the tile); M = 0 or N = 0 is a no-op; K = 0 gives D = C (or 0).
+ *  - Return value: SG_OK (0) or a negative SG_ERR_* code; on error nothing is
+ *    enqueued and gemm_last_error() describes the failure (thread-local).
+ */
+#ifndef SWIZZLED_GEMM_H
+#define SWIZZLED_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define SG_OK 0
+#define SG_ERR_NULL (-1)   /* a required pointer is NULL */
+#define SG_ERR_ALIGN (-2)  /* pointer not 16-byte aligned, or row pitch not a multiple of 16 B */
+#define SG_ERR_SHAPE (-3)  /* negative size, or beyond the supported extent */
+#define SG_ERR_DTYPE (-4)  /* unsupported element type combination */
+#define SG_ERR_MAJOR (-5)  /* majorness not SG_K_MAJOR / SG_MN_MAJOR */
+#define SG_ERR_GROUPS (-6) /* bad group count or offsets */
+#define SG_ERR_HIP (-7)    /* a HIP call failed; see gemm_last_error() */
+
+/* Element types. */
+#define SG_NONE 0
+#define SG_F16 1  /* IEEE binary16 */
+#define SG_BF16 2 /* bfloat16 */
+#define SG_F32 3  /* IEEE binary32 */
+#define SG_E4M3 4 /* OCP FP8 E4M3 (bias 7, max 448, no infinity) */
+#define SG_E8M0 5 /* OCP E8M0 scale, value 2^(e-127) */
+
+/* Operand majorness. */
+#define SG_K_MAJOR 0  /* K is the contiguous dimension */
+#define SG_MN_MAJOR 1 /* M (for A) or N (for B) is the contiguous dimension */
+
+/* Largest group count grouped_gemm_run accepts. */
+#define SG_MAX_GROUPS 128
+
+/*
+ * gemm_run -- D = A*B (+C), fp32 accumulation.
+ *   M, N, K    problem sizes (>= 0).
+ *   A          ab_dtype, K-major [M][K] or MN-major [K][M] (a_major).
+ *   B          ab_dtype, K-major [N][K] or MN-major [K][N] (b_major).
+ *   ab_dtype   SG_F16 or SG_BF16.
+ *   C          NULL (treated as zero) or [M][N] of c_dtype (SG_F32, SG_BF16,
+ *              SG_F16).  C may equal D (in-place accumulate) when c_dtype ==
+ *              d_dtype; any other overlap of C or D with inputs is undefined.
+ *   D          [M][N] of d_dtype: SG_F32, SG_BF16 or SG_F16 (the fp32
+ *              accumulator is rounded to nearest even).
+ * Errors: SG_ERR_NULL (A, B or D NULL with M, N > 0 -- A/B may be NULL when
+ * K = 0), SG_ERR_ALIGN, SG_ERR_SHAPE (a size < 0, or a per-tile operand
+ * extent of 2^31 bytes or more), SG_ERR_DTYPE, SG_ERR_MAJOR, SG_ERR_HIP.
+ */
+int gemm_run(int64_t M, int64_t N, int64_t K, const void* A, int a_major,
+             const void* B, int b_major, int ab_dtype, const void* C,
+             int c_dtype, void* D, int d_dtype, void* stream);
+
+/*
+ * grouped_gemm_run -- for each group g in [0, G):
+ *   D[off_g : off_{g+1}] = A[off_g : off_{g+1}] * B_g,
+ * the grouped GEMM named in "LBO, SBO and SWZ for a tcgen05 tile"
+ * (introduction); the pages give no further definition, so each group is the
+ * plain dense GEMM on its row range.  Groups share N and K.
+ *   G          number of groups, 1..SG_MAX_GROUPS.
+ *   m_offsets  HOST array of G+1 row offsets: m_offsets[0] = 0, non-
+ *              decreasing; group g owns rows [m_offsets[g], m_offsets[g+1]).
+ *              Empty groups are allowed.  Read during the call only.
+ *   A          ab_dtype, K-major [m_offsets[G]][K].
+ *   B          ab_dtype, G contiguous blocks, each K-major [N][K]
+ *              (b_major must be SG_K_MAJOR).
+ *   D          [m_offsets[G]][N] of d_dtype (SG_F32, SG_BF16, SG_F16).
+ * Errors: as gemm_run, plus SG_ERR_GROUPS (G out of range, m_offsets[0] != 0
+ * or decreasing offsets).
+ */
+int grouped_gemm_run(int G, const int64_t* m_offsets, int64_t N, int64_t K,
+                     const void* A, int a_major, const void* B, int b_major,
+                     int ab_dtype, void* D, int d_dtype, void* stream);
+
+/*
+ * mx_gemm_run -- block-scaled (MXFP8) GEMM:
+ *   D[m][n] = sum_blk 2^(SFA[m][blk]-127) * 2^(SFB[n][blk]-127)
+ *             * sum_{k in blk} A[m][k] * B[n][k],
+ * with 32-element K blocks: output (m, n) uses SFA[m, sfk] for A and
+ * SFB[n, sfk] for B ("06 Blackwell Tensor Core - tcgen05 MMA", section
+ * "Block-Scaled MMA").  fp32 accumulation.
+ *   A    e4m3 K-major [M][K];  SFA  e8m0 [M][K/32].
+ *   B    e4m3 K-major [N][K];  SFB  e8m0 [N][K/32].
+ *   D    [M][N] of d_dtype (SG_F32 or SG_BF16).
+ *   K    must be a multiple of 128 (four scale blocks per 16-byte row chunk
+ *        pair); M and N may be ragged.
+ * Scale byte 255 (NaN) propagates NaN.
+ * Errors: SG_ERR_NULL, SG_ERR_ALIGN, SG_ERR_SHAPE (K % 128 != 0 or extents),
+ * SG_ERR_DTYPE, SG_ERR_HIP.
+ */
+int mx_gemm_run(int64_t M, int64_t N, int64_t K, const void* A,
+                const void* SFA, const void* B, const void* SFB, void* D,
+                int d_dtype, void* stream);
+
+/* Thread-local text of the last failing call ("" if none).  Never NULL. */
+const char* gemm_last_error(void);
+
+/* Library version and build description.  Never NULL. */
+const char* gemm_version(void);
+
+/*
+ * gemm_lds_layout -- the LDS byte map the kernels use for a K-major operand
+ * tile (host-side, no GPU needed).  Writes out[r * (row_bytes/16) + c] = the
+ * byte offset within one LDS stage of logical 16-byte chunk c of tile row r,
+ * for r < rows.  row_bytes is 64, 128 or 256; rows a positive multiple of 8.
+ * The map is the XOR swizzle of "Swizzling explained properly" applied to
+ * (bank line, 16-byte unit within the line), never splitting a 16-byte atom.
+ * Returns SG_OK, SG_ERR_NULL or SG_ERR_SHAPE.
+ */
+int gemm_lds_layout(int rows, int row_bytes, int32_t* out);
+
+/*
+ * gemm_lds_image -- runs the kernels' global->LDS loader once for one operand
+ * tile and copies the LDS stage out byte for byte, unswizzled by nothing.
+ *   X         device operand, K-major [rows_total][K] of elem_bytes-sized
+ *             elements (2 for f16/bf16, 1 for e4m3).
+ *   tile_rows 128 or 256; the tile covers rows [row0, row0 + tile_rows)
+ *             and the 128-byte K slice starting at element k0 (k0 * elem_bytes
+ *             a multiple of 128).  Rows >= rows_total and k >= K read as zero.
+ *   out       device buffer of tile_rows * 128 bytes.
+ * Returns SG_OK or an SG_ERR_* code.
+ */
+int gemm_lds_image(const void* X, int64_t rows_total, int64_t K, int elem_bytes,
+                   int64_t row0, int64_t k0, int tile_rows, void* out,
+                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIZZLED_GEMM_H */

@@ -1,0 +1,141 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/swizzled_gemm.h declares, rejects every invalid argument with the
+documented code before touching the GPU, and its LDS byte map equals the
+oracle's swizzle bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import dense_gemm_swizzled_amd as sg
+from oracle import swizzle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swizzled_gemm.h")
+
+NULL, ALIGN, SHAPE, DTYPE, MAJOR, GROUPS = -1, -2, -3, -4, -5, -6
+P = 0x10000  # a 16-byte-aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"gemm_run", "grouped_gemm_run", "mx_gemm_run", "gemm_last_error",
+            "gemm_version", "gemm_lds_layout", "gemm_lds_image"} <= set(names)
+    lib = ctypes.CDLL(sg.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in sg.gemm_version()
+
+
+def _gemm(**kw):
+    a = dict(M=256, N=256, K=64, A=P, a_major=0, B=P, b_major=0, ab_dtype=sg.SG_BF16,
+             C=None, c_dtype=0, D=P, d_dtype=sg.SG_F32, stream=None)
+    a.update(kw)
+    return sg.gemm_run(a["M"], a["N"], a["K"], a["A"], a["a_major"], a["B"], a["b_major"],
+                       a["ab_dtype"], a["C"], a["c_dtype"], a["D"], a["d_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), SHAPE), (dict(K=-5), SHAPE),
+    (dict(ab_dtype=sg.SG_F32), DTYPE), (dict(ab_dtype=9), DTYPE),
+    (dict(d_dtype=sg.SG_E4M3), DTYPE), (dict(C=P + 4096, c_dtype=7), DTYPE),
+    (dict(C=P, c_dtype=sg.SG_BF16, d_dtype=sg.SG_F32), DTYPE),  # C == D, other dtype
+    (dict(a_major=2), MAJOR), (dict(b_major=-1), MAJOR),
+    (dict(D=None), NULL), (dict(A=None), NULL), (dict(B=None), NULL),
+    (dict(A=P + 8), ALIGN), (dict(B=P + 2), ALIGN), (dict(D=P + 4), ALIGN),
+    (dict(C=P + 4104, c_dtype=sg.SG_BF16), ALIGN),
+    (dict(K=60), ALIGN),                      # 120-byte K-major rows
+    (dict(M=100, a_major=1), ALIGN),          # 200-byte MN-major A rows
+    (dict(N=100, b_major=1), ALIGN),
+])
+def test_gemm_run_rejects(kw, code):
+    rc = _gemm(**kw)
+    assert rc == code, (kw, rc, sg.gemm_last_error())
+    assert sg.gemm_last_error()
+
+
+def test_gemm_run_bf16_output_pitch():
+    assert _gemm(N=260, d_dtype=sg.SG_BF16) == ALIGN   # 520-byte rows
+
+
+def test_gemm_run_oversized_panel():
+    # MN-major A of 2^30 elements spans 2^31 bytes.
+    assert _gemm(M=1 << 15, K=1 << 15, a_major=1) == SHAPE
+
+
+def test_empty_problems_are_noops_without_pointers():
+    assert _gemm(M=0, A=None, B=None, D=None) == sg.SG_OK
+    assert _gemm(N=0, A=None, B=None, D=None) == sg.SG_OK
+
+
+def _grouped(**kw):
+    a = dict(G=2, offs=[0, 128, 256], N=256, K=64, A=P, a_major=0, B=P, b_major=0,
+             ab_dtype=sg.SG_BF16, D=P, d_dtype=sg.SG_BF16)
+    a.update(kw)
+    return sg.grouped_gemm_run(a["G"], a["offs"], a["N"], a["K"], a["A"], a["a_major"],
+                               a["B"], a["b_major"], a["ab_dtype"], a["D"], a["d_dtype"],
+                               None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(G=0, offs=[0]), GROUPS), (dict(G=129, offs=list(range(130))), GROUPS),
+    (dict(offs=[1, 128, 256]), GROUPS), (dict(offs=[0, 200, 100]), GROUPS),
+    (dict(offs=None), NULL), (dict(D=None), NULL), (dict(A=None), NULL),
+    (dict(a_major=1), MAJOR), (dict(b_major=1), MAJOR),
+    (dict(ab_dtype=sg.SG_E4M3), DTYPE), (dict(d_dtype=0), DTYPE),
+    (dict(K=12), ALIGN), (dict(N=-1), SHAPE),
+])
+def test_grouped_rejects(kw, code):
+    assert _grouped(**kw) == code, sg.gemm_last_error()
+
+
+def test_grouped_all_empty_is_noop():
+    assert _grouped(offs=[0, 0, 0], A=None, B=None, D=None) == sg.SG_OK
+
+
+def _mx(**kw):
+    a = dict(M=256, N=256, K=256, A=P, SFA=P, B=P, SFB=P, D=P, d_dtype=sg.SG_BF16)
+    a.update(kw)
+    return sg.mx_gemm_run(a["M"], a["N"], a["K"], a["A"], a["SFA"], a["B"], a["SFB"],
+                          a["D"], a["d_dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=96), SHAPE), (dict(M=-2), SHAPE), (dict(d_dtype=sg.SG_F16), DTYPE),
+    (dict(SFA=None), NULL), (dict(D=None), NULL),
+    (dict(SFB=P + 2), ALIGN), (dict(A=P + 8), ALIGN), (dict(N=260), ALIGN),
+])
+def test_mx_rejects(kw, code):
+    assert _mx(**kw) == code, sg.gemm_last_error()
+
+
+@pytest.mark.parametrize("row_bytes", [64, 128, 256])
+@pytest.mark.parametrize("rows", [8, 128, 256])
+def test_lds_layout_equals_oracle_swizzle(rows, row_bytes):
+    got = sg.gemm_lds_layout(rows, row_bytes)
+    want = swizzle.lds_tile_map(rows, row_bytes, line_bytes=256)
+    assert np.array_equal(got, want)
+
+
+def test_lds_layout_rejects():
+    with pytest.raises(sg.GemmError):
+        sg.gemm_lds_layout(12, 128)
+    with pytest.raises(sg.GemmError):
+        sg.gemm_lds_layout(8, 96)
+
+
+def test_lds_image_rejects():
+    assert sg.gemm_lds_image(P, 100, 64, 2, 0, 0, 64, P, None) == SHAPE
+    assert sg.gemm_lds_image(P, 100, 64, 2, 0, 32, 128, P, None) == SHAPE
+    assert sg.gemm_lds_image(None, 100, 64, 2, 0, 0, 128, P, None) == NULL

@@ -1,0 +1,304 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every comparison is element by element: |D - ref| <= tau * (sum|a*b| + |c|)
+with tau = 1e-4 for fp32 outputs and 8e-3 for bf16/fp16 outputs, no NaN/Inf.
+Sizes the oracle finishes in seconds are compared in full; the 8192^3,
+grouped 16x4096^2 and MXFP8 8192^3 workloads are run at full size in the
+launch configuration the bench times and compared on sampled outputs the
+oracle evaluates one by one.  Layout maps are compared bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_swizzled_amd as sg
+import oracle
+import synth_inputs as si
+from oracle import swizzle
+from tests._tol import check_close
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sg.load()
+    return torch.device("cuda:0")
+
+
+def _np(d: torch.Tensor) -> np.ndarray:
+    return d.float().cpu().numpy().astype(np.float64)
+
+
+def run_dense(case: si.DenseCase, dev, out=None, c_override="keep"):
+    C = case.C if c_override == "keep" else c_override
+    A, B = case.A.to(dev), case.B.to(dev)
+    Cd = C.to(dev) if C is not None else None
+    if out is None:
+        out = torch.empty((case.M, case.N), dtype=DT[case.d_dtype], device=dev)
+    sg.gemm(A, B, a_major=case.a_major, b_major=case.b_major, C=Cd, out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_dense(case: si.DenseCase):
+    return oracle.gemm(case.M, case.N, case.K, case.A, case.a_major, case.B,
+                       case.b_major, case.ab_dtype, case.C, case.c_dtype)
+
+
+def sample_points(M, N, n, seed, tile=256):
+    rng = np.random.default_rng(seed)
+    rows = list(rng.integers(0, M, n))
+    cols = list(rng.integers(0, N, n))
+    edges_m = sorted({0, 1, 31, 32, 127, 128, 255, 256, M // 2, M - 2, M - 1} & set(range(M)))
+    edges_n = sorted({0, 3, 4, 31, 32, 127, 128, 255, 256, N // 2, N - 4, N - 1} & set(range(N)))
+    for r in edges_m:
+        for c in edges_n:
+            rows.append(r)
+            cols.append(c)
+    return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)
+
+
+# ------------------------------------------------------------- LDS image
+
+@pytest.mark.parametrize("rows_total,K,eb,row0,k0,tile_rows", [
+    (512, 256, 2, 0, 64, 256),     # interior bf16 tile
+    (300, 200, 2, 256, 192, 256),  # ragged rows and K tail (16 valid bytes)
+    (128, 384, 1, 0, 256, 128),    # fp8 tile of 128 rows
+    (200, 64, 2, 128, 0, 128),     # 72 valid rows
+])
+def test_lds_image_bit_exact(dev, rows_total, K, eb, row0, k0, tile_rows):
+    say(f"lds_image rows_total={rows_total} K={K} eb={eb} row0={row0} k0={k0} tile={tile_rows}")
+    rng = np.random.default_rng(rows_total + K)
+    X = rng.integers(0, 256, (rows_total, K * eb), dtype=np.uint8)
+    Xd = torch.from_numpy(X).to(dev)
+    out = torch.zeros(tile_rows * 128, dtype=torch.uint8, device=dev)
+    rc = sg.gemm_lds_image(Xd.data_ptr(), rows_total, K, eb, row0, k0, tile_rows,
+                           out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, sg.gemm_last_error()
+    torch.cuda.synchronize()
+    tile = np.zeros((tile_rows, 128), dtype=np.uint8)
+    r1 = min(rows_total, row0 + tile_rows)
+    b0, b1 = k0 * eb, min(K * eb, k0 * eb + 128)
+    tile[:r1 - row0, :b1 - b0] = X[row0:r1, b0:b1]
+    want = swizzle.lds_image(tile, line_bytes=256)
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
+# -------------------------------------------------------------- dense
+
+def test_single_tile_128x128x32_f16(dev):
+    case = si.single_tile(seed=1)
+    say(f"{case.name}")
+    d = run_dense(case, dev)
+    ref, bound = oracle_dense(case)
+    check_close(_np(d), ref, bound, "f32", case.name)
+
+
+def test_dense_1024_bf16_mn_major_b(dev):
+    case = si.dense_1024(seed=2)
+    say(f"{case.name}")
+    d = run_dense(case, dev)
+    ref, bound = oracle_dense(case)
+    check_close(_np(d), ref, bound, "f32", case.name)
+    # C = 0 passed explicitly gives the same bits as C = NULL.
+    z = torch.zeros(case.M, case.N, dtype=torch.float32)
+    d0 = run_dense(case, dev, c_override=z)
+    assert torch.equal(d, d0)
+
+
+@pytest.mark.parametrize("a_major", ["k", "mn"])
+@pytest.mark.parametrize("b_major", ["k", "mn"])
+@pytest.mark.parametrize("ab", ["bf16", "f16"])
+def test_dense_majorness_dtypes_ragged(dev, a_major, b_major, ab):
+    M, N, K = 200, 136, 264   # ragged vs 128-row tiles and 64-wide K steps
+    case = si.dense_case(M, N, K, 40 + len(a_major) + 2 * len(b_major), ab_dtype=ab,
+                         a_major=a_major, b_major=b_major, with_c=True, c_dtype="f32",
+                         d_dtype="f32")
+    say(f"dense {M}x{N}x{K} {ab} A:{a_major} B:{b_major}")
+    d = run_dense(case, dev)
+    ref, bound = oracle_dense(case)
+    check_close(_np(d), ref, bound, "f32", "majorness")
+
+
+@pytest.mark.parametrize("c_dtype,d_dtype", [(None, "bf16"), ("bf16", "bf16"),
+                                             ("f16", "f16"), ("f32", "bf16"),
+                                             ("bf16", "f32")])
+def test_dense_epilogue_dtypes(dev, c_dtype, d_dtype):
+    M, N, K = 136, 264, 72
+    case = si.dense_case(M, N, K, 7, ab_dtype="bf16", with_c=c_dtype is not None,
+                         c_dtype=c_dtype or "bf16", d_dtype=d_dtype)
+    say(f"epilogue C={c_dtype} D={d_dtype}")
+    d = run_dense(case, dev)
+    ref, bound = oracle_dense(case)
+    check_close(_np(d), ref, bound, "f32" if d_dtype == "f32" else "bf16", "epilogue")
+
+
+def test_dense_256_tiles_ragged(dev):
+    # 17 x 17 tiles of 256 -> the 256x256 variant, ragged in M, N and K.
+    M, N, K = 4100, 4104, 136
+    case = si.dense_case(M, N, K, 11, ab_dtype="bf16", with_c=True, c_dtype="bf16",
+                         d_dtype="bf16", scale=1.0 / np.sqrt(K))
+    say(f"dense 256-tile path {M}x{N}x{K}")
+    d = run_dense(case, dev)
+    ref, bound = oracle_dense(case)
+    check_close(_np(d), ref, bound, "bf16", "256 tiles")
+
+
+def test_dense_integer_inputs_exact(dev):
+    # Integer values in [-4, 4]: every partial sum is exact in fp32, so the
+    # result must be bit-exact whatever the summation order.
+    M, N, K = 520, 392, 648
+    a = si.integer_valued((M, K), 91)
+    b = si.integer_valued((N, K), 92)
+    A, B = si.to_bf16(a), si.to_bf16(b)
+    say("integer-valued exact")
+    d = sg.gemm(A.to(dev), B.to(dev), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = a.astype(np.int64) @ b.astype(np.int64).T
+    assert np.array_equal(d.cpu().numpy().astype(np.int64), want)
+
+
+def test_dense_in_place_c_equals_d(dev):
+    case = si.dense_case(128, 128, 96, 5, ab_dtype="bf16", with_c=True, c_dtype="f32",
+                         d_dtype="f32")
+    say("in-place C == D")
+    CD = case.C.to(dev).clone()
+    sg.gemm(case.A.to(dev), case.B.to(dev), C=CD, out=CD)
+    torch.cuda.synchronize()
+    ref, bound = oracle_dense(case)
+    check_close(_np(CD), ref, bound, "f32", "in-place")
+
+
+def test_dense_degenerate_shapes(dev):
+    say("degenerate shapes")
+    # K = 0: D = C exactly; and D = 0 without C.
+    C = torch.randn(40, 64, device=dev)
+    A = torch.empty(40, 0, dtype=torch.bfloat16, device=dev)
+    B = torch.empty(64, 0, dtype=torch.bfloat16, device=dev)
+    d = sg.gemm(A, B, C=C, out_dtype=torch.float32)
+    d0 = sg.gemm(A, B, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(d, C) and torch.count_nonzero(d0) == 0
+    # M = 0 and N = 0 leave D untouched.
+    D = torch.full((8, 8), 7.0, device=dev)
+    Bk = torch.zeros(8, 8, dtype=torch.bfloat16, device=dev)
+    rc = sg.gemm_run(0, 8, 8, None, 0, Bk.data_ptr(), 0, sg.SG_BF16, None, 0,
+                     D.data_ptr(), sg.SG_F32, None)
+    torch.cuda.synchronize()
+    assert rc == 0 and torch.all(D == 7.0)
+    # Smallest legal rows: M = 1, N = 8 (bf16 out), K = 8.
+    case = si.dense_case(1, 8, 8, 3, ab_dtype="bf16", d_dtype="bf16")
+    d = run_dense(case, dev)
+    ref, bound = oracle_dense(case)
+    check_close(_np(d), ref, bound, "bf16", "1x8x8")
+
+
+def test_dense_8192_full_size_sampled(dev):
+    case = si.dense_8192(seed=3)
+    say(f"{case.name} (sampled)")
+    d = run_dense(case, dev)
+    assert bool(torch.isfinite(d).all())
+    rows, cols = sample_points(case.M, case.N, 3000, 33)
+    ref, bound = oracle.gemm_points(case.M, case.N, case.K, case.A, "k", case.B, "k",
+                                    "bf16", rows, cols, case.C, "bf16")
+    got = _np(d[torch.from_numpy(rows).to(dev), torch.from_numpy(cols).to(dev)])
+    check_close(got, ref, bound, "bf16", case.name)
+
+
+# ------------------------------------------------------------- grouped
+
+def test_grouped_small_with_empty_groups(dev):
+    m_sizes = [0, 37, 128, 0, 300, 1, 256]
+    case = si.grouped_case(m_sizes, 264, 200, 8, d_dtype="f32")
+    say(f"grouped small {m_sizes}")
+    d = sg.grouped_gemm(case.A.to(dev), case.B.to(dev), case.m_offsets,
+                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, bound = oracle.grouped_gemm(case.m_offsets, case.N, case.K, case.A, case.B, "bf16")
+    check_close(_np(d), ref, bound, "f32", "grouped small")
+
+
+def test_grouped_single_group_equals_dense(dev):
+    case = si.grouped_case([300], 136, 72, 9, d_dtype="f32")
+    say("grouped G=1 vs dense")
+    A, B = case.A.to(dev), case.B.to(dev)
+    dg = sg.grouped_gemm(A, B, case.m_offsets, out_dtype=torch.float32)
+    dd = sg.gemm(A, B[0], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(dg, dd)
+
+
+def test_grouped_full_size_sampled(dev):
+    case = si.grouped(seed=4)
+    say(f"{case.name} m_sizes={case.m_sizes} (sampled)")
+    d = sg.grouped_gemm(case.A.to(dev), case.B.to(dev), case.m_offsets,
+                        out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(d).all())
+    Bn = case.B.reshape(case.G, case.N, case.K)
+    for g in range(case.G):
+        lo, hi = case.m_offsets[g], case.m_offsets[g + 1]
+        rows, cols = sample_points(hi - lo, case.N, 200, 100 + g)
+        ref, bound = oracle.gemm_points(hi - lo, case.N, case.K, case.A[lo:hi], "k",
+                                        Bn[g], "k", "bf16", rows, cols)
+        got = _np(d[torch.from_numpy(rows + lo).to(dev), torch.from_numpy(cols).to(dev)])
+        check_close(got, ref, bound, "bf16", f"group {g}")
+
+
+# ------------------------------------------------------------------ MX
+
+def run_mx(case: si.MXCase, dev, d_dtype="bf16"):
+    d = sg.mx_gemm(case.A.to(dev), case.SFA.to(dev), case.B.to(dev), case.SFB.to(dev),
+                   out_dtype=DT[d_dtype])
+    torch.cuda.synchronize()
+    return d
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 384), (128, 128, 128), (520, 136, 256)])
+def test_mx_small_full(dev, M, N, K):
+    case = si.mx_case(M, N, K, 17)
+    say(f"mx {M}x{N}x{K}")
+    d = run_mx(case, dev, "f32")
+    ref, bound = oracle.mx_gemm(M, N, K, case.A, case.SFA, case.B, case.SFB)
+    check_close(_np(d), ref, bound, "f32", "mx small")
+
+
+def test_mx_scales_wide_range_and_unit(dev):
+    M, N, K = 256, 264, 512
+    case = si.mx_case(M, N, K, 18)
+    rng = np.random.default_rng(5)
+    case.SFA = torch.from_numpy(rng.integers(110, 145, (M, K // 32)).astype(np.uint8))
+    case.SFB = torch.from_numpy(rng.integers(110, 145, (N, K // 32)).astype(np.uint8))
+    say("mx wide scales")
+    d = run_mx(case, dev, "f32")
+    ref, bound = oracle.mx_gemm(M, N, K, case.A, case.SFA, case.B, case.SFB)
+    check_close(_np(d), ref, bound, "f32", "mx wide scales")
+    case.SFA = torch.full((M, K // 32), 127, dtype=torch.uint8)
+    case.SFB = torch.full((N, K // 32), 127, dtype=torch.uint8)
+    d = run_mx(case, dev, "f32")
+    ref, bound = oracle.mx_gemm(M, N, K, case.A, case.SFA, case.B, case.SFB)
+    check_close(_np(d), ref, bound, "f32", "mx unit scales")
+
+
+def test_mx_8192_full_size_sampled(dev):
+    case = si.mxfp8(seed=5)
+    say(f"{case.name} (sampled)")
+    d = run_mx(case, dev, "bf16")
+    assert bool(torch.isfinite(d).all())
+    rows, cols = sample_points(case.M, case.N, 3000, 55)
+    ref, bound = oracle.mx_gemm_points(case.M, case.N, case.K, case.A, case.SFA, case.B,
+                                       case.SFB, rows, cols)
+    got = _np(d[torch.from_numpy(rows).to(dev), torch.from_numpy(cols).to(dev)])
+    check_close(got, ref, bound, "bf16", case.name)
