@@ -115,6 +115,19 @@ def build_workload(name: str, dev):
 
         return run, flops, "e4m3", cfg, oracle_sample, case.M
 
+    if name == "copy":
+        # A plain device copy of known size: the reference for scaling the
+        # FETCH_SIZE / WRITE_SIZE counters into bytes.
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+
+        def run():
+            dst.copy_(src)
+
+        cfg = {"workload": "copy_1GiB_f32", "bytes_read": 4 * n, "bytes_written": 4 * n}
+        return run, 0.0, "bf16", cfg, None, 0
+
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -140,7 +153,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dense_8192",
-                    choices=["dense_8192", "grouped", "mxfp8", "dense_1024", "single_tile"])
+                    choices=["dense_8192", "grouped", "mxfp8", "dense_1024", "single_tile",
+                             "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -185,7 +199,7 @@ def main():
         f"({100 * achieved / peak:.1f}% of {peak} TFLOP/s)")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and oracle_sample is not None:
         log("[bench] timing the CPU oracle on a row sample")
         cpu = cpu_baseline(oracle_sample, rows_total)
         log(f"[bench] cpu oracle: {cpu}")

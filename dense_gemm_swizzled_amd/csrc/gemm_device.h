@@ -63,36 +63,46 @@ __device__ __forceinline__ void lds_write16(char* lds, uint32_t off, u32x4 v) {
 // row (coalesced); the swizzle permutes only the LDS destination.
 // ---------------------------------------------------------------------------
 
-// K-major source [rows][K]: chunk (row, c) lives at row*pitch + kbyte0 + 16c.
-// Thread t, step i: row = i*32 + t/8, chunk = t%8.
-template <int Rows>
-struct KMajorLoader {
-  static constexpr int kSteps = Rows * 8 / kThreads;  // 16-byte loads per thread
-  u32x4 v[kSteps];
+// Direct global -> LDS loader for a K-major operand tile (Rows x 128 B).
+// buffer_load_dwordx4 ... lds writes lane l's 16 bytes to LDS at M0 + 16*l,
+// so one instruction fills 1 KiB of LDS with no VGPR staging and no
+// ds_write.  The tile is cut into Rows/8 regions of 1 KiB; region r = 4*i +
+// wave.  Lane l of a region fills physical bytes [1 KiB*r + 16l, +16); the
+// swizzle is an involution, so it fetches the logical chunk whose swizzled
+// offset that is.  The XOR key of a line is (line index mod 16), the same for
+// every region a lane fills, so the lane's K chunk is fixed and its row
+// advances by 32 per region.
+template <int Rows, int Swz>
+struct DmaLoader {
+  static constexpr int kSteps = Rows / 32;  // regions per wave
+  uint32_t base;    // row0 * pitch + 16 * chunk
+  uint32_t chunk16; // 16 * chunk
+  int row0;
+  uint32_t pitch;
 
-  // row_pitch: bytes per source row; rows_valid: rows of this tile that
-  // exist; kbytes_total: bytes of K per row that exist (K * elem size).
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int tid,
-                                       uint32_t row_pitch, int rows_valid,
-                                       uint32_t kbyte0, uint32_t kbytes_total) {
-    const int c = tid & 7;
-    const uint32_t kb = kbyte0 + 16u * c;
-    const bool k_ok = kb < kbytes_total;
-#pragma unroll
-    for (int i = 0; i < kSteps; ++i) {
-      const int row = i * 32 + (tid >> 3);
-      const bool ok = k_ok && row < rows_valid;
-      v[i] = buffer_load16(r, ok ? row * row_pitch + kb : kOutOfRange);
-    }
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t row_pitch) {
+    const uint32_t phys = (uint32_t)wave * 1024u + 16u * (uint32_t)lane;
+    const uint32_t logical = swz_bytes<Swz>(phys);
+    row0 = (int)(logical >> 7);
+    chunk16 = logical & 127u;
+    pitch = row_pitch;
+    base = (uint32_t)row0 * row_pitch + chunk16;
   }
 
-  template <int Swz>
-  __device__ __forceinline__ void store(char* lds, int tid) const {
-    const int c = tid & 7;
+  // Issues the loads of K bytes [kbyte0, kbyte0 + 128) of every row into the
+  // tile at `lds` (generic pointer to the tile's first byte).  Rows at or
+  // beyond rows_valid and bytes at or beyond kbytes_total read as zero.
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char* lds, int wave,
+                                        int rows_valid, uint32_t kbyte0,
+                                        uint32_t kbytes_total) const {
+    const bool k_ok = kbyte0 + chunk16 < kbytes_total;
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
-      const int row = i * 32 + (tid >> 3);
-      lds_write16(lds, lds_offset<128, Swz>(row, c), v[i]);
+      const bool ok = k_ok && row0 + 32 * i < rows_valid;
+      const uint32_t off = ok ? base + (uint32_t)(32 * i) * pitch + kbyte0 : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds + (4 * i + wave) * 1024), 16,
+          off, 0, 0, 0);
     }
   }
 };
@@ -140,6 +150,46 @@ struct MNMajorLoader {
     }
   }
 };
+
+// One operand's loader with a common interface: issue() starts the global
+// reads of one K tile into an LDS tile, commit() finishes it (a no-op for the
+// direct-to-LDS path, the transposed ds_writes for MN-major sources).
+// ElemBytes = 2 for fp16/bf16, 1 for fp8.
+template <int Rows, bool Mn, int Swz, int ElemBytes>
+struct OperandLoader;
+
+template <int Rows, int Swz, int ElemBytes>
+struct OperandLoader<Rows, false, Swz, ElemBytes> {
+  DmaLoader<Rows, Swz> d;
+  __device__ __forceinline__ void init(int tid, uint32_t pitch) {
+    d.init(__builtin_amdgcn_readfirstlane(tid >> 6), tid & 63, pitch);
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char* lds, int tid,
+                                        int rows_valid, int k0, int K) {
+    d.issue(r, lds, __builtin_amdgcn_readfirstlane(tid >> 6), rows_valid, (uint32_t)k0 * ElemBytes,
+            (uint32_t)K * ElemBytes);
+  }
+  __device__ __forceinline__ void commit(char*, int) const {}
+};
+
+template <int Rows, int Swz, int ElemBytes>
+struct OperandLoader<Rows, true, Swz, ElemBytes> {
+  static_assert(ElemBytes == 2, "MN-major sources are 16-bit");
+  MNMajorLoader<Rows> m;
+  uint32_t pitch;
+  __device__ __forceinline__ void init(int, uint32_t p) { pitch = p; }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char*, int tid,
+                                        int rows_valid, int k0, int K) {
+    m.load(r, tid, pitch, rows_valid, k0, K);
+  }
+  __device__ __forceinline__ void commit(char* lds, int tid) const {
+    m.template store<Swz>(lds, tid);
+  }
+};
+
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
 // ---------------------------------------------------------------------------
 // MFMA wrappers (v_mfma_f32_32x32x16_{bf16,f16}, v_mfma_scale_f32_32x32x64_

@@ -96,37 +96,136 @@ struct GemmTile {
   static constexpr int kATileBytes = BM * kRowBytes;
   static constexpr int kBTileBytes = BN * kRowBytes;
   static constexpr int kStageBytes = kATileBytes + kBTileBytes;
-  static constexpr int kLdsBytes = 2 * kStageBytes;
   static constexpr int kWM = BM / 2, kWN = BN / 2;  // per-wave block
   static constexpr int kFM = kWM / 32, kFN = kWN / 32;
   static_assert(kStageBytes % 4096 == 0, "stage bases must keep the swizzle phase");
 
-  using ALoader = typename std::conditional<AMn, MNMajorLoader<BM>, KMajorLoader<BM>>::type;
-  using BLoader = typename std::conditional<BMn, MNMajorLoader<BN>, KMajorLoader<BN>>::type;
+  using ALoader = OperandLoader<BM, AMn, Swz, 2>;
+  using BLoader = OperandLoader<BN, BMn, Swz, 2>;
 
-  __device__ __forceinline__ static void load(ALoader& la, BLoader& lb,
-                                              const TileJob& j,
-                                              __amdgpu_buffer_rsrc_t ra,
-                                              __amdgpu_buffer_rsrc_t rb, int tid,
-                                              int k0, int K) {
-    if constexpr (AMn)
-      la.load(ra, tid, j.a_pitch, j.m_valid, k0, K);
-    else
-      la.load(ra, tid, j.a_pitch, j.m_valid, (uint32_t)k0 * 2u, (uint32_t)K * 2u);
-    if constexpr (BMn)
-      lb.load(rb, tid, j.b_pitch, j.n_valid, k0, K);
-    else
-      lb.load(rb, tid, j.b_pitch, j.n_valid, (uint32_t)k0 * 2u, (uint32_t)K * 2u);
+  // Fragments of one 16-wide K step: lane l holds row l%32 of each 32-row
+  // fragment and K chunk 2*kk + l/32.
+  struct Frags {
+    u32x4 a[kFM], b[kFN];
+  };
+
+  // Per-lane LDS byte offsets of fragment 0 for each 16-wide K step.  Rows
+  // 32 apart share the XOR key (it depends on the row only through the bank
+  // line index modulo 16, i.e. row/2 mod 16, or row mod 8 for 128-byte
+  // lines), so fragment f sits exactly f * 32 * 128 bytes further: a
+  // constant the ds_read offset field absorbs.
+  struct FragOffsets {
+    uint32_t a[kBK / 16], b[kBK / 16];
+  };
+
+  __device__ __forceinline__ static FragOffsets frag_offsets(int wm, int wn, int lrow,
+                                                             int lhalf) {
+    FragOffsets o;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      o.a[kk] = lds_offset<kRowBytes, Swz>(wm * kWM + lrow, 2 * kk + lhalf);
+      o.b[kk] = lds_offset<kRowBytes, Swz>(wn * kWN + lrow, 2 * kk + lhalf);
+    }
+    return o;
   }
 
-  // Runs the mainloop over K and the epilogue for one tile.
-  __device__ __forceinline__ static void run(char* smem, const TileJob& j,
+  __device__ __forceinline__ static void read_frags(Frags& f, const char* As,
+                                                    const char* Bs, const FragOffsets& o,
+                                                    int kk) {
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm)
+      f.a[fm] = lds_read16(As, o.a[kk] + fm * 32 * kRowBytes);
+#pragma unroll
+    for (int fn = 0; fn < kFN; ++fn)
+      f.b[fn] = lds_read16(Bs, o.b[kk] + fn * 32 * kRowBytes);
+  }
+
+  // MFMA rows take B rows (n), columns take A rows (m): each lane then ends
+  // up holding 4 consecutive n of one m (wide epilogue stores).
+  __device__ __forceinline__ static void mfmas(f32x16 (&acc)[kFM][kFN], const Frags& f) {
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < kFN; ++fn)
+        acc[fm][fn] = mfma32x32x16<IsBF16>(f.b[fn], f.a[fm], acc[fm][fn]);
+  }
+
+  // Instruction-scheduling hints (LLVM AMDGPU sched_group_barrier masks).
+  static constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
+
+  // One 16-wide K step: the next step's fragment reads (kFM + kFN ds_reads)
+  // are interleaved one per two MFMAs of this step, and `vmem` buffer loads
+  // of the next K tile are spread over the same stretch, so that the wave's
+  // LDS and global traffic issues in the shadow of the matrix core.
+  template <int Vmem>
+  __device__ __forceinline__ static void step(f32x16 (&acc)[kFM][kFN], const Frags& cur,
+                                              Frags& nxt, const char* As, const char* Bs,
+                                              const FragOffsets& o, int kk) {
+    read_frags(nxt, As, Bs, o, kk);
+    mfmas(acc, cur);
+    constexpr int kReads = kFM + kFN, kMfma = kFM * kFN;
+    constexpr int kPerRead = kMfma / kReads;
+#pragma unroll
+    for (int i = 0; i < kReads; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      if constexpr (Vmem > 0)
+        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (Vmem + kReads - 1) / kReads, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPerRead, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // One K tile: compute on stage `cur` while the next tile loads into `nxt`.
+  //
+  // The loads of tile kt+1 are issued into `nxt` first (that stage was last
+  // read before the previous barrier); each 16-wide K step reads the next
+  // step's fragments while its own MFMAs run.  The barrier sits before the
+  // last step's MFMAs: by then every wave has issued (and, by the barrier's
+  // LDS wait, completed) all its reads of `cur`, and its own loads into `nxt`
+  // have landed, so the last step can already read `nxt`'s first fragments.
+  // `cur` and `nxt` are distinct __shared__ objects, which lets the compiler
+  // see that reads of one never alias the direct-to-LDS writes into the
+  // other (otherwise it waits for those loads before every LDS read).
+  __device__ __forceinline__ static void k_tile(f32x16 (&acc)[kFM][kFN], Frags& f0,
+                                                Frags& f1, ALoader& la, BLoader& lb,
+                                                __amdgpu_buffer_rsrc_t ra,
+                                                __amdgpu_buffer_rsrc_t rb, char* cur,
+                                                char* nxt, const TileJob& j, int tid,
+                                                const FragOffsets& o, int kt, int kt_total,
+                                                int Ki) {
+    constexpr int kVmem = (AMn ? 0 : BM / 32) + (BMn ? 0 : BN / 32);
+    const bool more = kt + 1 < kt_total;
+    if (more) {
+      la.issue(ra, nxt, tid, j.m_valid, (kt + 1) * kBK, Ki);
+      lb.issue(rb, nxt + kATileBytes, tid, j.n_valid, (kt + 1) * kBK, Ki);
+    }
+    step<kVmem>(acc, f0, f1, cur, cur + kATileBytes, o, 1);
+    step<0>(acc, f1, f0, cur, cur + kATileBytes, o, 2);
+    step<0>(acc, f0, f1, cur, cur + kATileBytes, o, 3);
+    if (more) {
+      la.commit(nxt, tid);
+      lb.commit(nxt + kATileBytes, tid);
+    }
+    wait_vmem();
+    __syncthreads();
+    // After the last tile this reads stale LDS into f0, which is never
+    // used; keeping the step unconditional keeps the accumulators out of any
+    // control-flow merge (which would cost register copies).
+    step<0>(acc, f1, f0, nxt, nxt + kATileBytes, o, 0);
+  }
+
+  // Runs the mainloop over K and the epilogue for one tile; s0 and s1 are
+  // the two LDS stages (kStageBytes each).
+  __device__ __forceinline__ static void run(char* s0, char* s1, const TileJob& j,
                                              int64_t K, const void* C,
                                              int c_dtype, void* D, int d_dtype,
                                              int64_t ldd) {
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // The wave index is uniform across the wave; readfirstlane lets the
+    // compiler keep it (and every LDS base derived from it) in SGPRs.
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
+    const int lrow = lane & 31, lhalf = lane >> 5;
 
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(j.a, j.a_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(j.b, j.b_bytes);
@@ -137,56 +236,34 @@ struct GemmTile {
 #pragma unroll
       for (int k = 0; k < kFN; ++k) acc[i][k] = f32x16{};
 
-    const int kt_total = (int)((K + kBK - 1) / kBK);
+    const int Ki = (int)K;
+    const int kt_total = (Ki + kBK - 1) / kBK;
     ALoader la;
     BLoader lb;
+    la.init(tid, j.a_pitch);
+    lb.init(tid, j.b_pitch);
     if (kt_total > 0) {
-      load(la, lb, j, ra, rb, tid, 0, (int)K);
-      la.template store<Swz>(smem, tid);
-      lb.template store<Swz>(smem + kATileBytes, tid);
+      la.issue(ra, s0, tid, j.m_valid, 0, Ki);
+      lb.issue(rb, s0 + kATileBytes, tid, j.n_valid, 0, Ki);
+      la.commit(s0, tid);
+      lb.commit(s0 + kATileBytes, tid);
     }
+    wait_vmem();
     __syncthreads();
 
-    // Per-lane LDS read offsets: row (l%32) of each 32-row fragment, K
-    // chunk 2*kk + l/32.  Fragments 32 rows apart share the XOR key (the
-    // key depends on the line index modulo 16 = row/2 modulo 16), so they
-    // differ by a constant 4096 bytes.
-    const int lrow = lane & 31, lhalf = lane >> 5;
+    const FragOffsets o = frag_offsets(wm, wn, lrow, lhalf);
+    Frags f0, f1;
+    if (kt_total > 0) read_frags(f0, s0, s0 + kATileBytes, o, 0);
 
-    for (int kt = 0; kt < kt_total; ++kt) {
-      const int stage = kt & 1;
-      const bool more = kt + 1 < kt_total;
-      if (more) load(la, lb, j, ra, rb, tid, (kt + 1) * kBK, (int)K);
-
-      const char* As = smem + stage * kStageBytes;
-      const char* Bs = As + kATileBytes;
-#pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        u32x4 af[kFM], bfr[kFN];
-#pragma unroll
-        for (int fm = 0; fm < kFM; ++fm)
-          af[fm] = lds_read16(As, lds_offset<kRowBytes, Swz>(
-                                      wm * kWM + fm * 32 + lrow, 2 * kk + lhalf));
-#pragma unroll
-        for (int fn = 0; fn < kFN; ++fn)
-          bfr[fn] = lds_read16(Bs, lds_offset<kRowBytes, Swz>(
-                                       wn * kWN + fn * 32 + lrow, 2 * kk + lhalf));
-        // MFMA rows take B rows (n), columns take A rows (m): each lane then
-        // ends up holding 4 consecutive n of one m (wide epilogue stores).
-#pragma unroll
-        for (int fm = 0; fm < kFM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < kFN; ++fn)
-            acc[fm][fn] = mfma32x32x16<IsBF16>(bfr[fn], af[fm], acc[fm][fn]);
-      }
-
-      if (more) {
-        char* nxt = smem + (stage ^ 1) * kStageBytes;
-        la.template store<Swz>(nxt, tid);
-        lb.template store<Swz>(nxt + kATileBytes, tid);
-      }
-      __syncthreads();
+    // Two K tiles per trip so that each tile's stage is a fixed object; an
+    // odd last tile is peeled (an exit between the two tiles of a trip makes
+    // the register allocator spill the accumulators).
+    int kt = 0;
+    for (; kt + 1 < kt_total; kt += 2) {
+      k_tile(acc, f0, f1, la, lb, ra, rb, s0, s1, j, tid, o, kt, kt_total, Ki);
+      k_tile(acc, f0, f1, la, lb, ra, rb, s1, s0, j, tid, o, kt + 1, kt_total, Ki);
     }
+    if (kt < kt_total) k_tile(acc, f0, f1, la, lb, ra, rb, s0, s1, j, tid, o, kt, kt_total, Ki);
 
     epilogue(acc, j, C, c_dtype, D, d_dtype, ldd, lane, wm, wn);
   }
@@ -255,7 +332,8 @@ template <int BM, int BN, bool IsBF16, bool AMn, bool BMn, int Swz>
 __global__ void __launch_bounds__(kThreads, 1)
     dense_gemm_kernel(const DenseParams p) {
   using Tile = GemmTile<BM, BN, IsBF16, AMn, BMn, Swz>;
-  __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+  __shared__ __attribute__((aligned(4096))) char s0[Tile::kStageBytes];
+  __shared__ __attribute__((aligned(4096))) char s1[Tile::kStageBytes];
 
   const int total = p.tiles_m * p.tiles_n;
   const int t = xcd_remap(blockIdx.x, total);
@@ -287,14 +365,15 @@ __global__ void __launch_bounds__(kThreads, 1)
   }
   j.d_row0 = m0;
   j.n0 = n0;
-  Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.N);
+  Tile::run(s0, s1, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.N);
 }
 
 template <int BM, int BN, bool IsBF16, int Swz>
 __global__ void __launch_bounds__(kThreads, 1)
     grouped_gemm_kernel(const GroupedParams p) {
   using Tile = GemmTile<BM, BN, IsBF16, false, false, Swz>;
-  __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+  __shared__ __attribute__((aligned(4096))) char s0[Tile::kStageBytes];
+  __shared__ __attribute__((aligned(4096))) char s1[Tile::kStageBytes];
 
   const int total = p.tile_start[p.G];
   const int t = xcd_remap(blockIdx.x, total);
@@ -323,7 +402,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   j.b_bytes = (uint32_t)(j.n_valid * p.K * es);
   j.d_row0 = p.m_off[g] + m0;
   j.n0 = n0;
-  Tile::run(smem, j, p.K, nullptr, SG_NONE, p.D, p.d_dtype, p.N);
+  Tile::run(s0, s1, j, p.K, nullptr, SG_NONE, p.D, p.d_dtype, p.N);
 }
 
 }  // namespace sg

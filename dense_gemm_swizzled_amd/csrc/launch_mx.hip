@@ -14,7 +14,7 @@ hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Runs the K-major tile loader once (rows [row0, row0 + Rows), bytes
+// Runs the K-major (direct-to-LDS) tile loader once (rows [row0, row0 + Rows), bytes
 // [k0*eb, k0*eb + 128) of each row) into LDS under the kernels' swizzle and
 // copies the LDS stage out linearly.
 template <int Rows>
@@ -23,9 +23,10 @@ __global__ void __launch_bounds__(kThreads, 1)
                      uint32_t kbyte0, uint32_t kbytes_total, char* out) {
   __shared__ __attribute__((aligned(4096))) char smem[Rows * 128];
   const int tid = threadIdx.x;
-  KMajorLoader<Rows> ld;
-  ld.load(make_rsrc(X, x_bytes), tid, pitch, rows_valid, kbyte0, kbytes_total);
-  ld.template store<kSwzDefault>(smem, tid);
+  DmaLoader<Rows, kSwzDefault> ld;
+  ld.init(tid >> 6, tid & 63, pitch);
+  ld.issue(make_rsrc(X, x_bytes), smem, tid >> 6, rows_valid, kbyte0, kbytes_total);
+  wait_vmem();
   __syncthreads();
   for (int i = tid; i < Rows * 128 / 16; i += kThreads)
     reinterpret_cast<u32x4*>(out)[i] = reinterpret_cast<const u32x4*>(smem)[i];

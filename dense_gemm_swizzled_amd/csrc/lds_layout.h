@@ -45,6 +45,18 @@ SG_HD constexpr uint32_t lds_offset(uint32_t row, uint32_t chunk) {
   }
 }
 
+// The same XOR applied to a byte offset within a stage (it is its own
+// inverse: the key bits, above bit 7 or 8, are left unchanged).
+template <int Swz>
+SG_HD constexpr uint32_t swz_bytes(uint32_t off) {
+  if constexpr (Swz == 0) {
+    return off;
+  } else {
+    constexpr uint32_t line_shift = Swz == 8 ? 7 : 8;
+    return off ^ (((off >> line_shift) & (uint32_t)(Swz - 1)) << 4);
+  }
+}
+
 // Runtime-dispatched form for host tools.
 SG_HD uint32_t lds_offset_rt(int row_bytes, int swz, uint32_t row,
                              uint32_t chunk) {

@@ -58,7 +58,6 @@ struct MxTile {
   static constexpr int kATileBytes = BM * kRowBytes;
   static constexpr int kBTileBytes = BN * kRowBytes;
   static constexpr int kStageBytes = kATileBytes + kBTileBytes;
-  static constexpr int kLdsBytes = 2 * kStageBytes;
   static constexpr int kWM = BM / 2, kWN = BN / 2;
   static constexpr int kFM = kWM / 32, kFN = kWN / 32;
   static_assert(kStageBytes % 4096 == 0, "stage bases must keep the swizzle phase");
@@ -87,12 +86,103 @@ struct MxTile {
     }
   }
 
-  __device__ __forceinline__ static void run(char* smem, const TileJob& j,
+  struct Frags {
+    u32x4 a[kFM][2], b[kFN][2];
+  };
+
+  // Lane half h = l/32 supplies 16-byte chunk 4*kk + h (block 2*kk) then
+  // chunk 4*kk + 2 + h (block 2*kk + 1).
+  __device__ __forceinline__ static void read_frags(Frags& f, const char* As,
+                                                    const char* Bs, int wm, int wn,
+                                                    int lrow, int lhalf, int kk) {
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        f.a[fm][h] = lds_read16(As, lds_offset<kRowBytes, Swz>(
+                                        wm * kWM + fm * 32 + lrow, 4 * kk + 2 * h + lhalf));
+#pragma unroll
+    for (int fn = 0; fn < kFN; ++fn)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        f.b[fn][h] = lds_read16(Bs, lds_offset<kRowBytes, Swz>(
+                                        wn * kWN + fn * 32 + lrow, 4 * kk + 2 * h + lhalf));
+  }
+
+  __device__ __forceinline__ static void mfmas(f32x16 (&acc)[kFM][kFN], const Frags& f,
+                                               const uint32_t (&sa)[kFM],
+                                               const uint32_t (&sb)[kFN], int kk) {
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < kFN; ++fn)
+        acc[fm][fn] = mfma_scale_f8(f.b[fn], f.a[fm], acc[fm][fn], sb[fn], sa[fm], kk);
+  }
+
+  static constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
+
+  // One 64-wide K step: the next step's 2*(kFM+kFN) fragment reads are
+  // interleaved with this step's MFMAs, with `Vmem` loads of the next K tile
+  // spread over the same stretch.
+  template <int Vmem>
+  __device__ __forceinline__ static void step(f32x16 (&acc)[kFM][kFN], const Frags& cur,
+                                              Frags& nxt, const char* As, const char* Bs,
+                                              int wm, int wn, int lrow, int lhalf,
+                                              int kk_next, const uint32_t (&sa)[kFM],
+                                              const uint32_t (&sb)[kFN], int kk) {
+    read_frags(nxt, As, Bs, wm, wn, lrow, lhalf, kk_next);
+    mfmas(acc, cur, sa, sb, kk);
+    constexpr int kReads = 2 * (kFM + kFN), kMfma = kFM * kFN;
+    constexpr int kPer = kMfma / kReads > 0 ? kMfma / kReads : 1;
+#pragma unroll
+    for (int i = 0; i < kReads; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      if constexpr (Vmem > 0)
+        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (Vmem + kReads - 1) / kReads, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPer, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // One K tile of 128: compute on stage `cur` while tile kt+1 (operands by
+  // direct-to-LDS DMA into `nxt`, scales into VGPRs) loads.  Same barrier
+  // placement and distinct-stage-object rule as the 16-bit kernels.
+  __device__ __forceinline__ static void k_tile(
+      f32x16 (&acc)[kFM][kFN], Frags& f0, Frags& f1,
+      OperandLoader<BM, false, Swz, 1>& la, OperandLoader<BN, false, Swz, 1>& lb,
+      Scales& sc, Scales& sc_next, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+      __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb, uint32_t sf_pitch, char* cur,
+      char* nxt, const TileJob& j, int tid, int lane, int wm, int wn, int lrow, int lhalf,
+      int kt, int kt_total, int Ki) {
+    constexpr int kVmem = BM / 32 + BN / 32;
+    const bool more = kt + 1 < kt_total;
+    if (more) {
+      la.issue(ra, nxt, tid, j.m_valid, (kt + 1) * kBK, Ki);
+      lb.issue(rb, nxt + kATileBytes, tid, j.n_valid, (kt + 1) * kBK, Ki);
+      load_scales(sc_next, rsa, rsb, sf_pitch, kt + 1, lane, wm, wn, j.m_valid, j.n_valid);
+    }
+    uint32_t sa[kFM], sb[kFN];
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm) sa[fm] = sc.a[fm] >> (8 * lhalf);
+#pragma unroll
+    for (int fn = 0; fn < kFN; ++fn) sb[fn] = sc.b[fn] >> (8 * lhalf);
+    step<kVmem>(acc, f0, f1, cur, cur + kATileBytes, wm, wn, lrow, lhalf, 1, sa, sb, 0);
+    wait_vmem();
+    __syncthreads();
+    // Unconditional (see the 16-bit kernels): after the last tile the reads
+    // of `nxt` are stale and unused.
+    step<0>(acc, f1, f0, nxt, nxt + kATileBytes, wm, wn, lrow, lhalf, 0, sa, sb, 1);
+    sc = sc_next;
+  }
+
+  __device__ __forceinline__ static void run(char* s0, char* s1, const TileJob& j,
                                              const char* sfa, const char* sfb,
                                              int64_t K, void* D, int d_dtype,
                                              int64_t ldd) {
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // The wave index is uniform across the wave; readfirstlane lets the
+    // compiler keep it (and every LDS base derived from it) in SGPRs.
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int lrow = lane & 31, lhalf = lane >> 5;
 
@@ -108,68 +198,35 @@ struct MxTile {
 #pragma unroll
       for (int k = 0; k < kFN; ++k) acc[i][k] = f32x16{};
 
-    const int kt_total = (int)(K / kBK);
-    KMajorLoader<BM> la;
-    KMajorLoader<BN> lb;
+    const int Ki = (int)K;
+    const int kt_total = Ki / kBK;
+    OperandLoader<BM, false, Swz, 1> la;
+    OperandLoader<BN, false, Swz, 1> lb;
+    la.init(tid, j.a_pitch);
+    lb.init(tid, j.b_pitch);
     Scales sc, sc_next;
     if (kt_total > 0) {
-      la.load(ra, tid, j.a_pitch, j.m_valid, 0, (uint32_t)K);
-      lb.load(rb, tid, j.b_pitch, j.n_valid, 0, (uint32_t)K);
+      la.issue(ra, s0, tid, j.m_valid, 0, Ki);
+      lb.issue(rb, s0 + kATileBytes, tid, j.n_valid, 0, Ki);
       load_scales(sc, rsa, rsb, sf_pitch, 0, lane, wm, wn, j.m_valid, j.n_valid);
-      la.template store<Swz>(smem, tid);
-      lb.template store<Swz>(smem + kATileBytes, tid);
     }
+    wait_vmem();
     __syncthreads();
 
-    for (int kt = 0; kt < kt_total; ++kt) {
-      const int stage = kt & 1;
-      const bool more = kt + 1 < kt_total;
-      if (more) {
-        la.load(ra, tid, j.a_pitch, j.m_valid, (uint32_t)(kt + 1) * kBK, (uint32_t)K);
-        lb.load(rb, tid, j.b_pitch, j.n_valid, (uint32_t)(kt + 1) * kBK, (uint32_t)K);
-        load_scales(sc_next, rsa, rsb, sf_pitch, kt + 1, lane, wm, wn, j.m_valid,
-                    j.n_valid);
-      }
-      uint32_t sa[kFM], sb[kFN];
-#pragma unroll
-      for (int fm = 0; fm < kFM; ++fm) sa[fm] = sc.a[fm] >> (8 * lhalf);
-#pragma unroll
-      for (int fn = 0; fn < kFN; ++fn) sb[fn] = sc.b[fn] >> (8 * lhalf);
+    Frags f0, f1;
+    if (kt_total > 0) read_frags(f0, s0, s0 + kATileBytes, wm, wn, lrow, lhalf, 0);
 
-      const char* As = smem + stage * kStageBytes;
-      const char* Bs = As + kATileBytes;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // Lane half h = l/32 supplies 16-byte chunk 4*kk + h (block 2*kk)
-        // then chunk 4*kk + 2 + h (block 2*kk + 1).
-        u32x4 af[kFM][2], bfr[kFN][2];
-#pragma unroll
-        for (int fm = 0; fm < kFM; ++fm)
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            af[fm][h] = lds_read16(As, lds_offset<kRowBytes, Swz>(
-                                           wm * kWM + fm * 32 + lrow, 4 * kk + 2 * h + lhalf));
-#pragma unroll
-        for (int fn = 0; fn < kFN; ++fn)
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            bfr[fn][h] = lds_read16(Bs, lds_offset<kRowBytes, Swz>(
-                                            wn * kWN + fn * 32 + lrow, 4 * kk + 2 * h + lhalf));
-#pragma unroll
-        for (int fm = 0; fm < kFM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < kFN; ++fn)
-            acc[fm][fn] = mfma_scale_f8(bfr[fn], af[fm], acc[fm][fn], sb[fn], sa[fm], kk);
-      }
-
-      if (more) {
-        char* nxt = smem + (stage ^ 1) * kStageBytes;
-        la.template store<Swz>(nxt, tid);
-        lb.template store<Swz>(nxt + kATileBytes, tid);
-        sc = sc_next;
-      }
-      __syncthreads();
+    // Two K tiles per trip (fixed stage objects), odd last tile peeled.
+    int kt = 0;
+    for (; kt + 1 < kt_total; kt += 2) {
+      k_tile(acc, f0, f1, la, lb, sc, sc_next, ra, rb, rsa, rsb, sf_pitch, s0, s1, j, tid,
+             lane, wm, wn, lrow, lhalf, kt, kt_total, Ki);
+      k_tile(acc, f0, f1, la, lb, sc, sc_next, ra, rb, rsa, rsb, sf_pitch, s1, s0, j, tid,
+             lane, wm, wn, lrow, lhalf, kt + 1, kt_total, Ki);
     }
+    if (kt < kt_total)
+      k_tile(acc, f0, f1, la, lb, sc, sc_next, ra, rb, rsa, rsb, sf_pitch, s0, s1, j, tid,
+             lane, wm, wn, lrow, lhalf, kt, kt_total, Ki);
 
     GemmTile<BM, BN, true, false, false, Swz>::epilogue(acc, j, nullptr, SG_NONE, D,
                                                         d_dtype, ldd, lane, wm, wn);
@@ -179,7 +236,8 @@ struct MxTile {
 template <int BM, int BN, int Swz>
 __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(const MxParams p) {
   using Tile = MxTile<BM, BN, Swz>;
-  __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+  __shared__ __attribute__((aligned(4096))) char s0[Tile::kStageBytes];
+  __shared__ __attribute__((aligned(4096))) char s1[Tile::kStageBytes];
 
   const int total = p.tiles_m * p.tiles_n;
   const int t = xcd_remap(blockIdx.x, total);
@@ -200,7 +258,7 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(const MxParams p) 
   j.n0 = n0;
   const char* sfa = static_cast<const char*>(p.SFA) + m0 * (p.K / 32);
   const char* sfb = static_cast<const char*>(p.SFB) + n0 * (p.K / 32);
-  Tile::run(smem, j, sfa, sfb, p.K, p.D, p.d_dtype, p.N);
+  Tile::run(s0, s1, j, sfa, sfb, p.K, p.D, p.d_dtype, p.N);
 }
 
 }  // namespace sg
