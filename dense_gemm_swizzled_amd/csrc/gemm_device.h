@@ -90,14 +90,16 @@ struct DmaLoader {
   }
 
   // Issues the loads of K bytes [kbyte0, kbyte0 + 128) of every row into the
-  // tile at `lds` (generic pointer to the tile's first byte).  Rows at or
-  // beyond rows_valid and bytes at or beyond kbytes_total read as zero.
+  // tile at `lds` (generic pointer to the tile's first byte) for this wave's
+  // regions I0 <= i < I1.  Rows at or beyond rows_valid and bytes at or
+  // beyond kbytes_total read as zero.
+  template <int I0 = 0, int I1 = kSteps>
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char* lds, int wave,
                                         int rows_valid, uint32_t kbyte0,
                                         uint32_t kbytes_total) const {
     const bool k_ok = kbyte0 + chunk16 < kbytes_total;
 #pragma unroll
-    for (int i = 0; i < kSteps; ++i) {
+    for (int i = I0; i < (I1 < kSteps ? I1 : kSteps); ++i) {
       const bool ok = k_ok && row0 + 32 * i < rows_valid;
       const uint32_t off = ok ? base + (uint32_t)(32 * i) * pitch + kbyte0 : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -160,14 +162,17 @@ struct OperandLoader;
 
 template <int Rows, int Swz, int ElemBytes>
 struct OperandLoader<Rows, false, Swz, ElemBytes> {
+  static constexpr int kIssues = DmaLoader<Rows, Swz>::kSteps;  // loads per thread
   DmaLoader<Rows, Swz> d;
   __device__ __forceinline__ void init(int tid, uint32_t pitch) {
     d.init(__builtin_amdgcn_readfirstlane(tid >> 6), tid & 63, pitch);
   }
+  // Issues this thread's loads I0 <= i < I1 of one K tile.
+  template <int I0 = 0, int I1 = kIssues>
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char* lds, int tid,
                                         int rows_valid, int k0, int K) {
-    d.issue(r, lds, __builtin_amdgcn_readfirstlane(tid >> 6), rows_valid, (uint32_t)k0 * ElemBytes,
-            (uint32_t)K * ElemBytes);
+    d.template issue<I0, I1>(r, lds, __builtin_amdgcn_readfirstlane(tid >> 6), rows_valid,
+                             (uint32_t)k0 * ElemBytes, (uint32_t)K * ElemBytes);
   }
   __device__ __forceinline__ void commit(char*, int) const {}
 };
@@ -175,12 +180,14 @@ struct OperandLoader<Rows, false, Swz, ElemBytes> {
 template <int Rows, int Swz, int ElemBytes>
 struct OperandLoader<Rows, true, Swz, ElemBytes> {
   static_assert(ElemBytes == 2, "MN-major sources are 16-bit");
+  static constexpr int kIssues = 1;  // one batch of register loads
   MNMajorLoader<Rows> m;
   uint32_t pitch;
   __device__ __forceinline__ void init(int, uint32_t p) { pitch = p; }
+  template <int I0 = 0, int I1 = kIssues>
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char*, int tid,
                                         int rows_valid, int k0, int K) {
-    m.load(r, tid, pitch, rows_valid, k0, K);
+    if constexpr (I0 == 0 && I1 > 0) m.load(r, tid, pitch, rows_valid, k0, K);
   }
   __device__ __forceinline__ void commit(char* lds, int tid) const {
     m.template store<Swz>(lds, tid);
@@ -212,14 +219,10 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
 // Epilogue element conversions (round to nearest even).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  // RNE to bfloat16 of finite values; NaN stays NaN (quiet bit forced).
-  auto cvt = [](float f) -> uint32_t {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu))
-      return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  };
-  return cvt(lo) | (cvt(hi) << 16);
+  // Converts with v_cvt_pk_bf16_f32 (round to nearest even).
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {

@@ -175,17 +175,52 @@ struct GemmTile {
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  // Loads of the next K tile issued during 16-wide K step `kk` (1..3): the
+  // tile's direct-to-LDS loads are spread over the three steps that run
+  // before the barrier, so that the vector-memory path is never asked for
+  // more than about half a K tile's worth per step (issuing them all in one
+  // step stalls the wave on a full load queue and drains the MFMA pipe).
+  template <int Loader, int KK>
+  struct Share {
+    static constexpr int kA = ALoader::kIssues, kB = BLoader::kIssues;
+    static constexpr int kTotal = kA + kB;
+    static constexpr int begin = kTotal * (KK - 1) / 3, end = kTotal * KK / 3;
+    // Range of this loader's own issue indices inside [begin, end).
+    static constexpr int lo = Loader == 0 ? (begin < kA ? begin : kA) : (begin > kA ? begin - kA : 0);
+    static constexpr int hi = Loader == 0 ? (end < kA ? end : kA) : (end > kA ? end - kA : 0);
+    static constexpr int count = hi > lo ? hi - lo : 0;
+  };
+
+  template <int KK>
+  __device__ __forceinline__ static void issue_share(ALoader& la, BLoader& lb,
+                                                     __amdgpu_buffer_rsrc_t ra,
+                                                     __amdgpu_buffer_rsrc_t rb, char* nxt,
+                                                     const TileJob& j, int tid, int k0,
+                                                     int Ki) {
+    using SA = Share<0, KK>;
+    using SB = Share<1, KK>;
+    if constexpr (SA::count > 0)
+      la.template issue<SA::lo, SA::hi>(ra, nxt, tid, j.m_valid, k0, Ki);
+    if constexpr (SB::count > 0)
+      lb.template issue<SB::lo, SB::hi>(rb, nxt + kATileBytes, tid, j.n_valid, k0, Ki);
+  }
+
+  template <int KK>
+  static constexpr int vmem_count() {
+    return (AMn ? 0 : Share<0, KK>::count) + (BMn ? 0 : Share<1, KK>::count);
+  }
+
   // One K tile: compute on stage `cur` while the next tile loads into `nxt`.
   //
-  // The loads of tile kt+1 are issued into `nxt` first (that stage was last
-  // read before the previous barrier); each 16-wide K step reads the next
-  // step's fragments while its own MFMAs run.  The barrier sits before the
-  // last step's MFMAs: by then every wave has issued (and, by the barrier's
-  // LDS wait, completed) all its reads of `cur`, and its own loads into `nxt`
-  // have landed, so the last step can already read `nxt`'s first fragments.
-  // `cur` and `nxt` are distinct __shared__ objects, which lets the compiler
-  // see that reads of one never alias the direct-to-LDS writes into the
-  // other (otherwise it waits for those loads before every LDS read).
+  // The loads of tile kt+1 go into `nxt` (last read before the previous
+  // barrier), spread over the first three 16-wide K steps; each step reads
+  // the next step's fragments while its own MFMAs run.  The barrier sits
+  // before the last step's MFMAs: by then every wave has issued (and, by the
+  // barrier's LDS wait, completed) all its reads of `cur`, and its own loads
+  // into `nxt` have landed, so the last step can already read `nxt`'s first
+  // fragments.  `cur` and `nxt` are distinct __shared__ objects, which lets
+  // the compiler see that reads of one never alias the direct-to-LDS writes
+  // into the other (otherwise it waits for those loads before every read).
   __device__ __forceinline__ static void k_tile(f32x16 (&acc)[kFM][kFN], Frags& f0,
                                                 Frags& f1, ALoader& la, BLoader& lb,
                                                 __amdgpu_buffer_rsrc_t ra,
@@ -193,19 +228,19 @@ struct GemmTile {
                                                 char* nxt, const TileJob& j, int tid,
                                                 const FragOffsets& o, int kt, int kt_total,
                                                 int Ki) {
-    constexpr int kVmem = (AMn ? 0 : BM / 32) + (BMn ? 0 : BN / 32);
-    const bool more = kt + 1 < kt_total;
-    if (more) {
-      la.issue(ra, nxt, tid, j.m_valid, (kt + 1) * kBK, Ki);
-      lb.issue(rb, nxt + kATileBytes, tid, j.n_valid, (kt + 1) * kBK, Ki);
-    }
-    step<kVmem>(acc, f0, f1, cur, cur + kATileBytes, o, 1);
-    step<0>(acc, f1, f0, cur, cur + kATileBytes, o, 2);
-    step<0>(acc, f0, f1, cur, cur + kATileBytes, o, 3);
-    if (more) {
-      la.commit(nxt, tid);
-      lb.commit(nxt + kATileBytes, tid);
-    }
+    // The loads are unconditional so that they share a basic block with the
+    // MFMAs they interleave with; after the last tile they start at k = K,
+    // where every chunk is out of range and fills `nxt` (read by nobody
+    // again) with zeros.
+    const int k1 = kt + 1 < kt_total ? (kt + 1) * kBK : Ki;
+    issue_share<1>(la, lb, ra, rb, nxt, j, tid, k1, Ki);
+    step<vmem_count<1>()>(acc, f0, f1, cur, cur + kATileBytes, o, 1);
+    issue_share<2>(la, lb, ra, rb, nxt, j, tid, k1, Ki);
+    step<vmem_count<2>()>(acc, f1, f0, cur, cur + kATileBytes, o, 2);
+    issue_share<3>(la, lb, ra, rb, nxt, j, tid, k1, Ki);
+    step<vmem_count<3>()>(acc, f0, f1, cur, cur + kATileBytes, o, 3);
+    la.commit(nxt, tid);
+    lb.commit(nxt + kATileBytes, tid);
     wait_vmem();
     __syncthreads();
     // After the last tile this reads stale LDS into f0, which is never

@@ -155,12 +155,15 @@ struct MxTile {
       char* nxt, const TileJob& j, int tid, int lane, int wm, int wn, int lrow, int lhalf,
       int kt, int kt_total, int Ki) {
     constexpr int kVmem = BM / 32 + BN / 32;
+    // Unconditional loads (same basic block as the MFMAs they interleave
+    // with); after the last tile they start at k = K and only zero-fill
+    // `nxt`, and the scale loads re-read the last tile's scales.
     const bool more = kt + 1 < kt_total;
-    if (more) {
-      la.issue(ra, nxt, tid, j.m_valid, (kt + 1) * kBK, Ki);
-      lb.issue(rb, nxt + kATileBytes, tid, j.n_valid, (kt + 1) * kBK, Ki);
-      load_scales(sc_next, rsa, rsb, sf_pitch, kt + 1, lane, wm, wn, j.m_valid, j.n_valid);
-    }
+    const int k1 = more ? (kt + 1) * kBK : Ki;
+    la.issue(ra, nxt, tid, j.m_valid, k1, Ki);
+    lb.issue(rb, nxt + kATileBytes, tid, j.n_valid, k1, Ki);
+    load_scales(sc_next, rsa, rsb, sf_pitch, more ? kt + 1 : kt, lane, wm, wn, j.m_valid,
+                j.n_valid);
     uint32_t sa[kFM], sb[kFN];
 #pragma unroll
     for (int fm = 0; fm < kFM; ++fm) sa[fm] = sc.a[fm] >> (8 * lhalf);
