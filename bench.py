@@ -31,6 +31,36 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2}
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    """sha256 of the kernel sources and the C header: HBM traffic measured
+    with rocprofv3 is reported only while it still describes this code."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_swizzled_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "swizzled_gemm.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM-side bytes per launch from the committed FETCH_SIZE / WRITE_SIZE
+    passes, or None when they were taken on other kernel sources."""
+    import json
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    w = t.get("workloads", {}).get(workload)
+    return None if w is None else w["bytes"]
 
 
 def log(*a):
@@ -221,7 +251,9 @@ def main():
         "pct_of_bf16_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None, "kernel_ms_mean": round(mean_ms, 5),
+                     "traffic": measured_traffic(args.workload),
+                     "traffic_unit": "bytes per launch (HBM side)",
+                     "kernel_ms_mean": round(mean_ms, 5),
                      "kernel_ms_median": round(median_ms, 5)},
         "cpu_baseline": cpu,
     }

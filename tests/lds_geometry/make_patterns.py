@@ -73,8 +73,10 @@ def main(path, pairs=True, pairs_only=False, ops=None):
         return
     # GEMM operand-tile patterns.
     for kind in ("none", "x8", "x16"):
-        # MXFP8 operand (128-byte rows): lane l reads 32 bytes of row l%32,
-        # chunks 4*kk + 2*(l/32) + h, as two ds_read_b128 (h = 0, 1).
+        # A 32-byte-per-lane operand read (128-byte rows): lane l reads
+        # chunks 4*kk + 2*(l/32) + h of row l%32 as two ds_read_b128 (h = 0,
+        # 1).  (The MX kernels' actual order, chunk 4*kk + 2*h + l/32, is the
+        # mfma32 pattern below.)
         for kk in range(2):
             for h in range(2):
                 a = [swz(l % 32, 4 * kk + 2 * (l // 32) + h, 128, kind) for l in range(64)]
