@@ -20,7 +20,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaveSize = 64;
-constexpr int kThreads = 256;  // 4 waves per workgroup
+constexpr int kThreads = 256;  // default workgroup: 4 waves
 
 // Byte offset past every extent the library accepts: a buffer load there
 // returns zeros (raw buffer range check), which is how ragged M/N/K edges
@@ -63,18 +63,20 @@ __device__ __forceinline__ void lds_write16(char* lds, uint32_t off, u32x4 v) {
 // row (coalesced); the swizzle permutes only the LDS destination.
 // ---------------------------------------------------------------------------
 
-// Direct global -> LDS loader for a K-major operand tile (Rows x 128 B).
+// Direct global -> LDS loader for a K-major operand tile (Rows x 128 B),
+// shared by the workgroup's Waves waves.
 // buffer_load_dwordx4 ... lds writes lane l's 16 bytes to LDS at M0 + 16*l,
 // so one instruction fills 1 KiB of LDS with no VGPR staging and no
-// ds_write.  The tile is cut into Rows/8 regions of 1 KiB; region r = 4*i +
-// wave.  Lane l of a region fills physical bytes [1 KiB*r + 16l, +16); the
-// swizzle is an involution, so it fetches the logical chunk whose swizzled
-// offset that is.  The XOR key of a line is (line index mod 16), the same for
-// every region a lane fills, so the lane's K chunk is fixed and its row
-// advances by 32 per region.
-template <int Rows, int Swz>
+// ds_write.  The tile is cut into Rows/8 regions of 1 KiB; region r =
+// Waves*i + wave.  Lane l of a region fills physical bytes [1 KiB*r + 16l,
+// +16); the swizzle is an involution, so it fetches the logical chunk whose
+// swizzled offset that is.  The XOR key of a 256-byte line is (line index
+// mod 16) and a region spans 4 lines, so regions Waves*i + wave share the key
+// for every i: the lane's K chunk is fixed and its row advances by 8*Waves.
+template <int Rows, int Swz, int Waves = 4>
 struct DmaLoader {
-  static constexpr int kSteps = Rows / 32;  // regions per wave
+  static constexpr int kSteps = Rows / (8 * Waves);  // regions per wave
+  static_assert(kSteps * 8 * Waves == Rows, "tile rows must fill the waves' regions");
   uint32_t base;    // row0 * pitch + 16 * chunk
   uint32_t chunk16; // 16 * chunk
   int row0;
@@ -100,10 +102,11 @@ struct DmaLoader {
     const bool k_ok = kbyte0 + chunk16 < kbytes_total;
 #pragma unroll
     for (int i = I0; i < (I1 < kSteps ? I1 : kSteps); ++i) {
-      const bool ok = k_ok && row0 + 32 * i < rows_valid;
-      const uint32_t off = ok ? base + (uint32_t)(32 * i) * pitch + kbyte0 : kOutOfRange;
+      const bool ok = k_ok && row0 + 8 * Waves * i < rows_valid;
+      const uint32_t off =
+          ok ? base + (uint32_t)(8 * Waves * i) * pitch + kbyte0 : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(lds + (4 * i + wave) * 1024), 16,
+          r, (__attribute__((address_space(3))) void*)(lds + (Waves * i + wave) * 1024), 16,
           off, 0, 0, 0);
     }
   }
@@ -157,13 +160,13 @@ struct MNMajorLoader {
 // reads of one K tile into an LDS tile, commit() finishes it (a no-op for the
 // direct-to-LDS path, the transposed ds_writes for MN-major sources).
 // ElemBytes = 2 for fp16/bf16, 1 for fp8.
-template <int Rows, bool Mn, int Swz, int ElemBytes>
+template <int Rows, bool Mn, int Swz, int ElemBytes, int Waves = 4>
 struct OperandLoader;
 
-template <int Rows, int Swz, int ElemBytes>
-struct OperandLoader<Rows, false, Swz, ElemBytes> {
-  static constexpr int kIssues = DmaLoader<Rows, Swz>::kSteps;  // loads per thread
-  DmaLoader<Rows, Swz> d;
+template <int Rows, int Swz, int ElemBytes, int Waves>
+struct OperandLoader<Rows, false, Swz, ElemBytes, Waves> {
+  static constexpr int kIssues = DmaLoader<Rows, Swz, Waves>::kSteps;  // loads per thread
+  DmaLoader<Rows, Swz, Waves> d;
   __device__ __forceinline__ void init(int tid, uint32_t pitch) {
     d.init(__builtin_amdgcn_readfirstlane(tid >> 6), tid & 63, pitch);
   }
@@ -177,8 +180,8 @@ struct OperandLoader<Rows, false, Swz, ElemBytes> {
   __device__ __forceinline__ void commit(char*, int) const {}
 };
 
-template <int Rows, int Swz, int ElemBytes>
-struct OperandLoader<Rows, true, Swz, ElemBytes> {
+template <int Rows, int Swz, int ElemBytes, int Waves>
+struct OperandLoader<Rows, true, Swz, ElemBytes, Waves> {
   static_assert(ElemBytes == 2, "MN-major sources are 16-bit");
   static constexpr int kIssues = 1;  // one batch of register loads
   MNMajorLoader<Rows> m;

@@ -89,19 +89,24 @@ struct TileJob {
   int64_t n0;           // first output column
 };
 
-template <int BM, int BN, bool IsBF16, bool AMn, bool BMn, int Swz>
+// Waves = 4: one wave per SIMD, each wave owns a (BM/2) x (BN/2) block.
+// Waves = 8: two waves per SIMD (the hardware interleaves them, and twice as
+// many waves issue the direct-to-LDS loads), each owning (BM/2) x (BN/4).
+template <int BM, int BN, bool IsBF16, bool AMn, bool BMn, int Swz, int Waves = 4>
 struct GemmTile {
   static constexpr int kBK = 64;            // K elements per stage
   static constexpr int kRowBytes = 128;     // kBK * 2 bytes
   static constexpr int kATileBytes = BM * kRowBytes;
   static constexpr int kBTileBytes = BN * kRowBytes;
   static constexpr int kStageBytes = kATileBytes + kBTileBytes;
-  static constexpr int kWM = BM / 2, kWN = BN / 2;  // per-wave block
+  static constexpr int kWavesN = Waves / 2;         // waves along N (2 along M)
+  static constexpr int kWM = BM / 2, kWN = BN / kWavesN;  // per-wave block
   static constexpr int kFM = kWM / 32, kFN = kWN / 32;
   static_assert(kStageBytes % 4096 == 0, "stage bases must keep the swizzle phase");
+  static_assert(kFM >= 1 && kFN >= 1, "each wave needs at least one 32x32 block");
 
-  using ALoader = OperandLoader<BM, AMn, Swz, 2>;
-  using BLoader = OperandLoader<BN, BMn, Swz, 2>;
+  using ALoader = OperandLoader<BM, AMn, Swz, 2, Waves>;
+  using BLoader = OperandLoader<BN, BMn, Swz, 2, Waves>;
 
   // Fragments of one 16-wide K step: lane l holds row l%32 of each 32-row
   // fragment and K chunk 2*kk + l/32.
@@ -175,16 +180,20 @@ struct GemmTile {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // Loads of the next K tile issued during 16-wide K step `kk` (1..3): the
-  // tile's direct-to-LDS loads are spread over the three steps that run
-  // before the barrier, so that the vector-memory path is never asked for
-  // more than about half a K tile's worth per step (issuing them all in one
-  // step stalls the wave on a full load queue and drains the MFMA pipe).
+  // Loads of the next K tile issued during 16-wide K step `kk` (1..3).  With
+  // one wave per SIMD the tile's direct-to-LDS loads are spread over the
+  // three steps that run before the barrier (issuing them all in one step
+  // stalls the wave on a full load queue and drains the MFMA pipe).  With two
+  // waves per SIMD each wave has half as many loads and the other wave keeps
+  // the matrix core busy, so they go out at the start of the tile, which
+  // gives them the most time to land (measured faster at 8192^3).
   template <int Loader, int KK>
   struct Share {
     static constexpr int kA = ALoader::kIssues, kB = BLoader::kIssues;
     static constexpr int kTotal = kA + kB;
-    static constexpr int begin = kTotal * (KK - 1) / 3, end = kTotal * KK / 3;
+    static constexpr int kSpread = Waves == 8 ? 1 : 3;  // steps the loads cover
+    static constexpr int begin = KK > kSpread ? kTotal : kTotal * (KK - 1) / kSpread;
+    static constexpr int end = KK >= kSpread ? kTotal : kTotal * KK / kSpread;
     // Range of this loader's own issue indices inside [begin, end).
     static constexpr int lo = Loader == 0 ? (begin < kA ? begin : kA) : (begin > kA ? begin - kA : 0);
     static constexpr int hi = Loader == 0 ? (end < kA ? end : kA) : (end > kA ? end - kA : 0);
@@ -259,7 +268,7 @@ struct GemmTile {
     // The wave index is uniform across the wave; readfirstlane lets the
     // compiler keep it (and every LDS base derived from it) in SGPRs.
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
     const int lrow = lane & 31, lhalf = lane >> 5;
 
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(j.a, j.a_bytes);
@@ -363,10 +372,10 @@ struct GemmTile {
   }
 };
 
-template <int BM, int BN, bool IsBF16, bool AMn, bool BMn, int Swz>
-__global__ void __launch_bounds__(kThreads, 1)
+template <int BM, int BN, bool IsBF16, bool AMn, bool BMn, int Swz, int Waves>
+__global__ void __launch_bounds__(64 * Waves, 1)
     dense_gemm_kernel(const DenseParams p) {
-  using Tile = GemmTile<BM, BN, IsBF16, AMn, BMn, Swz>;
+  using Tile = GemmTile<BM, BN, IsBF16, AMn, BMn, Swz, Waves>;
   __shared__ __attribute__((aligned(4096))) char s0[Tile::kStageBytes];
   __shared__ __attribute__((aligned(4096))) char s1[Tile::kStageBytes];
 
@@ -403,10 +412,10 @@ __global__ void __launch_bounds__(kThreads, 1)
   Tile::run(s0, s1, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.N);
 }
 
-template <int BM, int BN, bool IsBF16, int Swz>
-__global__ void __launch_bounds__(kThreads, 1)
+template <int BM, int BN, bool IsBF16, int Swz, int Waves>
+__global__ void __launch_bounds__(64 * Waves, 1)
     grouped_gemm_kernel(const GroupedParams p) {
-  using Tile = GemmTile<BM, BN, IsBF16, false, false, Swz>;
+  using Tile = GemmTile<BM, BN, IsBF16, false, false, Swz, Waves>;
   __shared__ __attribute__((aligned(4096))) char s0[Tile::kStageBytes];
   __shared__ __attribute__((aligned(4096))) char s1[Tile::kStageBytes];
 

@@ -6,11 +6,18 @@ namespace sg {
 
 namespace {
 
+// 256x256 tiles with K-major operands run with 8 waves (two per SIMD);
+// 128x128 tiles, and tiles with MN-major operands (whose register
+// transposes need the registers of a one-wave-per-SIMD layout), with 4.
+template <int BM, bool AMn, bool BMn>
+constexpr int waves_for() { return BM == 256 && !AMn && !BMn ? 8 : 4; }
+
 template <int BM, int BN, bool BF, bool AMn, bool BMn, int Swz>
 hipError_t go_dense(const DenseParams& p, hipStream_t s) {
   const int grid = p.tiles_m * p.tiles_n;
-  hipLaunchKernelGGL((dense_gemm_kernel<BM, BN, BF, AMn, BMn, Swz>), dim3(grid),
-                     dim3(kThreads), 0, s, p);
+  constexpr int W = waves_for<BM, AMn, BMn>();
+  hipLaunchKernelGGL((dense_gemm_kernel<BM, BN, BF, AMn, BMn, Swz, W>), dim3(grid),
+                     dim3(64 * W), 0, s, p);
   return hipGetLastError();
 }
 
@@ -49,18 +56,18 @@ hipError_t launch_grouped(TileShape tile, bool bf16, int swz, const GroupedParam
   if (swz != 16) return hipErrorInvalidValue;
   if (tile == kTile256) {
     if (bf16)
-      hipLaunchKernelGGL((grouped_gemm_kernel<256, 256, true, 16>), dim3(grid),
-                         dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((grouped_gemm_kernel<256, 256, true, 16, 8>), dim3(grid),
+                         dim3(64 * 8), 0, s, p);
     else
-      hipLaunchKernelGGL((grouped_gemm_kernel<256, 256, false, 16>), dim3(grid),
-                         dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((grouped_gemm_kernel<256, 256, false, 16, 8>), dim3(grid),
+                         dim3(64 * 8), 0, s, p);
   } else {
     if (bf16)
-      hipLaunchKernelGGL((grouped_gemm_kernel<128, 128, true, 16>), dim3(grid),
-                         dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((grouped_gemm_kernel<128, 128, true, 16, 4>), dim3(grid),
+                         dim3(64 * 4), 0, s, p);
     else
-      hipLaunchKernelGGL((grouped_gemm_kernel<128, 128, false, 16>), dim3(grid),
-                         dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((grouped_gemm_kernel<128, 128, false, 16, 4>), dim3(grid),
+                         dim3(64 * 4), 0, s, p);
   }
   return hipGetLastError();
 }
