@@ -167,9 +167,13 @@ def cpu_baseline(oracle_sample, rows_total, target_s=12.0):
     cores = oracle.default_threads()
     rows = min(32, rows_total)
     t, fl = oracle_sample(rows)
-    rows2 = int(min(rows_total, max(rows, rows * target_s / max(t, 1e-3))))
-    rows2 = max(cores, rows2 - rows2 % cores) if rows_total >= cores else rows2
-    if rows2 > rows:
+    # Small samples under-use the threads, so the first estimate runs short:
+    # grow the sample until it takes at least ~2/3 of the target.
+    for _ in range(4):
+        if t >= 0.66 * target_s or rows >= rows_total:
+            break
+        rows2 = int(min(rows_total, max(2 * rows, rows * target_s / max(t, 1e-3))))
+        rows2 = max(cores, rows2 - rows2 % cores) if rows2 >= cores else rows2
         t, fl = oracle_sample(rows2)
         rows = rows2
     return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
