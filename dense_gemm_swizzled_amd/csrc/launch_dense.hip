@@ -1,6 +1,7 @@
 // launch_dense.hip -- instantiations and launchers of the 16-bit dense and
 // grouped kernels.
 #include "launch.h"
+#include "pingpong.h"
 
 namespace sg {
 
@@ -21,9 +22,18 @@ hipError_t go_dense(const DenseParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 256x256 tiles with both operands K-major run the ping-pong mainloop.
+template <bool BF, int Swz>
+hipError_t go_pingpong(const DenseParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((pingpong_gemm_kernel<BF, Swz>), dim3(p.tiles_m * p.tiles_n), dim3(512),
+                     0, s, p);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, bool BF, int Swz>
 hipError_t dense_by_major(bool a_mn, bool b_mn, const DenseParams& p, hipStream_t s) {
-  if (!a_mn && !b_mn) return go_dense<BM, BN, BF, false, false, Swz>(p, s);
+  if (!a_mn && !b_mn)
+    return BM == 256 ? go_pingpong<BF, Swz>(p, s) : go_dense<BM, BN, BF, false, false, Swz>(p, s);
   if (!a_mn && b_mn) return go_dense<BM, BN, BF, false, true, Swz>(p, s);
   if (a_mn && !b_mn) return go_dense<BM, BN, BF, true, false, Swz>(p, s);
   return go_dense<BM, BN, BF, true, true, Swz>(p, s);
