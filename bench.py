@@ -184,8 +184,8 @@ def cpu_baseline(oracle_sample, rows_total, target_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="dense_8192",
                     choices=["dense_8192", "grouped", "mxfp8", "dense_1024", "single_tile",
                              "copy"])

@@ -372,15 +372,12 @@ struct GemmTile {
   }
 };
 
-template <int BM, int BN, bool IsBF16, bool AMn, bool BMn, int Swz, int Waves>
-__global__ void __launch_bounds__(64 * Waves, 1)
-    dense_gemm_kernel(const DenseParams p) {
-  using Tile = GemmTile<BM, BN, IsBF16, AMn, BMn, Swz, Waves>;
-  __shared__ __attribute__((aligned(4096))) char s0[Tile::kStageBytes];
-  __shared__ __attribute__((aligned(4096))) char s1[Tile::kStageBytes];
-
+// Workgroup -> output tile of the dense GEMM and the operand panels it
+// reads (XCD-aware remap, then the GROUP_M raster).
+template <int BM, int BN, bool AMn, bool BMn>
+__device__ __forceinline__ TileJob dense_tile_job(const DenseParams& p, int wg) {
   const int total = p.tiles_m * p.tiles_n;
-  const int t = xcd_remap(blockIdx.x, total);
+  const int t = xcd_remap(wg, total);
   int tm, tn;
   raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -409,18 +406,15 @@ __global__ void __launch_bounds__(64 * Waves, 1)
   }
   j.d_row0 = m0;
   j.n0 = n0;
-  Tile::run(s0, s1, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.N);
+  return j;
 }
 
-template <int BM, int BN, bool IsBF16, int Swz, int Waves>
-__global__ void __launch_bounds__(64 * Waves, 1)
-    grouped_gemm_kernel(const GroupedParams p) {
-  using Tile = GemmTile<BM, BN, IsBF16, false, false, Swz, Waves>;
-  __shared__ __attribute__((aligned(4096))) char s0[Tile::kStageBytes];
-  __shared__ __attribute__((aligned(4096))) char s1[Tile::kStageBytes];
-
+// Workgroup -> (group, output tile) of the grouped GEMM (A rows of group g
+// are [m_off[g], m_off[g+1]), B of group g is [N][K] at g*N*K).
+template <int BM, int BN>
+__device__ __forceinline__ TileJob grouped_tile_job(const GroupedParams& p, int wg) {
   const int total = p.tile_start[p.G];
-  const int t = xcd_remap(blockIdx.x, total);
+  const int t = xcd_remap(wg, total);
   // Group of tile t: the last g with tile_start[g] <= t (binary search).
   int lo = 0, hi = p.G - 1;
   while (lo < hi) {
@@ -446,6 +440,28 @@ __global__ void __launch_bounds__(64 * Waves, 1)
   j.b_bytes = (uint32_t)(j.n_valid * p.K * es);
   j.d_row0 = p.m_off[g] + m0;
   j.n0 = n0;
+  return j;
+}
+
+template <int BM, int BN, bool IsBF16, bool AMn, bool BMn, int Swz, int Waves>
+__global__ void __launch_bounds__(64 * Waves, 1)
+    dense_gemm_kernel(const DenseParams p) {
+  using Tile = GemmTile<BM, BN, IsBF16, AMn, BMn, Swz, Waves>;
+  __shared__ __attribute__((aligned(4096))) char s0[Tile::kStageBytes];
+  __shared__ __attribute__((aligned(4096))) char s1[Tile::kStageBytes];
+
+  const TileJob j = dense_tile_job<BM, BN, AMn, BMn>(p, blockIdx.x);
+  Tile::run(s0, s1, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.N);
+}
+
+template <int BM, int BN, bool IsBF16, int Swz, int Waves>
+__global__ void __launch_bounds__(64 * Waves, 1)
+    grouped_gemm_kernel(const GroupedParams p) {
+  using Tile = GemmTile<BM, BN, IsBF16, false, false, Swz, Waves>;
+  __shared__ __attribute__((aligned(4096))) char s0[Tile::kStageBytes];
+  __shared__ __attribute__((aligned(4096))) char s1[Tile::kStageBytes];
+
+  const TileJob j = grouped_tile_job<BM, BN>(p, blockIdx.x);
   Tile::run(s0, s1, j, p.K, nullptr, SG_NONE, p.D, p.d_dtype, p.N);
 }
 

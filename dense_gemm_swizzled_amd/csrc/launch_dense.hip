@@ -66,11 +66,9 @@ hipError_t launch_grouped(TileShape tile, bool bf16, int swz, const GroupedParam
   if (swz != 16) return hipErrorInvalidValue;
   if (tile == kTile256) {
     if (bf16)
-      hipLaunchKernelGGL((grouped_gemm_kernel<256, 256, true, 16, 8>), dim3(grid),
-                         dim3(64 * 8), 0, s, p);
+      hipLaunchKernelGGL((pingpong_grouped_kernel<true, 16>), dim3(grid), dim3(512), 0, s, p);
     else
-      hipLaunchKernelGGL((grouped_gemm_kernel<256, 256, false, 16, 8>), dim3(grid),
-                         dim3(64 * 8), 0, s, p);
+      hipLaunchKernelGGL((pingpong_grouped_kernel<false, 16>), dim3(grid), dim3(512), 0, s, p);
   } else {
     if (bf16)
       hipLaunchKernelGGL((grouped_gemm_kernel<128, 128, true, 16, 4>), dim3(grid),

@@ -253,25 +253,16 @@ template <bool IsBF16, int Swz>
 __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(const DenseParams p) {
   using Tile = PingPongTile<IsBF16, Swz>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
-
-  const int total = p.tiles_m * p.tiles_n;
-  const int t = xcd_remap(blockIdx.x, total);
-  int tm, tn;
-  raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-  const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
-
-  TileJob j;
-  j.m_valid = (int)min<int64_t>(256, p.M - m0);
-  j.n_valid = (int)min<int64_t>(256, p.N - n0);
-  j.a = static_cast<const char*>(p.A) + m0 * p.K * 2;
-  j.a_pitch = (uint32_t)(p.K * 2);
-  j.a_bytes = (uint32_t)(j.m_valid * p.K * 2);
-  j.b = static_cast<const char*>(p.B) + n0 * p.K * 2;
-  j.b_pitch = (uint32_t)(p.K * 2);
-  j.b_bytes = (uint32_t)(j.n_valid * p.K * 2);
-  j.d_row0 = m0;
-  j.n0 = n0;
+  const TileJob j = dense_tile_job<256, 256, false, false>(p, blockIdx.x);
   Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.N);
+}
+
+template <bool IsBF16, int Swz>
+__global__ void __launch_bounds__(512, 1) pingpong_grouped_kernel(const GroupedParams p) {
+  using Tile = PingPongTile<IsBF16, Swz>;
+  __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+  const TileJob j = grouped_tile_job<256, 256>(p, blockIdx.x);
+  Tile::run(smem, j, p.K, nullptr, SG_NONE, p.D, p.d_dtype, p.N);
 }
 
 }  // namespace sg
