@@ -1,13 +1,13 @@
 // launch_mx.hip -- MXFP8 kernel launchers and the LDS-image debug kernel.
 #include "launch.h"
+#include "pingpong.h"
 
 namespace sg {
 
 hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s) {
   const int grid = p.tiles_m * p.tiles_n;
   if (tile == kTile256)
-    hipLaunchKernelGGL((mx_gemm_kernel<256, 256, kSwzDefault>), dim3(grid),
-                       dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault>), dim3(grid), dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL((mx_gemm_kernel<128, 128, kSwzDefault>), dim3(grid),
                        dim3(kThreads), 0, s, p);

@@ -31,6 +31,7 @@
 #pragma once
 
 #include "gemm_kernels.h"
+#include "mx_kernels.h"
 
 namespace sg {
 
@@ -47,6 +48,18 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t voff, uint32_t lds) {
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %0, %2, 0 offen lds"
+      :
+      : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// buffer_load_dword ... lds: lane l's 4 bytes at byte `voff` go to LDS
+// address m0 + 4 l.
+__device__ __forceinline__ void dma4(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %2, 0 offen lds"
       :
       : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(rsrc)
       : "memory", "m0");
@@ -263,6 +276,247 @@ __global__ void __launch_bounds__(512, 1) pingpong_grouped_kernel(const GroupedP
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
   const TileJob j = grouped_tile_job<256, 256>(p, blockIdx.x);
   Tile::run(smem, j, p.K, nullptr, SG_NONE, p.D, p.d_dtype, p.N);
+}
+
+}  // namespace sg
+
+namespace sg {
+
+// The ping-pong mainloop for the block-scaled (MXFP8) GEMM: e4m3 operands,
+// 128 elements (= 128 bytes, four 32-element scale blocks) of K per tile, so
+// the operand halves have exactly the geometry of the 16-bit kernel's.  A
+// phase is one 64-wide K step: eight v_mfma_scale_f32_32x32x64_f8f6f4 of the
+// wave's 4x2 blocks (the same 512 cycles as sixteen 16-bit MFMAs).
+//
+// LDS (148 KiB): A ring of two tiles, B ring of two tiles, a ring of two
+// tiles of scales (the e8m0 dwords of the tile's 256 A rows, then of its 256
+// B rows), all filled by direct-to-LDS loads so every wait is explicit, and
+// a 16 KiB sink.  Each group loads the scales of its own 128 rows of A and of
+// B with one 4-byte-per-lane load per wave.  Schedule (phases 4t..4t+3 of
+// tile t; group 1 one phase behind):
+//   group 0: B_lo(t+1) in its first memory phase of tile t; A_lo(t+2) and
+//            its scales during its second compute phase of tile t;
+//   group 1: A_hi(t+2), its scales and B_hi(t+2) during its second compute
+//            phase of tile t.
+// A slot t mod 2 is free once its group's second memory phase of tile t is
+// over, B slot t mod 2 once both groups' are; every load has three to five
+// phases to land.  Both groups run the same instruction stream: the B loads
+// one group skips are issued out of range into the sink (zero fill, no
+// memory traffic), so the code has no group-dependent branch (the compiler
+// moves MFMAs across such branches, and with them across the barriers).
+template <int Swz>
+struct PingPongMxTile {
+  using Base = GemmTile<256, 256, true, false, false, Swz, 8>;
+  static constexpr int kHalfBytes = 16384;
+  static constexpr int kTileBytes = 2 * kHalfBytes;
+  static constexpr int kBK = 128;                          // e4m3 elements (bytes)
+  static constexpr int kScaleBytes = 2048;                 // 256 A + 256 B dwords
+  static constexpr int kBOff = 2 * kTileBytes, kSOff = 4 * kTileBytes;
+  static constexpr int kSinkOff = kSOff + 2 * kScaleBytes;
+  static constexpr int kLdsBytes = kSinkOff + kHalfBytes;  // 148 KiB
+  static constexpr int kFM = 4, kFN = 2;
+
+  // Fragments of one 64-wide K step: per block two 16-byte chunks.
+  struct Frags {
+    u32x4 a[kFM][2], b[kFN][2];
+  };
+
+  struct Offsets {
+    uint32_t a[2][2], b[2][2];  // [kk][chunk pair]
+  };
+
+  // Lane half h supplies chunk 4kk + h (block 2kk) and chunk 4kk + 2 + h
+  // (block 2kk + 1) of the 64-wide step kk.
+  __device__ __forceinline__ static Offsets offsets(int g, int w4, int lrow, int lhalf) {
+    Offsets o;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t c = 4 * kk + 2 * h + lhalf;
+        o.a[kk][h] = g * kHalfBytes + lds_offset<128, Swz>(lrow, c);
+        o.b[kk][h] = (w4 >> 1) * kHalfBytes + lds_offset<128, Swz>((w4 & 1) * 64 + lrow, c);
+      }
+    return o;
+  }
+
+  __device__ __forceinline__ static void read(Frags& f, const char* at, const char* bt,
+                                              const Offsets& o, int kk) {
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) f.a[fm][h] = lds_read16(at, o.a[kk][h] + fm * 4096);
+#pragma unroll
+    for (int fn = 0; fn < kFN; ++fn)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) f.b[fn][h] = lds_read16(bt, o.b[kk][h] + fn * 4096);
+  }
+
+  // The scale dwords of the wave's rows; the lane's block (lane half) is
+  // shifted into the even bytes so that op-select 2kk picks block 2kk + h.
+  __device__ __forceinline__ static void read_scales(uint32_t (&sa)[kFM], uint32_t (&sb)[kFN],
+                                                     const char* s, int g, int w4, int lrow,
+                                                     int lhalf) {
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm)
+      sa[fm] = *reinterpret_cast<const uint32_t*>(s + 4 * (128 * g + 32 * fm + lrow)) >>
+               (8 * lhalf);
+#pragma unroll
+    for (int fn = 0; fn < kFN; ++fn)
+      sb[fn] = *reinterpret_cast<const uint32_t*>(s + 1024 + 4 * (64 * w4 + 32 * fn + lrow)) >>
+               (8 * lhalf);
+  }
+
+  // 8 scaled MFMAs; N loads (given by `issue(q)`) go out between them.
+  template <int N, class Issue>
+  __device__ __forceinline__ static void compute(f32x16 (&acc)[kFM][kFN], const Frags& f,
+                                                 const uint32_t (&sa)[kFM],
+                                                 const uint32_t (&sb)[kFN], int kk,
+                                                 const Issue& issue) {
+#pragma unroll
+    for (int m = 0; m < kFM * kFN; ++m) {
+      const int fm = m >> 1, fn = m & 1;
+      acc[fm][fn] = mfma_scale_f8(f.b[fn], f.a[fm], acc[fm][fn], sb[fn], sa[fm], kk);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (N > 0) {
+        if (m < N) issue(m);
+        if (m + 8 < N) issue(m + 8);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  __device__ __forceinline__ static void barrier() { PingPongTile<true, Swz>::barrier(); }
+
+  __device__ __forceinline__ static void run(char* smem, const TileJob& j, const char* sfa,
+                                             const char* sfb, int64_t K, void* D,
+                                             int d_dtype, int64_t ldd) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = wave >> 2, w4 = wave & 3;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+
+    const uint32_t sf_pitch = (uint32_t)(K / 32);
+    const u32x4 ra = rsrc_words(j.a, j.a_bytes), rb = rsrc_words(j.b, j.b_bytes);
+    const u32x4 rsa = rsrc_words(sfa, (uint32_t)j.m_valid * sf_pitch);
+    const u32x4 rsb = rsrc_words(sfb, (uint32_t)j.n_valid * sf_pitch);
+    const int a_rows = j.m_valid - 128 * g, b_rows = j.n_valid - 128 * g;
+    HalfLoader<Swz> la, lb;
+    la.init(w4, lane, j.a_pitch);
+    lb.init(w4, lane, j.b_pitch);
+    la.base += (uint32_t)(128 * g) * j.a_pitch;
+    lb.base += (uint32_t)(128 * g) * j.b_pitch;
+    // Scales: wave w4 of group g loads the dwords of rows 128g + 64(w4&1)
+    // + lane of A (w4 < 2) or B (w4 >= 2).
+    const int s_row = 128 * g + 64 * (w4 & 1) + lane;
+    const bool s_is_b = w4 >= 2;
+    const u32x4 rs = s_is_b ? rsb : rsa;
+    const int s_valid = s_is_b ? j.n_valid : j.m_valid;
+    const uint32_t s_lds_off = (s_is_b ? 1024u : 0u) + 4u * (uint32_t)(128 * g + 64 * (w4 & 1));
+
+    const uint32_t s0 = lds_addr(smem);
+    const uint32_t a_ring = s0 + g * kHalfBytes, b_ring = s0 + kBOff + g * kHalfBytes;
+    const uint32_t s_ring = s0 + kSOff + s_lds_off;
+    const uint32_t kbytes = (uint32_t)K;
+    const int T = (int)(K / kBK);
+
+    auto ld_a = [&](int t, int i) {
+      la.issue(ra, a_ring + (t & 1) * kTileBytes, w4, i, a_rows, (uint32_t)t * 128u, kbytes);
+    };
+    // B half of tile t when `real`, else an out-of-range load into the sink.
+    const uint32_t sink = s0 + kSinkOff;
+    auto ld_b = [&](int t, int i, bool real) {
+      lb.issue(rb, real ? b_ring + (t & 1) * kTileBytes : sink, w4, i, real ? b_rows : 0,
+               (uint32_t)t * 128u, kbytes);
+    };
+    auto ld_s = [&](int t) {
+      const bool ok = t < T && s_row < s_valid;
+      dma4(rs, ok ? (uint32_t)s_row * sf_pitch + 4u * (uint32_t)t : kOutOfRange,
+           s_ring + (t & 1) * kScaleBytes);
+    };
+
+    // Prologue: tile 0 whole and A(1) with its scales; group 1 also B_hi(1)
+    // (group 0 loads B_lo(1) in its first memory phase).  Per wave: 9 + 9.
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ld_a(t, i);
+      ld_s(t);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ld_b(t, i, t == 0 || g);
+    }
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0 has landed
+    barrier();
+
+    const Offsets o = offsets(g, w4, lrow, lhalf);
+    f32x16 acc[kFM][kFN];
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int k = 0; k < kFN; ++k) acc[i][k] = f32x16{};
+
+    if (g) barrier();  // group 1 runs one phase behind group 0
+    for (int t = 0; t < T; ++t) {
+      const char* at = smem + (t & 1) * kTileBytes;
+      const char* bt = smem + kBOff + (t & 1) * kTileBytes;
+      const char* st = smem + kSOff + (t & 1) * kScaleBytes;
+      Frags f;
+      uint32_t sa[kFM], sb[kFN];
+      // Memory phase, first K step; then B_lo(t+1) (group 0).
+      read(f, at, bt, o, 0);
+      read_scales(sa, sb, st, g, w4, lrow, lhalf);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ld_b(t + 1, i, !g);
+      barrier();
+      compute<0>(acc, f, sa, sb, 0, [&](int) {});
+      barrier();
+      // Memory phase, second K step.  Of the wave's loads only the 4 newest
+      // (the B loads just issued) may still be in flight: group 1's share of
+      // tile t+1 is then in LDS before the barrier that lets group 0 read it.
+      read(f, at, bt, o, 1);
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+      barrier();
+      // Compute phase, second K step, with the loads of tile t+2: A half,
+      // scales, B half (group 1).  Afterwards only those 9 may be in flight:
+      // group 0's share of tile t+1 has landed.
+      compute<9>(acc, f, sa, sb, 1, [&](int q) {
+        if (q < 4) ld_a(t + 2, q);
+        else if (q == 4) ld_s(t + 2);
+        else ld_b(t + 2, q - 5, g != 0);
+      });
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      barrier();
+    }
+    if (!g) barrier();
+    wait_vmem();
+
+    Base::epilogue(acc, j, nullptr, SG_NONE, D, d_dtype, ldd, lane, g, w4);
+  }
+};
+
+template <int Swz>
+__global__ void __launch_bounds__(512, 1) pingpong_mx_kernel(const MxParams p) {
+  using Tile = PingPongMxTile<Swz>;
+  __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+  const int total = p.tiles_m * p.tiles_n;
+  const int t = xcd_remap(blockIdx.x, total);
+  int tm, tn;
+  raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
+  TileJob j;
+  j.m_valid = (int)min<int64_t>(256, p.M - m0);
+  j.n_valid = (int)min<int64_t>(256, p.N - n0);
+  j.a = static_cast<const char*>(p.A) + m0 * p.K;
+  j.a_pitch = (uint32_t)p.K;
+  j.a_bytes = (uint32_t)(j.m_valid * p.K);
+  j.b = static_cast<const char*>(p.B) + n0 * p.K;
+  j.b_pitch = (uint32_t)p.K;
+  j.b_bytes = (uint32_t)(j.n_valid * p.K);
+  j.d_row0 = m0;
+  j.n0 = n0;
+  Tile::run(smem, j, static_cast<const char*>(p.SFA) + m0 * (p.K / 32),
+            static_cast<const char*>(p.SFB) + n0 * (p.K / 32), p.K, p.D, p.d_dtype, p.N);
 }
 
 }  // namespace sg

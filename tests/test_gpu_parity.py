@@ -156,6 +156,19 @@ def test_dense_256_tiles_ragged(dev):
     check_close(_np(d), ref, bound, "bf16", "256 tiles")
 
 
+@pytest.mark.parametrize("K", [8, 64])
+def test_dense_256_tiles_single_k_tile(dev, K):
+    # 256x256 tiles with one (partial or whole) K tile: the ring's prologue
+    # already covers every load and the rest are zero-filled.
+    M, N = 4096, 4352
+    case = si.dense_case(M, N, K, 12 + K, ab_dtype="bf16", with_c=True, c_dtype="f32",
+                         d_dtype="f32", scale=1.0 / np.sqrt(K))
+    say(f"dense 256-tile path {M}x{N}x{K}")
+    d = run_dense(case, dev)
+    ref, bound = oracle_dense(case)
+    check_close(_np(d), ref, bound, "f32", f"256 tiles K={K}")
+
+
 def test_dense_integer_inputs_exact(dev):
     # Integer values in [-4, 4]: every partial sum is exact in fp32, so the
     # result must be bit-exact whatever the summation order.
@@ -230,6 +243,19 @@ def test_grouped_small_with_empty_groups(dev):
     check_close(_np(d), ref, bound, "f32", "grouped small")
 
 
+def test_grouped_256_tiles_ragged(dev):
+    # Enough tiles for the 256x256 variant; group sizes off the tile grid,
+    # an empty group, and K = 3 * 64 + 8.
+    m_sizes = [300, 1, 0, 777, 2000, 513, 1200]
+    case = si.grouped_case(m_sizes, 4096, 200, 13, d_dtype="f32")
+    say(f"grouped 256-tile path {m_sizes} x 4096 x 200")
+    d = sg.grouped_gemm(case.A.to(dev), case.B.to(dev), case.m_offsets,
+                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, bound = oracle.grouped_gemm(case.m_offsets, case.N, case.K, case.A, case.B, "bf16")
+    check_close(_np(d), ref, bound, "f32", "grouped 256 tiles")
+
+
 def test_grouped_single_group_equals_dense(dev):
     case = si.grouped_case([300], 136, 72, 9, d_dtype="f32")
     say("grouped G=1 vs dense")
@@ -290,6 +316,20 @@ def test_mx_scales_wide_range_and_unit(dev):
     d = run_mx(case, dev, "f32")
     ref, bound = oracle.mx_gemm(M, N, K, case.A, case.SFA, case.B, case.SFB)
     check_close(_np(d), ref, bound, "f32", "mx unit scales")
+
+
+def test_mx_256_tiles_ragged(dev):
+    # 17 x 17 tiles of 256 (the 256x256 variant), ragged M and N, an odd
+    # number of 128-wide K tiles, scales spread over 2^-17 .. 2^17.
+    M, N, K = 4100, 4104, 384
+    case = si.mx_case(M, N, K, 19)
+    rng = np.random.default_rng(6)
+    case.SFA = torch.from_numpy(rng.integers(110, 145, (M, K // 32)).astype(np.uint8))
+    case.SFB = torch.from_numpy(rng.integers(110, 145, (N, K // 32)).astype(np.uint8))
+    say(f"mx 256-tile path {M}x{N}x{K}")
+    d = run_mx(case, dev, "f32")
+    ref, bound = oracle.mx_gemm(M, N, K, case.A, case.SFA, case.B, case.SFB)
+    check_close(_np(d), ref, bound, "f32", "mx 256 tiles")
 
 
 def test_mx_8192_full_size_sampled(dev):
