@@ -67,7 +67,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_workload(name: str, dev):
+def build_workload(name: str, dev, layout=None):
     """Returns (run callable, flops per step, dtype, config dict, oracle
     sample callable(rows) -> seconds, rows_total)."""
     import torch
@@ -83,13 +83,22 @@ def build_workload(name: str, dev):
         dt = {"f32": torch.float32, "bf16": torch.bfloat16}[case.d_dtype]
         D = torch.empty(case.M, case.N, dtype=dt, device=dev)
 
-        def run():
-            sg.gemm(A, B, a_major=case.a_major, b_major=case.b_major, C=C, out=D)
+        if layout is None:
+            def run():
+                sg.gemm(A, B, a_major=case.a_major, b_major=case.b_major, C=C, out=D)
+        else:
+            if case.ab_dtype != "bf16" or case.a_major != "k" or case.b_major != "k":
+                raise SystemExit("--layout needs a bf16 workload with K-major A and B")
+
+            def run():
+                sg.gemm_layout(A, B, layout, C=C, out=D)
 
         flops = 2.0 * case.M * case.N * case.K
         cfg = {"workload": case.name, "M": case.M, "N": case.N, "K": case.K,
                "a_major": case.a_major, "b_major": case.b_major,
                "ab_dtype": case.ab_dtype, "c": case.c_dtype, "d_dtype": case.d_dtype}
+        if layout is not None:
+            cfg["lds_layout"] = {16: "xor_256B_lines", 8: "xor_128B_lines", 0: "none"}[layout]
 
         def oracle_sample(rows):
             import oracle
@@ -190,6 +199,10 @@ def main():
                     choices=["dense_8192", "grouped", "mxfp8", "dense_1024", "single_tile",
                              "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", type=int, choices=[16, 8, 0], default=None,
+                    help="run the dense workload through gemm_layout_run with this LDS "
+                         "layout (16 = the library's XOR swizzle over 256-byte lines, "
+                         "8 = over 128-byte lines, 0 = none)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -199,7 +212,7 @@ def main():
     import torch
     dev = torch.device("cuda:0")
     log(f"[bench] workload {args.workload}: generating inputs")
-    run, flops, dtype, cfg, oracle_sample, rows_total = build_workload(args.workload, dev)
+    run, flops, dtype, cfg, oracle_sample, rows_total = build_workload(args.workload, dev, args.layout)
     stream = torch.cuda.current_stream(dev)
 
     log(f"[bench] warmup {args.warmup}")
@@ -255,7 +268,7 @@ def main():
         "pct_of_bf16_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(args.workload),
+                     "traffic": measured_traffic(args.workload) if args.layout is None else None,
                      "traffic_unit": "bytes per launch (HBM side)",
                      "kernel_ms_mean": round(mean_ms, 5),
                      "kernel_ms_median": round(median_ms, 5)},

@@ -24,9 +24,9 @@ import numpy as np
 __all__ = [
     "SG_OK", "SG_F16", "SG_BF16", "SG_F32", "SG_E4M3", "SG_E8M0", "SG_NONE",
     "SG_K_MAJOR", "SG_MN_MAJOR", "SG_MAX_GROUPS", "GemmError",
-    "gemm_run", "grouped_gemm_run", "mx_gemm_run", "gemm_last_error",
+    "gemm_run", "grouped_gemm_run", "mx_gemm_run", "gemm_layout_run", "gemm_last_error",
     "gemm_version", "gemm_lds_layout", "gemm_lds_image",
-    "gemm", "grouped_gemm", "mx_gemm", "library_path", "load",
+    "gemm", "grouped_gemm", "mx_gemm", "gemm_layout", "library_path", "load",
 ]
 
 SG_OK = 0
@@ -67,9 +67,10 @@ def load():
     lib.grouped_gemm_run.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), i64, i64, vp,
                                      i32, vp, i32, i32, vp, i32, vp]
     lib.mx_gemm_run.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
+    lib.gemm_layout_run.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, vp, i32, vp]
     lib.gemm_lds_layout.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int32)]
     lib.gemm_lds_image.argtypes = [vp, i64, i64, i32, i64, i64, i32, vp, vp]
-    for f in (lib.gemm_run, lib.grouped_gemm_run, lib.mx_gemm_run,
+    for f in (lib.gemm_run, lib.grouped_gemm_run, lib.mx_gemm_run, lib.gemm_layout_run,
               lib.gemm_lds_layout, lib.gemm_lds_image):
         f.restype = ctypes.c_int
     lib.gemm_last_error.argtypes = []
@@ -99,6 +100,10 @@ def grouped_gemm_run(G, m_offsets, N, K, A, a_major, B, b_major, ab_dtype, D,
 
 def mx_gemm_run(M, N, K, A, SFA, B, SFB, D, d_dtype, stream) -> int:
     return load().mx_gemm_run(M, N, K, A, SFA, B, SFB, D, d_dtype, stream)
+
+
+def gemm_layout_run(swz_units, M, N, K, A, B, C, c_dtype, D, d_dtype, stream) -> int:
+    return load().gemm_layout_run(swz_units, M, N, K, A, B, C, c_dtype, D, d_dtype, stream)
 
 
 def gemm_last_error() -> str:
@@ -170,6 +175,22 @@ def gemm(A, B, *, a_major: str = "k", b_major: str = "k", C=None,
                     C.data_ptr() if C is not None else None,
                     _dt(C.dtype) if C is not None else SG_NONE, out.data_ptr(),
                     _dt(out.dtype), _stream(A.device)))
+    return out
+
+
+def gemm_layout(A, B, swz_units: int, *, C=None, out_dtype=None, out=None):
+    """gemm() for bf16 K-major A [M][K] and B [N][K] on the 256x256-tile
+    kernel with the LDS layout swz_units (16 = the library's XOR swizzle
+    over 256-byte lines, 8 = over 128-byte lines, 0 = none)."""
+    import torch
+    M, K = A.shape
+    N = B.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=A.device)
+    _check(gemm_layout_run(swz_units, M, N, K, A.data_ptr(), B.data_ptr(),
+                           C.data_ptr() if C is not None else None,
+                           _dt(C.dtype) if C is not None else SG_NONE, out.data_ptr(),
+                           _dt(out.dtype), _stream(A.device)))
     return out
 
 

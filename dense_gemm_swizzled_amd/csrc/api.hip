@@ -71,56 +71,47 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(SG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* gemm_last_error(void) { return g_last_error.c_str(); }
-
-const char* gemm_version(void) {
-  return "swizzled_gemm 0.1 (gfx950; 16-bit MFMA 32x32x16, MXFP8 scaled MFMA "
-         "32x32x64; LDS XOR swizzle over 256-byte bank lines)";
-}
-
-int gemm_run(int64_t M, int64_t N, int64_t K, const void* A, int a_major,
-             const void* B, int b_major, int ab_dtype, const void* C, int c_dtype,
-             void* D, int d_dtype, void* stream) {
+// gemm_run and gemm_layout_run: validation, plan and launch.  swz is the
+// LDS layout (16 = the library's); force256 selects the 256x256 tiles
+// whatever the problem size.
+int dense_run(const char* who, int swz, bool force256, int64_t M, int64_t N, int64_t K,
+              const void* A, int a_major, const void* B, int b_major, int ab_dtype,
+              const void* C, int c_dtype, void* D, int d_dtype, void* stream) {
   if (M < 0 || N < 0 || K < 0)
-    return fail(SG_ERR_SHAPE, "gemm_run: negative size M=%lld N=%lld K=%lld",
+    return fail(SG_ERR_SHAPE, "%s: negative size M=%lld N=%lld K=%lld", who,
                 (long long)M, (long long)N, (long long)K);
   if (ab_dtype != SG_F16 && ab_dtype != SG_BF16)
-    return fail(SG_ERR_DTYPE, "gemm_run: ab_dtype %d is not SG_F16/SG_BF16", ab_dtype);
+    return fail(SG_ERR_DTYPE, "%s: ab_dtype %d is not SG_F16/SG_BF16", who, ab_dtype);
   if (!is_out_dtype(d_dtype))
-    return fail(SG_ERR_DTYPE, "gemm_run: d_dtype %d is not SG_F32/SG_BF16/SG_F16", d_dtype);
+    return fail(SG_ERR_DTYPE, "%s: d_dtype %d is not SG_F32/SG_BF16/SG_F16", who, d_dtype);
   if (C && !is_out_dtype(c_dtype))
-    return fail(SG_ERR_DTYPE, "gemm_run: c_dtype %d is not SG_F32/SG_BF16/SG_F16", c_dtype);
+    return fail(SG_ERR_DTYPE, "%s: c_dtype %d is not SG_F32/SG_BF16/SG_F16", who, c_dtype);
   if (C && C == D && c_dtype != d_dtype)
-    return fail(SG_ERR_DTYPE, "gemm_run: in-place C == D needs c_dtype == d_dtype");
+    return fail(SG_ERR_DTYPE, "%s: in-place C == D needs c_dtype == d_dtype", who);
   if ((a_major != SG_K_MAJOR && a_major != SG_MN_MAJOR) ||
       (b_major != SG_K_MAJOR && b_major != SG_MN_MAJOR))
-    return fail(SG_ERR_MAJOR, "gemm_run: majorness must be SG_K_MAJOR or SG_MN_MAJOR");
+    return fail(SG_ERR_MAJOR, "%s: majorness must be SG_K_MAJOR or SG_MN_MAJOR", who);
   if (M == 0 || N == 0) return ok();
-  if (!D) return fail(SG_ERR_NULL, "gemm_run: D is NULL");
-  if (K > 0 && (!A || !B)) return fail(SG_ERR_NULL, "gemm_run: A or B is NULL");
+  if (!D) return fail(SG_ERR_NULL, "%s: D is NULL", who);
+  if (K > 0 && (!A || !B)) return fail(SG_ERR_NULL, "%s: A or B is NULL", who);
   const int eb = 2, db = elem_bytes(d_dtype), cb = C ? elem_bytes(c_dtype) : 0;
   if ((K > 0 && (!aligned16(A) || !aligned16(B))) || !aligned16(D) || (C && !aligned16(C)))
-    return fail(SG_ERR_ALIGN, "gemm_run: every pointer must be 16-byte aligned");
+    return fail(SG_ERR_ALIGN, "%s: every pointer must be 16-byte aligned", who);
   const int64_t a_pitch = (a_major == SG_K_MAJOR ? K : M) * eb;
   const int64_t b_pitch = (b_major == SG_K_MAJOR ? K : N) * eb;
   if ((K > 0 && (a_pitch % 16 || b_pitch % 16)) || (N * db) % 16 || (C && (N * cb) % 16))
     return fail(SG_ERR_ALIGN,
-                "gemm_run: row pitches must be multiples of 16 bytes (A %lld, B %lld, "
-                "D %lld bytes)", (long long)a_pitch, (long long)b_pitch,
-                (long long)(N * db));
+                "%s: row pitches must be multiples of 16 bytes (A %lld, B %lld, D %lld bytes)",
+                who, (long long)a_pitch, (long long)b_pitch, (long long)(N * db));
   const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256);
-  const sg::TileShape tile = pick_tile(tiles256);
+  const sg::TileShape tile = force256 ? sg::kTile256 : pick_tile(tiles256);
   const int64_t T = tile == sg::kTile256 ? 256 : 128;
   if (panel_extent(a_major, M, K, T, eb) >= kMaxExtent ||
       panel_extent(b_major, N, K, T, eb) >= kMaxExtent)
-    return fail(SG_ERR_SHAPE, "gemm_run: an operand panel spans 2^31 bytes or more");
+    return fail(SG_ERR_SHAPE, "%s: an operand panel spans 2^31 bytes or more", who);
   const int64_t tiles_m = cdiv(M, T), tiles_n = cdiv(N, T);
   if (tiles_m * tiles_n >= kMaxExtent || tiles_m * tiles_n > 0x7fffffffLL)
-    return fail(SG_ERR_SHAPE, "gemm_run: too many tiles");
+    return fail(SG_ERR_SHAPE, "%s: too many tiles", who);
 
   sg::DenseParams p;
   p.A = A;
@@ -136,10 +127,37 @@ int gemm_run(int64_t M, int64_t N, int64_t K, const void* A, int a_major,
   p.tiles_n = (int)tiles_n;
   p.group_m = kGroupM;
   hipError_t e = sg::launch_dense(tile, ab_dtype == SG_BF16, a_major == SG_MN_MAJOR,
-                                  b_major == SG_MN_MAJOR, sg::kSwzDefault, p,
+                                  b_major == SG_MN_MAJOR, swz, p,
                                   static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "gemm_run launch");
+  if (e != hipSuccess) return hip_fail(e, who);
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gemm_last_error(void) { return g_last_error.c_str(); }
+
+const char* gemm_version(void) {
+  return "swizzled_gemm 0.1 (gfx950; 16-bit MFMA 32x32x16, MXFP8 scaled MFMA "
+         "32x32x64; LDS XOR swizzle over 256-byte bank lines)";
+}
+
+int gemm_run(int64_t M, int64_t N, int64_t K, const void* A, int a_major,
+             const void* B, int b_major, int ab_dtype, const void* C, int c_dtype,
+             void* D, int d_dtype, void* stream) {
+  return dense_run("gemm_run", sg::kSwzDefault, false, M, N, K, A, a_major, B, b_major,
+                   ab_dtype, C, c_dtype, D, d_dtype, stream);
+}
+
+int gemm_layout_run(int swz_units, int64_t M, int64_t N, int64_t K, const void* A,
+                    const void* B, const void* C, int c_dtype, void* D, int d_dtype,
+                    void* stream) {
+  if (swz_units != 0 && swz_units != 8 && swz_units != 16)
+    return fail(SG_ERR_SHAPE, "gemm_layout_run: swz_units %d is not 0, 8 or 16", swz_units);
+  return dense_run("gemm_layout_run", swz_units, true, M, N, K, A, SG_K_MAJOR, B, SG_K_MAJOR,
+                   SG_BF16, C, c_dtype, D, d_dtype, stream);
 }
 
 int grouped_gemm_run(int G, const int64_t* m_offsets, int64_t N, int64_t K,

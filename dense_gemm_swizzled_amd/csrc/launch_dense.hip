@@ -54,10 +54,10 @@ hipError_t launch_dense(TileShape tile, bool bf16, bool a_mn, bool b_mn, int swz
     return tile == kTile256 ? dense_by_dtype<256, 256, 16>(bf16, a_mn, b_mn, p, s)
                             : dense_by_dtype<128, 128, 16>(bf16, a_mn, b_mn, p, s);
   }
-  // Layout ablation variants: bf16, K-major operands, 256x256 tiles only.
+  // Layout ablation variants: bf16, K-major operands, 256x256 ping-pong tiles.
   if (tile != kTile256 || !bf16 || a_mn || b_mn) return hipErrorInvalidValue;
-  if (swz == 8) return go_dense<256, 256, true, false, false, 8>(p, s);
-  if (swz == 0) return go_dense<256, 256, true, false, false, 0>(p, s);
+  if (swz == 8) return go_pingpong<true, 8>(p, s);
+  if (swz == 0) return go_pingpong<true, 0>(p, s);
   return hipErrorInvalidValue;
 }
 

@@ -127,6 +127,23 @@ int mx_gemm_run(int64_t M, int64_t N, int64_t K, const void* A,
                 const void* SFA, const void* B, const void* SFB, void* D,
                 int d_dtype, void* stream);
 
+/*
+ * gemm_layout_run -- gemm_run's bf16 GEMM with A and B K-major (and optional
+ * C) on the 256x256-tile kernel, with a chosen LDS operand layout: the layout
+ * experiment of "Swizzling explained properly" (sections "Why swizzle?" and
+ * "Results") on gfx950.
+ *   swz_units  16: the library's layout (the 16-byte unit index XORed with
+ *              the 256-byte bank-line index: ds_read_b128 reads 64 banks of
+ *              4 bytes); 8: the same XOR over 128-byte lines; 0: no swizzle.
+ * Every layout gives the same D; only LDS bank conflicts and speed differ.
+ * The other arguments are gemm_run's (ab_dtype = SG_BF16, both operands
+ * SG_K_MAJOR).  Errors: as gemm_run, and SG_ERR_SHAPE for swz_units not in
+ * {0, 8, 16}.
+ */
+int gemm_layout_run(int swz_units, int64_t M, int64_t N, int64_t K, const void* A,
+                    const void* B, const void* C, int c_dtype, void* D, int d_dtype,
+                    void* stream);
+
 /* Thread-local text of the last failing call ("" if none).  Never NULL. */
 const char* gemm_last_error(void);
 

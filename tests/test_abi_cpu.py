@@ -27,11 +27,33 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert {"gemm_run", "grouped_gemm_run", "mx_gemm_run", "gemm_last_error",
-            "gemm_version", "gemm_lds_layout", "gemm_lds_image"} <= set(names)
+    assert {"gemm_run", "grouped_gemm_run", "mx_gemm_run", "gemm_layout_run",
+            "gemm_last_error", "gemm_version", "gemm_lds_layout",
+            "gemm_lds_image"} <= set(names)
     lib = ctypes.CDLL(sg.library_path())
     for n in names:
         assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(swz=4), SHAPE), (dict(swz=32), SHAPE), (dict(swz=-1), SHAPE),
+    (dict(M=-1), SHAPE), (dict(D=None), NULL), (dict(A=None), NULL),
+    (dict(A=P + 8), ALIGN), (dict(K=60), ALIGN), (dict(d_dtype=sg.SG_E4M3), DTYPE),
+    (dict(C=P + 4096, c_dtype=9), DTYPE),
+])
+def test_gemm_layout_run_rejects(kw, code):
+    a = dict(swz=16, M=256, N=256, K=64, A=P, B=P, C=None, c_dtype=0, D=P,
+             d_dtype=sg.SG_F32)
+    a.update(kw)
+    rc = sg.gemm_layout_run(a["swz"], a["M"], a["N"], a["K"], a["A"], a["B"], a["C"],
+                            a["c_dtype"], a["D"], a["d_dtype"], None)
+    assert rc == code, sg.gemm_last_error()
+    assert sg.gemm_last_error().startswith("gemm_layout_run")
+
+
+def test_gemm_layout_run_empty_is_ok():
+    for swz in (0, 8, 16):
+        assert sg.gemm_layout_run(swz, 0, 256, 64, P, P, None, 0, P, sg.SG_F32, None) == 0
 
 
 def test_version_and_empty_error():

@@ -169,6 +169,23 @@ def test_dense_256_tiles_single_k_tile(dev, K):
     check_close(_np(d), ref, bound, "f32", f"256 tiles K={K}")
 
 
+def test_layout_variants_bit_identical(dev):
+    # The LDS layout moves operands around in LDS, not the order of the sums:
+    # the unswizzled, 128-byte-line and 256-byte-line layouts must give the
+    # same bits, and the library's layout must match the oracle.
+    M, N, K = 1000, 1032, 200
+    case = si.dense_case(M, N, K, 21, ab_dtype="bf16", with_c=True, c_dtype="bf16",
+                         d_dtype="f32", scale=1.0 / np.sqrt(K))
+    A, B, C = case.A.to(dev), case.B.to(dev), case.C.to(dev)
+    say(f"layout variants {M}x{N}x{K}")
+    outs = {swz: sg.gemm_layout(A, B, swz, C=C, out_dtype=torch.float32) for swz in (16, 8, 0)}
+    torch.cuda.synchronize()
+    ref, bound = oracle_dense(case)
+    check_close(_np(outs[16]), ref, bound, "f32", "layout 16")
+    assert torch.equal(outs[16], outs[8])
+    assert torch.equal(outs[16], outs[0])
+
+
 def test_dense_integer_inputs_exact(dev):
     # Integer values in [-4, 4]: every partial sum is exact in fp32, so the
     # result must be bit-exact whatever the summation order.
