@@ -315,13 +315,75 @@ struct GemmTile {
   // Accumulator layout of v_mfma_f32_32x32x*: lane l, register r holds MFMA
   // row 8*(r/4) + 4*(l/32) + r%4 and column l%32; with the operand swap
   // above that is n = 8q + 4*(l/32) + {0..3} (q = r/4) and m = l%32.
+  //
+  // The element types are dispatched once per tile.  Each 32-row block of
+  // the wave's output is 4*kFN chunks of 4 consecutive n per lane; the C
+  // chunks of block fm+1 are loaded while block fm is added and stored, and
+  // the loads are unconditional (row and column clamped into the tile: a
+  // clamped chunk is read but never stored; D's row pitch makes N, hence
+  // every tile's valid width, a multiple of 4), so the block's loads go out
+  // together and the wave waits for memory once per block rather than once
+  // per chunk.
   __device__ __forceinline__ static void epilogue(const f32x16 (&acc)[kFM][kFN],
                                                   const TileJob& j, const void* C,
                                                   int c_dtype, void* D, int d_dtype,
                                                   int64_t ldd, int lane, int wm,
                                                   int wn) {
+    const int cd = C ? c_dtype : SG_NONE;
+    if (d_dtype == SG_F32) {
+      if (cd == SG_F32) return epilogue_t<SG_F32, SG_F32>(acc, j, C, D, ldd, lane, wm, wn);
+      if (cd == SG_BF16) return epilogue_t<SG_BF16, SG_F32>(acc, j, C, D, ldd, lane, wm, wn);
+      if (cd == SG_F16) return epilogue_t<SG_F16, SG_F32>(acc, j, C, D, ldd, lane, wm, wn);
+      return epilogue_t<SG_NONE, SG_F32>(acc, j, C, D, ldd, lane, wm, wn);
+    }
+    if (d_dtype == SG_BF16) {
+      if (cd == SG_F32) return epilogue_t<SG_F32, SG_BF16>(acc, j, C, D, ldd, lane, wm, wn);
+      if (cd == SG_BF16) return epilogue_t<SG_BF16, SG_BF16>(acc, j, C, D, ldd, lane, wm, wn);
+      if (cd == SG_F16) return epilogue_t<SG_F16, SG_BF16>(acc, j, C, D, ldd, lane, wm, wn);
+      return epilogue_t<SG_NONE, SG_BF16>(acc, j, C, D, ldd, lane, wm, wn);
+    }
+    if (cd == SG_F32) return epilogue_t<SG_F32, SG_F16>(acc, j, C, D, ldd, lane, wm, wn);
+    if (cd == SG_BF16) return epilogue_t<SG_BF16, SG_F16>(acc, j, C, D, ldd, lane, wm, wn);
+    if (cd == SG_F16) return epilogue_t<SG_F16, SG_F16>(acc, j, C, D, ldd, lane, wm, wn);
+    return epilogue_t<SG_NONE, SG_F16>(acc, j, C, D, ldd, lane, wm, wn);
+  }
+
+  // One chunk of C (4 elements) as loaded: f32x4 for fp32, u32x2 for 16-bit.
+  template <int CD>
+  using CChunk = typename std::conditional<CD == SG_F32, f32x4, u32x2>::type;
+
+  template <int CD>
+  __device__ __forceinline__ static void load_c_block(CChunk<CD> (&c)[4 * kFN],
+                                                      const TileJob& j, const void* C,
+                                                      int64_t ldd, int lane, int wm, int wn,
+                                                      int fm) {
+    if constexpr (CD != SG_NONE) {
+      const int ml = min(wm * kWM + fm * 32 + (lane & 31), j.m_valid - 1);
+      const int64_t base = (j.d_row0 + ml) * ldd + j.n0;
+#pragma unroll
+      for (int fn = 0; fn < kFN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = min(wn * kWN + fn * 32 + 8 * q + 4 * (lane >> 5), j.n_valid - 4);
+          if constexpr (CD == SG_F32)
+            c[4 * fn + q] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(C) +
+                                                            base + nl);
+          else
+            c[4 * fn + q] = *reinterpret_cast<const u32x2*>(
+                static_cast<const uint16_t*>(C) + base + nl);
+        }
+    }
+  }
+
+  template <int CD, int DD>
+  __device__ __forceinline__ static void epilogue_t(const f32x16 (&acc)[kFM][kFN],
+                                                    const TileJob& j, const void* C, void* D,
+                                                    int64_t ldd, int lane, int wm, int wn) {
+    CChunk<CD> cb[2][4 * kFN];
+    load_c_block<CD>(cb[0], j, C, ldd, lane, wm, wn, 0);
 #pragma unroll
     for (int fm = 0; fm < kFM; ++fm) {
+      if (fm + 1 < kFM) load_c_block<CD>(cb[(fm + 1) & 1], j, C, ldd, lane, wm, wn, fm + 1);
       const int ml = wm * kWM + fm * 32 + (lane & 31);
       if (ml >= j.m_valid) continue;
       const int64_t row = j.d_row0 + ml;
@@ -334,30 +396,25 @@ struct GemmTile {
           const int64_t idx = row * ldd + j.n0 + nl;
           f32x4 v = {acc[fm][fn][4 * q + 0], acc[fm][fn][4 * q + 1],
                      acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
-          if (C) {
-            if (c_dtype == SG_F32) {
-              v += *reinterpret_cast<const f32x4*>(static_cast<const float*>(C) + idx);
-            } else {
-              const u32x2 c2 = *reinterpret_cast<const u32x2*>(
-                  static_cast<const uint16_t*>(C) + idx);
-              if (c_dtype == SG_BF16) {
-                v[0] += bf16_to_f32(c2[0] & 0xffffu);
-                v[1] += bf16_to_f32(c2[0] >> 16);
-                v[2] += bf16_to_f32(c2[1] & 0xffffu);
-                v[3] += bf16_to_f32(c2[1] >> 16);
-              } else {
-                v[0] += f16_to_f32(c2[0] & 0xffffu);
-                v[1] += f16_to_f32(c2[0] >> 16);
-                v[2] += f16_to_f32(c2[1] & 0xffffu);
-                v[3] += f16_to_f32(c2[1] >> 16);
-              }
-            }
+          const CChunk<CD>& c2 = cb[fm & 1][4 * fn + q];
+          if constexpr (CD == SG_F32) {
+            v += c2;
+          } else if constexpr (CD == SG_BF16) {
+            v[0] += bf16_to_f32(c2[0] & 0xffffu);
+            v[1] += bf16_to_f32(c2[0] >> 16);
+            v[2] += bf16_to_f32(c2[1] & 0xffffu);
+            v[3] += bf16_to_f32(c2[1] >> 16);
+          } else if constexpr (CD == SG_F16) {
+            v[0] += f16_to_f32(c2[0] & 0xffffu);
+            v[1] += f16_to_f32(c2[0] >> 16);
+            v[2] += f16_to_f32(c2[1] & 0xffffu);
+            v[3] += f16_to_f32(c2[1] >> 16);
           }
-          if (d_dtype == SG_F32) {
+          if constexpr (DD == SG_F32) {
             *reinterpret_cast<f32x4*>(static_cast<float*>(D) + idx) = v;
           } else {
             u32x2 o;
-            if (d_dtype == SG_BF16) {
+            if constexpr (DD == SG_BF16) {
               o[0] = pack_bf16x2(v[0], v[1]);
               o[1] = pack_bf16x2(v[2], v[3]);
             } else {
