@@ -151,7 +151,9 @@ struct PingPongTile {
   }
 
   // 16 MFMAs with the four loads of one half tile between them, one per
-  // four MFMAs.
+  // four MFMAs (without the MFMAs for a wave whose output rows are all past
+  // M: it still loads its share of B and keeps the barriers).
+  template <bool Active>
   __device__ __forceinline__ static void compute(f32x16 (&acc)[kFM][kFN], const Frags& f,
                                                  const HalfLoader<Swz>& ld, u32x4 rsrc,
                                                  uint32_t half, int w4, int rows_valid,
@@ -162,7 +164,8 @@ struct PingPongTile {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int fm = ((q & 1) << 1) | (m >> 1), fn = m & 1;
-        acc[fm][fn] = mfma32x32x16<IsBF16>(f.b[kk][fn], f.a[kk][fm], acc[fm][fn]);
+        if constexpr (Active)
+          acc[fm][fn] = mfma32x32x16<IsBF16>(f.b[kk][fn], f.a[kk][fm], acc[fm][fn]);
       }
       __builtin_amdgcn_sched_barrier(0);
       ld.issue(rsrc, half, w4, q, rows_valid, kbyte0, kbytes);
@@ -189,6 +192,35 @@ struct PingPongTile {
   __device__ __forceinline__ static void end_phase() {
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
     barrier();
+  }
+
+  template <bool Active>
+  __device__ __forceinline__ static void mainloop(f32x16 (&acc)[kFM][kFN],
+                                                  const HalfLoader<Swz>& la,
+                                                  const HalfLoader<Swz>& lb, u32x4 ra, u32x4 rb,
+                                                  int a_rows, int b_rows, uint32_t a_ring,
+                                                  uint32_t b_ring, const char* a_rd,
+                                                  const char* b_rd, const Offsets& o, int g,
+                                                  int w4, int T, uint32_t kbytes) {
+    if (g) barrier();  // group 1 runs one phase behind group 0
+    int bs = 0;        // t mod 3
+    for (int t = 0; t < T; ++t) {
+      const int as = t & 1, bs2 = bs == 0 ? 2 : bs - 1;  // (t+2) mod 2, (t+2) mod 3
+      const char* at = a_rd + as * kTileBytes;
+      const char* bt = b_rd + bs * kTileBytes;
+      const uint32_t k2 = (uint32_t)(t + 2) * 128u;
+      Frags f;
+      if constexpr (Active) read(f, at, bt, o, 0);
+      end_phase();
+      compute<Active>(acc, f, lb, rb, b_ring + bs2 * kTileBytes, w4, b_rows, k2, kbytes);
+      end_phase();
+      if constexpr (Active) read(f, at, bt, o, 1);
+      end_phase();
+      compute<Active>(acc, f, la, ra, a_ring + as * kTileBytes, w4, a_rows, k2, kbytes);
+      end_phase();
+      bs = bs == 2 ? 0 : bs + 1;
+    }
+    if (!g) barrier();
   }
 
   // Mainloop and epilogue of one tile; `smem` is the 160 KiB of LDS.
@@ -237,25 +269,14 @@ struct PingPongTile {
 #pragma unroll
       for (int k = 0; k < kFN; ++k) acc[i][k] = f32x16{};
 
-    if (g) barrier();  // group 1 runs one phase behind group 0
-    int bs = 0;        // t mod 3
-    for (int t = 0; t < T; ++t) {
-      const int as = t & 1, bs2 = bs == 0 ? 2 : bs - 1;  // (t+2) mod 2, (t+2) mod 3
-      const char* at = a_rd + as * kTileBytes;
-      const char* bt = b_rd + bs * kTileBytes;
-      const uint32_t k2 = (uint32_t)(t + 2) * 128u;
-      Frags f;
-      read(f, at, bt, o, 0);
-      end_phase();
-      compute(acc, f, lb, rb, b_ring + bs2 * kTileBytes, w4, b_rows, k2, kbytes);
-      end_phase();
-      read(f, at, bt, o, 1);
-      end_phase();
-      compute(acc, f, la, ra, a_ring + as * kTileBytes, w4, a_rows, k2, kbytes);
-      end_phase();
-      bs = bs == 2 ? 0 : bs + 1;
-    }
-    if (!g) barrier();
+    // A wave whose 128 output rows all lie past M (the second group of a tile
+    // with at most 128 valid rows) runs the mainloop without its MFMAs.
+    if (a_rows > 0)
+      mainloop<true>(acc, la, lb, ra, rb, a_rows, b_rows, a_ring, b_ring, a_rd, b_rd, o, g, w4,
+                     T, kbytes);
+    else
+      mainloop<false>(acc, la, lb, ra, rb, a_rows, b_rows, a_ring, b_ring, a_rd, b_rd, o, g,
+                      w4, T, kbytes);
     wait_vmem();  // the zero-filled loads past K
 
     Base::epilogue(acc, j, C, c_dtype, D, d_dtype, ldd, lane, g, w4);
