@@ -38,7 +38,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gemm_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-_DT = {"f16": 1, "bf16": 2, "f32": 3, "e4m3": 4, "e8m0": 5}
+_DT = {"f16": 1, "bf16": 2, "f32": 3, "e4m3": 4, "e8m0": 5, "e2m1": 6}
 _MAJ = {"k": 0, "mn": 1}
 
 _lib = None
@@ -69,9 +69,13 @@ def _load():
         lib.oracle_mx_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, dp, dp, ip]
         lib.oracle_mx_gemm_points.argtypes = [i64, i64, i64, vp, vp, vp, vp,
                                               i64, vp, vp, dp, dp]
+        lib.oracle_mx_gemm_fmt.argtypes = [ip, i64, i64, i64, vp, vp, vp, vp, dp, dp, ip]
+        lib.oracle_mx_gemm_points_fmt.argtypes = [ip, i64, i64, i64, vp, vp, vp, vp,
+                                                  i64, vp, vp, dp, dp]
         lib.oracle_default_threads.argtypes = []
         for f in (lib.oracle_decode, lib.oracle_gemm, lib.oracle_gemm_points,
                   lib.oracle_mx_gemm, lib.oracle_mx_gemm_points,
+                  lib.oracle_mx_gemm_fmt, lib.oracle_mx_gemm_points_fmt,
                   lib.oracle_default_threads):
             f.restype = ctypes.c_int
         _lib = lib
@@ -105,8 +109,16 @@ def _ptr(a: Optional[np.ndarray]):
 
 def decode(dtype: str, data) -> np.ndarray:
     """Decode raw storage of ``dtype`` ("f16", "bf16", "f32", "e4m3",
-    "e8m0") to fp64, element by element."""
+    "e8m0", "e2m1") to fp64, element by element.  e2m1 packs two elements
+    per byte (element 2i in the low nibble of byte i) and returns a flat
+    array of 2 * nbytes values."""
     a = _bytes(data)
+    if dtype == "e2m1":
+        n = a.nbytes * 2
+        out = np.empty(n, dtype=np.float64)
+        if _load().oracle_decode(_DT[dtype], _ptr(a), n, _ptr(out)) != 0:
+            raise ValueError("oracle_decode failed")
+        return out
     width = {"f16": 2, "bf16": 2, "f32": 4, "e4m3": 1, "e8m0": 1}[dtype]
     n = a.nbytes // width
     out = np.empty(n, dtype=np.float64)
@@ -176,28 +188,30 @@ def grouped_gemm(m_offsets: Sequence[int], N: int, K: int, A, B,
 
 
 def mx_gemm(M: int, N: int, K: int, A, SFA, B, SFB, nthreads: int = 0,
-            with_bound: bool = True):
-    """Block-scaled e4m3 GEMM with e8m0 scales per 32-element K block."""
+            with_bound: bool = True, fmt: str = "e4m3"):
+    """Block-scaled GEMM with e8m0 scales per 32-element K block; the
+    elements are e4m3 (A [M][K] bytes) or e2m1 (fmt "e2m1", A [M][K/2]
+    bytes, two elements per byte)."""
     a, sa, b, sb = _bytes(A), _bytes(SFA), _bytes(B), _bytes(SFB)
     ref = np.empty((M, N), dtype=np.float64)
     bound = np.empty((M, N), dtype=np.float64) if with_bound else None
-    rc = _load().oracle_mx_gemm(M, N, K, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
-                                _ptr(ref), _ptr(bound), nthreads)
+    rc = _load().oracle_mx_gemm_fmt(_DT[fmt], M, N, K, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
+                                    _ptr(ref), _ptr(bound), nthreads)
     if rc != 0:
         raise ValueError("oracle_mx_gemm rejected its arguments")
     return ref, bound
 
 
 def mx_gemm_points(M: int, N: int, K: int, A, SFA, B, SFB,
-                   rows: Sequence[int], cols: Sequence[int]):
+                   rows: Sequence[int], cols: Sequence[int], fmt: str = "e4m3"):
     a, sa, b, sb = _bytes(A), _bytes(SFA), _bytes(B), _bytes(SFB)
     r = np.ascontiguousarray(rows, dtype=np.int64)
     q = np.ascontiguousarray(cols, dtype=np.int64)
     ref = np.empty(len(r), dtype=np.float64)
     bound = np.empty(len(r), dtype=np.float64)
-    rc = _load().oracle_mx_gemm_points(M, N, K, _ptr(a), _ptr(sa), _ptr(b),
-                                       _ptr(sb), len(r), _ptr(r), _ptr(q),
-                                       _ptr(ref), _ptr(bound))
+    rc = _load().oracle_mx_gemm_points_fmt(_DT[fmt], M, N, K, _ptr(a), _ptr(sa), _ptr(b),
+                                           _ptr(sb), len(r), _ptr(r), _ptr(q),
+                                           _ptr(ref), _ptr(bound))
     if rc != 0:
         raise ValueError("oracle_mx_gemm_points rejected its arguments")
     return ref, bound

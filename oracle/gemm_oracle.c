@@ -21,7 +21,8 @@
  *     Block-scaled MMA: output (m,n) uses scale SFA[m,sfk] for A and
  *     SFB[n,sfk] for B ("06 Blackwell Tensor Core", Block-Scaled MMA).  The
  *     32-element K block and the e8m0 scale type are not on that page; they
- *     are the MXFP8 workload's definition.
+ *     are the MXFP8 workload's definition.  MXFP4 is the same sum over e2m1
+ *     elements (two per byte, element 2i in the low nibble of byte i).
  *
  * Products of two 16-bit floats (and of two e4m3) are exact in fp64; the
  * fp64 sum of K terms is within (K-1)*2^-53 * bound of the exact value.
@@ -35,7 +36,7 @@
 #include <string.h>
 #include <unistd.h>
 
-enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_F32 = 3, ORC_E4M3 = 4, ORC_E8M0 = 5 };
+enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_F32 = 3, ORC_E4M3 = 4, ORC_E8M0 = 5, ORC_E2M1 = 6 };
 enum { ORC_K_MAJOR = 0, ORC_MN_MAJOR = 1 };
 
 /* ---------------------------------------------------------------- decode */
@@ -81,6 +82,18 @@ static double dec_e4m3(uint8_t b) {
     return s ? -v : v;
 }
 
+/* OCP FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 fraction bit; no infinity
+ * or NaN; the largest magnitude is 6. */
+static double dec_e2m1(uint8_t nib) {
+    int s = (nib >> 3) & 1, e = (nib >> 1) & 3, m = nib & 1;
+    double v;
+    if (e == 0)
+        v = 0.5 * m;                           /* m/2 * 2^(1-1) */
+    else
+        v = ldexp((double)(2 + m), e - 2);     /* (1 + m/2) * 2^(e-1) */
+    return s ? -v : v;
+}
+
 /* OCP E8M0 scale: 2^(e-127); 0xFF is NaN. */
 static double dec_e8m0(uint8_t b) {
     return b == 255 ? NAN : ldexp(1.0, (int)b - 127);
@@ -91,6 +104,7 @@ static int elem_size(int dt) {
     case ORC_F16: case ORC_BF16: return 2;
     case ORC_F32: return 4;
     case ORC_E4M3: case ORC_E8M0: return 1;
+    case ORC_E2M1: return 1;  /* two elements per byte; indices count elements */
     default: return 0;
     }
 }
@@ -103,6 +117,7 @@ static double dec_at(int dt, const void *base, int64_t idx) {
     case ORC_F32: return dec_f32(p + 4 * idx);
     case ORC_E4M3: return dec_e4m3(p[idx]);
     case ORC_E8M0: return dec_e8m0(p[idx]);
+    case ORC_E2M1: return dec_e2m1((idx & 1) ? (uint8_t)(p[idx >> 1] >> 4) : (uint8_t)(p[idx >> 1] & 15));
     default: return NAN;
     }
 }
@@ -261,7 +276,7 @@ int oracle_gemm_points(int64_t M, int64_t N, int64_t K, const void *A,
 
 typedef struct {
     int64_t M, N, K, nblk;
-    const double *a, *b;      /* decoded e4m3, [rows][K] */
+    const double *a, *b;      /* decoded elements, [rows][K] */
     const double *sa, *sb;    /* decoded e8m0, [rows][K/32] */
     double *ref, *bound;
 } mx_ctx;
@@ -290,10 +305,12 @@ static void mx_rows(void *vctx, int64_t i0, int64_t i1) {
     }
 }
 
-/* A e4m3 [M][K], SFA e8m0 [M][K/32], B e4m3 [N][K], SFB e8m0 [N][K/32]. */
-int oracle_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A,
-                   const uint8_t *SFA, const uint8_t *B, const uint8_t *SFB,
-                   double *ref, double *bound, int nthreads) {
+/* A [M][K], SFA e8m0 [M][K/32], B [N][K], SFB e8m0 [N][K/32]; the elements
+ * are e4m3 (fmt ORC_E4M3, one per byte) or e2m1 (ORC_E2M1, two per byte). */
+int oracle_mx_gemm_fmt(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                       const uint8_t *SFA, const uint8_t *B, const uint8_t *SFB,
+                       double *ref, double *bound, int nthreads) {
+    if (fmt != ORC_E4M3 && fmt != ORC_E2M1) return -1;
     if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || !ref) return -1;
     if (K > 0 && ((M > 0 && (!A || !SFA)) || (N > 0 && (!B || !SFB)))) return -1;
     int64_t nblk = K / 32;
@@ -303,8 +320,8 @@ int oracle_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A,
     double *sb = (double *)malloc(sizeof(double) * (size_t)(N * nblk + 1));
     if (!a || !b || !sa || !sb) { free(a); free(b); free(sa); free(sb); return -1; }
     if (K > 0) {
-        oracle_decode(ORC_E4M3, A, M * K, a);
-        oracle_decode(ORC_E4M3, B, N * K, b);
+        oracle_decode(fmt, A, M * K, a);
+        oracle_decode(fmt, B, N * K, b);
         oracle_decode(ORC_E8M0, SFA, M * nblk, sa);
         oracle_decode(ORC_E8M0, SFB, N * nblk, sb);
     }
@@ -314,11 +331,18 @@ int oracle_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A,
     return 0;
 }
 
-int oracle_mx_gemm_points(int64_t M, int64_t N, int64_t K, const uint8_t *A,
-                          const uint8_t *SFA, const uint8_t *B,
-                          const uint8_t *SFB, int64_t npts,
-                          const int64_t *rows, const int64_t *cols,
-                          double *ref, double *bound) {
+int oracle_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                   const uint8_t *SFA, const uint8_t *B, const uint8_t *SFB,
+                   double *ref, double *bound, int nthreads) {
+    return oracle_mx_gemm_fmt(ORC_E4M3, M, N, K, A, SFA, B, SFB, ref, bound, nthreads);
+}
+
+int oracle_mx_gemm_points_fmt(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                              const uint8_t *SFA, const uint8_t *B,
+                              const uint8_t *SFB, int64_t npts,
+                              const int64_t *rows, const int64_t *cols,
+                              double *ref, double *bound) {
+    if (fmt != ORC_E4M3 && fmt != ORC_E2M1) return -1;
     if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || npts < 0 || !ref ||
         (npts && (!rows || !cols)))
         return -1;
@@ -330,8 +354,8 @@ int oracle_mx_gemm_points(int64_t M, int64_t N, int64_t K, const uint8_t *A,
         for (int64_t blk = 0; blk < nblk; ++blk) {
             double bs = 0.0, bsa = 0.0;
             for (int k = 0; k < 32; ++k) {
-                double pr = dec_e4m3(A[i * K + blk * 32 + k]) *
-                            dec_e4m3(B[j * K + blk * 32 + k]);
+                double pr = dec_at(fmt, A, i * K + blk * 32 + k) *
+                            dec_at(fmt, B, j * K + blk * 32 + k);
                 bs += pr;
                 bsa += fabs(pr);
             }
@@ -343,4 +367,13 @@ int oracle_mx_gemm_points(int64_t M, int64_t N, int64_t K, const uint8_t *A,
         if (bound) bound[p] = sabs;
     }
     return 0;
+}
+
+int oracle_mx_gemm_points(int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                          const uint8_t *SFA, const uint8_t *B,
+                          const uint8_t *SFB, int64_t npts,
+                          const int64_t *rows, const int64_t *cols,
+                          double *ref, double *bound) {
+    return oracle_mx_gemm_points_fmt(ORC_E4M3, M, N, K, A, SFA, B, SFB, npts, rows, cols,
+                                     ref, bound);
 }

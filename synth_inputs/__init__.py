@@ -35,7 +35,8 @@ import torch
 __all__ = [
     "Operand", "DenseCase", "GroupedCase", "MXCase",
     "uniform", "normal", "to_fp16", "to_bf16", "mx_quantize",
-    "single_tile", "dense_1024", "dense_8192", "grouped", "mxfp8",
+    "single_tile", "dense_1024", "dense_8192", "grouped", "mxfp8", "mxfp4",
+    "mxfp4_quantize",
     "dense_case", "grouped_case", "mx_case", "integer_valued",
 ]
 
@@ -114,12 +115,13 @@ class MXCase:
     M: int
     N: int
     K: int
-    A: torch.Tensor          # uint8 e4m3 [M][K]
+    A: torch.Tensor          # uint8 e4m3 [M][K], or e2m1 [M][K/2] (two per byte)
     SFA: torch.Tensor        # uint8 e8m0 [M][K/32]
-    B: torch.Tensor          # uint8 e4m3 [N][K]
+    B: torch.Tensor          # uint8 e4m3 [N][K], or e2m1 [N][K/2]
     SFB: torch.Tensor        # uint8 e8m0 [N][K/32]
     d_dtype: str
     name: str = ""
+    fmt: str = "e4m3"        # element format: "e4m3" or "e2m1"
 
 
 def _layout(x_logical: np.ndarray, major: str) -> np.ndarray:
@@ -221,18 +223,60 @@ def mx_quantize(x: np.ndarray, block: int = 32):
     return codes, scales
 
 
-def mx_case(M, N, K, seed, *, d_dtype="bf16", name="") -> MXCase:
+# e2m1 magnitudes by code, and the rounding thresholds between neighbours:
+# a tie goes to the even code (fraction bit 0).
+_E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+_E2M1_MIDS = (_E2M1_VALUES[:-1] + _E2M1_VALUES[1:]) / 2
+
+
+def mxfp4_quantize(x: np.ndarray, block: int = 32):
+    """Quantise fp32 rows [R][K] to e2m1 with one e8m0 scale per K block.
+
+    The scale is X = 2^(floor(log2(absmax)) - 2) of the block (X = 1 for an
+    all-zero block), which puts the block's largest magnitude in [4, 8), the
+    top binade of e2m1 (largest value 6; larger magnitudes become 6).
+    Elements are x / X rounded to the nearest e2m1 value, ties to the even
+    code.  Two elements per byte, element 2i in the low nibble of byte i.
+    Returns (packed uint8 [R][K/2], scales uint8 [R][K/block]).
+    """
+    R, K = x.shape
+    assert K % block == 0 and K % 2 == 0
+    xb = x.reshape(R, K // block, block)
+    amax = np.abs(xb).max(axis=2)
+    e = np.zeros_like(amax, dtype=np.int32)
+    nz = amax > 0
+    _, ex = np.frexp(amax[nz])
+    e[nz] = ex - 1 - 2
+    e = np.clip(e, -127, 127)
+    y = (xb / np.ldexp(np.float32(1.0), e)[:, :, None].astype(np.float32)).reshape(R, K)
+    mag = np.minimum(np.abs(y), np.float32(6.0))
+    code = np.zeros(mag.shape, dtype=np.uint8)
+    for i, t in enumerate(_E2M1_MIDS):
+        # between codes i and i+1: a tie rounds to the even one
+        code += (mag >= t) if i % 2 else (mag > t)
+    code |= ((y < 0) & (code != 0)).astype(np.uint8) << 3
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return torch.from_numpy(np.ascontiguousarray(packed)), torch.from_numpy((e + 127).astype(np.uint8))
+
+
+def mx_case(M, N, K, seed, *, d_dtype="bf16", name="", fmt="e4m3") -> MXCase:
     rng = _rng(seed)
     a = normal(rng, (M, K))
     b = normal(rng, (N, K))
-    A, SFA = mx_quantize(a)
-    B, SFB = mx_quantize(b)
-    return MXCase(M, N, K, A, SFA, B, SFB, d_dtype, name)
+    q = mx_quantize if fmt == "e4m3" else mxfp4_quantize
+    A, SFA = q(a)
+    B, SFB = q(b)
+    return MXCase(M, N, K, A, SFA, B, SFB, d_dtype, name, fmt)
 
 
 def mxfp8(seed: int = 5, M: int = 8192, N: int = 8192, K: int = 8192) -> MXCase:
     """MXFP8 8192^3: e4m3 with per-32 K-block e8m0 scales, bf16 out."""
     return mx_case(M, N, K, seed, name=f"mxfp8_{M}x{N}x{K}")
+
+
+def mxfp4(seed: int = 7, M: int = 8192, N: int = 8192, K: int = 8192) -> MXCase:
+    """MXFP4 8192^3: e2m1 (two per byte) with per-32 K-block e8m0 scales, bf16 out."""
+    return mx_case(M, N, K, seed, name=f"mxfp4_{M}x{N}x{K}", fmt="e2m1")
 
 
 def integer_valued(shape, seed, lo=-4, hi=4) -> np.ndarray:

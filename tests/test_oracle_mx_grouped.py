@@ -2,6 +2,8 @@
 
 MX: the e4m3 / e8m0 decode is checked on all 256 codes against torch's
 float8_e4m3fn / float8_e8m0fnu conversions and against closed-form values;
+the e2m1 (MXFP4) decode against the format's documented value set, its
+nibble order and exact representability in e4m3 (torch's cast);
 the GEMM against numpy on special cases (unit scales = plain fp8 GEMM, a
 single rescaled block, integer values with power-of-two scales).
 Grouped: G = 1 equals the dense GEMM; the result is the concatenation of
@@ -115,6 +117,100 @@ def test_mx_quantizer_scale_is_power_of_two_at_or_below_absmax():
     # Dequantised values are within half an e4m3 step (2^-3 relative) of x.
     deq = dec * X[:, :, None]
     assert np.all(np.abs(deq - xb) <= 2.0 ** -4 * X[:, :, None] + 1e-30)
+
+
+# ------------------------------------------------------------------ MXFP4
+
+# The OCP FP4 E2M1 value set: positive codes 0..7 in order, negative codes
+# 8..15 their mirror.  Written as a literal list, not from the encoding.
+E2M1_DOCUMENTED = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _unpack4(packed: torch.Tensor) -> np.ndarray:
+    """numpy decode of packed e2m1 through the documented value list."""
+    p = packed.numpy().astype(np.int64)
+    lo, hi = p & 15, p >> 4
+    table = np.array(E2M1_DOCUMENTED + [-v for v in E2M1_DOCUMENTED])
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],))
+    out[..., 0::2] = table[lo]
+    out[..., 1::2] = table[hi]
+    return out
+
+
+def test_e2m1_all_codes_match_documented_values():
+    codes = np.arange(16, dtype=np.uint8)
+    ours = oracle.decode("e2m1", codes | (codes << 4))   # byte c holds c twice
+    assert np.array_equal(ours[0::2], ours[1::2])
+    vals = ours[0::2]
+    assert vals[:8].tolist() == E2M1_DOCUMENTED
+    assert vals[8:].tolist() == [-v for v in E2M1_DOCUMENTED]
+    # every value is exactly an e4m3 value (torch's cast is a library routine)
+    t = torch.tensor(vals).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(t, vals)
+    # element 2i is the low nibble of byte i
+    assert oracle.decode("e2m1", np.array([0x71], dtype=np.uint8)).tolist() == [0.5, 6.0]
+
+
+def test_e2m1_unit_scales_equal_plain_fp4_gemm():
+    M, N, K = 6, 5, 128
+    rng = np.random.default_rng(11)
+    A = torch.from_numpy(rng.integers(0, 256, (M, K // 2)).astype(np.uint8))
+    B = torch.from_numpy(rng.integers(0, 256, (N, K // 2)).astype(np.uint8))
+    SFA = torch.full((M, K // 32), 127, dtype=torch.uint8)
+    SFB = torch.full((N, K // 32), 127, dtype=torch.uint8)
+    ref, bound = oracle.mx_gemm(M, N, K, A, SFA, B, SFB, fmt="e2m1")
+    a, b = _unpack4(A), _unpack4(B)
+    # e2m1 values are multiples of 1/2 below 8: every product and sum is exact
+    assert np.array_equal(ref, a @ b.T)
+    assert np.array_equal(bound, np.abs(a) @ np.abs(b).T)
+
+
+def test_e2m1_each_scale_applies_to_its_own_block():
+    M, N, K = 3, 4, 96
+    rng = np.random.default_rng(12)
+    A = torch.from_numpy(rng.integers(0, 256, (M, K // 2)).astype(np.uint8))
+    B = torch.from_numpy(rng.integers(0, 256, (N, K // 2)).astype(np.uint8))
+    sa = rng.integers(118, 137, (M, K // 32)).astype(np.uint8)
+    sb = rng.integers(118, 137, (N, K // 32)).astype(np.uint8)
+    ref, _ = oracle.mx_gemm(M, N, K, A, torch.from_numpy(sa), B, torch.from_numpy(sb),
+                            fmt="e2m1")
+    a, b = _unpack4(A), _unpack4(B)
+    expect = np.zeros((M, N))
+    for blk in range(K // 32):
+        sl = slice(32 * blk, 32 * blk + 32)
+        expect += (a[:, sl] @ b[:, sl].T) * np.ldexp(1.0, sa[:, blk].astype(np.int64) - 127)[:, None] \
+            * np.ldexp(1.0, sb[:, blk].astype(np.int64) - 127)[None, :]
+    assert np.array_equal(ref, expect)
+
+
+def test_e2m1_points_agree_with_full():
+    case = si.mx_case(33, 20, 256, 13, fmt="e2m1")
+    ref, bound = oracle.mx_gemm(case.M, case.N, case.K, case.A, case.SFA, case.B, case.SFB,
+                                fmt="e2m1")
+    rows, cols = [0, 32, 7], [19, 0, 11]
+    rp, bp = oracle.mx_gemm_points(case.M, case.N, case.K, case.A, case.SFA, case.B, case.SFB,
+                                   rows, cols, fmt="e2m1")
+    assert np.array_equal(rp, ref[rows, cols]) and np.array_equal(bp, bound[rows, cols])
+
+
+def test_mxfp4_quantizer_scale_and_rounding():
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((5, 128)).astype(np.float32)
+    x[1, 64:96] = 0.0
+    packed, scales = si.mxfp4_quantize(x)
+    assert packed.shape == (5, 64) and scales.shape == (5, 4)
+    xb = x.reshape(5, 4, 32)
+    amax = np.abs(xb).max(axis=2)
+    X = np.ldexp(1.0, scales.numpy().astype(np.int64) - 127)
+    nz = amax > 0
+    # the block's absmax lands in [4X, 8X): e2m1's top binade
+    assert np.all(4 * X[nz] <= amax[nz]) and np.all(amax[nz] < 8 * X[nz])
+    assert X[1, 2] == 1.0
+    dec = _unpack4(packed).reshape(5, 4, 32) * X[:, :, None]
+    # nearest e2m1 value: within half a step (the step is X/2 below 2X... 2X above 4X)
+    step = np.where(np.abs(xb) < 2 * X[:, :, None], 0.5, np.where(np.abs(xb) < 4 * X[:, :, None], 1.0, 2.0)) * X[:, :, None]
+    clipped = np.clip(xb, -6 * X[:, :, None], 6 * X[:, :, None])
+    assert np.all(np.abs(dec - clipped) <= step / 2 + 1e-30)
 
 
 def test_grouped_single_group_equals_dense():
