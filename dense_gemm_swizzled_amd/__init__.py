@@ -24,9 +24,10 @@ import numpy as np
 __all__ = [
     "SG_OK", "SG_F16", "SG_BF16", "SG_F32", "SG_E4M3", "SG_E8M0", "SG_NONE",
     "SG_K_MAJOR", "SG_MN_MAJOR", "SG_MAX_GROUPS", "GemmError",
-    "gemm_run", "grouped_gemm_run", "mx_gemm_run", "gemm_layout_run", "gemm_last_error",
+    "gemm_run", "grouped_gemm_run", "mx_gemm_run", "mxfp4_gemm_run", "gemm_layout_run",
+    "gemm_last_error",
     "gemm_version", "gemm_lds_layout", "gemm_lds_image",
-    "gemm", "grouped_gemm", "mx_gemm", "gemm_layout", "library_path", "load",
+    "gemm", "grouped_gemm", "mx_gemm", "mxfp4_gemm", "gemm_layout", "library_path", "load",
 ]
 
 SG_OK = 0
@@ -67,10 +68,12 @@ def load():
     lib.grouped_gemm_run.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), i64, i64, vp,
                                      i32, vp, i32, i32, vp, i32, vp]
     lib.mx_gemm_run.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
+    lib.mxfp4_gemm_run.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
     lib.gemm_layout_run.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, vp, i32, vp]
     lib.gemm_lds_layout.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int32)]
     lib.gemm_lds_image.argtypes = [vp, i64, i64, i32, i64, i64, i32, vp, vp]
-    for f in (lib.gemm_run, lib.grouped_gemm_run, lib.mx_gemm_run, lib.gemm_layout_run,
+    for f in (lib.gemm_run, lib.grouped_gemm_run, lib.mx_gemm_run, lib.mxfp4_gemm_run,
+              lib.gemm_layout_run,
               lib.gemm_lds_layout, lib.gemm_lds_image):
         f.restype = ctypes.c_int
     lib.gemm_last_error.argtypes = []
@@ -100,6 +103,10 @@ def grouped_gemm_run(G, m_offsets, N, K, A, a_major, B, b_major, ab_dtype, D,
 
 def mx_gemm_run(M, N, K, A, SFA, B, SFB, D, d_dtype, stream) -> int:
     return load().mx_gemm_run(M, N, K, A, SFA, B, SFB, D, d_dtype, stream)
+
+
+def mxfp4_gemm_run(M, N, K, A, SFA, B, SFB, D, d_dtype, stream) -> int:
+    return load().mxfp4_gemm_run(M, N, K, A, SFA, B, SFB, D, d_dtype, stream)
 
 
 def gemm_layout_run(swz_units, M, N, K, A, B, C, c_dtype, D, d_dtype, stream) -> int:
@@ -220,4 +227,18 @@ def mx_gemm(A, SFA, B, SFB, *, out_dtype=None, out=None):
     _check(mx_gemm_run(M, N, K, A.data_ptr(), SFA.data_ptr(), B.data_ptr(),
                        SFB.data_ptr(), out.data_ptr(), _dt(out.dtype),
                        _stream(A.device)))
+    return out
+
+
+def mxfp4_gemm(A, SFA, B, SFB, *, out_dtype=None, out=None):
+    """Block-scaled e2m1 GEMM: A [M][K/2], B [N][K/2] (uint8, two e2m1 per
+    byte, element 2i in the low nibble), SFA [M][K/32], SFB [N][K/32] (uint8
+    e8m0 codes)."""
+    import torch
+    M, K = A.shape[0], A.shape[1] * 2
+    N = B.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=A.device)
+    _check(mxfp4_gemm_run(M, N, K, A.data_ptr(), SFA.data_ptr(), B.data_ptr(),
+                          SFB.data_ptr(), out.data_ptr(), _dt(out.dtype), _stream(A.device)))
     return out

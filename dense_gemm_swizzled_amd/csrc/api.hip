@@ -224,6 +224,48 @@ int grouped_gemm_run(int G, const int64_t* m_offsets, int64_t N, int64_t K,
   return ok();
 }
 
+int mxfp4_gemm_run(int64_t M, int64_t N, int64_t K, const void* A, const void* SFA,
+                   const void* B, const void* SFB, void* D, int d_dtype, void* stream) {
+  if (M < 0 || N < 0 || K < 0)
+    return fail(SG_ERR_SHAPE, "mxfp4_gemm_run: negative size");
+  if (K % 256)
+    return fail(SG_ERR_SHAPE, "mxfp4_gemm_run: K=%lld is not a multiple of 256", (long long)K);
+  if (d_dtype != SG_F32 && d_dtype != SG_BF16)
+    return fail(SG_ERR_DTYPE, "mxfp4_gemm_run: d_dtype %d is not SG_F32/SG_BF16", d_dtype);
+  if (M == 0 || N == 0) return ok();
+  if (!D) return fail(SG_ERR_NULL, "mxfp4_gemm_run: D is NULL");
+  if (K > 0 && (!A || !B || !SFA || !SFB))
+    return fail(SG_ERR_NULL, "mxfp4_gemm_run: A, B, SFA or SFB is NULL");
+  const int db = elem_bytes(d_dtype);
+  if ((K > 0 && (!aligned16(A) || !aligned16(B))) || !aligned16(D) ||
+      (K > 0 && ((reinterpret_cast<uintptr_t>(SFA) | reinterpret_cast<uintptr_t>(SFB)) & 3u)))
+    return fail(SG_ERR_ALIGN,
+                "mxfp4_gemm_run: A, B, D must be 16-byte aligned, SFA and SFB 4-byte aligned");
+  if ((N * db) % 16)
+    return fail(SG_ERR_ALIGN, "mxfp4_gemm_run: D row pitch must be a multiple of 16 bytes");
+  if (256 * (K / 2) >= kMaxExtent)
+    return fail(SG_ERR_SHAPE, "mxfp4_gemm_run: an operand panel spans 2^31 bytes or more");
+  const int64_t tiles_m = cdiv(M, 256), tiles_n = cdiv(N, 256);
+  if (tiles_m * tiles_n > 0x7fffffffLL)
+    return fail(SG_ERR_SHAPE, "mxfp4_gemm_run: too many tiles");
+  sg::MxParams p;
+  p.A = A;
+  p.SFA = SFA;
+  p.B = B;
+  p.SFB = SFB;
+  p.D = D;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.d_dtype = d_dtype;
+  p.tiles_m = (int)tiles_m;
+  p.tiles_n = (int)tiles_n;
+  p.group_m = kGroupM;
+  hipError_t e = sg::launch_mxfp4(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mxfp4_gemm_run launch");
+  return ok();
+}
+
 int mx_gemm_run(int64_t M, int64_t N, int64_t K, const void* A, const void* SFA,
                 const void* B, const void* SFB, void* D, int d_dtype, void* stream) {
   if (M < 0 || N < 0 || K < 0)

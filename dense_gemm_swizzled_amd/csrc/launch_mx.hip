@@ -7,10 +7,16 @@ namespace sg {
 hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s) {
   const int grid = p.tiles_m * p.tiles_n;
   if (tile == kTile256)
-    hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault>), dim3(grid), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, false>), dim3(grid), dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL((mx_gemm_kernel<128, 128, kSwzDefault>), dim3(grid),
                        dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp4(const MxParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, true>), dim3(p.tiles_m * p.tiles_n),
+                     dim3(512), 0, s, p);
   return hipGetLastError();
 }
 

@@ -303,17 +303,25 @@ __global__ void __launch_bounds__(512, 1) pingpong_grouped_kernel(const GroupedP
 
 namespace sg {
 
-// The ping-pong mainloop for the block-scaled (MXFP8) GEMM: e4m3 operands,
-// 128 elements (= 128 bytes, four 32-element scale blocks) of K per tile, so
-// the operand halves have exactly the geometry of the 16-bit kernel's.  A
-// phase is one 64-wide K step: eight v_mfma_scale_f32_32x32x64_f8f6f4 of the
-// wave's 4x2 blocks (the same 512 cycles as sixteen 16-bit MFMAs).
+// The ping-pong mainloop for the block-scaled GEMMs: MXFP8 (e4m3 elements)
+// and MXFP4 (e2m1 elements, two per byte).  A K tile is 128 bytes of every
+// row (128 e4m3 or 256 e2m1 values: four or eight 32-element scale blocks),
+// so the operand halves have exactly the geometry of the 16-bit kernel's.
+// Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 (checked on the GPU
+// with one-hot operands): lane l supplies row l%32; with e4m3 its 32 bytes
+// are K [16h, 16h+16) and [32+16h, 32+16h+16) of the 64-wide step, with e2m1
+// its first 16 bytes are the 32 values of block h of the step (h = l/32, the
+// other 16 bytes are ignored); the e8m0 byte of lane l scales block h.  So a
+// lane reads 16-byte chunk 4kk + 2c + h of the row for chunk c of e4m3 step
+// kk, or for step 2kk + c of e2m1: one offset table serves both.  A phase
+// is eight e4m3 MFMAs (one 64-wide step) or sixteen e2m1 MFMAs (two steps),
+// the same 512 cycles as sixteen 16-bit MFMAs.
 //
-// LDS (148 KiB): A ring of two tiles, B ring of two tiles, a ring of two
-// tiles of scales (the e8m0 dwords of the tile's 256 A rows, then of its 256
-// B rows), all filled by direct-to-LDS loads so every wait is explicit, and
-// a 16 KiB sink.  Each group loads the scales of its own 128 rows of A and of
-// B with one 4-byte-per-lane load per wave.  Schedule (phases 4t..4t+3 of
+// LDS: A ring of two tiles, B ring of two tiles, a ring of two tiles of
+// scales (the e8m0 dwords of the tile's 256 A rows, then of its 256 B rows;
+// dword d of every row together), all filled by direct-to-LDS loads so every
+// wait is explicit, and a 16 KiB sink.  Each group loads the scales of its
+// own 128 rows of A and of B, 4 bytes per lane.  Schedule (phases 4t..4t+3 of
 // tile t; group 1 one phase behind):
 //   group 0: B_lo(t+1) in its first memory phase of tile t; A_lo(t+2) and
 //            its scales during its second compute phase of tile t;
@@ -325,38 +333,39 @@ namespace sg {
 // one group skips are issued out of range into the sink (zero fill, no
 // memory traffic), so the code has no group-dependent branch (the compiler
 // moves MFMAs across such branches, and with them across the barriers).
-template <int Swz>
+template <int Swz, bool Fp4>
 struct PingPongMxTile {
   using Base = GemmTile<256, 256, true, false, false, Swz, 8>;
   static constexpr int kHalfBytes = 16384;
   static constexpr int kTileBytes = 2 * kHalfBytes;
-  static constexpr int kBK = 128;                          // e4m3 elements (bytes)
-  static constexpr int kScaleBytes = 2048;                 // 256 A + 256 B dwords
+  static constexpr int kBK = Fp4 ? 256 : 128;              // elements of K per tile
+  static constexpr int kScaleDw = Fp4 ? 2 : 1;             // scale dwords per row per tile
+  static constexpr int kScaleBytes = 2 * 256 * 4 * kScaleDw;
   static constexpr int kBOff = 2 * kTileBytes, kSOff = 4 * kTileBytes;
   static constexpr int kSinkOff = kSOff + 2 * kScaleBytes;
-  static constexpr int kLdsBytes = kSinkOff + kHalfBytes;  // 148 KiB
+  static constexpr int kLdsBytes = kSinkOff + kHalfBytes;  // 148 or 152 KiB
+  static constexpr int kLoads = 4 + kScaleDw + 4;          // a wave's loads of one tile
+  static constexpr int kMfmas = Fp4 ? 16 : 8;              // per compute phase
   static constexpr int kFM = 4, kFN = 2;
 
-  // Fragments of one 64-wide K step: per block two 16-byte chunks.
+  // One phase's fragments: chunk c of every 32-row block (see above).
   struct Frags {
     u32x4 a[kFM][2], b[kFN][2];
   };
 
   struct Offsets {
-    uint32_t a[2][2], b[2][2];  // [kk][chunk pair]
+    uint32_t a[2][2], b[2][2];  // [kk][c]
   };
 
-  // Lane half h supplies chunk 4kk + h (block 2kk) and chunk 4kk + 2 + h
-  // (block 2kk + 1) of the 64-wide step kk.
   __device__ __forceinline__ static Offsets offsets(int g, int w4, int lrow, int lhalf) {
     Offsets o;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t c = 4 * kk + 2 * h + lhalf;
-        o.a[kk][h] = g * kHalfBytes + lds_offset<128, Swz>(lrow, c);
-        o.b[kk][h] = (w4 >> 1) * kHalfBytes + lds_offset<128, Swz>((w4 & 1) * 64 + lrow, c);
+      for (int c = 0; c < 2; ++c) {
+        const uint32_t ch = 4 * kk + 2 * c + lhalf;
+        o.a[kk][c] = g * kHalfBytes + lds_offset<128, Swz>(lrow, ch);
+        o.b[kk][c] = (w4 >> 1) * kHalfBytes + lds_offset<128, Swz>((w4 & 1) * 64 + lrow, ch);
       }
     return o;
   }
@@ -366,42 +375,72 @@ struct PingPongMxTile {
 #pragma unroll
     for (int fm = 0; fm < kFM; ++fm)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) f.a[fm][h] = lds_read16(at, o.a[kk][h] + fm * 4096);
+      for (int c = 0; c < 2; ++c) f.a[fm][c] = lds_read16(at, o.a[kk][c] + fm * 4096);
 #pragma unroll
     for (int fn = 0; fn < kFN; ++fn)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) f.b[fn][h] = lds_read16(bt, o.b[kk][h] + fn * 4096);
+      for (int c = 0; c < 2; ++c) f.b[fn][c] = lds_read16(bt, o.b[kk][c] + fn * 4096);
   }
 
-  // The scale dwords of the wave's rows; the lane's block (lane half) is
-  // shifted into the even bytes so that op-select 2kk picks block 2kk + h.
+  // Scale dword d of the wave's rows; the lane's block (lane half) is shifted
+  // into the even bytes so that op-select 2c picks block 2c + h of the dword.
   __device__ __forceinline__ static void read_scales(uint32_t (&sa)[kFM], uint32_t (&sb)[kFN],
-                                                     const char* s, int g, int w4, int lrow,
-                                                     int lhalf) {
+                                                     const char* s, int d, int g, int w4,
+                                                     int lrow, int lhalf) {
 #pragma unroll
     for (int fm = 0; fm < kFM; ++fm)
-      sa[fm] = *reinterpret_cast<const uint32_t*>(s + 4 * (128 * g + 32 * fm + lrow)) >>
+      sa[fm] = *reinterpret_cast<const uint32_t*>(s + 1024 * d + 4 * (128 * g + 32 * fm + lrow)) >>
                (8 * lhalf);
 #pragma unroll
     for (int fn = 0; fn < kFN; ++fn)
-      sb[fn] = *reinterpret_cast<const uint32_t*>(s + 1024 + 4 * (64 * w4 + 32 * fn + lrow)) >>
+      sb[fn] = *reinterpret_cast<const uint32_t*>(s + 1024 * (kScaleDw + d) +
+                                                  4 * (64 * w4 + 32 * fn + lrow)) >>
                (8 * lhalf);
   }
 
-  // 8 scaled MFMAs; N loads (given by `issue(q)`) go out between them.
+  // One scaled MFMA: e4m3 takes both chunks (32 bytes) of the step with
+  // op-select 2kk; e2m1 takes chunk c (16 bytes) with op-select 2c.
+  template <int Sel>
+  __device__ __forceinline__ static f32x16 mfma(const u32x4& a0, const u32x4& a1,
+                                                const u32x4& b0, const u32x4& b1, f32x16 acc,
+                                                uint32_t sa, uint32_t sb) {
+    const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                      (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    const i32x8 bv = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                      (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    constexpr int kFmt = Fp4 ? 4 : 0;  // operand format: e2m1 or e4m3
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc, kFmt, kFmt, Sel,
+                                                           (int)sb, Sel, (int)sa);
+  }
+
+  // kMfmas MFMAs of phase kk; N loads (given by `issue(q)`) go out between
+  // them, the first after the first MFMA.
   template <int N, class Issue>
   __device__ __forceinline__ static void compute(f32x16 (&acc)[kFM][kFN], const Frags& f,
                                                  const uint32_t (&sa)[kFM],
                                                  const uint32_t (&sb)[kFN], int kk,
                                                  const Issue& issue) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int m = 0; m < kFM * kFN; ++m) {
-      const int fm = m >> 1, fn = m & 1;
-      acc[fm][fn] = mfma_scale_f8(f.b[fn], f.a[fm], acc[fm][fn], sb[fn], sa[fm], kk);
+    for (int m = 0; m < kMfmas; ++m) {
+      const int c = m / (kFM * kFN), fm = (m >> 1) % kFM, fn = m & 1;
+      if constexpr (Fp4) {
+        if (c == 0)
+          acc[fm][fn] = mfma<0>(f.a[fm][0], z, f.b[fn][0], z, acc[fm][fn], sa[fm], sb[fn]);
+        else
+          acc[fm][fn] = mfma<2>(f.a[fm][1], z, f.b[fn][1], z, acc[fm][fn], sa[fm], sb[fn]);
+      } else {
+        if (kk == 0)
+          acc[fm][fn] = mfma<0>(f.a[fm][0], f.a[fm][1], f.b[fn][0], f.b[fn][1], acc[fm][fn],
+                                sa[fm], sb[fn]);
+        else
+          acc[fm][fn] = mfma<2>(f.a[fm][0], f.a[fm][1], f.b[fn][0], f.b[fn][1], acc[fm][fn],
+                                sa[fm], sb[fn]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (N > 0) {
         if (m < N) issue(m);
-        if (m + 8 < N) issue(m + 8);
+        if (m + kMfmas < N) issue(m + kMfmas);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -433,12 +472,13 @@ struct PingPongMxTile {
     const bool s_is_b = w4 >= 2;
     const u32x4 rs = s_is_b ? rsb : rsa;
     const int s_valid = s_is_b ? j.n_valid : j.m_valid;
-    const uint32_t s_lds_off = (s_is_b ? 1024u : 0u) + 4u * (uint32_t)(128 * g + 64 * (w4 & 1));
+    const uint32_t s_lds_off =
+        (s_is_b ? 1024u * kScaleDw : 0u) + 4u * (uint32_t)(128 * g + 64 * (w4 & 1));
 
     const uint32_t s0 = lds_addr(smem);
     const uint32_t a_ring = s0 + g * kHalfBytes, b_ring = s0 + kBOff + g * kHalfBytes;
     const uint32_t s_ring = s0 + kSOff + s_lds_off;
-    const uint32_t kbytes = (uint32_t)K;
+    const uint32_t kbytes = (uint32_t)(Fp4 ? K / 2 : K);
     const int T = (int)(K / kBK);
 
     auto ld_a = [&](int t, int i) {
@@ -450,23 +490,26 @@ struct PingPongMxTile {
       lb.issue(rb, real ? b_ring + (t & 1) * kTileBytes : sink, w4, i, real ? b_rows : 0,
                (uint32_t)t * 128u, kbytes);
     };
-    auto ld_s = [&](int t) {
+    // Scale dword d of tile t.
+    auto ld_s = [&](int t, int d) {
       const bool ok = t < T && s_row < s_valid;
-      dma4(rs, ok ? (uint32_t)s_row * sf_pitch + 4u * (uint32_t)t : kOutOfRange,
-           s_ring + (t & 1) * kScaleBytes);
+      dma4(rs, ok ? (uint32_t)s_row * sf_pitch + 4u * (uint32_t)(kScaleDw * t + d) : kOutOfRange,
+           s_ring + (t & 1) * kScaleBytes + 1024u * d);
     };
 
     // Prologue: tile 0 whole and A(1) with its scales; group 1 also B_hi(1)
-    // (group 0 loads B_lo(1) in its first memory phase).  Per wave: 9 + 9.
+    // (group 0 loads B_lo(1) in its first memory phase).  Per wave: kLoads
+    // loads per tile.
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) ld_a(t, i);
-      ld_s(t);
+#pragma unroll
+      for (int d = 0; d < kScaleDw; ++d) ld_s(t, d);
 #pragma unroll
       for (int i = 0; i < 4; ++i) ld_b(t, i, t == 0 || g);
     }
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0 has landed
+    wait_loads_but<kLoads>();  // tile 0 has landed
     barrier();
 
     const Offsets o = offsets(g, w4, lrow, lhalf);
@@ -483,30 +526,31 @@ struct PingPongMxTile {
       const char* st = smem + kSOff + (t & 1) * kScaleBytes;
       Frags f;
       uint32_t sa[kFM], sb[kFN];
-      // Memory phase, first K step; then B_lo(t+1) (group 0).
+      // First memory phase; then B_lo(t+1) (group 0).
       read(f, at, bt, o, 0);
-      read_scales(sa, sb, st, g, w4, lrow, lhalf);
+      read_scales(sa, sb, st, 0, g, w4, lrow, lhalf);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
       for (int i = 0; i < 4; ++i) ld_b(t + 1, i, !g);
       barrier();
       compute<0>(acc, f, sa, sb, 0, [&](int) {});
       barrier();
-      // Memory phase, second K step.  Of the wave's loads only the 4 newest
-      // (the B loads just issued) may still be in flight: group 1's share of
-      // tile t+1 is then in LDS before the barrier that lets group 0 read it.
+      // Second memory phase.  Of the wave's loads only the 4 newest (the B
+      // loads just issued) may still be in flight: group 1's share of tile
+      // t+1 is then in LDS before the barrier that lets group 0 read it.
       read(f, at, bt, o, 1);
+      if constexpr (Fp4) read_scales(sa, sb, st, 1, g, w4, lrow, lhalf);
       asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
       barrier();
-      // Compute phase, second K step, with the loads of tile t+2: A half,
-      // scales, B half (group 1).  Afterwards only those 9 may be in flight:
+      // Second compute phase, with the loads of tile t+2: A half, scales,
+      // B half (group 1).  Afterwards only those kLoads may be in flight:
       // group 0's share of tile t+1 has landed.
-      compute<9>(acc, f, sa, sb, 1, [&](int q) {
+      compute<kLoads>(acc, f, sa, sb, 1, [&](int q) {
         if (q < 4) ld_a(t + 2, q);
-        else if (q == 4) ld_s(t + 2);
-        else ld_b(t + 2, q - 5, g != 0);
+        else if (q < 4 + kScaleDw) ld_s(t + 2, q - 4);
+        else ld_b(t + 2, q - 4 - kScaleDw, g != 0);
       });
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      wait_loads_but<kLoads>();
       barrier();
     }
     if (!g) barrier();
@@ -514,26 +558,36 @@ struct PingPongMxTile {
 
     Base::epilogue(acc, j, nullptr, SG_NONE, D, d_dtype, ldd, lane, g, w4);
   }
+
+  template <int N>
+  __device__ __forceinline__ static void wait_loads_but() {
+    if constexpr (N == 9)
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    static_assert(N == 9 || N == 10, "vmcnt immediate");
+  }
 };
 
-template <int Swz>
+template <int Swz, bool Fp4>
 __global__ void __launch_bounds__(512, 1) pingpong_mx_kernel(const MxParams p) {
-  using Tile = PingPongMxTile<Swz>;
+  using Tile = PingPongMxTile<Swz, Fp4>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
   const int total = p.tiles_m * p.tiles_n;
   const int t = xcd_remap(blockIdx.x, total);
   int tm, tn;
   raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
+  const int64_t row_bytes = Fp4 ? p.K / 2 : p.K;
   TileJob j;
   j.m_valid = (int)min<int64_t>(256, p.M - m0);
   j.n_valid = (int)min<int64_t>(256, p.N - n0);
-  j.a = static_cast<const char*>(p.A) + m0 * p.K;
-  j.a_pitch = (uint32_t)p.K;
-  j.a_bytes = (uint32_t)(j.m_valid * p.K);
-  j.b = static_cast<const char*>(p.B) + n0 * p.K;
-  j.b_pitch = (uint32_t)p.K;
-  j.b_bytes = (uint32_t)(j.n_valid * p.K);
+  j.a = static_cast<const char*>(p.A) + m0 * row_bytes;
+  j.a_pitch = (uint32_t)row_bytes;
+  j.a_bytes = (uint32_t)(j.m_valid * row_bytes);
+  j.b = static_cast<const char*>(p.B) + n0 * row_bytes;
+  j.b_pitch = (uint32_t)row_bytes;
+  j.b_bytes = (uint32_t)(j.n_valid * row_bytes);
   j.d_row0 = m0;
   j.n0 = n0;
   Tile::run(smem, j, static_cast<const char*>(p.SFA) + m0 * (p.K / 32),

@@ -128,6 +128,25 @@ int mx_gemm_run(int64_t M, int64_t N, int64_t K, const void* A,
                 int d_dtype, void* stream);
 
 /*
+ * mxfp4_gemm_run -- the block-scaled GEMM of mx_gemm_run with OCP FP4 E2M1
+ * elements (MXFP4): 1 sign, 2 exponent bits (bias 1), 1 fraction bit,
+ * values +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}; two elements per byte, element 2i
+ * in the low nibble of byte i.  The scale rule is mx_gemm_run's ("06
+ * Blackwell Tensor Core - tcgen05 MMA", section "Block-Scaled MMA"); the
+ * 32-element block and e8m0 scales as there.  fp32 accumulation.
+ *   A    e2m1 K-major [M][K/2] bytes;  SFA  e8m0 [M][K/32].
+ *   B    e2m1 K-major [N][K/2] bytes;  SFB  e8m0 [N][K/32].
+ *   D    [M][N] of d_dtype (SG_F32 or SG_BF16).
+ *   K    must be a multiple of 256 (one 128-byte row chunk per K tile);
+ *        M and N may be ragged.
+ * Errors: SG_ERR_NULL, SG_ERR_ALIGN, SG_ERR_SHAPE (K % 256 != 0 or
+ * extents), SG_ERR_DTYPE, SG_ERR_HIP.
+ */
+int mxfp4_gemm_run(int64_t M, int64_t N, int64_t K, const void* A,
+                   const void* SFA, const void* B, const void* SFB, void* D,
+                   int d_dtype, void* stream);
+
+/*
  * gemm_layout_run -- gemm_run's bf16 GEMM with A and B K-major (and optional
  * C) on the 256x256-tile kernel, with a chosen LDS operand layout: the layout
  * experiment of "Swizzling explained properly" (sections "Why swizzle?" and

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert {"gemm_run", "grouped_gemm_run", "mx_gemm_run", "gemm_layout_run",
+    assert {"gemm_run", "grouped_gemm_run", "mx_gemm_run", "mxfp4_gemm_run", "gemm_layout_run",
             "gemm_last_error", "gemm_version", "gemm_lds_layout",
             "gemm_lds_image"} <= set(names)
     lib = ctypes.CDLL(sg.library_path())
@@ -140,6 +140,28 @@ def _mx(**kw):
 ])
 def test_mx_rejects(kw, code):
     assert _mx(**kw) == code, sg.gemm_last_error()
+
+
+def _mx4(**kw):
+    a = dict(M=256, N=256, K=512, A=P, SFA=P, B=P, SFB=P, D=P, d_dtype=sg.SG_BF16)
+    a.update(kw)
+    return sg.mxfp4_gemm_run(a["M"], a["N"], a["K"], a["A"], a["SFA"], a["B"], a["SFB"],
+                             a["D"], a["d_dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=128), SHAPE), (dict(K=384), SHAPE), (dict(N=-1), SHAPE),
+    (dict(d_dtype=sg.SG_F16), DTYPE), (dict(d_dtype=sg.SG_E4M3), DTYPE),
+    (dict(A=None), NULL), (dict(SFB=None), NULL), (dict(D=None), NULL),
+    (dict(B=P + 8), ALIGN), (dict(SFA=P + 1), ALIGN), (dict(N=260), ALIGN),
+])
+def test_mxfp4_rejects(kw, code):
+    assert _mx4(**kw) == code, sg.gemm_last_error()
+    assert sg.gemm_last_error().startswith("mxfp4_gemm_run")
+
+
+def test_mxfp4_empty_is_ok():
+    assert _mx4(M=0) == 0 and _mx4(N=0) == 0
 
 
 @pytest.mark.parametrize("row_bytes", [64, 128, 256])

@@ -349,6 +349,55 @@ def test_mx_256_tiles_ragged(dev):
     check_close(_np(d), ref, bound, "f32", "mx 256 tiles")
 
 
+def run_mx4(case: si.MXCase, dev, d_dtype="bf16"):
+    d = sg.mxfp4_gemm(case.A.to(dev), case.SFA.to(dev), case.B.to(dev), case.SFB.to(dev),
+                      out_dtype=DT[d_dtype])
+    torch.cuda.synchronize()
+    return d
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 512), (4100, 4104, 768)])
+def test_mxfp4_ragged(dev, M, N, K):
+    # e2m1 elements; ragged M and N, an odd number of 256-wide K tiles in the
+    # second case, scales spread over 2^-17 .. 2^17.
+    case = si.mx_case(M, N, K, 23, fmt="e2m1")
+    rng = np.random.default_rng(7)
+    case.SFA = torch.from_numpy(rng.integers(110, 145, (M, K // 32)).astype(np.uint8))
+    case.SFB = torch.from_numpy(rng.integers(110, 145, (N, K // 32)).astype(np.uint8))
+    say(f"mxfp4 {M}x{N}x{K}")
+    d = run_mx4(case, dev, "f32")
+    ref, bound = oracle.mx_gemm(M, N, K, case.A, case.SFA, case.B, case.SFB, fmt="e2m1")
+    check_close(_np(d), ref, bound, "f32", "mxfp4")
+
+
+def test_mxfp4_unit_scales_exact(dev):
+    # e2m1 values are multiples of 1/2 below 8 and the scales are 1: every
+    # partial sum is exact in fp32, so the result must be bit-exact.
+    M, N, K = 520, 392, 1024
+    rng = np.random.default_rng(24)
+    A = torch.from_numpy(rng.integers(0, 256, (M, K // 2)).astype(np.uint8))
+    B = torch.from_numpy(rng.integers(0, 256, (N, K // 2)).astype(np.uint8))
+    SFA = torch.full((M, K // 32), 127, dtype=torch.uint8)
+    SFB = torch.full((N, K // 32), 127, dtype=torch.uint8)
+    case = si.MXCase(M, N, K, A, SFA, B, SFB, "f32", "mxfp4 exact", "e2m1")
+    say("mxfp4 unit scales exact")
+    d = run_mx4(case, dev, "f32")
+    ref, _ = oracle.mx_gemm(M, N, K, A, SFA, B, SFB, fmt="e2m1")
+    assert np.array_equal(_np(d), ref)
+
+
+def test_mxfp4_8192_full_size_sampled(dev):
+    case = si.mxfp4()
+    say(f"{case.name} (sampled)")
+    d = run_mx4(case, dev, "bf16")
+    assert bool(torch.isfinite(d).all())
+    rows, cols = sample_points(case.M, case.N, 3000, 56)
+    ref, bound = oracle.mx_gemm_points(case.M, case.N, case.K, case.A, case.SFA, case.B,
+                                       case.SFB, rows, cols, fmt="e2m1")
+    got = _np(d[torch.from_numpy(rows).to(dev), torch.from_numpy(cols).to(dev)])
+    check_close(got, ref, bound, "bf16", case.name)
+
+
 def test_mx_8192_full_size_sampled(dev):
     case = si.mxfp8(seed=5)
     say(f"{case.name} (sampled)")
