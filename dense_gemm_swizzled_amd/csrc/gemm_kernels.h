@@ -20,8 +20,8 @@
 //      first K step starts from zero (the accumulate-flag rule of "06
 //      Blackwell Tensor Core", section "How tcgen05.mma Executes");
 //   5. epilogue: registers -> global with optional C, no LDS staging (the
-//      output-tile swizzle "does practically nothing" per the Results of
-//      "Swizzling explained properly").
+//      Results of "Swizzling explained properly" measure no gain from
+//      swizzling the output tile).
 #pragma once
 
 #include <type_traits>
