@@ -71,10 +71,10 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(SG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// gemm_run and gemm_layout_run: validation, plan and launch.  swz is the
-// LDS layout (16 = the library's); force256 selects the 256x256 tiles
-// whatever the problem size.
-int dense_run(const char* who, int swz, bool force256, int64_t M, int64_t N, int64_t K,
+// gemm_run and gemm_layout_run: validation, plan and launch.  swz < 0 runs
+// the library's kernels; swz = 0, 8 or 16 runs the layout ablation kernel
+// with that LDS layout on 256x256 tiles whatever the problem size.
+int dense_run(const char* who, int swz, int64_t M, int64_t N, int64_t K,
               const void* A, int a_major, const void* B, int b_major, int ab_dtype,
               const void* C, int c_dtype, void* D, int d_dtype, void* stream) {
   if (M < 0 || N < 0 || K < 0)
@@ -104,7 +104,7 @@ int dense_run(const char* who, int swz, bool force256, int64_t M, int64_t N, int
                 "%s: row pitches must be multiples of 16 bytes (A %lld, B %lld, D %lld bytes)",
                 who, (long long)a_pitch, (long long)b_pitch, (long long)(N * db));
   const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256);
-  const sg::TileShape tile = force256 ? sg::kTile256 : pick_tile(tiles256);
+  const sg::TileShape tile = swz >= 0 ? sg::kTile256 : pick_tile(tiles256);
   const int64_t T = tile == sg::kTile256 ? 256 : 128;
   if (panel_extent(a_major, M, K, T, eb) >= kMaxExtent ||
       panel_extent(b_major, N, K, T, eb) >= kMaxExtent)
@@ -126,9 +126,11 @@ int dense_run(const char* who, int swz, bool force256, int64_t M, int64_t N, int
   p.tiles_m = (int)tiles_m;
   p.tiles_n = (int)tiles_n;
   p.group_m = kGroupM;
-  hipError_t e = sg::launch_dense(tile, ab_dtype == SG_BF16, a_major == SG_MN_MAJOR,
-                                  b_major == SG_MN_MAJOR, swz, p,
-                                  static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = swz >= 0 ? sg::launch_layout(swz, p, s)
+                                : sg::launch_dense(tile, ab_dtype == SG_BF16,
+                                                   a_major == SG_MN_MAJOR,
+                                                   b_major == SG_MN_MAJOR, p, s);
   if (e != hipSuccess) return hip_fail(e, who);
   return ok();
 }
@@ -140,14 +142,14 @@ extern "C" {
 const char* gemm_last_error(void) { return g_last_error.c_str(); }
 
 const char* gemm_version(void) {
-  return "swizzled_gemm 0.1 (gfx950; 16-bit MFMA 32x32x16, MXFP8 scaled MFMA "
-         "32x32x64; LDS XOR swizzle over 256-byte bank lines)";
+  return "swizzled_gemm 0.2 (gfx950; 16-bit MFMA 16x16x32 and 32x32x16, MXFP8/MXFP4 "
+         "scaled MFMA 32x32x64; LDS XOR swizzle over 256-byte bank lines)";
 }
 
 int gemm_run(int64_t M, int64_t N, int64_t K, const void* A, int a_major,
              const void* B, int b_major, int ab_dtype, const void* C, int c_dtype,
              void* D, int d_dtype, void* stream) {
-  return dense_run("gemm_run", sg::kSwzDefault, false, M, N, K, A, a_major, B, b_major,
+  return dense_run("gemm_run", -1, M, N, K, A, a_major, B, b_major,
                    ab_dtype, C, c_dtype, D, d_dtype, stream);
 }
 
@@ -156,7 +158,7 @@ int gemm_layout_run(int swz_units, int64_t M, int64_t N, int64_t K, const void* 
                     void* stream) {
   if (swz_units != 0 && swz_units != 8 && swz_units != 16)
     return fail(SG_ERR_SHAPE, "gemm_layout_run: swz_units %d is not 0, 8 or 16", swz_units);
-  return dense_run("gemm_layout_run", swz_units, true, M, N, K, A, SG_K_MAJOR, B, SG_K_MAJOR,
+  return dense_run("gemm_layout_run", swz_units, M, N, K, A, SG_K_MAJOR, B, SG_K_MAJOR,
                    SG_BF16, C, c_dtype, D, d_dtype, stream);
 }
 

@@ -218,6 +218,19 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
         __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_{bf16,f16}: lane l supplies row l%16 of its operand and
+// the 16-byte K chunk l/16 of the 32-wide K step; lane l receives rows
+// 4(l/16) .. 4(l/16)+3 of column l%16 of the 16x16 result.
+template <bool IsBF16>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (IsBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // Epilogue element conversions (round to nearest even).
 // ---------------------------------------------------------------------------

@@ -89,6 +89,117 @@ struct TileJob {
   int64_t n0;           // first output column
 };
 
+// Epilogue element work shared by every kernel.  One chunk is 4 consecutive
+// n of one output row: C as loaded (f32x4 for fp32, u32x2 for 16-bit), then
+// D = acc + C in fp32, rounded to D's type (round to nearest even).
+template <int CD>
+using c_chunk_t = typename std::conditional<CD == SG_F32, f32x4, u32x2>::type;
+
+template <int CD>
+__device__ __forceinline__ c_chunk_t<CD> load_c_chunk(const void* C, int64_t idx) {
+  if constexpr (CD == SG_F32)
+    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(C) + idx);
+  else
+    return *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(C) + idx);
+}
+
+template <int CD, int DD>
+__device__ __forceinline__ void store_d_chunk(f32x4 v, const c_chunk_t<CD>& c, void* D,
+                                              int64_t idx) {
+  if constexpr (CD == SG_F32) {
+    v += c;
+  } else if constexpr (CD == SG_BF16) {
+    v[0] += bf16_to_f32(c[0] & 0xffffu);
+    v[1] += bf16_to_f32(c[0] >> 16);
+    v[2] += bf16_to_f32(c[1] & 0xffffu);
+    v[3] += bf16_to_f32(c[1] >> 16);
+  } else if constexpr (CD == SG_F16) {
+    v[0] += f16_to_f32(c[0] & 0xffffu);
+    v[1] += f16_to_f32(c[0] >> 16);
+    v[2] += f16_to_f32(c[1] & 0xffffu);
+    v[3] += f16_to_f32(c[1] >> 16);
+  }
+  if constexpr (DD == SG_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(D) + idx) = v;
+  } else {
+    u32x2 o;
+    if constexpr (DD == SG_BF16) {
+      o[0] = pack_bf16x2(v[0], v[1]);
+      o[1] = pack_bf16x2(v[2], v[3]);
+    } else {
+      o[0] = pack_f16x2(v[0], v[1]);
+      o[1] = pack_f16x2(v[2], v[3]);
+    }
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(D) + idx) = o;
+  }
+}
+
+// Epilogue of a wave's NI x NJ blocks of 16x16 accumulators (v_mfma_f32_
+// 16x16x32 with B rows as MFMA rows): lane l of block (i, jn) holds output
+// row mw + 16i + l%16 and columns nw + 16jn + 4(l/16) .. +3 of the tile.  C
+// of the next block row is loaded before the current one is stored; C
+// addresses are clamped into the valid rectangle, stores are masked.
+template <int NJ, int CD>
+__device__ __forceinline__ void load_c_row16(c_chunk_t<CD> (&c)[NJ], const TileJob& j,
+                                             const void* C, int64_t ldd, int lane, int mw,
+                                             int nw, int i) {
+  if constexpr (CD != SG_NONE) {
+    const int ml = min(mw + 16 * i + (lane & 15), j.m_valid - 1);
+    const int64_t base = (j.d_row0 + ml) * ldd + j.n0;
+#pragma unroll
+    for (int jn = 0; jn < NJ; ++jn) {
+      const int nl = min(nw + 16 * jn + 4 * (lane >> 4), j.n_valid - 4);
+      c[jn] = load_c_chunk<CD>(C, base + nl);
+    }
+  }
+}
+
+template <int NI, int NJ, int CD, int DD>
+__device__ __forceinline__ void epilogue16_t(const f32x4 (&acc)[NI][NJ], const TileJob& j,
+                                             const void* C, void* D, int64_t ldd, int lane,
+                                             int mw, int nw) {
+  c_chunk_t<CD> cb[2][NJ];
+  load_c_row16<NJ, CD>(cb[0], j, C, ldd, lane, mw, nw, 0);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (i + 1 < NI) load_c_row16<NJ, CD>(cb[(i + 1) & 1], j, C, ldd, lane, mw, nw, i + 1);
+    const int ml = mw + 16 * i + (lane & 15);
+    if (ml >= j.m_valid) continue;
+    const int64_t row = (j.d_row0 + ml) * ldd + j.n0;
+#pragma unroll
+    for (int jn = 0; jn < NJ; ++jn) {
+      const int nl = nw + 16 * jn + 4 * (lane >> 4);
+      if (nl >= j.n_valid) continue;
+      store_d_chunk<CD, DD>(acc[i][jn], cb[i & 1][jn], D, row + nl);
+    }
+  }
+}
+
+// The same with the element types chosen at run time.
+template <int NI, int NJ>
+__device__ __forceinline__ void epilogue16(const f32x4 (&acc)[NI][NJ], const TileJob& j,
+                                           const void* C, int c_dtype, void* D, int d_dtype,
+                                           int64_t ldd, int lane, int mw, int nw) {
+#define SG_EPI(CD, DD) return epilogue16_t<NI, NJ, CD, DD>(acc, j, C, D, ldd, lane, mw, nw)
+  if (d_dtype == SG_F32) {
+    if (c_dtype == SG_F32) SG_EPI(SG_F32, SG_F32);
+    if (c_dtype == SG_BF16) SG_EPI(SG_BF16, SG_F32);
+    if (c_dtype == SG_F16) SG_EPI(SG_F16, SG_F32);
+    SG_EPI(SG_NONE, SG_F32);
+  }
+  if (d_dtype == SG_BF16) {
+    if (c_dtype == SG_F32) SG_EPI(SG_F32, SG_BF16);
+    if (c_dtype == SG_BF16) SG_EPI(SG_BF16, SG_BF16);
+    if (c_dtype == SG_F16) SG_EPI(SG_F16, SG_BF16);
+    SG_EPI(SG_NONE, SG_BF16);
+  }
+  if (c_dtype == SG_F32) SG_EPI(SG_F32, SG_F16);
+  if (c_dtype == SG_BF16) SG_EPI(SG_BF16, SG_F16);
+  if (c_dtype == SG_F16) SG_EPI(SG_F16, SG_F16);
+  SG_EPI(SG_NONE, SG_F16);
+#undef SG_EPI
+}
+
 // Waves = 4: one wave per SIMD, each wave owns a (BM/2) x (BN/2) block.
 // Waves = 8: two waves per SIMD (the hardware interleaves them, and twice as
 // many waves issue the direct-to-LDS loads), each owning (BM/2) x (BN/4).
@@ -348,9 +459,8 @@ struct GemmTile {
     return epilogue_t<SG_NONE, SG_F16>(acc, j, C, D, ldd, lane, wm, wn);
   }
 
-  // One chunk of C (4 elements) as loaded: f32x4 for fp32, u32x2 for 16-bit.
   template <int CD>
-  using CChunk = typename std::conditional<CD == SG_F32, f32x4, u32x2>::type;
+  using CChunk = c_chunk_t<CD>;
 
   template <int CD>
   __device__ __forceinline__ static void load_c_block(CChunk<CD> (&c)[4 * kFN],
@@ -365,12 +475,7 @@ struct GemmTile {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int nl = min(wn * kWN + fn * 32 + 8 * q + 4 * (lane >> 5), j.n_valid - 4);
-          if constexpr (CD == SG_F32)
-            c[4 * fn + q] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(C) +
-                                                            base + nl);
-          else
-            c[4 * fn + q] = *reinterpret_cast<const u32x2*>(
-                static_cast<const uint16_t*>(C) + base + nl);
+          c[4 * fn + q] = load_c_chunk<CD>(C, base + nl);
         }
     }
   }
@@ -394,35 +499,9 @@ struct GemmTile {
           const int nl = wn * kWN + fn * 32 + 8 * q + 4 * (lane >> 5);
           if (nl >= j.n_valid) continue;
           const int64_t idx = row * ldd + j.n0 + nl;
-          f32x4 v = {acc[fm][fn][4 * q + 0], acc[fm][fn][4 * q + 1],
-                     acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
-          const CChunk<CD>& c2 = cb[fm & 1][4 * fn + q];
-          if constexpr (CD == SG_F32) {
-            v += c2;
-          } else if constexpr (CD == SG_BF16) {
-            v[0] += bf16_to_f32(c2[0] & 0xffffu);
-            v[1] += bf16_to_f32(c2[0] >> 16);
-            v[2] += bf16_to_f32(c2[1] & 0xffffu);
-            v[3] += bf16_to_f32(c2[1] >> 16);
-          } else if constexpr (CD == SG_F16) {
-            v[0] += f16_to_f32(c2[0] & 0xffffu);
-            v[1] += f16_to_f32(c2[0] >> 16);
-            v[2] += f16_to_f32(c2[1] & 0xffffu);
-            v[3] += f16_to_f32(c2[1] >> 16);
-          }
-          if constexpr (DD == SG_F32) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(D) + idx) = v;
-          } else {
-            u32x2 o;
-            if constexpr (DD == SG_BF16) {
-              o[0] = pack_bf16x2(v[0], v[1]);
-              o[1] = pack_bf16x2(v[2], v[3]);
-            } else {
-              o[0] = pack_f16x2(v[0], v[1]);
-              o[1] = pack_f16x2(v[2], v[3]);
-            }
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(D) + idx) = o;
-          }
+          const f32x4 v = {acc[fm][fn][4 * q + 0], acc[fm][fn][4 * q + 1],
+                           acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
+          store_d_chunk<CD, DD>(v, cb[fm & 1][4 * fn + q], D, idx);
         }
       }
     }

@@ -11,10 +11,13 @@ namespace sg {
 // Tile shapes the planner chooses between.
 enum TileShape { kTile256 = 0, kTile128 = 1 };
 
-// Launches the dense kernel for (tile, dtype, majorness); swz selects the
-// LDS layout (0, 8 or 16 units per line).  Returns the launch status.
+// Launches the dense kernel for (tile, dtype, majorness).  Returns the
+// launch status.
 hipError_t launch_dense(TileShape tile, bool bf16, bool a_mn, bool b_mn,
-                        int swz, const DenseParams& p, hipStream_t s);
+                        const DenseParams& p, hipStream_t s);
+// The layout ablation: bf16, K-major operands, 256x256 tiles on the 32x32x16
+// ping-pong kernel with the LDS layout swz (0, 8 or 16 units per line).
+hipError_t launch_layout(int swz, const DenseParams& p, hipStream_t s);
 hipError_t launch_grouped(TileShape tile, bool bf16, int swz,
                           const GroupedParams& p, int grid, hipStream_t s);
 hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s);

@@ -2,6 +2,7 @@
 // grouped kernels.
 #include "launch.h"
 #include "pingpong.h"
+#include "pingpong16.h"
 
 namespace sg {
 
@@ -22,11 +23,21 @@ hipError_t go_dense(const DenseParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 256x256 tiles with both operands K-major run the ping-pong mainloop.
+// 256x256 tiles with both operands K-major run the ping-pong mainloop with
+// 16x16x32 MFMAs.
 template <bool BF, int Swz>
 hipError_t go_pingpong(const DenseParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((pingpong_gemm_kernel<BF, Swz>), dim3(p.tiles_m * p.tiles_n), dim3(512),
+  hipLaunchKernelGGL((pingpong16_gemm_kernel<BF, Swz>), dim3(p.tiles_m * p.tiles_n), dim3(512),
                      0, s, p);
+  return hipGetLastError();
+}
+
+// The layout ablation runs the ping-pong mainloop with 32x32x16 MFMAs, the
+// kernel its measurements were taken with.
+template <int Swz>
+hipError_t go_pingpong32(const DenseParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((pingpong_gemm_kernel<true, Swz>), dim3(p.tiles_m * p.tiles_n),
+                     dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
@@ -48,16 +59,16 @@ hipError_t dense_by_dtype(bool bf16, bool a_mn, bool b_mn, const DenseParams& p,
 
 }  // namespace
 
-hipError_t launch_dense(TileShape tile, bool bf16, bool a_mn, bool b_mn, int swz,
+hipError_t launch_dense(TileShape tile, bool bf16, bool a_mn, bool b_mn,
                         const DenseParams& p, hipStream_t s) {
-  if (swz == 16) {
-    return tile == kTile256 ? dense_by_dtype<256, 256, 16>(bf16, a_mn, b_mn, p, s)
-                            : dense_by_dtype<128, 128, 16>(bf16, a_mn, b_mn, p, s);
-  }
-  // Layout ablation variants: bf16, K-major operands, 256x256 ping-pong tiles.
-  if (tile != kTile256 || !bf16 || a_mn || b_mn) return hipErrorInvalidValue;
-  if (swz == 8) return go_pingpong<true, 8>(p, s);
-  if (swz == 0) return go_pingpong<true, 0>(p, s);
+  return tile == kTile256 ? dense_by_dtype<256, 256, 16>(bf16, a_mn, b_mn, p, s)
+                          : dense_by_dtype<128, 128, 16>(bf16, a_mn, b_mn, p, s);
+}
+
+hipError_t launch_layout(int swz, const DenseParams& p, hipStream_t s) {
+  if (swz == 16) return go_pingpong32<16>(p, s);
+  if (swz == 8) return go_pingpong32<8>(p, s);
+  if (swz == 0) return go_pingpong32<0>(p, s);
   return hipErrorInvalidValue;
 }
 
@@ -66,9 +77,9 @@ hipError_t launch_grouped(TileShape tile, bool bf16, int swz, const GroupedParam
   if (swz != 16) return hipErrorInvalidValue;
   if (tile == kTile256) {
     if (bf16)
-      hipLaunchKernelGGL((pingpong_grouped_kernel<true, 16>), dim3(grid), dim3(512), 0, s, p);
+      hipLaunchKernelGGL((pingpong16_grouped_kernel<true, 16>), dim3(grid), dim3(512), 0, s, p);
     else
-      hipLaunchKernelGGL((pingpong_grouped_kernel<false, 16>), dim3(grid), dim3(512), 0, s, p);
+      hipLaunchKernelGGL((pingpong16_grouped_kernel<false, 16>), dim3(grid), dim3(512), 0, s, p);
   } else {
     if (bf16)
       hipLaunchKernelGGL((grouped_gemm_kernel<128, 128, true, 16, 4>), dim3(grid),

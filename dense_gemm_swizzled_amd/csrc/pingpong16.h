@@ -1,0 +1,297 @@
+// pingpong16.h -- the 8-wave ping-pong mainloop (pingpong.h) computed with
+// v_mfma_f32_16x16x32 instead of v_mfma_f32_32x32x16.
+//
+// Why.  The GEMM runs at the clock its power allows, and the power depends on
+// the data.  Measured on MI355X with random operands and the MFMA pipe 96%
+// busy, 16x16x32 MFMAs hold 2.37 GHz where 32x32x16 MFMAs of the same FLOPs
+// drop to 2.08 GHz.  A 16x16x32 MFMA takes 16 cycles, so one wave per SIMD
+// cannot issue its fragment reads and loads between them; the ping-pong's
+// second wave per SIMD does that work.
+//
+// Everything but the MFMA shape is the ping-pong of pingpong.h: the roles,
+// phases, LDS rings, loads, waits and barriers.  Wave w4 of group g owns
+// output rows [128g, +128) and columns [64 w4, +64) as 8x4 blocks of 16x16
+// accumulators (128 accumulator registers).  A phase covers 32 of K: 12
+// fragment reads (lane l: row l%16 of a 16-row block, 16-byte chunk 4kh +
+// l/16 of the row, conflict-free under the swizzle) and 32 MFMAs with the
+// four loads of a half tile between them, one per eight MFMAs.
+#pragma once
+
+#include "pingpong.h"
+
+namespace sg {
+
+// buffer_load_dwordx4 ... lds with the LDS address m0 = lds_base + imm and an
+// SGPR byte offset `soff` added to the global address (three instructions:
+// the m0 write, the wait state it needs, the load).
+template <int Imm>
+__device__ __forceinline__ void dma16_so(u32x4 rsrc, uint32_t voff, uint32_t soff,
+                                         uint32_t lds_base) {
+  asm volatile(
+      "s_add_u32 m0, %1, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %2, %3 offen lds"
+      :
+      : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(rsrc),
+        "s"(__builtin_amdgcn_readfirstlane(soff)), "i"(Imm)
+      : "memory", "m0", "scc");
+}
+
+// The half-tile loader for K a multiple of 64: each lane's four row offsets
+// (out of range for rows past the operand) are fixed per tile job, and the K
+// position of a load travels in the instruction's SGPR offset; a K tile past
+// the end is loaded through a descriptor with no records (zero fill).
+template <int Swz>
+struct KExactHalfLoader {
+  uint32_t voff[4];
+
+  __device__ __forceinline__ void init(const HalfLoader<Swz>& h, int rows_valid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      voff[i] = h.row + 32 * i < rows_valid ? h.base + (uint32_t)(32 * i) * h.pitch
+                                            : kOutOfRange;
+  }
+
+  template <int I>
+  __device__ __forceinline__ void issue(u32x4 rsrc, uint32_t half, int w4,
+                                        uint32_t kbyte0) const {
+    dma16_so<I * 4096>(rsrc, voff[I], kbyte0, half + (uint32_t)w4 * 1024u);
+  }
+};
+
+template <bool IsBF16, int Swz>
+struct PingPong16Tile {
+  using PP = PingPongTile<IsBF16, Swz>;
+  static constexpr int kHalfBytes = PP::kHalfBytes;
+  static constexpr int kTileBytes = PP::kTileBytes;
+  static constexpr int kBK = PP::kBK;
+  static constexpr int kARing = PP::kARing, kBRing = PP::kBRing;
+  static constexpr int kLdsBytes = PP::kLdsBytes;  // 160 KiB
+  static constexpr int kI = 8, kJ = 4;              // 16x16 blocks per wave (M, N)
+
+  // Fragments of one 32-wide K half of a tile.
+  struct Frags {
+    u32x4 a[kI], b[kJ];
+  };
+
+  // Per-lane byte offsets inside an operand's K tile: [K half][block
+  // parity]; block 2p+q is 4096 p bytes past entry q (blocks 32 rows apart
+  // share the XOR key).
+  struct Offsets {
+    uint32_t a[2][2], b[2][2];
+  };
+
+  __device__ __forceinline__ static Offsets offsets(int g, int w4, int lane) {
+    const int r = lane & 15, c = lane >> 4;
+    Offsets o;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        o.a[kh][q] = g * kHalfBytes + lds_offset<128, Swz>(16 * q + r, 4 * kh + c);
+        o.b[kh][q] = (w4 >> 1) * kHalfBytes +
+                     lds_offset<128, Swz>((w4 & 1) * 64 + 16 * q + r, 4 * kh + c);
+      }
+    return o;
+  }
+
+  __device__ __forceinline__ static void read(Frags& f, const char* at, const char* bt,
+                                              const Offsets& o, int kh) {
+#pragma unroll
+    for (int i = 0; i < kI; ++i) f.a[i] = lds_read16(at, o.a[kh][i & 1] + (i >> 1) * 4096);
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) f.b[j] = lds_read16(bt, o.b[kh][j & 1] + (j >> 1) * 4096);
+  }
+
+  // 32 MFMAs with the four loads of one half tile between them, one per
+  // eight MFMAs (without the MFMAs for a wave whose output rows are all past
+  // M: it still loads its share and keeps the barriers).  MFMA rows take B
+  // rows (n), columns take A rows (m).
+  template <bool Active>
+  __device__ __forceinline__ static void compute(f32x4 (&acc)[kI][kJ], const Frags& f,
+                                                 const HalfLoader<Swz>& ld, u32x4 rsrc,
+                                                 uint32_t half, int w4, int rows_valid,
+                                                 uint32_t kbyte0, uint32_t kbytes) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int mm = 8 * q + m, i = mm >> 2, j = mm & 3;
+        if constexpr (Active) acc[i][j] = mfma16x16x32<IsBF16>(f.b[j], f.a[i], acc[i][j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      ld.issue(rsrc, half, w4, q, rows_valid, kbyte0, kbytes);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // The same with the K-exact loader.
+  template <bool Active>
+  __device__ __forceinline__ static void compute_x(f32x4 (&acc)[kI][kJ], const Frags& f,
+                                                   const KExactHalfLoader<Swz>& ld, u32x4 rsrc,
+                                                   uint32_t half, int w4, uint32_t kbyte0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int mm = 8 * q + m, i = mm >> 2, j = mm & 3;
+        if constexpr (Active) acc[i][j] = mfma16x16x32<IsBF16>(f.b[j], f.a[i], acc[i][j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (q == 0) ld.template issue<0>(rsrc, half, w4, kbyte0);
+      if (q == 1) ld.template issue<1>(rsrc, half, w4, kbyte0);
+      if (q == 2) ld.template issue<2>(rsrc, half, w4, kbyte0);
+      if (q == 3) ld.template issue<3>(rsrc, half, w4, kbyte0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Mainloop for K a multiple of 64: the K tiles t+2 >= T load through the
+  // empty descriptors `ra0`, `rb0`.
+  template <bool Active>
+  __device__ __forceinline__ static void mainloop_x(f32x4 (&acc)[kI][kJ],
+                                                    const KExactHalfLoader<Swz>& la,
+                                                    const KExactHalfLoader<Swz>& lb, u32x4 ra,
+                                                    u32x4 rb, u32x4 ra0, u32x4 rb0,
+                                                    uint32_t a_ring, uint32_t b_ring,
+                                                    const char* a_rd, const char* b_rd,
+                                                    const Offsets& o, int g, int w4, int T) {
+    if (g) PP::barrier();  // group 1 runs one phase behind group 0
+    int bs = 0;            // t mod 3
+    for (int t = 0; t < T; ++t) {
+      const int as = t & 1, bs2 = bs == 0 ? 2 : bs - 1;  // (t+2) mod 2, (t+2) mod 3
+      const char* at = a_rd + as * kTileBytes;
+      const char* bt = b_rd + bs * kTileBytes;
+      const uint32_t k2 = (uint32_t)(t + 2) * 128u;
+      const bool in_k = t + 2 < T;
+      const u32x4 rat = in_k ? ra : ra0, rbt = in_k ? rb : rb0;
+      Frags f;
+      if constexpr (Active) read(f, at, bt, o, 0);
+      PP::end_phase();
+      compute_x<Active>(acc, f, lb, rbt, b_ring + bs2 * kTileBytes, w4, k2);
+      PP::end_phase();
+      if constexpr (Active) read(f, at, bt, o, 1);
+      PP::end_phase();
+      compute_x<Active>(acc, f, la, rat, a_ring + as * kTileBytes, w4, k2);
+      PP::end_phase();
+      bs = bs == 2 ? 0 : bs + 1;
+    }
+    if (!g) PP::barrier();
+  }
+
+  template <bool Active>
+  __device__ __forceinline__ static void mainloop(f32x4 (&acc)[kI][kJ],
+                                                  const HalfLoader<Swz>& la,
+                                                  const HalfLoader<Swz>& lb, u32x4 ra, u32x4 rb,
+                                                  int a_rows, int b_rows, uint32_t a_ring,
+                                                  uint32_t b_ring, const char* a_rd,
+                                                  const char* b_rd, const Offsets& o, int g,
+                                                  int w4, int T, uint32_t kbytes) {
+    if (g) PP::barrier();  // group 1 runs one phase behind group 0
+    int bs = 0;            // t mod 3
+    for (int t = 0; t < T; ++t) {
+      const int as = t & 1, bs2 = bs == 0 ? 2 : bs - 1;  // (t+2) mod 2, (t+2) mod 3
+      const char* at = a_rd + as * kTileBytes;
+      const char* bt = b_rd + bs * kTileBytes;
+      const uint32_t k2 = (uint32_t)(t + 2) * 128u;
+      Frags f;
+      if constexpr (Active) read(f, at, bt, o, 0);
+      PP::end_phase();
+      compute<Active>(acc, f, lb, rb, b_ring + bs2 * kTileBytes, w4, b_rows, k2, kbytes);
+      PP::end_phase();
+      if constexpr (Active) read(f, at, bt, o, 1);
+      PP::end_phase();
+      compute<Active>(acc, f, la, ra, a_ring + as * kTileBytes, w4, a_rows, k2, kbytes);
+      PP::end_phase();
+      bs = bs == 2 ? 0 : bs + 1;
+    }
+    if (!g) PP::barrier();
+  }
+
+  // Mainloop and epilogue of one tile; `smem` is the 160 KiB of LDS.
+  __device__ __forceinline__ static void run(char* smem, const TileJob& j, int64_t K,
+                                             const void* C, int c_dtype, void* D,
+                                             int d_dtype, int64_t ldd) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = wave >> 2, w4 = wave & 3;
+
+    // Group g loads rows [128g, 128g+128) of both operands.
+    const u32x4 ra = rsrc_words(j.a, j.a_bytes), rb = rsrc_words(j.b, j.b_bytes);
+    const int a_rows = j.m_valid - 128 * g, b_rows = j.n_valid - 128 * g;
+    HalfLoader<Swz> la, lb;
+    la.init(w4, lane, j.a_pitch);
+    lb.init(w4, lane, j.b_pitch);
+    la.base += (uint32_t)(128 * g) * j.a_pitch;
+    lb.base += (uint32_t)(128 * g) * j.b_pitch;
+
+    const uint32_t s0 = lds_addr(smem);
+    const uint32_t a_ring = s0 + g * kHalfBytes;                       // + (t%2) tiles
+    const uint32_t b_ring = s0 + kARing * kTileBytes + g * kHalfBytes; // + (t%3) tiles
+    const char* a_rd = smem;
+    const char* b_rd = smem + kARing * kTileBytes;
+
+    const uint32_t kbytes = (uint32_t)K * 2u;
+    const int T = (int)((K + kBK - 1) / kBK);
+
+    // Tiles 0 and 1 (B before A, the order the mainloop keeps).
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lb.issue(rb, b_ring + t * kTileBytes, w4, i, b_rows, t * 128u, kbytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        la.issue(ra, a_ring + t * kTileBytes, w4, i, a_rows, t * 128u, kbytes);
+    }
+    PP::end_phase();
+
+    const Offsets o = offsets(g, w4, lane);
+    f32x4 acc[kI][kJ];
+#pragma unroll
+    for (int i = 0; i < kI; ++i)
+#pragma unroll
+      for (int k = 0; k < kJ; ++k) acc[i][k] = f32x4{};
+
+    // A wave whose 128 output rows all lie past M (the second group of a tile
+    // with at most 128 valid rows) runs the mainloop without its MFMAs.
+    if ((K & (kBK - 1)) == 0) {
+      KExactHalfLoader<Swz> xa, xb;
+      xa.init(la, a_rows);
+      xb.init(lb, b_rows);
+      const u32x4 ra0 = rsrc_words(j.a, 0), rb0 = rsrc_words(j.b, 0);
+      if (a_rows > 0)
+        mainloop_x<true>(acc, xa, xb, ra, rb, ra0, rb0, a_ring, b_ring, a_rd, b_rd, o, g, w4, T);
+      else
+        mainloop_x<false>(acc, xa, xb, ra, rb, ra0, rb0, a_ring, b_ring, a_rd, b_rd, o, g, w4,
+                          T);
+    } else if (a_rows > 0) {
+      mainloop<true>(acc, la, lb, ra, rb, a_rows, b_rows, a_ring, b_ring, a_rd, b_rd, o, g, w4,
+                     T, kbytes);
+    } else {
+      mainloop<false>(acc, la, lb, ra, rb, a_rows, b_rows, a_ring, b_ring, a_rd, b_rd, o, g,
+                      w4, T, kbytes);
+    }
+    wait_vmem();  // the zero-filled loads past K
+
+    epilogue16<kI, kJ>(acc, j, C, c_dtype, D, d_dtype, ldd, lane, 128 * g, 64 * w4);
+  }
+};
+
+template <bool IsBF16, int Swz>
+__global__ void __launch_bounds__(512, 1) pingpong16_gemm_kernel(const DenseParams p) {
+  using Tile = PingPong16Tile<IsBF16, Swz>;
+  __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+  const TileJob j = dense_tile_job<256, 256, false, false>(p, blockIdx.x);
+  Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.N);
+}
+
+template <bool IsBF16, int Swz>
+__global__ void __launch_bounds__(512, 1) pingpong16_grouped_kernel(const GroupedParams p) {
+  using Tile = PingPong16Tile<IsBF16, Swz>;
+  __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+  const TileJob j = grouped_tile_job<256, 256>(p, blockIdx.x);
+  Tile::run(smem, j, p.K, nullptr, SG_NONE, p.D, p.d_dtype, p.N);
+}
+
+}  // namespace sg

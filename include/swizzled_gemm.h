@@ -147,10 +147,11 @@ int mxfp4_gemm_run(int64_t M, int64_t N, int64_t K, const void* A,
                    int d_dtype, void* stream);
 
 /*
- * gemm_layout_run -- gemm_run's bf16 GEMM with A and B K-major (and optional
- * C) on the 256x256-tile kernel, with a chosen LDS operand layout: the layout
- * experiment of "Swizzling explained properly" (sections "Why swizzle?" and
- * "Results") on gfx950.
+ * gemm_layout_run -- the bf16 GEMM with A and B K-major (and optional C) on
+ * 256x256 tiles of the 8-wave ping-pong kernel with 32x32x16 MFMAs (the
+ * 16x16x32 variant of gemm_run reads fragments in another lane pattern), with
+ * a chosen LDS operand layout: the layout experiment of "Swizzling explained
+ * properly" (sections "Why swizzle?" and "Results") on gfx950.
  *   swz_units  16: the library's layout (the 16-byte unit index XORed with
  *              the 256-byte bank-line index: ds_read_b128 reads 64 banks of
  *              4 bytes); 8: the same XOR over 128-byte lines; 0: no swizzle.

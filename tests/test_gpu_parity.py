@@ -145,9 +145,13 @@ def test_dense_epilogue_dtypes(dev, c_dtype, d_dtype):
     check_close(_np(d), ref, bound, "f32" if d_dtype == "f32" else "bf16", "epilogue")
 
 
-def test_dense_256_tiles_ragged(dev):
-    # 17 x 17 tiles of 256 -> the 256x256 variant, ragged in M, N and K.
-    M, N, K = 4100, 4104, 136
+@pytest.mark.parametrize("K", [136, 192])
+def test_dense_256_tiles_ragged(dev, K):
+    # 17 x 17 tiles of 256 -> the 256x256 variant, ragged in M and N (the last
+    # tile row has 4 valid rows: its second wave group skips its MFMAs); K =
+    # 136 takes the loader with per-load K checks, K = 192 (a multiple of 64)
+    # the loader with fixed row offsets.
+    M, N = 4100, 4104
     case = si.dense_case(M, N, K, 11, ab_dtype="bf16", with_c=True, c_dtype="bf16",
                          d_dtype="bf16", scale=1.0 / np.sqrt(K))
     say(f"dense 256-tile path {M}x{N}x{K}")
@@ -194,6 +198,20 @@ def test_dense_integer_inputs_exact(dev):
     b = si.integer_valued((N, K), 92)
     A, B = si.to_bf16(a), si.to_bf16(b)
     say("integer-valued exact")
+    d = sg.gemm(A.to(dev), B.to(dev), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = a.astype(np.int64) @ b.astype(np.int64).T
+    assert np.array_equal(d.cpu().numpy().astype(np.int64), want)
+
+
+def test_dense_256_tiles_integer_inputs_exact(dev):
+    # The same on the 256x256 variant (17 x 17 tiles, ragged M and N): every
+    # partial sum of values in [-4, 4] over K = 256 is exact in fp32.
+    M, N, K = 4100, 4104, 256
+    a = si.integer_valued((M, K), 93)
+    b = si.integer_valued((N, K), 94)
+    A, B = si.to_bf16(a), si.to_bf16(b)
+    say(f"integer-valued exact, 256 tiles {M}x{N}x{K}")
     d = sg.gemm(A.to(dev), B.to(dev), out_dtype=torch.float32)
     torch.cuda.synchronize()
     want = a.astype(np.int64) @ b.astype(np.int64).T
@@ -260,12 +278,13 @@ def test_grouped_small_with_empty_groups(dev):
     check_close(_np(d), ref, bound, "f32", "grouped small")
 
 
-def test_grouped_256_tiles_ragged(dev):
-    # Enough tiles for the 256x256 variant; group sizes off the tile grid,
-    # an empty group, and K = 3 * 64 + 8.
+@pytest.mark.parametrize("K", [200, 256])
+def test_grouped_256_tiles_ragged(dev, K):
+    # Enough tiles for the 256x256 variant; group sizes off the tile grid, an
+    # empty group, and K = 3 * 64 + 8 (per-load K checks) or 4 * 64.
     m_sizes = [300, 1, 0, 777, 2000, 513, 1200]
-    case = si.grouped_case(m_sizes, 4096, 200, 13, d_dtype="f32")
-    say(f"grouped 256-tile path {m_sizes} x 4096 x 200")
+    case = si.grouped_case(m_sizes, 4096, K, 13, d_dtype="f32")
+    say(f"grouped 256-tile path {m_sizes} x 4096 x {K}")
     d = sg.grouped_gemm(case.A.to(dev), case.B.to(dev), case.m_offsets,
                         out_dtype=torch.float32)
     torch.cuda.synchronize()

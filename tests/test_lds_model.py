@@ -9,8 +9,8 @@ this module derives the model (bank line = the smallest conflicting stride;
 lane phases = groups of lanes that conflict with one another), checks that
 the oracle's bank simulator then reproduces every measured counter exactly,
 and finally checks that every LDS instruction the GEMM kernels issue --
-operand reads of the 16-bit and MX kernels, K-major and MN-major loader
-stores -- has degree 1 (no conflict) under that model, using the kernels'
+operand reads of the 16-bit (32x32x16 and 16x16x32) and MX kernels, K-major
+and MN-major loader stores -- has degree 1 (no conflict) under that model, using the kernels'
 own LDS map exported through the C ABI.
 """
 import importlib.util
@@ -131,6 +131,13 @@ def test_kernel_operand_reads_conflict_free(model, tile):
             for kk in range(4):
                 a = [int(lds[base + l % 32, 2 * kk + l // 32]) for l in range(64)]
                 worst = max(worst, _degree(model, "r128", a))
+            # 16-bit MFMA 16x16x32 (256x256 tiles): lane l -> row l%16 of a
+            # 16-row block, chunk 4*kk + l/16.
+            for sub in range(2):
+                for kk in range(2):
+                    a = [int(lds[base + 16 * sub + l % 16, 4 * kk + l // 16])
+                         for l in range(64)]
+                    worst = max(worst, _degree(model, "r128", a))
             # MXFP8 32x32x64: two reads, chunks 4*kk + 2*h + l/32.
             for kk in range(2):
                 for h in range(2):
