@@ -158,19 +158,35 @@ template <int NI, int NJ, int CD, int DD>
 __device__ __forceinline__ void epilogue16_t(const f32x4 (&acc)[NI][NJ], const TileJob& j,
                                              const void* C, void* D, int64_t ldd, int lane,
                                              int mw, int nw) {
-  c_chunk_t<CD> cb[2][NJ];
-  load_c_row16<NJ, CD>(cb[0], j, C, ldd, lane, mw, nw, 0);
+  // C is loaded a group of kG block rows at a time, the next group before
+  // the current one is stored: all of the wave's C at once when it fits in
+  // 64 registers (16-bit C of 8x4 blocks), else groups of 32 registers.
+  constexpr int kRegs = CD == SG_F32 ? 4 : 2;  // registers per chunk
+  constexpr int kAll = NI * NJ * kRegs <= 64;
+  constexpr int kG0 = 32 / (NJ * kRegs);
+  constexpr int kG = kAll ? NI : (kG0 < 1 ? 1 : kG0);
+  c_chunk_t<CD> cb[2][kG][NJ];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    if (i + 1 < NI) load_c_row16<NJ, CD>(cb[(i + 1) & 1], j, C, ldd, lane, mw, nw, i + 1);
-    const int ml = mw + 16 * i + (lane & 15);
-    if (ml >= j.m_valid) continue;
-    const int64_t row = (j.d_row0 + ml) * ldd + j.n0;
+  for (int i = 0; i < kG; ++i) load_c_row16<NJ, CD>(cb[0][i], j, C, ldd, lane, mw, nw, i);
 #pragma unroll
-    for (int jn = 0; jn < NJ; ++jn) {
-      const int nl = nw + 16 * jn + 4 * (lane >> 4);
-      if (nl >= j.n_valid) continue;
-      store_d_chunk<CD, DD>(acc[i][jn], cb[i & 1][jn], D, row + nl);
+  for (int g0 = 0; g0 < NI; g0 += kG) {
+    if (g0 + kG < NI) {
+#pragma unroll
+      for (int i = 0; i < kG; ++i)
+        load_c_row16<NJ, CD>(cb[((g0 / kG) + 1) & 1][i], j, C, ldd, lane, mw, nw, g0 + kG + i);
+    }
+#pragma unroll
+    for (int ii = 0; ii < kG; ++ii) {
+      const int i = g0 + ii;
+      const int ml = mw + 16 * i + (lane & 15);
+      if (ml >= j.m_valid) continue;
+      const int64_t row = (j.d_row0 + ml) * ldd + j.n0;
+#pragma unroll
+      for (int jn = 0; jn < NJ; ++jn) {
+        const int nl = nw + 16 * jn + 4 * (lane >> 4);
+        if (nl >= j.n_valid) continue;
+        store_d_chunk<CD, DD>(acc[i][jn], cb[(g0 / kG) & 1][ii][jn], D, row + nl);
+      }
     }
   }
 }

@@ -106,7 +106,10 @@ struct PingPong16Tile {
   // 32 MFMAs with the four loads of one half tile between them, one per
   // eight MFMAs (without the MFMAs for a wave whose output rows are all past
   // M: it still loads its share and keeps the barriers).  MFMA rows take B
-  // rows (n), columns take A rows (m).
+  // rows (n), columns take A rows (m).  The blocks go in snake order (row i
+  // of blocks left to right, row i+1 right to left), so consecutive MFMAs
+  // always share an operand: measured 1.5-2% more clock at the power limit
+  // than restarting each row at block 0.
   template <bool Active>
   __device__ __forceinline__ static void compute(f32x4 (&acc)[kI][kJ], const Frags& f,
                                                  const HalfLoader<Swz>& ld, u32x4 rsrc,
@@ -116,7 +119,7 @@ struct PingPong16Tile {
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const int mm = 8 * q + m, i = mm >> 2, j = mm & 3;
+        const int mm = 8 * q + m, i = mm >> 2, j = (i & 1) ? 3 - (mm & 3) : (mm & 3);
         if constexpr (Active) acc[i][j] = mfma16x16x32<IsBF16>(f.b[j], f.a[i], acc[i][j]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -134,7 +137,7 @@ struct PingPong16Tile {
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const int mm = 8 * q + m, i = mm >> 2, j = mm & 3;
+        const int mm = 8 * q + m, i = mm >> 2, j = (i & 1) ? 3 - (mm & 3) : (mm & 3);
         if constexpr (Active) acc[i][j] = mfma16x16x32<IsBF16>(f.b[j], f.a[i], acc[i][j]);
       }
       __builtin_amdgcn_sched_barrier(0);
