@@ -27,7 +27,8 @@ __all__ = [
     "gemm_run", "grouped_gemm_run", "mx_gemm_run", "mxfp4_gemm_run", "gemm_layout_run",
     "gemm_last_error",
     "gemm_version", "gemm_lds_layout", "gemm_lds_image",
-    "gemm", "grouped_gemm", "mx_gemm", "mxfp4_gemm", "gemm_layout", "library_path", "load",
+    "gemm", "gemm_strided", "grouped_gemm", "mx_gemm", "mxfp4_gemm", "gemm_layout",
+    "library_path", "load",
 ]
 
 SG_OK = 0
@@ -65,6 +66,9 @@ def load():
     lib = ctypes.CDLL(_LIB_PATH)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     lib.gemm_run.argtypes = [i64, i64, i64, vp, i32, vp, i32, i32, vp, i32, vp, i32, vp]
+    f32 = ctypes.c_float
+    lib.gemm_strided_run.argtypes = [i64, i64, i64, f32, vp, i64, i32, vp, i64, i32, i32,
+                                     f32, vp, i64, i32, vp, i64, i32, vp]
     lib.grouped_gemm_run.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), i64, i64, vp,
                                      i32, vp, i32, i32, vp, i32, vp]
     lib.mx_gemm_run.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
@@ -72,7 +76,8 @@ def load():
     lib.gemm_layout_run.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, vp, i32, vp]
     lib.gemm_lds_layout.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int32)]
     lib.gemm_lds_image.argtypes = [vp, i64, i64, i32, i64, i64, i32, vp, vp]
-    for f in (lib.gemm_run, lib.grouped_gemm_run, lib.mx_gemm_run, lib.mxfp4_gemm_run,
+    for f in (lib.gemm_run, lib.gemm_strided_run, lib.grouped_gemm_run, lib.mx_gemm_run,
+              lib.mxfp4_gemm_run,
               lib.gemm_layout_run,
               lib.gemm_lds_layout, lib.gemm_lds_image):
         f.restype = ctypes.c_int
@@ -90,6 +95,12 @@ def gemm_run(M, N, K, A, a_major, B, b_major, ab_dtype, C, c_dtype, D, d_dtype,
              stream) -> int:
     return load().gemm_run(M, N, K, A, a_major, B, b_major, ab_dtype, C, c_dtype,
                            D, d_dtype, stream)
+
+
+def gemm_strided_run(M, N, K, alpha, A, lda, a_major, B, ldb, b_major, ab_dtype, beta, C,
+                     ldc, c_dtype, D, ldd, d_dtype, stream) -> int:
+    return load().gemm_strided_run(M, N, K, alpha, A, lda, a_major, B, ldb, b_major,
+                                   ab_dtype, beta, C, ldc, c_dtype, D, ldd, d_dtype, stream)
 
 
 def grouped_gemm_run(G, m_offsets, N, K, A, a_major, B, b_major, ab_dtype, D,
@@ -182,6 +193,40 @@ def gemm(A, B, *, a_major: str = "k", b_major: str = "k", C=None,
                     C.data_ptr() if C is not None else None,
                     _dt(C.dtype) if C is not None else SG_NONE, out.data_ptr(),
                     _dt(out.dtype), _stream(A.device)))
+    return out
+
+
+def _ld(t, name: str) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise GemmError(-2, f"{name} must be 2-D with unit column stride")
+    return t.stride(0)
+
+
+def gemm_strided(A, B, *, a_major: str = "k", b_major: str = "k", C=None, alpha: float = 1.0,
+                 beta: float = 1.0, out_dtype=None, out=None):
+    """D = alpha * A*B + beta * C on 2-D torch CUDA tensors whose rows may be
+    padded (views with unit column stride): leading dimensions are the row
+    strides.  Shapes as in gemm(); `out` may itself be a padded view."""
+    import torch
+    if a_major == "k":
+        M, K = A.shape
+    else:
+        K, M = A.shape
+    if b_major == "k":
+        N, Kb = B.shape
+    else:
+        Kb, N = B.shape
+    if Kb != K or A.dtype != B.dtype:
+        raise GemmError(-3, "A and B disagree on K or dtype")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=A.device)
+    _check(gemm_strided_run(M, N, K, float(alpha), A.data_ptr(), _ld(A, "A"),
+                            0 if a_major == "k" else 1, B.data_ptr(), _ld(B, "B"),
+                            0 if b_major == "k" else 1, _dt(A.dtype), float(beta),
+                            C.data_ptr() if C is not None else None,
+                            _ld(C, "C") if C is not None else N,
+                            _dt(C.dtype) if C is not None else SG_NONE, out.data_ptr(),
+                            _ld(out, "out"), _dt(out.dtype), _stream(A.device)))
     return out
 
 

@@ -55,10 +55,13 @@ constexpr int64_t kMaxExtent = (int64_t)1 << 31;  // buffer offsets are 32-bit
 constexpr int kCUs = 256;                          // MI355X compute units
 constexpr int kGroupM = 8;
 
-// Largest byte extent one workgroup addresses through a buffer resource.
-int64_t panel_extent(int major, int64_t rows, int64_t K, int64_t tile_rows, int eb) {
-  return major == SG_K_MAJOR ? (rows < tile_rows ? rows : tile_rows) * K * eb
-                             : rows * K * eb;
+// Largest byte extent one workgroup addresses through a buffer resource
+// (ld = the operand's leading dimension in elements).
+int64_t panel_extent(int major, int64_t rows, int64_t K, int64_t ld, int64_t tile_rows,
+                     int eb) {
+  if (K == 0) return 0;
+  return major == SG_K_MAJOR ? ((rows < tile_rows ? rows : tile_rows) - 1) * ld * eb + K * eb
+                             : (K - 1) * ld * eb + rows * eb;
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -71,12 +74,14 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(SG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// gemm_run and gemm_layout_run: validation, plan and launch.  swz < 0 runs
-// the library's kernels; swz = 0, 8 or 16 runs the layout ablation kernel
-// with that LDS layout on 256x256 tiles whatever the problem size.
-int dense_run(const char* who, int swz, int64_t M, int64_t N, int64_t K,
-              const void* A, int a_major, const void* B, int b_major, int ab_dtype,
-              const void* C, int c_dtype, void* D, int d_dtype, void* stream) {
+// gemm_run, gemm_strided_run and gemm_layout_run: validation, plan and
+// launch.  swz < 0 runs the library's kernels; swz = 0, 8 or 16 runs the
+// layout ablation kernel with that LDS layout on 256x256 tiles whatever the
+// problem size.  Leading dimensions are in elements.
+int dense_run(const char* who, int swz, int64_t M, int64_t N, int64_t K, float alpha,
+              const void* A, int64_t lda, int a_major, const void* B, int64_t ldb,
+              int b_major, int ab_dtype, float beta, const void* C, int64_t ldc, int c_dtype,
+              void* D, int64_t ldd, int d_dtype, void* stream) {
   if (M < 0 || N < 0 || K < 0)
     return fail(SG_ERR_SHAPE, "%s: negative size M=%lld N=%lld K=%lld", who,
                 (long long)M, (long long)N, (long long)K);
@@ -86,28 +91,38 @@ int dense_run(const char* who, int swz, int64_t M, int64_t N, int64_t K,
     return fail(SG_ERR_DTYPE, "%s: d_dtype %d is not SG_F32/SG_BF16/SG_F16", who, d_dtype);
   if (C && !is_out_dtype(c_dtype))
     return fail(SG_ERR_DTYPE, "%s: c_dtype %d is not SG_F32/SG_BF16/SG_F16", who, c_dtype);
-  if (C && C == D && c_dtype != d_dtype)
-    return fail(SG_ERR_DTYPE, "%s: in-place C == D needs c_dtype == d_dtype", who);
+  if (C && C == D && (c_dtype != d_dtype || ldc != ldd))
+    return fail(SG_ERR_DTYPE, "%s: in-place C == D needs c_dtype == d_dtype and ldc == ldd",
+                who);
   if ((a_major != SG_K_MAJOR && a_major != SG_MN_MAJOR) ||
       (b_major != SG_K_MAJOR && b_major != SG_MN_MAJOR))
     return fail(SG_ERR_MAJOR, "%s: majorness must be SG_K_MAJOR or SG_MN_MAJOR", who);
+  if (lda < (a_major == SG_K_MAJOR ? K : M) || ldb < (b_major == SG_K_MAJOR ? K : N) ||
+      ldd < N || (C && ldc < N))
+    return fail(SG_ERR_SHAPE,
+                "%s: a leading dimension is below its minimum (lda %lld, ldb %lld, ldc %lld, "
+                "ldd %lld)", who, (long long)lda, (long long)ldb, (long long)ldc,
+                (long long)ldd);
   if (M == 0 || N == 0) return ok();
   if (!D) return fail(SG_ERR_NULL, "%s: D is NULL", who);
+  // alpha == 0: A and B are not read; beta == 0: C is not read.
+  if (alpha == 0.0f) K = 0;
+  if (beta == 0.0f) C = nullptr;
   if (K > 0 && (!A || !B)) return fail(SG_ERR_NULL, "%s: A or B is NULL", who);
   const int eb = 2, db = elem_bytes(d_dtype), cb = C ? elem_bytes(c_dtype) : 0;
   if ((K > 0 && (!aligned16(A) || !aligned16(B))) || !aligned16(D) || (C && !aligned16(C)))
     return fail(SG_ERR_ALIGN, "%s: every pointer must be 16-byte aligned", who);
-  const int64_t a_pitch = (a_major == SG_K_MAJOR ? K : M) * eb;
-  const int64_t b_pitch = (b_major == SG_K_MAJOR ? K : N) * eb;
-  if ((K > 0 && (a_pitch % 16 || b_pitch % 16)) || (N * db) % 16 || (C && (N * cb) % 16))
+  if ((K > 0 && ((lda * eb) % 16 || (ldb * eb) % 16)) || (ldd * db) % 16 ||
+      (C && (ldc * cb) % 16))
     return fail(SG_ERR_ALIGN,
                 "%s: row pitches must be multiples of 16 bytes (A %lld, B %lld, D %lld bytes)",
-                who, (long long)a_pitch, (long long)b_pitch, (long long)(N * db));
+                who, (long long)(lda * eb), (long long)(ldb * eb), (long long)(ldd * db));
   const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256);
   const sg::TileShape tile = swz >= 0 ? sg::kTile256 : pick_tile(tiles256);
   const int64_t T = tile == sg::kTile256 ? 256 : 128;
-  if (panel_extent(a_major, M, K, T, eb) >= kMaxExtent ||
-      panel_extent(b_major, N, K, T, eb) >= kMaxExtent)
+  if (panel_extent(a_major, M, K, lda, T, eb) >= kMaxExtent ||
+      panel_extent(b_major, N, K, ldb, T, eb) >= kMaxExtent ||
+      lda * eb >= kMaxExtent || ldb * eb >= kMaxExtent)
     return fail(SG_ERR_SHAPE, "%s: an operand panel spans 2^31 bytes or more", who);
   const int64_t tiles_m = cdiv(M, T), tiles_n = cdiv(N, T);
   if (tiles_m * tiles_n >= kMaxExtent || tiles_m * tiles_n > 0x7fffffffLL)
@@ -121,6 +136,12 @@ int dense_run(const char* who, int swz, int64_t M, int64_t N, int64_t K,
   p.M = M;
   p.N = N;
   p.K = K;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = C ? ldc : 0;
+  p.ldd = ldd;
+  p.alpha = alpha;
+  p.beta = C ? beta : 0.0f;
   p.c_dtype = C ? c_dtype : SG_NONE;
   p.d_dtype = d_dtype;
   p.tiles_m = (int)tiles_m;
@@ -149,8 +170,17 @@ const char* gemm_version(void) {
 int gemm_run(int64_t M, int64_t N, int64_t K, const void* A, int a_major,
              const void* B, int b_major, int ab_dtype, const void* C, int c_dtype,
              void* D, int d_dtype, void* stream) {
-  return dense_run("gemm_run", -1, M, N, K, A, a_major, B, b_major,
-                   ab_dtype, C, c_dtype, D, d_dtype, stream);
+  return dense_run("gemm_run", -1, M, N, K, 1.0f, A, a_major == SG_K_MAJOR ? K : M, a_major,
+                   B, b_major == SG_K_MAJOR ? K : N, b_major, ab_dtype, 1.0f, C, N, c_dtype,
+                   D, N, d_dtype, stream);
+}
+
+int gemm_strided_run(int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                     int64_t lda, int a_major, const void* B, int64_t ldb, int b_major,
+                     int ab_dtype, float beta, const void* C, int64_t ldc, int c_dtype,
+                     void* D, int64_t ldd, int d_dtype, void* stream) {
+  return dense_run("gemm_strided_run", -1, M, N, K, alpha, A, lda, a_major, B, ldb, b_major,
+                   ab_dtype, beta, C, ldc, c_dtype, D, ldd, d_dtype, stream);
 }
 
 int gemm_layout_run(int swz_units, int64_t M, int64_t N, int64_t K, const void* A,
@@ -158,8 +188,8 @@ int gemm_layout_run(int swz_units, int64_t M, int64_t N, int64_t K, const void* 
                     void* stream) {
   if (swz_units != 0 && swz_units != 8 && swz_units != 16)
     return fail(SG_ERR_SHAPE, "gemm_layout_run: swz_units %d is not 0, 8 or 16", swz_units);
-  return dense_run("gemm_layout_run", swz_units, M, N, K, A, SG_K_MAJOR, B, SG_K_MAJOR,
-                   SG_BF16, C, c_dtype, D, d_dtype, stream);
+  return dense_run("gemm_layout_run", swz_units, M, N, K, 1.0f, A, K, SG_K_MAJOR, B, K,
+                   SG_K_MAJOR, SG_BF16, 1.0f, C, N, c_dtype, D, N, d_dtype, stream);
 }
 
 int grouped_gemm_run(int G, const int64_t* m_offsets, int64_t N, int64_t K,

@@ -37,6 +37,8 @@ struct DenseParams {
   const void* C;
   void* D;
   int64_t M, N, K;
+  int64_t lda, ldb, ldc, ldd;  // leading dimensions in elements
+  float alpha, beta;           // D = alpha * A.B + beta * C
   int c_dtype, d_dtype;
   int tiles_m, tiles_n;
   int group_m;
@@ -87,6 +89,8 @@ struct TileJob {
   int n_valid;
   int64_t d_row0;       // first output row (absolute)
   int64_t n0;           // first output column
+  int64_t ldc;          // leading dimension of C in elements
+  float alpha, beta;    // D = alpha * acc + beta * C
 };
 
 // Epilogue element work shared by every kernel.  One chunk is 4 consecutive
@@ -105,19 +109,24 @@ __device__ __forceinline__ c_chunk_t<CD> load_c_chunk(const void* C, int64_t idx
 
 template <int CD, int DD>
 __device__ __forceinline__ void store_d_chunk(f32x4 v, const c_chunk_t<CD>& c, void* D,
-                                              int64_t idx) {
-  if constexpr (CD == SG_F32) {
-    v += c;
-  } else if constexpr (CD == SG_BF16) {
-    v[0] += bf16_to_f32(c[0] & 0xffffu);
-    v[1] += bf16_to_f32(c[0] >> 16);
-    v[2] += bf16_to_f32(c[1] & 0xffffu);
-    v[3] += bf16_to_f32(c[1] >> 16);
-  } else if constexpr (CD == SG_F16) {
-    v[0] += f16_to_f32(c[0] & 0xffffu);
-    v[1] += f16_to_f32(c[0] >> 16);
-    v[2] += f16_to_f32(c[1] & 0xffffu);
-    v[3] += f16_to_f32(c[1] >> 16);
+                                              int64_t idx, float alpha, float beta) {
+  if constexpr (CD != SG_NONE) {
+    f32x4 cf;
+    if constexpr (CD == SG_F32) {
+      cf = c;
+    } else if constexpr (CD == SG_BF16) {
+      cf = f32x4{bf16_to_f32(c[0] & 0xffffu), bf16_to_f32(c[0] >> 16),
+                 bf16_to_f32(c[1] & 0xffffu), bf16_to_f32(c[1] >> 16)};
+    } else {
+      cf = f32x4{f16_to_f32(c[0] & 0xffffu), f16_to_f32(c[0] >> 16),
+                 f16_to_f32(c[1] & 0xffffu), f16_to_f32(c[1] >> 16)};
+    }
+    // alpha * acc + (beta * c), one rounding each; with alpha = beta = 1
+    // this is the single fp32 add acc + c.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(alpha, v[e], beta * cf[e]);
+  } else {
+    v *= alpha;
   }
   if constexpr (DD == SG_F32) {
     *reinterpret_cast<f32x4*>(static_cast<float*>(D) + idx) = v;
@@ -145,7 +154,7 @@ __device__ __forceinline__ void load_c_row16(c_chunk_t<CD> (&c)[NJ], const TileJ
                                              int nw, int i) {
   if constexpr (CD != SG_NONE) {
     const int ml = min(mw + 16 * i + (lane & 15), j.m_valid - 1);
-    const int64_t base = (j.d_row0 + ml) * ldd + j.n0;
+    const int64_t base = (j.d_row0 + ml) * j.ldc + j.n0;
 #pragma unroll
     for (int jn = 0; jn < NJ; ++jn) {
       const int nl = min(nw + 16 * jn + 4 * (lane >> 4), j.n_valid - 4);
@@ -185,7 +194,8 @@ __device__ __forceinline__ void epilogue16_t(const f32x4 (&acc)[NI][NJ], const T
       for (int jn = 0; jn < NJ; ++jn) {
         const int nl = nw + 16 * jn + 4 * (lane >> 4);
         if (nl >= j.n_valid) continue;
-        store_d_chunk<CD, DD>(acc[i][jn], cb[(g0 / kG) & 1][ii][jn], D, row + nl);
+        store_d_chunk<CD, DD>(acc[i][jn], cb[(g0 / kG) & 1][ii][jn], D, row + nl, j.alpha,
+                              j.beta);
       }
     }
   }
@@ -485,7 +495,7 @@ struct GemmTile {
                                                       int fm) {
     if constexpr (CD != SG_NONE) {
       const int ml = min(wm * kWM + fm * 32 + (lane & 31), j.m_valid - 1);
-      const int64_t base = (j.d_row0 + ml) * ldd + j.n0;
+      const int64_t base = (j.d_row0 + ml) * j.ldc + j.n0;
 #pragma unroll
       for (int fn = 0; fn < kFN; ++fn)
 #pragma unroll
@@ -517,7 +527,7 @@ struct GemmTile {
           const int64_t idx = row * ldd + j.n0 + nl;
           const f32x4 v = {acc[fm][fn][4 * q + 0], acc[fm][fn][4 * q + 1],
                            acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
-          store_d_chunk<CD, DD>(v, cb[fm & 1][4 * fn + q], D, idx);
+          store_d_chunk<CD, DD>(v, cb[fm & 1][4 * fn + q], D, idx, j.alpha, j.beta);
         }
       }
     }
@@ -538,24 +548,29 @@ __device__ __forceinline__ TileJob dense_tile_job(const DenseParams& p, int wg) 
   const int64_t es = 2;
   j.m_valid = (int)min<int64_t>(BM, p.M - m0);
   j.n_valid = (int)min<int64_t>(BN, p.N - n0);
-  if constexpr (AMn) {  // A stored [K][M]
+  // Each buffer covers exactly the bytes the tile may read: up to the end of
+  // its last valid row (K-major) or of row K-1 (MN-major).
+  if constexpr (AMn) {  // A stored [K][lda], M contiguous
     j.a = static_cast<const char*>(p.A) + m0 * es;
-    j.a_pitch = (uint32_t)(p.M * es);
-    j.a_bytes = (uint32_t)(p.K * p.M * es - m0 * es);
-  } else {              // A stored [M][K]
-    j.a = static_cast<const char*>(p.A) + m0 * p.K * es;
-    j.a_pitch = (uint32_t)(p.K * es);
-    j.a_bytes = (uint32_t)(j.m_valid * p.K * es);
+    j.a_pitch = (uint32_t)(p.lda * es);
+    j.a_bytes = p.K > 0 ? (uint32_t)((p.K - 1) * p.lda * es + (p.M - m0) * es) : 0u;
+  } else {              // A stored [M][lda], K contiguous
+    j.a = static_cast<const char*>(p.A) + m0 * p.lda * es;
+    j.a_pitch = (uint32_t)(p.lda * es);
+    j.a_bytes = p.K > 0 ? (uint32_t)((j.m_valid - 1) * p.lda * es + p.K * es) : 0u;
   }
-  if constexpr (BMn) {  // B stored [K][N]
+  if constexpr (BMn) {  // B stored [K][ldb], N contiguous
     j.b = static_cast<const char*>(p.B) + n0 * es;
-    j.b_pitch = (uint32_t)(p.N * es);
-    j.b_bytes = (uint32_t)(p.K * p.N * es - n0 * es);
-  } else {              // B stored [N][K]
-    j.b = static_cast<const char*>(p.B) + n0 * p.K * es;
-    j.b_pitch = (uint32_t)(p.K * es);
-    j.b_bytes = (uint32_t)(j.n_valid * p.K * es);
+    j.b_pitch = (uint32_t)(p.ldb * es);
+    j.b_bytes = p.K > 0 ? (uint32_t)((p.K - 1) * p.ldb * es + (p.N - n0) * es) : 0u;
+  } else {              // B stored [N][ldb], K contiguous
+    j.b = static_cast<const char*>(p.B) + n0 * p.ldb * es;
+    j.b_pitch = (uint32_t)(p.ldb * es);
+    j.b_bytes = p.K > 0 ? (uint32_t)((j.n_valid - 1) * p.ldb * es + p.K * es) : 0u;
   }
+  j.ldc = p.ldc;
+  j.alpha = p.alpha;
+  j.beta = p.beta;
   j.d_row0 = m0;
   j.n0 = n0;
   return j;
@@ -592,6 +607,9 @@ __device__ __forceinline__ TileJob grouped_tile_job(const GroupedParams& p, int 
   j.b_bytes = (uint32_t)(j.n_valid * p.K * es);
   j.d_row0 = p.m_off[g] + m0;
   j.n0 = n0;
+  j.ldc = 0;
+  j.alpha = 1.0f;
+  j.beta = 0.0f;
   return j;
 }
 
@@ -603,7 +621,7 @@ __global__ void __launch_bounds__(64 * Waves, 1)
   __shared__ __attribute__((aligned(4096))) char s1[Tile::kStageBytes];
 
   const TileJob j = dense_tile_job<BM, BN, AMn, BMn>(p, blockIdx.x);
-  Tile::run(s0, s1, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.N);
+  Tile::run(s0, s1, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.ldd);
 }
 
 template <int BM, int BN, bool IsBF16, int Swz, int Waves>

@@ -259,6 +259,9 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(const MxParams p) 
   j.b_bytes = (uint32_t)(j.n_valid * p.K);
   j.d_row0 = m0;
   j.n0 = n0;
+  j.ldc = 0;
+  j.alpha = 1.0f;
+  j.beta = 0.0f;
   const char* sfa = static_cast<const char*>(p.SFA) + m0 * (p.K / 32);
   const char* sfb = static_cast<const char*>(p.SFB) + n0 * (p.K / 32);
   Tile::run(s0, s1, j, sfa, sfb, p.K, p.D, p.d_dtype, p.N);

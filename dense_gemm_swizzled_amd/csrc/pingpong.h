@@ -288,7 +288,7 @@ __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(const DenseParams
   using Tile = PingPongTile<IsBF16, Swz>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
   const TileJob j = dense_tile_job<256, 256, false, false>(p, blockIdx.x);
-  Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.N);
+  Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.ldd);
 }
 
 template <bool IsBF16, int Swz>
@@ -590,6 +590,9 @@ __global__ void __launch_bounds__(512, 1) pingpong_mx_kernel(const MxParams p) {
   j.b_bytes = (uint32_t)(j.n_valid * row_bytes);
   j.d_row0 = m0;
   j.n0 = n0;
+  j.ldc = 0;
+  j.alpha = 1.0f;
+  j.beta = 0.0f;
   Tile::run(smem, j, static_cast<const char*>(p.SFA) + m0 * (p.K / 32),
             static_cast<const char*>(p.SFB) + n0 * (p.K / 32), p.K, p.D, p.d_dtype, p.N);
 }

@@ -286,7 +286,7 @@ __global__ void __launch_bounds__(512, 1) pingpong16_gemm_kernel(const DensePara
   using Tile = PingPong16Tile<IsBF16, Swz>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
   const TileJob j = dense_tile_job<256, 256, false, false>(p, blockIdx.x);
-  Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.N);
+  Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.ldd);
 }
 
 template <bool IsBF16, int Swz>

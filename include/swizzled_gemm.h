@@ -87,6 +87,32 @@ int gemm_run(int64_t M, int64_t N, int64_t K, const void* A, int a_major,
              int c_dtype, void* D, int d_dtype, void* stream);
 
 /*
+ * gemm_strided_run -- D = alpha * A*B + beta * C with leading dimensions,
+ * fp32 accumulation.  Operands are addressed as "Tensor Cores, layouts, and
+ * swizzling" describes its tensor-memory tile copies (section on the Tensor
+ * Memory Accelerator): by dimensions and row strides that are multiples of
+ * 16 bytes, with elements past the edges read as zero.
+ *   alpha, beta  fp32 scalars.  D = round(alpha * acc + beta * C) with acc the
+ *                fp32 sum over K; alpha = beta = 1 gives gemm_run's result
+ *                bit for bit.  alpha == 0: A and B are not read (D = beta*C);
+ *                beta == 0 or C == NULL: C is not read.
+ *   A   K-major: element (m, k) at A[m*lda + k], lda >= K;
+ *       MN-major: element (m, k) at A[k*lda + m], lda >= M.
+ *   B   K-major: element (k, n) at B[n*ldb + k], ldb >= K;
+ *       MN-major: element (k, n) at B[k*ldb + n], ldb >= N.
+ *   C   element (m, n) at C[m*ldc + n], ldc >= N; D at D[m*ldd + n], ldd >= N.
+ *   Leading dimensions are in elements; every row pitch (ld * element size)
+ *   must be a multiple of 16 bytes and every pointer 16-byte aligned.  C may
+ *   equal D when c_dtype == d_dtype and ldc == ldd.  The other arguments and
+ *   the errors are gemm_run's, plus SG_ERR_SHAPE for a leading dimension below
+ *   its minimum.
+ */
+int gemm_strided_run(int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                     int64_t lda, int a_major, const void* B, int64_t ldb, int b_major,
+                     int ab_dtype, float beta, const void* C, int64_t ldc, int c_dtype,
+                     void* D, int64_t ldd, int d_dtype, void* stream);
+
+/*
  * grouped_gemm_run -- for each group g in [0, G):
  *   D[off_g : off_{g+1}] = A[off_g : off_{g+1}] * B_g,
  * the grouped GEMM named in "LBO, SBO and SWZ for a tcgen05 tile"

@@ -10,6 +10,11 @@ Contents
   over exactly decoded fp16/bf16 inputs, plus the per-element error bound
   ``sum_k |a*b| + |c|`` (``gemm_oracle.c``; the tensor-core operation of
   "Tensor Cores, layouts, and swizzling", opening section).
+* ``gemm_ex``: the same sum read from strided storage, D = alpha*A*B +
+  beta*C (leading dimensions as the tile copies of "Tensor Cores, layouts,
+  and swizzling", Tensor Memory Accelerator section, address a tensor; the
+  alpha/beta scaling is the plain reading of a scaled epilogue, the pages
+  define none), with bound ``|alpha| sum_k |a*b| + |beta| |c|``.
 * ``grouped_gemm``: the dense definition applied per group on rows
   ``[off_g, off_{g+1})`` with that group's B (the grouped GEMM named in
   "LBO, SBO and SWZ for a tcgen05 tile", introduction; the pages give no
@@ -64,6 +69,9 @@ def _load():
         lib.oracle_decode.argtypes = [ip, vp, i64, dp]
         lib.oracle_gemm.argtypes = [i64, i64, i64, vp, ip, vp, ip, ip, vp, ip,
                                     dp, dp, ip]
+        f64 = ctypes.c_double
+        lib.oracle_gemm_ex.argtypes = [i64, i64, i64, f64, vp, i64, ip, vp, i64, ip, ip,
+                                       f64, vp, i64, ip, dp, dp, ip]
         lib.oracle_gemm_points.argtypes = [i64, i64, i64, vp, ip, vp, ip, ip,
                                            vp, ip, i64, vp, vp, dp, dp]
         lib.oracle_mx_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, dp, dp, ip]
@@ -73,7 +81,7 @@ def _load():
         lib.oracle_mx_gemm_points_fmt.argtypes = [ip, i64, i64, i64, vp, vp, vp, vp,
                                                   i64, vp, vp, dp, dp]
         lib.oracle_default_threads.argtypes = []
-        for f in (lib.oracle_decode, lib.oracle_gemm, lib.oracle_gemm_points,
+        for f in (lib.oracle_decode, lib.oracle_gemm, lib.oracle_gemm_ex, lib.oracle_gemm_points,
                   lib.oracle_mx_gemm, lib.oracle_mx_gemm_points,
                   lib.oracle_mx_gemm_fmt, lib.oracle_mx_gemm_points_fmt,
                   lib.oracle_default_threads):
@@ -140,6 +148,26 @@ def gemm(M: int, N: int, K: int, A, a_major: str, B, b_major: str,
                              _ptr(ref), _ptr(bound), nthreads)
     if rc != 0:
         raise ValueError("oracle_gemm rejected its arguments")
+    return ref, bound
+
+
+def gemm_ex(M: int, N: int, K: int, alpha: float, A, lda: int, a_major: str, B, ldb: int,
+            b_major: str, ab_dtype: str, beta: float, C=None, ldc: int = 0,
+            c_dtype: Optional[str] = None, nthreads: int = 0, with_bound: bool = True):
+    """ref, bound = fp64 D = alpha*A*B + beta*C and |alpha|sum|a*b| + |beta||c|
+    from strided storage (leading dimensions in elements; A, B, C are the
+    whole buffers).  alpha == 0 reads neither A nor B; beta == 0 does not
+    read C."""
+    a, b, c = _bytes(A), _bytes(B), _bytes(C)
+    ref = np.empty((M, N), dtype=np.float64)
+    bound = np.empty((M, N), dtype=np.float64) if with_bound else None
+    rc = _load().oracle_gemm_ex(M, N, K, float(alpha), _ptr(a), lda, _MAJ[a_major],
+                                _ptr(b), ldb, _MAJ[b_major], _DT[ab_dtype],
+                                float(beta), _ptr(c), ldc,
+                                _DT[c_dtype] if c is not None else 0,
+                                _ptr(ref), _ptr(bound), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_gemm_ex rejected its arguments")
     return ref, bound
 
 

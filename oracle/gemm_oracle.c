@@ -183,7 +183,9 @@ typedef struct {
     int64_t M, N, K;
     const double *a;   /* [M][K] decoded, K contiguous */
     const double *b;   /* [N][K] decoded, K contiguous */
-    const void *C;
+    double alpha, beta;
+    const void *C;     /* element (i, j) at C[i * ldc + j]; NULL: no C */
+    int64_t ldc;
     int c_dtype;
     double *ref, *bound;
 } dense_ctx;
@@ -200,46 +202,65 @@ static void dense_rows(void *vctx, int64_t i0, int64_t i1) {
                 s += p;
                 sa += fabs(p);
             }
-            double c = x->C ? dec_at(x->c_dtype, x->C, i * x->N + j) : 0.0;
-            x->ref[i * x->N + j] = s + c;
-            if (x->bound) x->bound[i * x->N + j] = sa + fabs(c);
+            double c = x->C ? dec_at(x->c_dtype, x->C, i * x->ldc + j) : 0.0;
+            x->ref[i * x->N + j] = x->alpha * s + x->beta * c;
+            if (x->bound)
+                x->bound[i * x->N + j] = fabs(x->alpha) * sa + fabs(x->beta) * fabs(c);
         }
     }
 }
 
 /* Logical row r (0..R-1) of an operand whose logical shape is R x K,
- * decoded to fp64 with K contiguous.  major == K: X[r*K+k]; MN: X[k*R+r]. */
+ * decoded to fp64 with K contiguous.  major == K: X[r*ld+k]; MN: X[k*ld+r]. */
 static void expand_operand(int dt, const void *X, int major, int64_t R,
-                           int64_t K, double *out) {
+                           int64_t K, int64_t ld, double *out) {
     for (int64_t r = 0; r < R; ++r)
         for (int64_t k = 0; k < K; ++k)
-            out[r * K + k] = dec_at(dt, X, major == ORC_K_MAJOR ? r * K + k
-                                                                : k * R + r);
+            out[r * K + k] = dec_at(dt, X, major == ORC_K_MAJOR ? r * ld + k
+                                                                : k * ld + r);
 }
 
-/* ref/bound are [M][N] row-major fp64 (bound may be NULL). */
-int oracle_gemm(int64_t M, int64_t N, int64_t K, const void *A, int a_major,
-                const void *B, int b_major, int ab_dtype, const void *C,
-                int c_dtype, double *ref, double *bound, int nthreads) {
+/* D = alpha * sum_k A(m,k) B(k,n) + beta * C(m,n) with leading dimensions in
+ * elements: A(m,k) = A[m*lda+k] (K-major) or A[k*lda+m] (MN-major), B(k,n) =
+ * B[n*ldb+k] or B[k*ldb+n], C(m,n) = C[m*ldc+n].  alpha == 0: A and B are not
+ * read; beta == 0 or C == NULL: C is not read.  ref/bound are [M][N]
+ * row-major fp64 (bound may be NULL): bound = |alpha| sum|a*b| + |beta| |c|. */
+int oracle_gemm_ex(int64_t M, int64_t N, int64_t K, double alpha, const void *A,
+                   int64_t lda, int a_major, const void *B, int64_t ldb, int b_major,
+                   int ab_dtype, double beta, const void *C, int64_t ldc, int c_dtype,
+                   double *ref, double *bound, int nthreads) {
     if (M < 0 || N < 0 || K < 0 || !ref) return -1;
     if ((ab_dtype != ORC_F16 && ab_dtype != ORC_BF16) ||
         (a_major != ORC_K_MAJOR && a_major != ORC_MN_MAJOR) ||
         (b_major != ORC_K_MAJOR && b_major != ORC_MN_MAJOR))
         return -1;
-    if (C && elem_size(c_dtype) == 0) return -1;
+    if (alpha == 0.0) K = 0;
+    if (beta == 0.0) C = NULL;
+    if (C && (elem_size(c_dtype) == 0 || ldc < N)) return -1;
+    if (lda < (a_major == ORC_K_MAJOR ? K : M) || ldb < (b_major == ORC_K_MAJOR ? K : N))
+        return -1;
     if (K > 0 && ((M > 0 && !A) || (N > 0 && !B))) return -1;
     double *a = (double *)malloc(sizeof(double) * (size_t)(M * K + 1));
     double *b = (double *)malloc(sizeof(double) * (size_t)(N * K + 1));
     if (!a || !b) { free(a); free(b); return -1; }
     if (K > 0) {
-        expand_operand(ab_dtype, A, a_major, M, K, a);
-        expand_operand(ab_dtype, B, b_major, N, K, b);
+        expand_operand(ab_dtype, A, a_major, M, K, lda, a);
+        expand_operand(ab_dtype, B, b_major, N, K, ldb, b);
     }
-    dense_ctx x = {M, N, K, a, b, C, c_dtype, ref, bound};
+    dense_ctx x = {M, N, K, a, b, alpha, beta, C, ldc, c_dtype, ref, bound};
     parallel_rows(dense_rows, &x, M, nthreads);
     free(a);
     free(b);
     return 0;
+}
+
+/* D = A*B (+C) with packed operands: oracle_gemm_ex with alpha = beta = 1. */
+int oracle_gemm(int64_t M, int64_t N, int64_t K, const void *A, int a_major,
+                const void *B, int b_major, int ab_dtype, const void *C,
+                int c_dtype, double *ref, double *bound, int nthreads) {
+    return oracle_gemm_ex(M, N, K, 1.0, A, a_major == ORC_K_MAJOR ? K : M, a_major, B,
+                          b_major == ORC_K_MAJOR ? K : N, b_major, ab_dtype, 1.0, C, N,
+                          c_dtype, ref, bound, nthreads);
 }
 
 /* The same definition evaluated only at the listed (row, col) points, each

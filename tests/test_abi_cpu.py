@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert {"gemm_run", "grouped_gemm_run", "mx_gemm_run", "mxfp4_gemm_run", "gemm_layout_run",
+    assert {"gemm_run", "gemm_strided_run", "grouped_gemm_run", "mx_gemm_run", "mxfp4_gemm_run",
+            "gemm_layout_run",
             "gemm_last_error", "gemm_version", "gemm_lds_layout",
             "gemm_lds_image"} <= set(names)
     lib = ctypes.CDLL(sg.library_path())
@@ -49,6 +50,39 @@ def test_gemm_layout_run_rejects(kw, code):
                             a["c_dtype"], a["D"], a["d_dtype"], None)
     assert rc == code, sg.gemm_last_error()
     assert sg.gemm_last_error().startswith("gemm_layout_run")
+
+
+def _strided(**kw):
+    a = dict(M=300, N=264, K=136, alpha=1.0, A=P, lda=136, a_major=0, B=P, ldb=136, b_major=0,
+             ab=sg.SG_BF16, beta=1.0, C=None, ldc=264, c_dtype=0, D=P, ldd=264,
+             d_dtype=sg.SG_F32)
+    a.update(kw)
+    return sg.gemm_strided_run(a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"],
+                               a["a_major"], a["B"], a["ldb"], a["b_major"], a["ab"],
+                               a["beta"], a["C"], a["ldc"], a["c_dtype"], a["D"], a["ldd"],
+                               a["d_dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lda=128), SHAPE), (dict(ldb=100), SHAPE), (dict(ldd=256), SHAPE),
+    (dict(C=P + 8192, c_dtype=sg.SG_BF16, ldc=200), SHAPE),
+    (dict(a_major=1, lda=296), SHAPE),            # MN-major A needs lda >= M = 300
+    (dict(lda=140), ALIGN), (dict(ldb=137), ALIGN), (dict(ldd=266), ALIGN),
+    (dict(C=P + 8192, c_dtype=sg.SG_BF16, ldc=268), ALIGN),
+    (dict(C=P, c_dtype=sg.SG_F32, ldc=272), DTYPE),  # in place needs ldc == ldd
+    (dict(A=None), NULL), (dict(M=-1), SHAPE), (dict(a_major=7), MAJOR),
+])
+def test_gemm_strided_run_rejects(kw, code):
+    rc = _strided(**kw)
+    assert rc == code, sg.gemm_last_error()
+    assert sg.gemm_last_error().startswith("gemm_strided_run")
+
+
+def test_gemm_strided_run_unread_operands_may_be_null():
+    # alpha == 0 reads neither A nor B, beta == 0 does not read C: no
+    # launch happens for M = 0, and the checks that remain pass.
+    assert _strided(M=0, alpha=0.0, A=None, B=None) == 0
+    assert _strided(N=0, beta=0.0, C=P + 3, c_dtype=sg.SG_F32) == 0
 
 
 def test_gemm_layout_run_empty_is_ok():
