@@ -70,6 +70,17 @@ sg::TileShape pick_tile(int64_t tiles256) {
   return tiles256 >= kCUs ? sg::kTile256 : sg::kTile128;
 }
 
+// Dense GEMM: 256x256 tiles when they fill the CUs, else 128x128 tiles when
+// they fill half of them, else 64x64 tiles (small problems: 1024^3 has 64
+// tiles of 128 but 256 of 64).
+sg::TileShape pick_dense_tile(int64_t M, int64_t N) {
+  if (cdiv(M, 256) * cdiv(N, 256) >= kCUs) return sg::kTile256;
+  if (cdiv(M, 128) * cdiv(N, 128) >= kCUs / 2) return sg::kTile128;
+  return sg::kTile64;
+}
+
+int64_t tile_rows(sg::TileShape t) { return t == sg::kTile256 ? 256 : t == sg::kTile128 ? 128 : 64; }
+
 int hip_fail(hipError_t e, const char* what) {
   return fail(SG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -117,9 +128,8 @@ int dense_run(const char* who, int swz, int64_t M, int64_t N, int64_t K, float a
     return fail(SG_ERR_ALIGN,
                 "%s: row pitches must be multiples of 16 bytes (A %lld, B %lld, D %lld bytes)",
                 who, (long long)(lda * eb), (long long)(ldb * eb), (long long)(ldd * db));
-  const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256);
-  const sg::TileShape tile = swz >= 0 ? sg::kTile256 : pick_tile(tiles256);
-  const int64_t T = tile == sg::kTile256 ? 256 : 128;
+  const sg::TileShape tile = swz >= 0 ? sg::kTile256 : pick_dense_tile(M, N);
+  const int64_t T = tile_rows(tile);
   if (panel_extent(a_major, M, K, lda, T, eb) >= kMaxExtent ||
       panel_extent(b_major, N, K, ldb, T, eb) >= kMaxExtent ||
       lda * eb >= kMaxExtent || ldb * eb >= kMaxExtent)

@@ -9,7 +9,7 @@
 namespace sg {
 
 // Tile shapes the planner chooses between.
-enum TileShape { kTile256 = 0, kTile128 = 1 };
+enum TileShape { kTile256 = 0, kTile128 = 1, kTile64 = 2 };
 
 // Launches the dense kernel for (tile, dtype, majorness).  Returns the
 // launch status.

@@ -61,8 +61,9 @@ hipError_t dense_by_dtype(bool bf16, bool a_mn, bool b_mn, const DenseParams& p,
 
 hipError_t launch_dense(TileShape tile, bool bf16, bool a_mn, bool b_mn,
                         const DenseParams& p, hipStream_t s) {
-  return tile == kTile256 ? dense_by_dtype<256, 256, 16>(bf16, a_mn, b_mn, p, s)
-                          : dense_by_dtype<128, 128, 16>(bf16, a_mn, b_mn, p, s);
+  if (tile == kTile256) return dense_by_dtype<256, 256, 16>(bf16, a_mn, b_mn, p, s);
+  if (tile == kTile128) return dense_by_dtype<128, 128, 16>(bf16, a_mn, b_mn, p, s);
+  return dense_by_dtype<64, 64, 16>(bf16, a_mn, b_mn, p, s);
 }
 
 hipError_t launch_layout(int swz, const DenseParams& p, hipStream_t s) {

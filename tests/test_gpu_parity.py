@@ -132,6 +132,20 @@ def test_dense_majorness_dtypes_ragged(dev, a_major, b_major, ab):
     check_close(_np(d), ref, bound, "f32", "majorness")
 
 
+@pytest.mark.parametrize("a_major", ["k", "mn"])
+@pytest.mark.parametrize("b_major", ["k", "mn"])
+def test_dense_128_tiles_ragged(dev, a_major, b_major):
+    # 15 x 17 tiles of 128 (8 x 9 of 256): the 128x128 variant; smaller
+    # problems take 64x64 tiles, larger ones 256x256.
+    M, N, K = 1800, 2056, 200
+    case = si.dense_case(M, N, K, 17, a_major=a_major, b_major=b_major, ab_dtype="bf16",
+                         with_c=True, c_dtype="bf16", d_dtype="f32", scale=1.0 / np.sqrt(K))
+    say(f"dense 128-tile path {M}x{N}x{K} {a_major}/{b_major}")
+    d = run_dense(case, dev)
+    ref, bound = oracle_dense(case)
+    check_close(_np(d), ref, bound, "f32", "128 tiles")
+
+
 @pytest.mark.parametrize("c_dtype,d_dtype", [(None, "bf16"), ("bf16", "bf16"),
                                              ("f16", "f16"), ("f32", "bf16"),
                                              ("bf16", "f32")])
