@@ -92,15 +92,22 @@ def build_workload(name: str, dev, layout=None):
             if case.ab_dtype != "bf16" or case.a_major != "k" or case.b_major != "k":
                 raise SystemExit("--layout needs a bf16 workload with K-major A and B")
 
+            kernel, lay = layout
+
             def run():
-                sg.gemm_layout(A, B, layout, C=C, out=D)
+                if kernel == 256:
+                    sg.gemm_layout(A, B, lay, C=C, out=D)
+                else:
+                    sg.gemm_layout128(A, B, lay, C=C, out=D)
 
         flops = 2.0 * case.M * case.N * case.K
         cfg = {"workload": case.name, "M": case.M, "N": case.N, "K": case.K,
                "a_major": case.a_major, "b_major": case.b_major,
                "ab_dtype": case.ab_dtype, "c": case.c_dtype, "d_dtype": case.d_dtype}
         if layout is not None:
-            cfg["lds_layout"] = {16: "xor_256B_lines", 8: "xor_128B_lines", 0: "none"}[layout]
+            cfg["lds_layout"] = {16: "xor_256B_lines", 8: "xor_128B_lines", 0: "none",
+                                 sg.SG_LAYOUT_PAD16: "padded_16B"}[layout[1]]
+            cfg["tile"] = f"{layout[0]}x{layout[0]}"
 
         def oracle_sample(rows):
             import oracle
@@ -225,7 +232,10 @@ def main():
     ap.add_argument("--layout", type=int, choices=[16, 8, 0], default=None,
                     help="run the dense workload through gemm_layout_run with this LDS "
                          "layout (16 = the library's XOR swizzle over 256-byte lines, "
-                         "8 = over 128-byte lines, 0 = none)")
+                         "8 = over 128-byte lines, 0 = none) on the 256x256 ping-pong kernel")
+    ap.add_argument("--layout128", choices=["16", "8", "0", "pad"], default=None,
+                    help="the same through gemm_layout128_run on 128x128 tiles, where 'pad' "
+                         "(rows padded by 16 bytes) also fits")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -235,7 +245,13 @@ def main():
     import torch
     dev = torch.device("cuda:0")
     log(f"[bench] workload {args.workload}: generating inputs")
-    run, flops, dtype, cfg, oracle_sample, rows_total = build_workload(args.workload, dev, args.layout)
+    layout = None
+    if args.layout is not None:
+        layout = (256, args.layout)
+    elif args.layout128 is not None:
+        import dense_gemm_swizzled_amd as sg
+        layout = (128, sg.SG_LAYOUT_PAD16 if args.layout128 == "pad" else int(args.layout128))
+    run, flops, dtype, cfg, oracle_sample, rows_total = build_workload(args.workload, dev, layout)
     stream = torch.cuda.current_stream(dev)
 
     log(f"[bench] warmup {args.warmup}")
@@ -291,7 +307,7 @@ def main():
         "pct_of_bf16_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(args.workload) if args.layout is None else None,
+                     "traffic": measured_traffic(args.workload) if layout is None else None,
                      "traffic_unit": "bytes per launch (HBM side)",
                      "kernel_ms_mean": round(mean_ms, 5),
                      "kernel_ms_median": round(median_ms, 5)},

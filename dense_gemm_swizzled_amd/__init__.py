@@ -28,6 +28,7 @@ __all__ = [
     "gemm_last_error",
     "gemm_version", "gemm_lds_layout", "gemm_lds_image",
     "gemm", "gemm_strided", "grouped_gemm", "mx_gemm", "mxfp4_gemm", "gemm_layout",
+    "gemm_layout128", "SG_LAYOUT_PAD16",
     "library_path", "load",
 ]
 
@@ -35,6 +36,7 @@ SG_OK = 0
 SG_NONE, SG_F16, SG_BF16, SG_F32, SG_E4M3, SG_E8M0 = 0, 1, 2, 3, 4, 5
 SG_K_MAJOR, SG_MN_MAJOR = 0, 1
 SG_MAX_GROUPS = 128
+SG_LAYOUT_PAD16 = -1
 ERRORS = {-1: "SG_ERR_NULL", -2: "SG_ERR_ALIGN", -3: "SG_ERR_SHAPE",
           -4: "SG_ERR_DTYPE", -5: "SG_ERR_MAJOR", -6: "SG_ERR_GROUPS",
           -7: "SG_ERR_HIP"}
@@ -74,11 +76,12 @@ def load():
     lib.mx_gemm_run.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
     lib.mxfp4_gemm_run.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
     lib.gemm_layout_run.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, vp, i32, vp]
+    lib.gemm_layout128_run.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, vp, i32, vp]
     lib.gemm_lds_layout.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int32)]
     lib.gemm_lds_image.argtypes = [vp, i64, i64, i32, i64, i64, i32, vp, vp]
     for f in (lib.gemm_run, lib.gemm_strided_run, lib.grouped_gemm_run, lib.mx_gemm_run,
               lib.mxfp4_gemm_run,
-              lib.gemm_layout_run,
+              lib.gemm_layout_run, lib.gemm_layout128_run,
               lib.gemm_lds_layout, lib.gemm_lds_image):
         f.restype = ctypes.c_int
     lib.gemm_last_error.argtypes = []
@@ -122,6 +125,10 @@ def mxfp4_gemm_run(M, N, K, A, SFA, B, SFB, D, d_dtype, stream) -> int:
 
 def gemm_layout_run(swz_units, M, N, K, A, B, C, c_dtype, D, d_dtype, stream) -> int:
     return load().gemm_layout_run(swz_units, M, N, K, A, B, C, c_dtype, D, d_dtype, stream)
+
+
+def gemm_layout128_run(layout, M, N, K, A, B, C, c_dtype, D, d_dtype, stream) -> int:
+    return load().gemm_layout128_run(layout, M, N, K, A, B, C, c_dtype, D, d_dtype, stream)
 
 
 def gemm_last_error() -> str:
@@ -286,4 +293,19 @@ def mxfp4_gemm(A, SFA, B, SFB, *, out_dtype=None, out=None):
         out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=A.device)
     _check(mxfp4_gemm_run(M, N, K, A.data_ptr(), SFA.data_ptr(), B.data_ptr(),
                           SFB.data_ptr(), out.data_ptr(), _dt(out.dtype), _stream(A.device)))
+    return out
+
+
+def gemm_layout128(A, B, layout: int, *, C=None, out_dtype=None, out=None):
+    """gemm_layout() on 128x128 tiles, where layout may also be
+    SG_LAYOUT_PAD16 (rows padded by 16 bytes, no swizzle)."""
+    import torch
+    M, K = A.shape
+    N = B.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=A.device)
+    _check(gemm_layout128_run(layout, M, N, K, A.data_ptr(), B.data_ptr(),
+                              C.data_ptr() if C is not None else None,
+                              _dt(C.dtype) if C is not None else SG_NONE, out.data_ptr(),
+                              _dt(out.dtype), _stream(A.device)))
     return out

@@ -85,11 +85,16 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(SG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// gemm_run, gemm_strided_run and gemm_layout_run: validation, plan and
-// launch.  swz < 0 runs the library's kernels; swz = 0, 8 or 16 runs the
-// layout ablation kernel with that LDS layout on 256x256 tiles whatever the
-// problem size.  Leading dimensions are in elements.
-int dense_run(const char* who, int swz, int64_t M, int64_t N, int64_t K, float alpha,
+// Which kernels dense_run launches.
+enum DenseMode { kLibrary, kAblation256, kAblation128 };
+
+// gemm_run, gemm_strided_run, gemm_layout_run and gemm_layout128_run:
+// validation, plan and launch.  kLibrary runs the library's kernels; the
+// ablation modes run the layout `swz` (16, 8, 0, or padded on 128x128
+// tiles) on the 256x256 or 128x128 kernel whatever the problem size.
+// Leading dimensions are in elements.
+int dense_run(const char* who, DenseMode mode, int swz, int64_t M, int64_t N, int64_t K,
+              float alpha,
               const void* A, int64_t lda, int a_major, const void* B, int64_t ldb,
               int b_major, int ab_dtype, float beta, const void* C, int64_t ldc, int c_dtype,
               void* D, int64_t ldd, int d_dtype, void* stream) {
@@ -128,7 +133,9 @@ int dense_run(const char* who, int swz, int64_t M, int64_t N, int64_t K, float a
     return fail(SG_ERR_ALIGN,
                 "%s: row pitches must be multiples of 16 bytes (A %lld, B %lld, D %lld bytes)",
                 who, (long long)(lda * eb), (long long)(ldb * eb), (long long)(ldd * db));
-  const sg::TileShape tile = swz >= 0 ? sg::kTile256 : pick_dense_tile(M, N);
+  const sg::TileShape tile = mode == kAblation256   ? sg::kTile256
+                            : mode == kAblation128 ? sg::kTile128
+                                                   : pick_dense_tile(M, N);
   const int64_t T = tile_rows(tile);
   if (panel_extent(a_major, M, K, lda, T, eb) >= kMaxExtent ||
       panel_extent(b_major, N, K, ldb, T, eb) >= kMaxExtent ||
@@ -158,10 +165,11 @@ int dense_run(const char* who, int swz, int64_t M, int64_t N, int64_t K, float a
   p.tiles_n = (int)tiles_n;
   p.group_m = kGroupM;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = swz >= 0 ? sg::launch_layout(swz, p, s)
-                                : sg::launch_dense(tile, ab_dtype == SG_BF16,
-                                                   a_major == SG_MN_MAJOR,
-                                                   b_major == SG_MN_MAJOR, p, s);
+  const hipError_t e = mode == kAblation256   ? sg::launch_layout(swz, p, s)
+                       : mode == kAblation128 ? sg::launch_layout128(swz, p, s)
+                                              : sg::launch_dense(tile, ab_dtype == SG_BF16,
+                                                                 a_major == SG_MN_MAJOR,
+                                                                 b_major == SG_MN_MAJOR, p, s);
   if (e != hipSuccess) return hip_fail(e, who);
   return ok();
 }
@@ -180,7 +188,7 @@ const char* gemm_version(void) {
 int gemm_run(int64_t M, int64_t N, int64_t K, const void* A, int a_major,
              const void* B, int b_major, int ab_dtype, const void* C, int c_dtype,
              void* D, int d_dtype, void* stream) {
-  return dense_run("gemm_run", -1, M, N, K, 1.0f, A, a_major == SG_K_MAJOR ? K : M, a_major,
+  return dense_run("gemm_run", kLibrary, 0, M, N, K, 1.0f, A, a_major == SG_K_MAJOR ? K : M, a_major,
                    B, b_major == SG_K_MAJOR ? K : N, b_major, ab_dtype, 1.0f, C, N, c_dtype,
                    D, N, d_dtype, stream);
 }
@@ -189,7 +197,7 @@ int gemm_strided_run(int64_t M, int64_t N, int64_t K, float alpha, const void* A
                      int64_t lda, int a_major, const void* B, int64_t ldb, int b_major,
                      int ab_dtype, float beta, const void* C, int64_t ldc, int c_dtype,
                      void* D, int64_t ldd, int d_dtype, void* stream) {
-  return dense_run("gemm_strided_run", -1, M, N, K, alpha, A, lda, a_major, B, ldb, b_major,
+  return dense_run("gemm_strided_run", kLibrary, 0, M, N, K, alpha, A, lda, a_major, B, ldb, b_major,
                    ab_dtype, beta, C, ldc, c_dtype, D, ldd, d_dtype, stream);
 }
 
@@ -198,8 +206,21 @@ int gemm_layout_run(int swz_units, int64_t M, int64_t N, int64_t K, const void* 
                     void* stream) {
   if (swz_units != 0 && swz_units != 8 && swz_units != 16)
     return fail(SG_ERR_SHAPE, "gemm_layout_run: swz_units %d is not 0, 8 or 16", swz_units);
-  return dense_run("gemm_layout_run", swz_units, M, N, K, 1.0f, A, K, SG_K_MAJOR, B, K,
-                   SG_K_MAJOR, SG_BF16, 1.0f, C, N, c_dtype, D, N, d_dtype, stream);
+  return dense_run("gemm_layout_run", kAblation256, swz_units, M, N, K, 1.0f, A, K,
+                   SG_K_MAJOR, B, K, SG_K_MAJOR, SG_BF16, 1.0f, C, N, c_dtype, D, N, d_dtype,
+                   stream);
+}
+
+int gemm_layout128_run(int layout, int64_t M, int64_t N, int64_t K, const void* A,
+                       const void* B, const void* C, int c_dtype, void* D, int d_dtype,
+                       void* stream) {
+  if (layout != 0 && layout != 8 && layout != 16 && layout != SG_LAYOUT_PAD16)
+    return fail(SG_ERR_SHAPE, "gemm_layout128_run: layout %d is not 0, 8, 16 or "
+                "SG_LAYOUT_PAD16", layout);
+  return dense_run("gemm_layout128_run", kAblation128,
+                   layout == SG_LAYOUT_PAD16 ? sg::kSwzPad : layout, M, N, K, 1.0f, A, K,
+                   SG_K_MAJOR, B, K, SG_K_MAJOR, SG_BF16, 1.0f, C, N, c_dtype, D, N, d_dtype,
+                   stream);
 }
 
 int grouped_gemm_run(int G, const int64_t* m_offsets, int64_t N, int64_t K,

@@ -180,6 +180,39 @@ struct OperandLoader<Rows, false, Swz, ElemBytes, Waves> {
   __device__ __forceinline__ void commit(char*, int) const {}
 };
 
+// K-major operand tile for the padded layout: the direct-to-LDS path fills
+// 1 KiB of consecutive LDS per instruction, which padded rows do not tile,
+// so each thread loads 16-byte chunks into registers (consecutive threads
+// along a row: coalesced) and writes them to their padded place.  Thread t
+// owns chunk t%8 of rows t/8 + (64 Waves / 8) i.
+template <int Rows, int ElemBytes, int Waves>
+struct OperandLoader<Rows, false, kSwzPad, ElemBytes, Waves> {
+  static constexpr int kRowsPerPass = 64 * Waves / 8;
+  static constexpr int kIssues = Rows / kRowsPerPass;  // loads per thread
+  static_assert(kIssues * kRowsPerPass == Rows, "tile rows must fill the passes");
+  u32x4 v[kIssues];
+  uint32_t pitch;
+  __device__ __forceinline__ void init(int, uint32_t p) { pitch = p; }
+  template <int I0 = 0, int I1 = kIssues>
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char*, int tid,
+                                        int rows_valid, int k0, int K) {
+    const int chunk = tid & 7;
+    const uint32_t kb = (uint32_t)k0 * ElemBytes + 16u * (uint32_t)chunk;
+    const bool k_ok = kb < (uint32_t)K * ElemBytes;
+#pragma unroll
+    for (int i = I0; i < (I1 < kIssues ? I1 : kIssues); ++i) {
+      const int row = (tid >> 3) + kRowsPerPass * i;
+      v[i] = buffer_load16(r, k_ok && row < rows_valid ? (uint32_t)row * pitch + kb
+                                                        : kOutOfRange);
+    }
+  }
+  __device__ __forceinline__ void commit(char* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kIssues; ++i)
+      lds_write16(lds, lds_offset<128, kSwzPad>((tid >> 3) + kRowsPerPass * i, tid & 7), v[i]);
+  }
+};
+
 template <int Rows, int Swz, int ElemBytes, int Waves>
 struct OperandLoader<Rows, true, Swz, ElemBytes, Waves> {
   static_assert(ElemBytes == 2, "MN-major sources are 16-bit");

@@ -233,13 +233,15 @@ template <int BM, int BN, bool IsBF16, bool AMn, bool BMn, int Swz, int Waves = 
 struct GemmTile {
   static constexpr int kBK = 64;            // K elements per stage
   static constexpr int kRowBytes = 128;     // kBK * 2 bytes
-  static constexpr int kATileBytes = BM * kRowBytes;
-  static constexpr int kBTileBytes = BN * kRowBytes;
+  static constexpr int kRowStride = lds_row_stride<kRowBytes, Swz>();  // 144 when padded
+  static constexpr int kATileBytes = BM * kRowStride;
+  static constexpr int kBTileBytes = BN * kRowStride;
   static constexpr int kStageBytes = kATileBytes + kBTileBytes;
   static constexpr int kWavesN = Waves / 2;         // waves along N (2 along M)
   static constexpr int kWM = BM / 2, kWN = BN / kWavesN;  // per-wave block
   static constexpr int kFM = kWM / 32, kFN = kWN / 32;
-  static_assert(kStageBytes % 4096 == 0, "stage bases must keep the swizzle phase");
+  static_assert(kStageBytes % 4096 == 0 || Swz == kSwzPad,
+                "stage bases must keep the swizzle phase");
   static_assert(kFM >= 1 && kFN >= 1, "each wave needs at least one 32x32 block");
 
   using ALoader = OperandLoader<BM, AMn, Swz, 2, Waves>;
@@ -254,8 +256,8 @@ struct GemmTile {
   // Per-lane LDS byte offsets of fragment 0 for each 16-wide K step.  Rows
   // 32 apart share the XOR key (it depends on the row only through the bank
   // line index modulo 16, i.e. row/2 mod 16, or row mod 8 for 128-byte
-  // lines), so fragment f sits exactly f * 32 * 128 bytes further: a
-  // constant the ds_read offset field absorbs.
+  // lines), so fragment f sits exactly f * 32 row strides further (the
+  // padded layout is linear): a constant the ds_read offset field absorbs.
   struct FragOffsets {
     uint32_t a[kBK / 16], b[kBK / 16];
   };
@@ -276,10 +278,10 @@ struct GemmTile {
                                                     int kk) {
 #pragma unroll
     for (int fm = 0; fm < kFM; ++fm)
-      f.a[fm] = lds_read16(As, o.a[kk] + fm * 32 * kRowBytes);
+      f.a[fm] = lds_read16(As, o.a[kk] + fm * 32 * kRowStride);
 #pragma unroll
     for (int fn = 0; fn < kFN; ++fn)
-      f.b[fn] = lds_read16(Bs, o.b[kk] + fn * 32 * kRowBytes);
+      f.b[fn] = lds_read16(Bs, o.b[kk] + fn * 32 * kRowStride);
   }
 
   // MFMA rows take B rows (n), columns take A rows (m): each lane then ends

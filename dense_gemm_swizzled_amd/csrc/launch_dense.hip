@@ -73,6 +73,14 @@ hipError_t launch_layout(int swz, const DenseParams& p, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_layout128(int layout, const DenseParams& p, hipStream_t s) {
+  if (layout == 16) return go_dense<128, 128, true, false, false, 16>(p, s);
+  if (layout == 8) return go_dense<128, 128, true, false, false, 8>(p, s);
+  if (layout == 0) return go_dense<128, 128, true, false, false, 0>(p, s);
+  if (layout == kSwzPad) return go_dense<128, 128, true, false, false, kSwzPad>(p, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_grouped(TileShape tile, bool bf16, int swz, const GroupedParams& p,
                           int grid, hipStream_t s) {
   if (swz != 16) return hipErrorInvalidValue;

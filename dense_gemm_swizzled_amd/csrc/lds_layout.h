@@ -31,13 +31,25 @@ namespace sg {
 
 constexpr int kSwzDefault = 16;
 
+// The padded layout of "Swizzling explained properly" (the alternative it
+// weighs against the swizzle): no XOR, every row followed by 16 bytes of
+// padding (a 144-byte row stride for 128-byte rows), so consecutive rows
+// start 36 banks apart.  Selected by Swz = kSwzPad, for the layout ablation.
+constexpr int kSwzPad = -1;
+
+// Bytes from one tile row to the next.
+template <int RowBytes, int Swz>
+SG_HD constexpr uint32_t lds_row_stride() {
+  return Swz == kSwzPad ? RowBytes + 16 : RowBytes;
+}
+
 // Byte offset, within one stage, of logical 16-byte chunk `chunk` of tile
 // row `row`, for rows of RowBytes bytes and a line of Swz 16-byte units.
 template <int RowBytes, int Swz>
 SG_HD constexpr uint32_t lds_offset(uint32_t row, uint32_t chunk) {
-  static_assert(Swz == 0 || Swz == 8 || Swz == 16, "unsupported swizzle");
-  const uint32_t off = row * RowBytes + chunk * 16u;
-  if constexpr (Swz == 0) {
+  static_assert(Swz == 0 || Swz == 8 || Swz == 16 || Swz == kSwzPad, "unsupported layout");
+  const uint32_t off = row * lds_row_stride<RowBytes, Swz>() + chunk * 16u;
+  if constexpr (Swz == 0 || Swz == kSwzPad) {
     return off;
   } else {
     constexpr uint32_t line_shift = Swz == 8 ? 7 : 8;  // log2(line bytes)
@@ -49,6 +61,7 @@ SG_HD constexpr uint32_t lds_offset(uint32_t row, uint32_t chunk) {
 // inverse: the key bits, above bit 7 or 8, are left unchanged).
 template <int Swz>
 SG_HD constexpr uint32_t swz_bytes(uint32_t off) {
+  static_assert(Swz != kSwzPad, "the padded layout is not a permutation of a stage");
   if constexpr (Swz == 0) {
     return off;
   } else {
@@ -60,6 +73,7 @@ SG_HD constexpr uint32_t swz_bytes(uint32_t off) {
 // Runtime-dispatched form for host tools.
 SG_HD uint32_t lds_offset_rt(int row_bytes, int swz, uint32_t row,
                              uint32_t chunk) {
+  if (swz == kSwzPad) return row * (uint32_t)(row_bytes + 16) + chunk * 16u;
   const uint32_t off = row * (uint32_t)row_bytes + chunk * 16u;
   if (swz == 0) return off;
   const uint32_t line_shift = swz == 8 ? 7 : 8;

@@ -190,6 +190,23 @@ int gemm_layout_run(int swz_units, int64_t M, int64_t N, int64_t K, const void* 
                     const void* B, const void* C, int c_dtype, void* D, int d_dtype,
                     void* stream);
 
+/*
+ * gemm_layout128_run -- gemm_layout_run on 128x128 tiles of the 4-wave
+ * kernel (the 32x32x16 MFMA), where a padded layout also fits in LDS: the
+ * padding alternative to swizzling weighed in "Swizzling explained properly"
+ * (sections "Why swizzle?" and "Results").
+ *   layout  16, 8 or 0 as gemm_layout_run's swz_units, or SG_LAYOUT_PAD16:
+ *           no XOR, each 128-byte LDS row followed by 16 bytes of padding
+ *           (loaded through registers, since padded rows do not tile the
+ *           direct-to-LDS path's 1 KiB regions).
+ * Every layout gives the same D.  Errors: as gemm_layout_run, SG_ERR_SHAPE
+ * for another layout value.
+ */
+#define SG_LAYOUT_PAD16 (-1)
+int gemm_layout128_run(int layout, int64_t M, int64_t N, int64_t K, const void* A,
+                       const void* B, const void* C, int c_dtype, void* D, int d_dtype,
+                       void* stream);
+
 /* Thread-local text of the last failing call ("" if none).  Never NULL. */
 const char* gemm_last_error(void);
 

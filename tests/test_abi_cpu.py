@@ -28,7 +28,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"gemm_run", "gemm_strided_run", "grouped_gemm_run", "mx_gemm_run", "mxfp4_gemm_run",
-            "gemm_layout_run",
+            "gemm_layout_run", "gemm_layout128_run",
             "gemm_last_error", "gemm_version", "gemm_lds_layout",
             "gemm_lds_image"} <= set(names)
     lib = ctypes.CDLL(sg.library_path())
@@ -83,6 +83,25 @@ def test_gemm_strided_run_unread_operands_may_be_null():
     # launch happens for M = 0, and the checks that remain pass.
     assert _strided(M=0, alpha=0.0, A=None, B=None) == 0
     assert _strided(N=0, beta=0.0, C=P + 3, c_dtype=sg.SG_F32) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layout=4), SHAPE), (dict(layout=-2), SHAPE), (dict(M=-1), SHAPE), (dict(D=None), NULL),
+    (dict(A=P + 8), ALIGN), (dict(K=60), ALIGN), (dict(d_dtype=sg.SG_E4M3), DTYPE),
+])
+def test_gemm_layout128_run_rejects(kw, code):
+    a = dict(layout=sg.SG_LAYOUT_PAD16, M=256, N=256, K=64, A=P, B=P, C=None, c_dtype=0, D=P,
+             d_dtype=sg.SG_F32)
+    a.update(kw)
+    rc = sg.gemm_layout128_run(a["layout"], a["M"], a["N"], a["K"], a["A"], a["B"], a["C"],
+                               a["c_dtype"], a["D"], a["d_dtype"], None)
+    assert rc == code, sg.gemm_last_error()
+    assert sg.gemm_last_error().startswith("gemm_layout128_run")
+
+
+def test_gemm_layout128_run_empty_is_ok():
+    for layout in (0, 8, 16, sg.SG_LAYOUT_PAD16):
+        assert sg.gemm_layout128_run(layout, 0, 256, 64, P, P, None, 0, P, sg.SG_F32, None) == 0
 
 
 def test_gemm_layout_run_empty_is_ok():

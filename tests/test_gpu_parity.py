@@ -204,6 +204,23 @@ def test_layout_variants_bit_identical(dev):
     assert torch.equal(outs[16], outs[0])
 
 
+def test_layout128_variants_bit_identical(dev):
+    # The 128x128 kernel with the swizzles, no layout change and the padded
+    # rows: same bits, and the library's layout matches the oracle.
+    M, N, K = 1000, 1032, 200
+    case = si.dense_case(M, N, K, 22, ab_dtype="bf16", with_c=True, c_dtype="bf16",
+                         d_dtype="f32", scale=1.0 / np.sqrt(K))
+    A, B, C = case.A.to(dev), case.B.to(dev), case.C.to(dev)
+    say(f"layout128 variants {M}x{N}x{K}")
+    outs = {lay: sg.gemm_layout128(A, B, lay, C=C, out_dtype=torch.float32)
+            for lay in (16, 8, 0, sg.SG_LAYOUT_PAD16)}
+    torch.cuda.synchronize()
+    ref, bound = oracle_dense(case)
+    check_close(_np(outs[16]), ref, bound, "f32", "layout128 16")
+    for lay in (8, 0, sg.SG_LAYOUT_PAD16):
+        assert torch.equal(outs[16], outs[lay]), lay
+
+
 def test_dense_integer_inputs_exact(dev):
     # Integer values in [-4, 4]: every partial sum is exact in fp32, so the
     # result must be bit-exact whatever the summation order.

@@ -166,6 +166,23 @@ def test_kernel_loader_stores_conflict_free(model, tile):
     assert worst == 1
 
 
+def test_padded_layout_is_conflict_free(model):
+    # The padded layout of the layout ablation (144-byte rows, no XOR): the
+    # 32x32x16 fragment reads and the register-staged ds_write_b128 stores
+    # (thread t -> row t/8 + 32 i, chunk t%8) of the 128x128 kernel.
+    pad = lambda r, c: r * 144 + 16 * c
+    worst = 0
+    for base in range(0, 128, 32):
+        for kk in range(4):
+            worst = max(worst, _degree(model, "r128",
+                                       [pad(base + l % 32, 2 * kk + l // 32) for l in range(64)]))
+    for wave in range(4):
+        for i in range(4):
+            tids = [64 * wave + l for l in range(64)]
+            worst = max(worst, _degree(model, "w128", [pad(32 * i + t // 8, t % 8) for t in tids]))
+    assert worst == 1
+
+
 def test_unswizzled_layout_would_conflict(model):
     # The same 16-bit operand read on an unswizzled 128-byte-pitch tile.
     a = [(l % 32) * 128 + 16 * (l // 32) for l in range(64)]
