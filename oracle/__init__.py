@@ -20,8 +20,9 @@ Contents
   "LBO, SBO and SWZ for a tcgen05 tile", introduction; the pages give no
   further definition, so this is the plain reading).
 * ``mx_gemm`` / ``mx_gemm_points``: block-scaled GEMM with one e8m0 scale per
-  row and 32-element K block ("06 Blackwell Tensor Core", Block-Scaled MMA).
-* ``decode``: fp16 / bf16 / OCP e4m3 / e8m0 decode to fp64.
+  row and 32-element K block ("06 Blackwell Tensor Core", Block-Scaled MMA);
+  elements e4m3, e2m1 (two per byte) or e2m3 / e3m2 (a 6-bit stream).
+* ``decode``: fp16 / bf16 / OCP e4m3, e2m1, e2m3, e3m2 / e8m0 decode to fp64.
 * ``swizzle``: the XOR swizzle maps (``oracle.swizzle``).
 * ``banks``: the LDS / shared-memory bank-conflict simulator
   (``oracle.banks``).
@@ -43,7 +44,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gemm_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-_DT = {"f16": 1, "bf16": 2, "f32": 3, "e4m3": 4, "e8m0": 5, "e2m1": 6}
+_DT = {"f16": 1, "bf16": 2, "f32": 3, "e4m3": 4, "e8m0": 5, "e2m1": 6, "e2m3": 7,
+       "e3m2": 8}
 _MAJ = {"k": 0, "mn": 1}
 
 _lib = None
@@ -117,12 +119,14 @@ def _ptr(a: Optional[np.ndarray]):
 
 def decode(dtype: str, data) -> np.ndarray:
     """Decode raw storage of ``dtype`` ("f16", "bf16", "f32", "e4m3",
-    "e8m0", "e2m1") to fp64, element by element.  e2m1 packs two elements
-    per byte (element 2i in the low nibble of byte i) and returns a flat
-    array of 2 * nbytes values."""
+    "e8m0", "e2m1", "e2m3", "e3m2") to fp64, element by element.  e2m1 packs
+    two elements per byte (element 2i in the low nibble of byte i) and
+    returns a flat array of 2 * nbytes values; e2m3 and e3m2 are a 6-bit
+    stream (element k at bits [6k, 6k+6), little endian) and return
+    nbytes * 4 / 3 values."""
     a = _bytes(data)
-    if dtype == "e2m1":
-        n = a.nbytes * 2
+    if dtype in ("e2m1", "e2m3", "e3m2"):
+        n = a.nbytes * 2 if dtype == "e2m1" else a.nbytes * 4 // 3
         out = np.empty(n, dtype=np.float64)
         if _load().oracle_decode(_DT[dtype], _ptr(a), n, _ptr(out)) != 0:
             raise ValueError("oracle_decode failed")
@@ -218,8 +222,9 @@ def grouped_gemm(m_offsets: Sequence[int], N: int, K: int, A, B,
 def mx_gemm(M: int, N: int, K: int, A, SFA, B, SFB, nthreads: int = 0,
             with_bound: bool = True, fmt: str = "e4m3"):
     """Block-scaled GEMM with e8m0 scales per 32-element K block; the
-    elements are e4m3 (A [M][K] bytes) or e2m1 (fmt "e2m1", A [M][K/2]
-    bytes, two elements per byte)."""
+    elements are e4m3 (A [M][K] bytes), e2m1 (fmt "e2m1", A [M][K/2]
+    bytes, two elements per byte) or e2m3 / e3m2 (A [M][3K/4] bytes, a
+    6-bit stream per row)."""
     a, sa, b, sb = _bytes(A), _bytes(SFA), _bytes(B), _bytes(SFB)
     ref = np.empty((M, N), dtype=np.float64)
     bound = np.empty((M, N), dtype=np.float64) if with_bound else None

@@ -22,7 +22,9 @@
  *     SFB[n,sfk] for B ("06 Blackwell Tensor Core", Block-Scaled MMA).  The
  *     32-element K block and the e8m0 scale type are not on that page; they
  *     are the MXFP8 workload's definition.  MXFP4 is the same sum over e2m1
- *     elements (two per byte, element 2i in the low nibble of byte i).
+ *     elements (two per byte, element 2i in the low nibble of byte i);
+ *     MXFP6 over OCP e2m3 or e3m2 elements stored as a 6-bit stream per
+ *     row (element k at bits [6k, 6k+6), little endian).
  *
  * Products of two 16-bit floats (and of two e4m3) are exact in fp64; the
  * fp64 sum of K terms is within (K-1)*2^-53 * bound of the exact value.
@@ -36,7 +38,8 @@
 #include <string.h>
 #include <unistd.h>
 
-enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_F32 = 3, ORC_E4M3 = 4, ORC_E8M0 = 5, ORC_E2M1 = 6 };
+enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_F32 = 3, ORC_E4M3 = 4, ORC_E8M0 = 5, ORC_E2M1 = 6,
+       ORC_E2M3 = 7, ORC_E3M2 = 8 };
 enum { ORC_K_MAJOR = 0, ORC_MN_MAJOR = 1 };
 
 /* ---------------------------------------------------------------- decode */
@@ -94,6 +97,41 @@ static double dec_e2m1(uint8_t nib) {
     return s ? -v : v;
 }
 
+/* OCP FP6 E2M3: 1 sign, 2 exponent (bias 1), 3 fraction bits; no infinity
+ * or NaN; the largest magnitude is 7.5. */
+static double dec_e2m3(uint8_t c) {
+    int s = (c >> 5) & 1, e = (c >> 3) & 3, m = c & 7;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -3);              /* m/8 * 2^(1-1) */
+    else
+        v = ldexp((double)(8 + m), e - 4);     /* (1 + m/8) * 2^(e-1) */
+    return s ? -v : v;
+}
+
+/* OCP FP6 E3M2: 1 sign, 3 exponent (bias 3), 2 fraction bits; no infinity
+ * or NaN; the largest magnitude is 28. */
+static double dec_e3m2(uint8_t c) {
+    int s = (c >> 5) & 1, e = (c >> 2) & 7, m = c & 3;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -4);              /* m/4 * 2^(1-3) */
+    else
+        v = ldexp((double)(4 + m), e - 5);     /* (1 + m/4) * 2^(e-3) */
+    return s ? -v : v;
+}
+
+/* Element idx of a packed 6-bit stream: bits [6 idx, 6 idx + 6), little
+ * endian (bit 0 of the stream is bit 0 of byte 0). */
+static uint8_t code6_at(const uint8_t *p, int64_t idx) {
+    int64_t bit = 6 * idx;
+    int64_t byte = bit >> 3;
+    int sh = (int)(bit & 7);
+    unsigned w = p[byte];
+    if (sh > 2) w |= (unsigned)p[byte + 1] << 8;
+    return (uint8_t)((w >> sh) & 63);
+}
+
 /* OCP E8M0 scale: 2^(e-127); 0xFF is NaN. */
 static double dec_e8m0(uint8_t b) {
     return b == 255 ? NAN : ldexp(1.0, (int)b - 127);
@@ -105,6 +143,7 @@ static int elem_size(int dt) {
     case ORC_F32: return 4;
     case ORC_E4M3: case ORC_E8M0: return 1;
     case ORC_E2M1: return 1;  /* two elements per byte; indices count elements */
+    case ORC_E2M3: case ORC_E3M2: return 1;  /* four elements per three bytes */
     default: return 0;
     }
 }
@@ -118,6 +157,8 @@ static double dec_at(int dt, const void *base, int64_t idx) {
     case ORC_E4M3: return dec_e4m3(p[idx]);
     case ORC_E8M0: return dec_e8m0(p[idx]);
     case ORC_E2M1: return dec_e2m1((idx & 1) ? (uint8_t)(p[idx >> 1] >> 4) : (uint8_t)(p[idx >> 1] & 15));
+    case ORC_E2M3: return dec_e2m3(code6_at(p, idx));
+    case ORC_E3M2: return dec_e3m2(code6_at(p, idx));
     default: return NAN;
     }
 }
@@ -327,11 +368,12 @@ static void mx_rows(void *vctx, int64_t i0, int64_t i1) {
 }
 
 /* A [M][K], SFA e8m0 [M][K/32], B [N][K], SFB e8m0 [N][K/32]; the elements
- * are e4m3 (fmt ORC_E4M3, one per byte) or e2m1 (ORC_E2M1, two per byte). */
+ * are e4m3 (fmt ORC_E4M3, one per byte), e2m1 (ORC_E2M1, two per byte) or
+ * e2m3 / e3m2 (ORC_E2M3 / ORC_E3M2, a 6-bit stream: four per three bytes). */
 int oracle_mx_gemm_fmt(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t *A,
                        const uint8_t *SFA, const uint8_t *B, const uint8_t *SFB,
                        double *ref, double *bound, int nthreads) {
-    if (fmt != ORC_E4M3 && fmt != ORC_E2M1) return -1;
+    if (fmt != ORC_E4M3 && fmt != ORC_E2M1 && fmt != ORC_E2M3 && fmt != ORC_E3M2) return -1;
     if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || !ref) return -1;
     if (K > 0 && ((M > 0 && (!A || !SFA)) || (N > 0 && (!B || !SFB)))) return -1;
     int64_t nblk = K / 32;
@@ -363,7 +405,7 @@ int oracle_mx_gemm_points_fmt(int fmt, int64_t M, int64_t N, int64_t K, const ui
                               const uint8_t *SFB, int64_t npts,
                               const int64_t *rows, const int64_t *cols,
                               double *ref, double *bound) {
-    if (fmt != ORC_E4M3 && fmt != ORC_E2M1) return -1;
+    if (fmt != ORC_E4M3 && fmt != ORC_E2M1 && fmt != ORC_E2M3 && fmt != ORC_E3M2) return -1;
     if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || npts < 0 || !ref ||
         (npts && (!rows || !cols)))
         return -1;

@@ -1,7 +1,8 @@
 """Seeded synthetic inputs for the swizzled GEMM workloads.
 
 This module only draws random numbers and rounds them to the storage formats
-the GEMM consumes (fp16, bf16, OCP e4m3 with e8m0 block scales).  It holds
+the GEMM consumes (fp16, bf16, and the OCP MX element formats e4m3, e2m1,
+e2m3 and e3m2 with e8m0 block scales).  It holds
 none of the GEMM arithmetic: the same bytes it returns are handed to the CPU
 oracle and to the HIP path, and each side computes from them on its own.
 
@@ -22,6 +23,11 @@ Workloads (sizes, majorness and distributions of the five GEMM cases):
 * ``mxfp8``: M=N=K=8192, A ``[M][K]``, B ``[N][K]``, N(0,1) fp32 values
   quantised per 32-element K block to e4m3 with an e8m0 scale equal to the
   power of two at or below the block's absolute maximum.
+* ``mxfp4``: the same shape with e2m1 elements (two per byte), the scale
+  putting each block's absolute maximum in e2m1's top binade [4, 8).
+* ``mxfp6``: the same shape with e2m3 (or e3m2) elements in a 6-bit stream,
+  the scale putting each block's absolute maximum in the format's top
+  binade ([4, 8) for e2m3, [16, 32) for e3m2).
 """
 from __future__ import annotations
 
@@ -115,13 +121,13 @@ class MXCase:
     M: int
     N: int
     K: int
-    A: torch.Tensor          # uint8 e4m3 [M][K], or e2m1 [M][K/2] (two per byte)
+    A: torch.Tensor          # uint8 e4m3 [M][K], e2m1 [M][K/2] or fp6 [M][3K/4]
     SFA: torch.Tensor        # uint8 e8m0 [M][K/32]
-    B: torch.Tensor          # uint8 e4m3 [N][K], or e2m1 [N][K/2]
+    B: torch.Tensor          # uint8 e4m3 [N][K], e2m1 [N][K/2] or fp6 [N][3K/4]
     SFB: torch.Tensor        # uint8 e8m0 [N][K/32]
     d_dtype: str
     name: str = ""
-    fmt: str = "e4m3"        # element format: "e4m3" or "e2m1"
+    fmt: str = "e4m3"        # element format: "e4m3", "e2m1", "e2m3" or "e3m2"
 
 
 def _layout(x_logical: np.ndarray, major: str) -> np.ndarray:
@@ -259,11 +265,73 @@ def mxfp4_quantize(x: np.ndarray, block: int = 32):
     return torch.from_numpy(np.ascontiguousarray(packed)), torch.from_numpy((e + 127).astype(np.uint8))
 
 
+def _fp6_magnitudes(exp_bits: int, man_bits: int) -> np.ndarray:
+    """Magnitudes of the 32 non-negative codes of an OCP FP6 format with
+    1 + exp_bits + man_bits = 6 bits and no Inf/NaN (E2M3: bias 1, E3M2:
+    bias 3); code c has exponent field c >> man_bits, fraction c & mask."""
+    bias = (1 << (exp_bits - 1)) - 1
+    out = np.empty(32, dtype=np.float64)
+    for c in range(32):
+        e, m = c >> man_bits, c & ((1 << man_bits) - 1)
+        if e == 0:
+            out[c] = math.ldexp(m, 1 - bias - man_bits)
+        else:
+            out[c] = math.ldexp((1 << man_bits) + m, e - bias - man_bits)
+    return out
+
+
+# name -> (exponent bits, fraction bits, exponent of the top binade)
+_FP6 = {"e2m3": (2, 3, 2), "e3m2": (3, 2, 4)}
+
+
+def mxfp6_quantize(x: np.ndarray, fmt: str = "e2m3", block: int = 32):
+    """Quantise fp32 rows [R][K] to FP6 (``fmt`` "e2m3" or "e3m2") with one
+    e8m0 scale per K block.
+
+    The scale is X = 2^(floor(log2(absmax)) - emax) of the block (emax = 2
+    for E2M3, 4 for E3M2; X = 1 for an all-zero block), which puts the
+    block's largest magnitude in the format's top binade; magnitudes above
+    the largest value (7.5 resp. 28) become it.  Elements are x / X rounded
+    to the nearest value, ties to the even code.  The codes of a row form a
+    6-bit stream: element k at bits [6k, 6k + 6), little endian, so four
+    elements fill three bytes.
+    Returns (packed uint8 [R][3K/4], scales uint8 [R][K/block]).
+    """
+    eb, mb, emax = _FP6[fmt]
+    R, K = x.shape
+    assert K % block == 0 and K % 4 == 0
+    xb = x.reshape(R, K // block, block)
+    amax = np.abs(xb).max(axis=2)
+    e = np.zeros_like(amax, dtype=np.int32)
+    nz = amax > 0
+    _, ex = np.frexp(amax[nz])
+    e[nz] = ex - 1 - emax
+    e = np.clip(e, -127, 127)
+    y = (xb / np.ldexp(np.float32(1.0), e)[:, :, None].astype(np.float32)).reshape(R, K)
+    vals = _fp6_magnitudes(eb, mb).astype(np.float32)
+    mids = (vals[:-1] + vals[1:]) / 2
+    mag = np.minimum(np.abs(y), vals[-1])
+    code = np.zeros(mag.shape, dtype=np.uint32)
+    for i, t in enumerate(mids):
+        code += (mag >= t) if i % 2 else (mag > t)
+    code |= ((y < 0) & (code != 0)).astype(np.uint32) << 5
+    q = code.reshape(R, K // 4, 4)
+    w = q[:, :, 0] | (q[:, :, 1] << 6) | (q[:, :, 2] << 12) | (q[:, :, 3] << 18)
+    packed = np.stack([w & 255, (w >> 8) & 255, (w >> 16) & 255], axis=2).astype(np.uint8)
+    return (torch.from_numpy(np.ascontiguousarray(packed.reshape(R, 3 * K // 4))),
+            torch.from_numpy((e + 127).astype(np.uint8)))
+
+
 def mx_case(M, N, K, seed, *, d_dtype="bf16", name="", fmt="e4m3") -> MXCase:
     rng = _rng(seed)
     a = normal(rng, (M, K))
     b = normal(rng, (N, K))
-    q = mx_quantize if fmt == "e4m3" else mxfp4_quantize
+    if fmt == "e4m3":
+        q = mx_quantize
+    elif fmt == "e2m1":
+        q = mxfp4_quantize
+    else:
+        q = lambda v: mxfp6_quantize(v, fmt)  # noqa: E731
     A, SFA = q(a)
     B, SFB = q(b)
     return MXCase(M, N, K, A, SFA, B, SFB, d_dtype, name, fmt)
@@ -277,6 +345,13 @@ def mxfp8(seed: int = 5, M: int = 8192, N: int = 8192, K: int = 8192) -> MXCase:
 def mxfp4(seed: int = 7, M: int = 8192, N: int = 8192, K: int = 8192) -> MXCase:
     """MXFP4 8192^3: e2m1 (two per byte) with per-32 K-block e8m0 scales, bf16 out."""
     return mx_case(M, N, K, seed, name=f"mxfp4_{M}x{N}x{K}", fmt="e2m1")
+
+
+def mxfp6(seed: int = 8, M: int = 8192, N: int = 8192, K: int = 8192,
+          fmt: str = "e2m3") -> MXCase:
+    """MXFP6 8192^3: e2m3 (or e3m2) as a 6-bit stream with per-32 K-block
+    e8m0 scales, bf16 out."""
+    return mx_case(M, N, K, seed, name=f"mxfp6_{fmt}_{M}x{N}x{K}", fmt=fmt)
 
 
 def integer_valued(shape, seed, lo=-4, hi=4) -> np.ndarray:
