@@ -4,15 +4,15 @@
 A step is one call of the hot path on one batch of synthetic input that is
 already resident in HBM.  The default workload is the dense 8192^3 bf16 GEMM
 D = A*B + C (A and B K-major, C bf16, bf16 output, fp32 accumulation); the
-other workloads (--workload) are the grouped 16 x 4096^2 GEMM, the MXFP8
-8192^3 GEMM, the MXFP4 8192^3 GEMM, the 1024^3 and the 128x128x32 single-tile
-GEMMs.
+other workloads (--workload) are the grouped 16 x 4096^2 GEMM, the MXFP8,
+MXFP6 (e2m3, or e3m2 as mxfp6_e3m2) and MXFP4 8192^3 GEMMs, the 1024^3 and
+the 128x128x32 single-tile GEMMs.
 
 Prints ONE JSON line on stdout (everything else goes to stderr):
   value          whole-job TFLOP/s = 2*M*N*K / (measured seconds per step)
   roofline       the dominant kernel against MI355X's published dense MFMA
-                 peak for its dtype (bf16/fp16 2516.6, fp8 5033.2, fp4 10066.4
-                 TFLOP/s);
+                 peak for its dtype (bf16/fp16 2516.6, fp8 5033.2, fp6 and fp4
+                 10066.4 TFLOP/s);
                  achieved = algorithmic FLOP per launch / mean launch time
                  from HIP events recorded on the launch stream
   cpu_baseline   the CPU oracle (fp64 triple loop, all host cores) timed on a
@@ -31,7 +31,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.4}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.4,
+               "e2m3": 10066.4, "e3m2": 10066.4}
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -184,6 +185,27 @@ def build_workload(name: str, dev, layout=None):
 
         return run, flops, "e2m1", cfg, oracle_sample, case.M
 
+    if name in ("mxfp6", "mxfp6_e3m2"):
+        case = si.mxfp6(fmt="e3m2") if name == "mxfp6_e3m2" else si.mxfp6()
+        A, SFA, B, SFB = (t.to(dev) for t in (case.A, case.SFA, case.B, case.SFB))
+        D = torch.empty(case.M, case.N, dtype=torch.bfloat16, device=dev)
+
+        def run():
+            sg.mxfp6_gemm(A, SFA, B, SFB, fmt=case.fmt, out=D)
+
+        flops = 2.0 * case.M * case.N * case.K
+        cfg = {"workload": case.name, "M": case.M, "N": case.N, "K": case.K,
+               "block": 32, "ab_dtype": case.fmt, "scale": "e8m0", "d_dtype": "bf16"}
+
+        def oracle_sample(rows):
+            import oracle
+            t0 = time.perf_counter()
+            oracle.mx_gemm(rows, case.N, case.K, case.A[:rows], case.SFA[:rows], case.B,
+                           case.SFB, with_bound=False, fmt=case.fmt)
+            return time.perf_counter() - t0, 2.0 * rows * case.N * case.K
+
+        return run, flops, case.fmt, cfg, oracle_sample, case.M
+
     if name == "copy":
         # A plain device copy of known size: the reference for scaling the
         # FETCH_SIZE / WRITE_SIZE counters into bytes.
@@ -226,7 +248,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="dense_8192",
-                    choices=["dense_8192", "grouped", "mxfp8", "mxfp4", "dense_1024",
+                    choices=["dense_8192", "grouped", "mxfp8", "mxfp4", "mxfp6", "mxfp6_e3m2",
+                             "dense_1024",
                              "single_tile", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layout", type=int, choices=[16, 8, 0], default=None,

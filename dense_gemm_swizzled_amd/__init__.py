@@ -6,10 +6,13 @@ no CPU fallback: if the shared library is missing, every call raises.
 
 Two layers:
 
-* ``gemm_run``, ``grouped_gemm_run``, ``mx_gemm_run``, ``gemm_last_error``,
-  ``gemm_version``, ``gemm_lds_layout``, ``gemm_lds_image``: the C entry
-  points under the same names, taking integer device pointers.
-* ``gemm``, ``grouped_gemm``, ``mx_gemm``: the same calls on torch CUDA
+* ``gemm_run``, ``gemm_strided_run``, ``grouped_gemm_run``, ``mx_gemm_run``,
+  ``mxfp4_gemm_run``, ``mxfp6_gemm_run``, ``gemm_layout_run``,
+  ``gemm_layout128_run``, ``gemm_last_error``, ``gemm_version``,
+  ``gemm_lds_layout``, ``gemm_lds_layout_mxfp6``, ``gemm_lds_image``: the C
+  entry points under the same names, taking integer device pointers.
+* ``gemm``, ``gemm_strided``, ``grouped_gemm``, ``mx_gemm``, ``mxfp4_gemm``,
+  ``mxfp6_gemm``, ``gemm_layout``, ``gemm_layout128``: the same calls on torch CUDA
   tensors (shapes read from the tensors, output allocated by torch, launched
   on torch's current stream).
 """
@@ -24,16 +27,19 @@ import numpy as np
 __all__ = [
     "SG_OK", "SG_F16", "SG_BF16", "SG_F32", "SG_E4M3", "SG_E8M0", "SG_NONE",
     "SG_K_MAJOR", "SG_MN_MAJOR", "SG_MAX_GROUPS", "GemmError",
-    "gemm_run", "grouped_gemm_run", "mx_gemm_run", "mxfp4_gemm_run", "gemm_layout_run",
-    "gemm_last_error",
-    "gemm_version", "gemm_lds_layout", "gemm_lds_image",
-    "gemm", "gemm_strided", "grouped_gemm", "mx_gemm", "mxfp4_gemm", "gemm_layout",
+    "gemm_run", "gemm_strided_run", "grouped_gemm_run", "mx_gemm_run", "mxfp4_gemm_run",
+    "mxfp6_gemm_run", "gemm_layout_run", "gemm_layout128_run", "gemm_last_error",
+    "gemm_version", "gemm_lds_layout", "gemm_lds_layout_mxfp6", "gemm_lds_image",
+    "SG_E2M3", "SG_E3M2",
+    "gemm", "gemm_strided", "grouped_gemm", "mx_gemm", "mxfp4_gemm", "mxfp6_gemm",
+    "gemm_layout",
     "gemm_layout128", "SG_LAYOUT_PAD16",
     "library_path", "load",
 ]
 
 SG_OK = 0
 SG_NONE, SG_F16, SG_BF16, SG_F32, SG_E4M3, SG_E8M0 = 0, 1, 2, 3, 4, 5
+SG_E2M3, SG_E3M2 = 7, 8
 SG_K_MAJOR, SG_MN_MAJOR = 0, 1
 SG_MAX_GROUPS = 128
 SG_LAYOUT_PAD16 = -1
@@ -75,14 +81,16 @@ def load():
                                      i32, vp, i32, i32, vp, i32, vp]
     lib.mx_gemm_run.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
     lib.mxfp4_gemm_run.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
+    lib.mxfp6_gemm_run.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
     lib.gemm_layout_run.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, vp, i32, vp]
     lib.gemm_layout128_run.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, vp, i32, vp]
     lib.gemm_lds_layout.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int32)]
+    lib.gemm_lds_layout_mxfp6.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int32)]
     lib.gemm_lds_image.argtypes = [vp, i64, i64, i32, i64, i64, i32, vp, vp]
     for f in (lib.gemm_run, lib.gemm_strided_run, lib.grouped_gemm_run, lib.mx_gemm_run,
-              lib.mxfp4_gemm_run,
+              lib.mxfp4_gemm_run, lib.mxfp6_gemm_run,
               lib.gemm_layout_run, lib.gemm_layout128_run,
-              lib.gemm_lds_layout, lib.gemm_lds_image):
+              lib.gemm_lds_layout, lib.gemm_lds_layout_mxfp6, lib.gemm_lds_image):
         f.restype = ctypes.c_int
     lib.gemm_last_error.argtypes = []
     lib.gemm_last_error.restype = ctypes.c_char_p
@@ -123,6 +131,10 @@ def mxfp4_gemm_run(M, N, K, A, SFA, B, SFB, D, d_dtype, stream) -> int:
     return load().mxfp4_gemm_run(M, N, K, A, SFA, B, SFB, D, d_dtype, stream)
 
 
+def mxfp6_gemm_run(fmt, M, N, K, A, SFA, B, SFB, D, d_dtype, stream) -> int:
+    return load().mxfp6_gemm_run(fmt, M, N, K, A, SFA, B, SFB, D, d_dtype, stream)
+
+
 def gemm_layout_run(swz_units, M, N, K, A, B, C, c_dtype, D, d_dtype, stream) -> int:
     return load().gemm_layout_run(swz_units, M, N, K, A, B, C, c_dtype, D, d_dtype, stream)
 
@@ -147,6 +159,17 @@ def gemm_lds_layout(rows: int, row_bytes: int) -> np.ndarray:
     if rc != SG_OK:
         raise GemmError(rc, gemm_last_error())
     return out[:-1].reshape(rows, row_bytes // 16)
+
+
+def gemm_lds_layout_mxfp6(rows: int, unshifted: int = 32) -> np.ndarray:
+    """[rows][12] LDS byte offsets of bytes [8q, 8q+8) of each 96-byte row of
+    the MXFP6 kernel's operand tile."""
+    out = np.zeros(max(rows, 0) * 12 + 1, dtype=np.int32)
+    rc = load().gemm_lds_layout_mxfp6(rows, unshifted,
+                                      out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    if rc != SG_OK:
+        raise GemmError(rc, gemm_last_error())
+    return out[:-1].reshape(rows, 12)
 
 
 def gemm_lds_image(X, rows_total, K, elem_bytes, row0, k0, tile_rows, out,
@@ -292,6 +315,21 @@ def mxfp4_gemm(A, SFA, B, SFB, *, out_dtype=None, out=None):
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=A.device)
     _check(mxfp4_gemm_run(M, N, K, A.data_ptr(), SFA.data_ptr(), B.data_ptr(),
+                          SFB.data_ptr(), out.data_ptr(), _dt(out.dtype), _stream(A.device)))
+    return out
+
+
+def mxfp6_gemm(A, SFA, B, SFB, *, fmt: str = "e2m3", out_dtype=None, out=None):
+    """Block-scaled FP6 GEMM: A [M][3K/4], B [N][3K/4] (uint8, a 6-bit
+    stream of e2m3 or e3m2 codes per row, element k at bits [6k, 6k+6)),
+    SFA [M][K/32], SFB [N][K/32] (uint8 e8m0 codes)."""
+    import torch
+    code = {"e2m3": SG_E2M3, "e3m2": SG_E3M2}[fmt]
+    M, K = A.shape[0], A.shape[1] * 4 // 3
+    N = B.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=A.device)
+    _check(mxfp6_gemm_run(code, M, N, K, A.data_ptr(), SFA.data_ptr(), B.data_ptr(),
                           SFB.data_ptr(), out.data_ptr(), _dt(out.dtype), _stream(A.device)))
     return out
 

@@ -329,6 +329,51 @@ int mxfp4_gemm_run(int64_t M, int64_t N, int64_t K, const void* A, const void* S
   return ok();
 }
 
+int mxfp6_gemm_run(int fmt, int64_t M, int64_t N, int64_t K, const void* A, const void* SFA,
+                   const void* B, const void* SFB, void* D, int d_dtype, void* stream) {
+  if (fmt != SG_E2M3 && fmt != SG_E3M2)
+    return fail(SG_ERR_DTYPE, "mxfp6_gemm_run: fmt %d is not SG_E2M3/SG_E3M2", fmt);
+  if (M < 0 || N < 0 || K < 0)
+    return fail(SG_ERR_SHAPE, "mxfp6_gemm_run: negative size");
+  if (K % 128)
+    return fail(SG_ERR_SHAPE, "mxfp6_gemm_run: K=%lld is not a multiple of 128", (long long)K);
+  if (d_dtype != SG_F32 && d_dtype != SG_BF16)
+    return fail(SG_ERR_DTYPE, "mxfp6_gemm_run: d_dtype %d is not SG_F32/SG_BF16", d_dtype);
+  if (M == 0 || N == 0) return ok();
+  if (!D) return fail(SG_ERR_NULL, "mxfp6_gemm_run: D is NULL");
+  if (K > 0 && (!A || !B || !SFA || !SFB))
+    return fail(SG_ERR_NULL, "mxfp6_gemm_run: A, B, SFA or SFB is NULL");
+  const int db = elem_bytes(d_dtype);
+  if ((K > 0 && (!aligned16(A) || !aligned16(B))) || !aligned16(D) ||
+      (K > 0 && ((reinterpret_cast<uintptr_t>(SFA) | reinterpret_cast<uintptr_t>(SFB)) & 3u)))
+    return fail(SG_ERR_ALIGN,
+                "mxfp6_gemm_run: A, B, D must be 16-byte aligned, SFA and SFB 4-byte aligned");
+  if ((N * db) % 16)
+    return fail(SG_ERR_ALIGN, "mxfp6_gemm_run: D row pitch must be a multiple of 16 bytes");
+  // a tile's panel plus the 8 bytes its shifted rows may read beyond it
+  if (256 * (K / 4 * 3) + 8 >= kMaxExtent)
+    return fail(SG_ERR_SHAPE, "mxfp6_gemm_run: an operand panel spans 2^31 bytes or more");
+  const int64_t tiles_m = cdiv(M, 256), tiles_n = cdiv(N, 256);
+  if (tiles_m * tiles_n > 0x7fffffffLL)
+    return fail(SG_ERR_SHAPE, "mxfp6_gemm_run: too many tiles");
+  sg::MxParams p;
+  p.A = A;
+  p.SFA = SFA;
+  p.B = B;
+  p.SFB = SFB;
+  p.D = D;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.d_dtype = d_dtype;
+  p.tiles_m = (int)tiles_m;
+  p.tiles_n = (int)tiles_n;
+  p.group_m = kGroupM;
+  hipError_t e = sg::launch_mxfp6(fmt == SG_E3M2, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mxfp6_gemm_run launch");
+  return ok();
+}
+
 int mx_gemm_run(int64_t M, int64_t N, int64_t K, const void* A, const void* SFA,
                 const void* B, const void* SFB, void* D, int d_dtype, void* stream) {
   if (M < 0 || N < 0 || K < 0)
@@ -382,6 +427,17 @@ int gemm_lds_layout(int rows, int row_bytes, int32_t* out) {
   for (int r = 0; r < rows; ++r)
     for (int c = 0; c < chunks; ++c)
       out[r * chunks + c] = (int32_t)sg::lds_offset_rt(row_bytes, sg::kSwzDefault, r, c);
+  return ok();
+}
+
+int gemm_lds_layout_mxfp6(int rows, int unshifted, int32_t* out) {
+  if (!out) return fail(SG_ERR_NULL, "gemm_lds_layout_mxfp6: out is NULL");
+  if (rows <= 0 || rows % 32 || unshifted < 0 || unshifted > 32)
+    return fail(SG_ERR_SHAPE, "gemm_lds_layout_mxfp6: rows must be a positive multiple of 32 "
+                              "and unshifted in [0, 32]");
+  for (int r = 0; r < rows; ++r)
+    for (int q = 0; q < 12; ++q)
+      out[r * 12 + q] = (int32_t)sg::mxfp6_lds_offset(r, 8u * q, (uint32_t)unshifted);
   return ok();
 }
 

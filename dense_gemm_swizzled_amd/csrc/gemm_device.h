@@ -51,6 +51,13 @@ __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r,
 __device__ __forceinline__ u32x4 lds_read16(const char* lds, uint32_t off) {
   return *reinterpret_cast<const u32x4*>(lds + off);
 }
+// An 8-byte LDS read kept as its own ds_read_b64: a volatile access is never
+// merged with another into a ds_read2 (whose two results sit in adjacent
+// registers, which would keep them out of two different operand tuples).
+__device__ __forceinline__ u32x2 lds_read8(const char* lds, uint32_t off) {
+  typedef const volatile __attribute__((address_space(3))) u32x2 lds_u32x2;
+  return *(lds_u32x2*)(lds + off);
+}
 __device__ __forceinline__ void lds_write16(char* lds, uint32_t off, u32x4 v) {
   *reinterpret_cast<u32x4*>(lds + off) = v;
 }

@@ -25,6 +25,7 @@ hipError_t launch_grouped(TileShape tile, bool bf16, int swz,
                           const GroupedParams& p, int grid, hipStream_t s);
 hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s);
 hipError_t launch_mxfp4(const MxParams& p, hipStream_t s);  // 256x256 tiles
+hipError_t launch_mxfp6(bool e3m2, const MxParams& p, hipStream_t s);  // 256x256 tiles
 hipError_t launch_lds_image(const void* X, int64_t rows_total, int64_t K,
                             int elem_bytes, int64_t row0, int64_t k0,
                             int tile_rows, void* out, hipStream_t s);

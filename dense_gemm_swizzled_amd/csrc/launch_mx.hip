@@ -1,4 +1,4 @@
-// launch_mx.hip -- MXFP8 kernel launchers and the LDS-image debug kernel.
+// launch_mx.hip -- MXFP8 / MXFP6 / MXFP4 kernel launchers and the LDS-image debug kernel.
 #include "launch.h"
 #include "pingpong.h"
 
@@ -7,7 +7,7 @@ namespace sg {
 hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s) {
   const int grid = p.tiles_m * p.tiles_n;
   if (tile == kTile256)
-    hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, false>), dim3(grid), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, 0>), dim3(grid), dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL((mx_gemm_kernel<128, 128, kSwzDefault>), dim3(grid),
                        dim3(kThreads), 0, s, p);
@@ -15,8 +15,18 @@ hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s) {
 }
 
 hipError_t launch_mxfp4(const MxParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, true>), dim3(p.tiles_m * p.tiles_n),
+  hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, 4>), dim3(p.tiles_m * p.tiles_n),
                      dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp6(bool e3m2, const MxParams& p, hipStream_t s) {
+  if (e3m2)
+    hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, 3>), dim3(p.tiles_m * p.tiles_n),
+                       dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, 2>), dim3(p.tiles_m * p.tiles_n),
+                       dim3(512), 0, s, p);
   return hipGetLastError();
 }
 

@@ -80,4 +80,23 @@ SG_HD uint32_t lds_offset_rt(int row_bytes, int swz, uint32_t row,
   return off ^ (((off >> line_shift) & (uint32_t)(swz - 1)) << 4);
 }
 
+// The MXFP6 operand tile.  A K tile of a 6-bit operand row is 96 bytes (128
+// values), kept in the 128-byte rows of lds_offset<128, kSwzDefault>.  The
+// scaled MFMA takes a lane's 32 values as 24 bytes, so a fragment is read
+// with three 8-byte reads, each serving 32 lanes (rows R..R+31 of one
+// 32-row block, all at the same byte of the row) from the 64 banks at once.
+// The XOR moves whole 16-byte units, so on its own it gives those 32 reads
+// only 16 distinct 8-byte bank slots: rows 2a and 2(a ^ 8) + 1 collide.  Odd
+// rows are therefore stored 8 bytes further on (logical byte b of the row at
+// byte b + 8), which sets bit 3 of the slot from the row parity and makes
+// the read conflict-free.  A shifted row spills 8 bytes into a seventh unit
+// at each end; the loads fill both edges from the neighbouring bytes of the
+// operand, which exist for every row but the operand's last.  The rows of a
+// tile whose index within its 32-row block equals `unshifted` (the block
+// position of the operand's last row, or 32 for none) are not shifted.
+SG_HD uint32_t mxfp6_lds_offset(uint32_t row, uint32_t byte, uint32_t unshifted) {
+  const uint32_t b = byte + (((row & 1u) && (row & 31u) != unshifted) ? 8u : 0u);
+  return lds_offset<128, kSwzDefault>(row, b >> 4) + (b & 15u);
+}
+
 }  // namespace sg

@@ -30,6 +30,8 @@
 // reads across them; the waits are explicit.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_kernels.h"
 #include "mx_kernels.h"
 
@@ -51,6 +53,22 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t voff, uint32_t lds) {
       :
       : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(rsrc)
       : "memory", "m0");
+}
+
+// buffer_load_dwordx4 ... lds with the LDS address m0 = lds_base + imm and an
+// SGPR byte offset `soff` added to the global address (three instructions:
+// the m0 write, the wait state it needs, the load).
+template <int Imm>
+__device__ __forceinline__ void dma16_so(u32x4 rsrc, uint32_t voff, uint32_t soff,
+                                         uint32_t lds_base) {
+  asm volatile(
+      "s_add_u32 m0, %1, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %2, %3 offen lds"
+      :
+      : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(rsrc),
+        "s"(__builtin_amdgcn_readfirstlane(soff)), "i"(Imm)
+      : "memory", "m0", "scc");
 }
 
 // buffer_load_dword ... lds: lane l's 4 bytes at byte `voff` go to LDS
@@ -303,19 +321,25 @@ __global__ void __launch_bounds__(512, 1) pingpong_grouped_kernel(const GroupedP
 
 namespace sg {
 
-// The ping-pong mainloop for the block-scaled GEMMs: MXFP8 (e4m3 elements)
-// and MXFP4 (e2m1 elements, two per byte).  A K tile is 128 bytes of every
-// row (128 e4m3 or 256 e2m1 values: four or eight 32-element scale blocks),
-// so the operand halves have exactly the geometry of the 16-bit kernel's.
+// The ping-pong mainloop for the block-scaled GEMMs: MXFP8 (e4m3 elements),
+// MXFP6 (e2m3 or e3m2 elements, a 6-bit stream) and MXFP4 (e2m1 elements,
+// two per byte).  A K tile is 128 bytes of every row for MXFP8 and MXFP4
+// (128 e4m3 or 256 e2m1 values: four or eight 32-element scale blocks), so
+// the operand halves have exactly the geometry of the 16-bit kernel's; for
+// MXFP6 it is 96 bytes (128 values), kept in the same 128-byte LDS rows
+// under mxfp6_lds_offset.
 // Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 (checked on the GPU
 // with one-hot operands): lane l supplies row l%32; with e4m3 its 32 bytes
 // are K [16h, 16h+16) and [32+16h, 32+16h+16) of the 64-wide step, with e2m1
-// its first 16 bytes are the 32 values of block h of the step (h = l/32, the
-// other 16 bytes are ignored); the e8m0 byte of lane l scales block h.  So a
-// lane reads 16-byte chunk 4kk + 2c + h of the row for chunk c of e4m3 step
-// kk, or for step 2kk + c of e2m1: one offset table serves both.  A phase
-// is eight e4m3 MFMAs (one 64-wide step) or sixteen e2m1 MFMAs (two steps),
-// the same 512 cycles as sixteen 16-bit MFMAs.
+// its first 16 bytes are the 32 values of block h of the step, with e2m3 or
+// e3m2 its first 24 bytes are the 32 values of block h as a 6-bit stream
+// (h = l/32; the remaining bytes are ignored); the e8m0 byte of lane l
+// scales block h.  So a lane reads 16-byte chunk 4kk + 2c + h of the row for
+// chunk c of e4m3 step kk, or for step 2kk + c of e2m1: one offset table
+// serves both; for e2m3/e3m2 step kk it reads bytes [24(2kk + h), +24).  A
+// phase is eight e4m3 or fp6 MFMAs (one 64-wide step) or sixteen e2m1 MFMAs
+// (two steps): 512 cycles of MFMA for e4m3 and e2m1, 256 for fp6 (the
+// 6-bit MFMA runs at the 4-bit rate).
 //
 // LDS: A ring of two tiles, B ring of two tiles, a ring of two tiles of
 // scales (the e8m0 dwords of the tile's 256 A rows, then of its 256 B rows;
@@ -333,41 +357,66 @@ namespace sg {
 // one group skips are issued out of range into the sink (zero fill, no
 // memory traffic), so the code has no group-dependent branch (the compiler
 // moves MFMAs across such branches, and with them across the barriers).
-template <int Swz, bool Fp4>
+//
+// Fmt is the MFMA's operand format code: 0 e4m3, 2 e2m3, 3 e3m2, 4 e2m1.
+template <int Swz, int Fmt>
 struct PingPongMxTile {
+  static_assert(Fmt == 0 || Fmt == 2 || Fmt == 3 || Fmt == 4, "operand format");
+  static constexpr bool kFp4 = Fmt == 4, kFp6 = Fmt == 2 || Fmt == 3;
+  static_assert(!kFp6 || Swz == kSwzDefault, "the fp6 layout is built on the default swizzle");
   using Base = GemmTile<256, 256, true, false, false, Swz, 8>;
   static constexpr int kHalfBytes = 16384;
   static constexpr int kTileBytes = 2 * kHalfBytes;
-  static constexpr int kBK = Fp4 ? 256 : 128;              // elements of K per tile
-  static constexpr int kScaleDw = Fp4 ? 2 : 1;             // scale dwords per row per tile
+  static constexpr int kBK = kFp4 ? 256 : 128;             // elements of K per tile
+  static constexpr int kTileRowBytes = kFp6 ? 96 : 128;    // bytes of a row per tile
+  static constexpr int kScaleDw = kFp4 ? 2 : 1;            // scale dwords per row per tile
   static constexpr int kScaleBytes = 2 * 256 * 4 * kScaleDw;
   static constexpr int kBOff = 2 * kTileBytes, kSOff = 4 * kTileBytes;
   static constexpr int kSinkOff = kSOff + 2 * kScaleBytes;
   static constexpr int kLdsBytes = kSinkOff + kHalfBytes;  // 148 or 152 KiB
   static constexpr int kLoads = 4 + kScaleDw + 4;          // a wave's loads of one tile
-  static constexpr int kMfmas = Fp4 ? 16 : 8;              // per compute phase
+  static constexpr int kMfmas = kFp4 ? 16 : 8;             // per compute phase
   static constexpr int kFM = 4, kFN = 2;
+  static constexpr int kPieces = kFp6 ? 3 : 2;             // LDS reads per fragment
 
-  // One phase's fragments: chunk c of every 32-row block (see above).
+  // One phase's fragments: e4m3/e2m1 chunk c of every 32-row block (16
+  // bytes), or fp6 piece q (8 bytes) of the lane's 24.
+  using Piece = typename std::conditional<kFp6, u32x2, u32x4>::type;
   struct Frags {
-    u32x4 a[kFM][2], b[kFN][2];
+    Piece a[kFM][kPieces], b[kFN][kPieces];
   };
 
   struct Offsets {
-    uint32_t a[2][2], b[2][2];  // [kk][c]
+    uint32_t a[2][kPieces], b[2][kPieces];  // [kk][c or q]
   };
 
-  __device__ __forceinline__ static Offsets offsets(int g, int w4, int lrow, int lhalf) {
+  // `ua`, `ub`: the block position of the rows that mxfp6_lds_offset leaves
+  // unshifted (fp6 only).
+  __device__ __forceinline__ static Offsets offsets(int g, int w4, int lrow, int lhalf,
+                                                    uint32_t ua, uint32_t ub) {
     Offsets o;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint32_t ch = 4 * kk + 2 * c + lhalf;
-        o.a[kk][c] = g * kHalfBytes + lds_offset<128, Swz>(lrow, ch);
-        o.b[kk][c] = (w4 >> 1) * kHalfBytes + lds_offset<128, Swz>((w4 & 1) * 64 + lrow, ch);
+      for (int c = 0; c < kPieces; ++c) {
+        if constexpr (kFp6) {
+          const uint32_t byte = 24u * (2 * kk + lhalf) + 8u * c;
+          o.a[kk][c] = g * kHalfBytes + mxfp6_lds_offset(lrow, byte, ua);
+          o.b[kk][c] = (w4 >> 1) * kHalfBytes + mxfp6_lds_offset((w4 & 1) * 64 + lrow, byte, ub);
+        } else {
+          const uint32_t ch = 4 * kk + 2 * c + lhalf;
+          o.a[kk][c] = g * kHalfBytes + lds_offset<128, Swz>(lrow, ch);
+          o.b[kk][c] = (w4 >> 1) * kHalfBytes + lds_offset<128, Swz>((w4 & 1) * 64 + lrow, ch);
+        }
       }
     return o;
+  }
+
+  __device__ __forceinline__ static Piece read_piece(const char* t, uint32_t off) {
+    if constexpr (kFp6)
+      return lds_read8(t, off);
+    else
+      return lds_read16(t, off);
   }
 
   __device__ __forceinline__ static void read(Frags& f, const char* at, const char* bt,
@@ -375,11 +424,11 @@ struct PingPongMxTile {
 #pragma unroll
     for (int fm = 0; fm < kFM; ++fm)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) f.a[fm][c] = lds_read16(at, o.a[kk][c] + fm * 4096);
+      for (int c = 0; c < kPieces; ++c) f.a[fm][c] = read_piece(at, o.a[kk][c] + fm * 4096);
 #pragma unroll
     for (int fn = 0; fn < kFN; ++fn)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) f.b[fn][c] = lds_read16(bt, o.b[kk][c] + fn * 4096);
+      for (int c = 0; c < kPieces; ++c) f.b[fn][c] = read_piece(bt, o.b[kk][c] + fn * 4096);
   }
 
   // Scale dword d of the wave's rows; the lane's block (lane half) is shifted
@@ -398,19 +447,28 @@ struct PingPongMxTile {
                (8 * lhalf);
   }
 
-  // One scaled MFMA: e4m3 takes both chunks (32 bytes) of the step with
-  // op-select 2kk; e2m1 takes chunk c (16 bytes) with op-select 2c.
+  // One scaled MFMA on 8-dword operands.
   template <int Sel>
-  __device__ __forceinline__ static f32x16 mfma(const u32x4& a0, const u32x4& a1,
-                                                const u32x4& b0, const u32x4& b1, f32x16 acc,
+  __device__ __forceinline__ static f32x16 mfma(const i32x8& av, const i32x8& bv, f32x16 acc,
                                                 uint32_t sa, uint32_t sb) {
-    const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                      (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-    const i32x8 bv = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
-                      (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
-    constexpr int kFmt = Fp4 ? 4 : 0;  // operand format: e2m1 or e4m3
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc, kFmt, kFmt, Sel,
-                                                           (int)sb, Sel, (int)sa);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc, Fmt, Fmt, Sel, (int)sb,
+                                                           Sel, (int)sa);
+  }
+
+  // The operand of one MFMA: e4m3 both chunks of the step; e2m1 chunk c
+  // (the upper 16 bytes are ignored); fp6 the three pieces (the last 8
+  // bytes are ignored).
+  __device__ __forceinline__ static i32x8 operand(const Piece (&p)[kPieces], int c) {
+    if constexpr (kFp6) {
+      const u32x4 lo = __builtin_shufflevector(p[0], p[1], 0, 1, 2, 3);
+      const u32x4 hi = __builtin_shufflevector(p[2], p[2], 0, 1, -1, -1);
+      return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else if constexpr (kFp4) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      return __builtin_bit_cast(i32x8, __builtin_shufflevector(p[c], z, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return __builtin_bit_cast(i32x8, __builtin_shufflevector(p[0], p[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   }
 
   // kMfmas MFMAs of phase kk; N loads (given by `issue(q)`) go out between
@@ -420,23 +478,15 @@ struct PingPongMxTile {
                                                  const uint32_t (&sa)[kFM],
                                                  const uint32_t (&sb)[kFN], int kk,
                                                  const Issue& issue) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int m = 0; m < kMfmas; ++m) {
       const int c = m / (kFM * kFN), fm = (m >> 1) % kFM, fn = m & 1;
-      if constexpr (Fp4) {
-        if (c == 0)
-          acc[fm][fn] = mfma<0>(f.a[fm][0], z, f.b[fn][0], z, acc[fm][fn], sa[fm], sb[fn]);
-        else
-          acc[fm][fn] = mfma<2>(f.a[fm][1], z, f.b[fn][1], z, acc[fm][fn], sa[fm], sb[fn]);
-      } else {
-        if (kk == 0)
-          acc[fm][fn] = mfma<0>(f.a[fm][0], f.a[fm][1], f.b[fn][0], f.b[fn][1], acc[fm][fn],
-                                sa[fm], sb[fn]);
-        else
-          acc[fm][fn] = mfma<2>(f.a[fm][0], f.a[fm][1], f.b[fn][0], f.b[fn][1], acc[fm][fn],
-                                sa[fm], sb[fn]);
-      }
+      const i32x8 av = operand(f.a[fm], c), bv = operand(f.b[fn], c);
+      // op-select: block pair 2kk (e4m3, fp6) or 2c (e2m1) of the scale dword
+      if ((kFp4 ? c : kk) == 0)
+        acc[fm][fn] = mfma<0>(av, bv, acc[fm][fn], sa[fm], sb[fn]);
+      else
+        acc[fm][fn] = mfma<2>(av, bv, acc[fm][fn], sa[fm], sb[fn]);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (N > 0) {
         if (m < N) issue(m);
@@ -448,9 +498,50 @@ struct PingPongMxTile {
 
   __device__ __forceinline__ static void barrier() { PingPongTile<true, Swz>::barrier(); }
 
+  // The fp6 half-tile loader.  The physical slots a lane fills are those of
+  // HalfLoader; slot j of logical row r receives the operand bytes
+  // [16j - 8s, 16j - 8s + 16) of the K tile, s = 1 for a shifted row
+  // (mxfp6_lds_offset).  Slots holding none of the tile's 96 bytes are not
+  // loaded (out of range: zero fill, no traffic); so are rows past the
+  // operand.  The row offsets are fixed per tile job; the K position travels
+  // in the SGPR offset; tiles past the end load through an empty descriptor.
+  struct Fp6Loader {
+    uint32_t voff[4];
+
+    __device__ __forceinline__ void init(int w4, int lane, uint32_t pitch, int rows_valid,
+                                         uint32_t unshifted) {
+      HalfLoader<Swz> h;
+      h.init(w4, lane, pitch);
+      const uint32_t s = ((h.row & 1) && (uint32_t)h.row != unshifted) ? 8u : 0u;
+      const uint32_t j = h.chunk >> 4;
+      const bool used = 16u * j < 96u + s;  // the slot holds some of bytes [0, 96)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        voff[i] = used && h.row + 32 * i < rows_valid
+                      ? (uint32_t)(h.row + 32 * i) * pitch + 16u * j - s
+                      : kOutOfRange;
+    }
+
+    template <int I>
+    __device__ __forceinline__ void issue(u32x4 rsrc, uint32_t half, int w4,
+                                          uint32_t kbyte0) const {
+      dma16_so<I * 4096>(rsrc, voff[I], kbyte0, half + (uint32_t)w4 * 1024u);
+    }
+
+    __device__ __forceinline__ void issue_rt(int i, u32x4 rsrc, uint32_t half, int w4,
+                                             uint32_t kbyte0) const {
+      if (i == 0) issue<0>(rsrc, half, w4, kbyte0);
+      if (i == 1) issue<1>(rsrc, half, w4, kbyte0);
+      if (i == 2) issue<2>(rsrc, half, w4, kbyte0);
+      if (i == 3) issue<3>(rsrc, half, w4, kbyte0);
+    }
+  };
+
+  // ua, ub: fp6 only, see mxfp6_lds_offset.
   __device__ __forceinline__ static void run(char* smem, const TileJob& j, const char* sfa,
                                              const char* sfb, int64_t K, void* D,
-                                             int d_dtype, int64_t ldd) {
+                                             int d_dtype, int64_t ldd, uint32_t ua,
+                                             uint32_t ub) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = wave >> 2, w4 = wave & 3;
@@ -458,14 +549,26 @@ struct PingPongMxTile {
 
     const uint32_t sf_pitch = (uint32_t)(K / 32);
     const u32x4 ra = rsrc_words(j.a, j.a_bytes), rb = rsrc_words(j.b, j.b_bytes);
+    const u32x4 ra0 = rsrc_words(j.a, 0), rb0 = rsrc_words(j.b, 0);
     const u32x4 rsa = rsrc_words(sfa, (uint32_t)j.m_valid * sf_pitch);
     const u32x4 rsb = rsrc_words(sfb, (uint32_t)j.n_valid * sf_pitch);
     const int a_rows = j.m_valid - 128 * g, b_rows = j.n_valid - 128 * g;
     HalfLoader<Swz> la, lb;
-    la.init(w4, lane, j.a_pitch);
-    lb.init(w4, lane, j.b_pitch);
-    la.base += (uint32_t)(128 * g) * j.a_pitch;
-    lb.base += (uint32_t)(128 * g) * j.b_pitch;
+    Fp6Loader la6, lb6;
+    if constexpr (kFp6) {
+      la6.init(w4, lane, j.a_pitch, a_rows, ua);
+      lb6.init(w4, lane, j.b_pitch, b_rows, ub);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (la6.voff[i] != kOutOfRange) la6.voff[i] += (uint32_t)(128 * g) * j.a_pitch;
+        if (lb6.voff[i] != kOutOfRange) lb6.voff[i] += (uint32_t)(128 * g) * j.b_pitch;
+      }
+    } else {
+      la.init(w4, lane, j.a_pitch);
+      lb.init(w4, lane, j.b_pitch);
+      la.base += (uint32_t)(128 * g) * j.a_pitch;
+      lb.base += (uint32_t)(128 * g) * j.b_pitch;
+    }
     // Scales: wave w4 of group g loads the dwords of rows 128g + 64(w4&1)
     // + lane of A (w4 < 2) or B (w4 >= 2).
     const int s_row = 128 * g + 64 * (w4 & 1) + lane;
@@ -478,17 +581,25 @@ struct PingPongMxTile {
     const uint32_t s0 = lds_addr(smem);
     const uint32_t a_ring = s0 + g * kHalfBytes, b_ring = s0 + kBOff + g * kHalfBytes;
     const uint32_t s_ring = s0 + kSOff + s_lds_off;
-    const uint32_t kbytes = (uint32_t)(Fp4 ? K / 2 : K);
+    const uint32_t kbytes = (uint32_t)(kFp4 ? K / 2 : K);
     const int T = (int)(K / kBK);
 
     auto ld_a = [&](int t, int i) {
-      la.issue(ra, a_ring + (t & 1) * kTileBytes, w4, i, a_rows, (uint32_t)t * 128u, kbytes);
+      if constexpr (kFp6)
+        la6.issue_rt(i, t < T ? ra : ra0, a_ring + (t & 1) * kTileBytes, w4,
+                     (uint32_t)t * 96u);
+      else
+        la.issue(ra, a_ring + (t & 1) * kTileBytes, w4, i, a_rows, (uint32_t)t * 128u, kbytes);
     };
     // B half of tile t when `real`, else an out-of-range load into the sink.
     const uint32_t sink = s0 + kSinkOff;
     auto ld_b = [&](int t, int i, bool real) {
-      lb.issue(rb, real ? b_ring + (t & 1) * kTileBytes : sink, w4, i, real ? b_rows : 0,
-               (uint32_t)t * 128u, kbytes);
+      if constexpr (kFp6)
+        lb6.issue_rt(i, real && t < T ? rb : rb0, real ? b_ring + (t & 1) * kTileBytes : sink,
+                     w4, (uint32_t)t * 96u);
+      else
+        lb.issue(rb, real ? b_ring + (t & 1) * kTileBytes : sink, w4, i, real ? b_rows : 0,
+                 (uint32_t)t * 128u, kbytes);
     };
     // Scale dword d of tile t.
     auto ld_s = [&](int t, int d) {
@@ -512,7 +623,7 @@ struct PingPongMxTile {
     wait_loads_but<kLoads>();  // tile 0 has landed
     barrier();
 
-    const Offsets o = offsets(g, w4, lrow, lhalf);
+    const Offsets o = offsets(g, w4, lrow, lhalf, ua, ub);
     f32x16 acc[kFM][kFN];
 #pragma unroll
     for (int i = 0; i < kFM; ++i)
@@ -539,7 +650,7 @@ struct PingPongMxTile {
       // loads just issued) may still be in flight: group 1's share of tile
       // t+1 is then in LDS before the barrier that lets group 0 read it.
       read(f, at, bt, o, 1);
-      if constexpr (Fp4) read_scales(sa, sb, st, 1, g, w4, lrow, lhalf);
+      if constexpr (kFp4) read_scales(sa, sb, st, 1, g, w4, lrow, lhalf);
       asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
       barrier();
       // Second compute phase, with the loads of tile t+2: A half, scales,
@@ -569,16 +680,16 @@ struct PingPongMxTile {
   }
 };
 
-template <int Swz, bool Fp4>
+template <int Swz, int Fmt>
 __global__ void __launch_bounds__(512, 1) pingpong_mx_kernel(const MxParams p) {
-  using Tile = PingPongMxTile<Swz, Fp4>;
+  using Tile = PingPongMxTile<Swz, Fmt>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
   const int total = p.tiles_m * p.tiles_n;
   const int t = xcd_remap(blockIdx.x, total);
   int tm, tn;
   raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
-  const int64_t row_bytes = Fp4 ? p.K / 2 : p.K;
+  const int64_t row_bytes = Tile::kFp4 ? p.K / 2 : Tile::kFp6 ? p.K / 4 * 3 : p.K;
   TileJob j;
   j.m_valid = (int)min<int64_t>(256, p.M - m0);
   j.n_valid = (int)min<int64_t>(256, p.N - n0);
@@ -588,13 +699,24 @@ __global__ void __launch_bounds__(512, 1) pingpong_mx_kernel(const MxParams p) {
   j.b = static_cast<const char*>(p.B) + n0 * row_bytes;
   j.b_pitch = (uint32_t)row_bytes;
   j.b_bytes = (uint32_t)(j.n_valid * row_bytes);
+  // fp6: a shifted row reads 8 bytes past its end at the last K tile.  Below
+  // the operand's last tile that is the next tile's first row (in range of
+  // the descriptor once it covers 8 more bytes); in the last tile, the rows
+  // at the block position of the operand's last row stay unshifted.
+  uint32_t ua = 32, ub = 32;
+  if (Tile::kFp6) {
+    if (p.M - m0 > 256) j.a_bytes += 8;
+    else ua = (uint32_t)((p.M - 1 - m0) & 31);
+    if (p.N - n0 > 256) j.b_bytes += 8;
+    else ub = (uint32_t)((p.N - 1 - n0) & 31);
+  }
   j.d_row0 = m0;
   j.n0 = n0;
   j.ldc = 0;
   j.alpha = 1.0f;
   j.beta = 0.0f;
   Tile::run(smem, j, static_cast<const char*>(p.SFA) + m0 * (p.K / 32),
-            static_cast<const char*>(p.SFB) + n0 * (p.K / 32), p.K, p.D, p.d_dtype, p.N);
+            static_cast<const char*>(p.SFB) + n0 * (p.K / 32), p.K, p.D, p.d_dtype, p.N, ua, ub);
 }
 
 }  // namespace sg

@@ -21,22 +21,6 @@
 
 namespace sg {
 
-// buffer_load_dwordx4 ... lds with the LDS address m0 = lds_base + imm and an
-// SGPR byte offset `soff` added to the global address (three instructions:
-// the m0 write, the wait state it needs, the load).
-template <int Imm>
-__device__ __forceinline__ void dma16_so(u32x4 rsrc, uint32_t voff, uint32_t soff,
-                                         uint32_t lds_base) {
-  asm volatile(
-      "s_add_u32 m0, %1, %4\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %2, %3 offen lds"
-      :
-      : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(rsrc),
-        "s"(__builtin_amdgcn_readfirstlane(soff)), "i"(Imm)
-      : "memory", "m0", "scc");
-}
-
 // The half-tile loader for K a multiple of 64: each lane's four row offsets
 // (out of range for rows past the operand) are fixed per tile job, and the K
 // position of a load travels in the instruction's SGPR offset; a K tile past

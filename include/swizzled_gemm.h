@@ -59,6 +59,8 @@ extern "C" {
 #define SG_F32 3  /* IEEE binary32 */
 #define SG_E4M3 4 /* OCP FP8 E4M3 (bias 7, max 448, no infinity) */
 #define SG_E8M0 5 /* OCP E8M0 scale, value 2^(e-127) */
+#define SG_E2M3 7 /* OCP FP6 E2M3 (bias 1, max 7.5, no infinity or NaN) */
+#define SG_E3M2 8 /* OCP FP6 E3M2 (bias 3, max 28, no infinity or NaN) */
 
 /* Operand majorness. */
 #define SG_K_MAJOR 0  /* K is the contiguous dimension */
@@ -173,6 +175,28 @@ int mxfp4_gemm_run(int64_t M, int64_t N, int64_t K, const void* A,
                    int d_dtype, void* stream);
 
 /*
+ * mxfp6_gemm_run -- the block-scaled GEMM of mx_gemm_run with OCP FP6
+ * elements (MXFP6): fmt SG_E2M3 (1 sign, 2 exponent bits with bias 1, 3
+ * fraction bits; largest magnitude 7.5, smallest 0.125) or SG_E3M2 (1 sign,
+ * 3 exponent bits with bias 3, 2 fraction bits; largest 28, smallest
+ * 0.0625); neither has infinity or NaN.  A row is a 6-bit stream: element k
+ * at bits [6k, 6k+6) of the row's bytes, little endian (four elements in
+ * three bytes).  The scale rule is mx_gemm_run's ("06 Blackwell Tensor Core
+ * - tcgen05 MMA", section "Block-Scaled MMA"); the 32-element block and
+ * e8m0 scales as there.  fp32 accumulation.
+ *   A    fp6 K-major [M][3K/4] bytes;  SFA  e8m0 [M][K/32].
+ *   B    fp6 K-major [N][3K/4] bytes;  SFB  e8m0 [N][K/32].
+ *   D    [M][N] of d_dtype (SG_F32 or SG_BF16).
+ *   K    must be a multiple of 128 (96 bytes of every row per K tile);
+ *        M and N may be ragged.  The kernel reads only bytes of A and B.
+ * Errors: SG_ERR_NULL, SG_ERR_ALIGN, SG_ERR_SHAPE (K % 128 != 0 or
+ * extents), SG_ERR_DTYPE (fmt or d_dtype), SG_ERR_HIP.
+ */
+int mxfp6_gemm_run(int fmt, int64_t M, int64_t N, int64_t K, const void* A,
+                   const void* SFA, const void* B, const void* SFB, void* D,
+                   int d_dtype, void* stream);
+
+/*
  * gemm_layout_run -- the bf16 GEMM with A and B K-major (and optional C) on
  * 256x256 tiles of the 8-wave ping-pong kernel with 32x32x16 MFMAs (the
  * 16x16x32 variant of gemm_run reads fragments in another lane pattern), with
@@ -223,6 +247,21 @@ const char* gemm_version(void);
  * Returns SG_OK, SG_ERR_NULL or SG_ERR_SHAPE.
  */
 int gemm_lds_layout(int rows, int row_bytes, int32_t* out);
+
+/*
+ * gemm_lds_layout_mxfp6 -- the LDS byte map of mxfp6_gemm_run's operand
+ * tiles (host-side, no GPU needed).  Writes out[r * 12 + q] = the byte
+ * offset within one LDS stage of bytes [8q, 8q + 8) of the 96 bytes of tile
+ * row r, for r < rows.  The map is gemm_lds_layout's XOR swizzle for
+ * 128-byte rows with every odd row displaced by 8 bytes, except the rows at
+ * block position `unshifted` (row % 32 == unshifted; 32 for none), which the
+ * kernel uses for the tile holding the operand's last row.  The displacement
+ * lets 8-byte reads of 32 rows, which the XOR of 16-byte units alone maps
+ * to 16 bank slots, reach all 32 ("Swizzling explained properly", section
+ * "Why swizzle?": the bank arithmetic).  rows is a positive multiple of 32.
+ * Returns SG_OK, SG_ERR_NULL or SG_ERR_SHAPE.
+ */
+int gemm_lds_layout_mxfp6(int rows, int unshifted, int32_t* out);
 
 /*
  * gemm_lds_image -- runs the kernels' global->LDS loader once for one operand

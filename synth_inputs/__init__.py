@@ -311,9 +311,11 @@ def mxfp6_quantize(x: np.ndarray, fmt: str = "e2m3", block: int = 32):
     vals = _fp6_magnitudes(eb, mb).astype(np.float32)
     mids = (vals[:-1] + vals[1:]) / 2
     mag = np.minimum(np.abs(y), vals[-1])
-    code = np.zeros(mag.shape, dtype=np.uint32)
-    for i, t in enumerate(mids):
-        code += (mag >= t) if i % 2 else (mag > t)
+    # below = number of midpoints under mag; a tie between codes i and i+1
+    # (mag == mids[i], i = below) goes to the even one
+    below = np.searchsorted(mids, mag, side="left").astype(np.uint32)
+    tie = mag == mids[np.minimum(below, len(mids) - 1)]
+    code = below + (tie & (below % 2 == 1)).astype(np.uint32)
     code |= ((y < 0) & (code != 0)).astype(np.uint32) << 5
     q = code.reshape(R, K // 4, 4)
     w = q[:, :, 0] | (q[:, :, 1] << 6) | (q[:, :, 2] << 12) | (q[:, :, 3] << 18)

@@ -28,8 +28,8 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"gemm_run", "gemm_strided_run", "grouped_gemm_run", "mx_gemm_run", "mxfp4_gemm_run",
-            "gemm_layout_run", "gemm_layout128_run",
-            "gemm_last_error", "gemm_version", "gemm_lds_layout",
+            "mxfp6_gemm_run", "gemm_layout_run", "gemm_layout128_run",
+            "gemm_last_error", "gemm_version", "gemm_lds_layout", "gemm_lds_layout_mxfp6",
             "gemm_lds_image"} <= set(names)
     lib = ctypes.CDLL(sg.library_path())
     for n in names:
@@ -215,6 +215,54 @@ def test_mxfp4_rejects(kw, code):
 
 def test_mxfp4_empty_is_ok():
     assert _mx4(M=0) == 0 and _mx4(N=0) == 0
+
+
+def _mx6(**kw):
+    a = dict(fmt=sg.SG_E2M3, M=256, N=256, K=512, A=P, SFA=P, B=P, SFB=P, D=P,
+             d_dtype=sg.SG_BF16)
+    a.update(kw)
+    return sg.mxfp6_gemm_run(a["fmt"], a["M"], a["N"], a["K"], a["A"], a["SFA"], a["B"],
+                             a["SFB"], a["D"], a["d_dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(fmt=sg.SG_E4M3), DTYPE), (dict(fmt=6), DTYPE), (dict(fmt=9), DTYPE),
+    (dict(K=64), SHAPE), (dict(K=96), SHAPE), (dict(M=-1), SHAPE),
+    (dict(K=1 << 24), SHAPE),
+    (dict(d_dtype=sg.SG_F16), DTYPE), (dict(d_dtype=sg.SG_E2M3), DTYPE),
+    (dict(A=None), NULL), (dict(SFA=None), NULL), (dict(B=None), NULL), (dict(D=None), NULL),
+    (dict(A=P + 8), ALIGN), (dict(SFB=P + 2), ALIGN), (dict(D=P + 4), ALIGN),
+    (dict(N=260), ALIGN),
+])
+def test_mxfp6_rejects(kw, code):
+    assert _mx6(**kw) == code, sg.gemm_last_error()
+    assert sg.gemm_last_error().startswith("mxfp6_gemm_run")
+
+
+def test_mxfp6_empty_is_ok():
+    assert _mx6(M=0) == 0 and _mx6(N=0, fmt=sg.SG_E3M2) == 0
+    # K = 0 with M, N > 0 computes D = 0 and reads neither operand (needs a
+    # GPU, so only the argument checks are exercised here: NULL operands are
+    # accepted when K = 0)
+    assert _mx6(M=0, K=0, A=None, B=None, SFA=None, SFB=None) == 0
+
+
+def test_mxfp6_layout_is_the_xor_swizzle_with_odd_rows_shifted():
+    # Restated from the definition: byte b of row r sits at byte b + 8 of the
+    # row when r is odd (and not at the unshifted block position), in the
+    # 16-byte unit given by the 128-byte-row XOR map.
+    unit = swizzle.lds_tile_map(64, 128, line_bytes=256)
+    for e in (32, 5, 0):
+        got = sg.gemm_lds_layout_mxfp6(64, e)
+        for r in range(64):
+            s = 8 if (r % 2 == 1 and r % 32 != e) else 0
+            for q in range(12):
+                b = 8 * q + s
+                assert got[r, q] == unit[r, b // 16] + b % 16, (e, r, q)
+    with pytest.raises(sg.GemmError):
+        sg.gemm_lds_layout_mxfp6(48)
+    with pytest.raises(sg.GemmError):
+        sg.gemm_lds_layout_mxfp6(64, 33)
 
 
 @pytest.mark.parametrize("row_bytes", [64, 128, 256])

@@ -448,6 +448,82 @@ def test_mxfp4_8192_full_size_sampled(dev):
     check_close(got, ref, bound, "bf16", case.name)
 
 
+def run_mx6(case: si.MXCase, dev, d_dtype="bf16"):
+    d = sg.mxfp6_gemm(case.A.to(dev), case.SFA.to(dev), case.B.to(dev), case.SFB.to(dev),
+                      fmt=case.fmt, out_dtype=DT[d_dtype])
+    torch.cuda.synchronize()
+    return d
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+@pytest.mark.parametrize("M,N,K", [(300, 264, 512), (4100, 4104, 768), (257, 36, 128),
+                                   (31, 292, 256), (1, 4, 128)])
+def test_mxfp6_ragged(dev, fmt, M, N, K):
+    # 6-bit elements; ragged M and N with the operands' last rows at odd and
+    # even positions of their 32-row blocks (the rows the kernel leaves
+    # unshifted), one-tile and many-tile grids, scales over 2^-17 .. 2^17.
+    case = si.mx_case(M, N, K, 27, fmt=fmt)
+    rng = np.random.default_rng(8)
+    case.SFA = torch.from_numpy(rng.integers(110, 145, (M, K // 32)).astype(np.uint8))
+    case.SFB = torch.from_numpy(rng.integers(110, 145, (N, K // 32)).astype(np.uint8))
+    say(f"mxfp6 {fmt} {M}x{N}x{K}")
+    d = run_mx6(case, dev, "f32")
+    ref, bound = oracle.mx_gemm(M, N, K, case.A, case.SFA, case.B, case.SFB, fmt=fmt)
+    check_close(_np(d), ref, bound, "f32", f"mxfp6 {fmt}")
+
+
+def _pack6(codes: np.ndarray) -> torch.Tensor:
+    """Rows of 6-bit codes as the stream format: four codes in three bytes,
+    code k at bits [6k, 6k+6), little endian."""
+    q = codes.astype(np.uint32).reshape(codes.shape[0], -1, 4)
+    w = q[:, :, 0] | (q[:, :, 1] << 6) | (q[:, :, 2] << 12) | (q[:, :, 3] << 18)
+    b = np.stack([w & 255, (w >> 8) & 255, (w >> 16) & 255], axis=2).astype(np.uint8)
+    return torch.from_numpy(np.ascontiguousarray(b.reshape(codes.shape[0], -1)))
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_mxfp6_unit_scales_exact(dev, fmt):
+    # Unit scales and codes whose products and partial sums are exact in
+    # fp32 (e2m3: multiples of 1/8 below 8; e3m2: magnitudes below 2,
+    # multiples of 1/16): the result must be bit-exact.
+    M, N, K = 520, 392, 1024
+    rng = np.random.default_rng(25)
+    hi = 64 if fmt == "e2m3" else 16
+    ca = rng.integers(0, hi, (M, K)) | (rng.integers(0, 2, (M, K)) << 5)
+    cb = rng.integers(0, hi, (N, K)) | (rng.integers(0, 2, (N, K)) << 5)
+    A, B = _pack6(ca & 63), _pack6(cb & 63)
+    SFA = torch.full((M, K // 32), 127, dtype=torch.uint8)
+    SFB = torch.full((N, K // 32), 127, dtype=torch.uint8)
+    case = si.MXCase(M, N, K, A, SFA, B, SFB, "f32", f"mxfp6 {fmt} exact", fmt)
+    say(f"mxfp6 {fmt} unit scales exact")
+    d = run_mx6(case, dev, "f32")
+    ref, _ = oracle.mx_gemm(M, N, K, A, SFA, B, SFB, fmt=fmt)
+    assert np.array_equal(_np(d), ref)
+
+
+def test_mxfp6_k0_is_zero(dev):
+    M, N = 300, 264
+    out = torch.full((M, N), 7.0, dtype=torch.float32, device=dev)
+    e = torch.empty(0, dtype=torch.uint8, device=dev)
+    rc = sg.mxfp6_gemm_run(sg.SG_E3M2, M, N, 0, e.data_ptr(), e.data_ptr(), e.data_ptr(),
+                           e.data_ptr(), out.data_ptr(), sg.SG_F32,
+                           torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0 and bool((out == 0).all())
+
+
+def test_mxfp6_8192_full_size_sampled(dev):
+    case = si.mxfp6()
+    say(f"{case.name} (sampled)")
+    d = run_mx6(case, dev, "bf16")
+    assert bool(torch.isfinite(d).all())
+    rows, cols = sample_points(case.M, case.N, 3000, 57)
+    ref, bound = oracle.mx_gemm_points(case.M, case.N, case.K, case.A, case.SFA, case.B,
+                                       case.SFB, rows, cols, fmt=case.fmt)
+    got = _np(d[torch.from_numpy(rows).to(dev), torch.from_numpy(cols).to(dev)])
+    check_close(got, ref, bound, "bf16", case.name)
+
+
 def test_mx_8192_full_size_sampled(dev):
     case = si.mxfp8(seed=5)
     say(f"{case.name} (sampled)")

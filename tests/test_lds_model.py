@@ -9,7 +9,8 @@ this module derives the model (bank line = the smallest conflicting stride;
 lane phases = groups of lanes that conflict with one another), checks that
 the oracle's bank simulator then reproduces every measured counter exactly,
 and finally checks that every LDS instruction the GEMM kernels issue --
-operand reads of the 16-bit (32x32x16 and 16x16x32) and MX kernels, K-major
+operand reads of the 16-bit (32x32x16 and 16x16x32) and MX kernels (the
+MXFP6 8-byte reads on their own layout), K-major
 and MN-major loader stores -- has degree 1 (no conflict) under that model, using the kernels'
 own LDS map exported through the C ABI.
 """
@@ -164,6 +165,33 @@ def test_kernel_loader_stores_conflict_free(model, tile):
             if any(x is not None for x in a):
                 worst = max(worst, _degree(model, "w128", a))
     assert worst == 1
+
+
+@pytest.mark.parametrize("unshifted", [32, 7, 30])
+def test_mxfp6_operand_reads_conflict_free(model, unshifted):
+    # The MXFP6 fragment read: lane l -> row l%32 of a 32-row block, bytes
+    # [24(2kk + h) + 8q, +8) with h = l/32, one ds_read_b64 per piece q.  With
+    # every odd row shifted the reads are conflict-free; the block position
+    # left unshifted in the tile that holds an operand's last row costs at
+    # most one 2-way conflict.
+    lds = sg.gemm_lds_layout_mxfp6(256, unshifted)
+    worst = 0
+    for base in range(0, 256, 32):
+        for kk in range(2):
+            for q in range(3):
+                a = [int(lds[base + l % 32, (24 * (2 * kk + l // 32) + 8 * q) // 8])
+                     for l in range(64)]
+                worst = max(worst, _degree(model, "r64", a))
+    # (an even position changes nothing: even rows are never shifted)
+    assert worst == (2 if unshifted % 2 else 1)
+
+
+def test_mxfp6_reads_without_the_shift_would_conflict(model):
+    # The same reads on the plain XOR layout: the 16-byte units alone give 32
+    # rows only 16 distinct 8-byte bank slots.
+    lds = sg.gemm_lds_layout(32, 128)
+    a = [int(lds[l % 32, (24 * (l // 32)) // 16]) + (24 * (l // 32)) % 16 for l in range(64)]
+    assert _degree(model, "r64", a) == 2
 
 
 def test_padded_layout_is_conflict_free(model):
