@@ -336,6 +336,21 @@ def main():
                      "kernel_ms_median": round(median_ms, 5)},
         "cpu_baseline": cpu,
     }
+    if args.workload == "grouped":
+        # Per group the kernel can go no faster than its MFMA time or the HBM
+        # time of its own bytes (A_g, B_g, D_g), whichever is longer.
+        floor_s = 0.0
+        for m in cfg["m_sizes"]:
+            f_g = 2.0 * m * cfg["N"] * cfg["K"]
+            b_g = 2.0 * (m * cfg["K"] + cfg["N"] * cfg["K"] + m * cfg["N"])
+            floor_s += max(f_g / (peak * 1e12), b_g / (HBM_PEAK_GBS * 1e9))
+        out["roofline"]["attainable_ms"] = round(floor_s * 1e3, 5)
+        out["roofline"]["frac_of_attainable"] = round(floor_s * 1e3 / mean_ms, 4)
+    if args.workload == "single_tile":
+        # One workgroup on one CU: the share of the peak a single CU holds.
+        cu_peak = peak / 256
+        out["roofline"]["one_cu_peak"] = round(cu_peak, 3)
+        out["roofline"]["frac_of_one_cu"] = round(achieved / cu_peak, 4)
     print(json.dumps(out), flush=True)
 
 

@@ -181,7 +181,7 @@ extern "C" {
 const char* gemm_last_error(void) { return g_last_error.c_str(); }
 
 const char* gemm_version(void) {
-  return "swizzled_gemm 0.2 (gfx950; 16-bit MFMA 16x16x32 and 32x32x16, MXFP8/MXFP4 "
+  return "swizzled_gemm 0.3 (gfx950; 16-bit MFMA 16x16x32 and 32x32x16, MXFP8/MXFP6/MXFP4 "
          "scaled MFMA 32x32x64; LDS XOR swizzle over 256-byte bank lines)";
 }
 
