@@ -121,6 +121,28 @@ struct HalfLoader {
   }
 };
 
+// The half-tile loader for K a multiple of 64: each lane's four row offsets
+// (out of range for rows past the operand) are fixed per tile job, and the K
+// position of a load travels in the instruction's SGPR offset; a K tile past
+// the end is loaded through a descriptor with no records (zero fill).
+template <int Swz>
+struct KExactHalfLoader {
+  uint32_t voff[4];
+
+  __device__ __forceinline__ void init(const HalfLoader<Swz>& h, int rows_valid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      voff[i] = h.row + 32 * i < rows_valid ? h.base + (uint32_t)(32 * i) * h.pitch
+                                            : kOutOfRange;
+  }
+
+  template <int I>
+  __device__ __forceinline__ void issue(u32x4 rsrc, uint32_t half, int w4,
+                                        uint32_t kbyte0) const {
+    dma16_so<I * 4096>(rsrc, voff[I], kbyte0, half + (uint32_t)w4 * 1024u);
+  }
+};
+
 template <bool IsBF16, int Swz>
 struct PingPongTile {
   using Base = GemmTile<256, 256, IsBF16, false, false, Swz, 8>;
@@ -341,22 +363,15 @@ namespace sg {
 // (two steps): 512 cycles of MFMA for e4m3 and e2m1, 256 for fp6 (the
 // 6-bit MFMA runs at the 4-bit rate).
 //
-// LDS: A ring of two tiles, B ring of two tiles, a ring of two tiles of
-// scales (the e8m0 dwords of the tile's 256 A rows, then of its 256 B rows;
-// dword d of every row together), all filled by direct-to-LDS loads so every
-// wait is explicit, and a 16 KiB sink.  Each group loads the scales of its
-// own 128 rows of A and of B, 4 bytes per lane.  Schedule (phases 4t..4t+3 of
-// tile t; group 1 one phase behind):
-//   group 0: B_lo(t+1) in its first memory phase of tile t; A_lo(t+2) and
-//            its scales during its second compute phase of tile t;
-//   group 1: A_hi(t+2), its scales and B_hi(t+2) during its second compute
-//            phase of tile t.
-// A slot t mod 2 is free once its group's second memory phase of tile t is
-// over, B slot t mod 2 once both groups' are; every load has three to five
-// phases to land.  Both groups run the same instruction stream: the B loads
-// one group skips are issued out of range into the sink (zero fill, no
-// memory traffic), so the code has no group-dependent branch (the compiler
-// moves MFMAs across such branches, and with them across the barriers).
+// Schedule: the 16-bit ping-pong's.  LDS holds an A ring of two tiles and a
+// B ring of three (160 KiB); group g loads half g of every tile of both
+// operands, B(t+2) during its compute phase over the first K step of tile
+// t and A(t+2) during the one over the second step, so every load has five
+// phases to land and both groups run the same instruction stream.  The
+// e8m0 scales do not fit in LDS beside the rings: each wave loads the
+// scale dwords of its own rows (four A rows and two B rows per lane, one or
+// two dwords each) straight into registers, with the A half of the same
+// tile, into one of three register sets (tile t mod 3).
 //
 // Fmt is the MFMA's operand format code: 0 e4m3, 2 e2m3, 3 e3m2, 4 e2m1.
 template <int Swz, int Fmt>
@@ -370,14 +385,18 @@ struct PingPongMxTile {
   static constexpr int kBK = kFp4 ? 256 : 128;             // elements of K per tile
   static constexpr int kTileRowBytes = kFp6 ? 96 : 128;    // bytes of a row per tile
   static constexpr int kScaleDw = kFp4 ? 2 : 1;            // scale dwords per row per tile
-  static constexpr int kScaleBytes = 2 * 256 * 4 * kScaleDw;
-  static constexpr int kBOff = 2 * kTileBytes, kSOff = 4 * kTileBytes;
-  static constexpr int kSinkOff = kSOff + 2 * kScaleBytes;
-  static constexpr int kLdsBytes = kSinkOff + kHalfBytes;  // 148 or 152 KiB
-  static constexpr int kLoads = 4 + kScaleDw + 4;          // a wave's loads of one tile
+  static constexpr int kARing = 2, kBRing = 3;
+  static constexpr int kLdsBytes = (kARing + kBRing) * kTileBytes;  // 160 KiB
   static constexpr int kMfmas = kFp4 ? 16 : 8;             // per compute phase
   static constexpr int kFM = 4, kFN = 2;
   static constexpr int kPieces = kFp6 ? 3 : 2;             // LDS reads per fragment
+  // Scales: a 16-byte load covers kScaleTiles K tiles (four for e4m3 and
+  // fp6, two for e2m1 with its two dwords a tile) of 64 scale rows: lanes
+  // 0-31 take the rows of one 32-row fragment block, lanes 32-63 those of
+  // the next (A blocks 0|1 and 2|3, B blocks 0|1), and a swap of the lane
+  // halves gives every lane both.
+  static constexpr int kScaleTiles = kFp4 ? 2 : 4;
+  static constexpr int kScaleLoads = 3;  // per wave and scale group
 
   // One phase's fragments: e4m3/e2m1 chunk c of every 32-row block (16
   // bytes), or fp6 piece q (8 bytes) of the lane's 24.
@@ -388,6 +407,12 @@ struct PingPongMxTile {
 
   struct Offsets {
     uint32_t a[2][kPieces], b[2][kPieces];  // [kk][c or q]
+  };
+
+  // The raw scale dwords of one scale group: [block pair], dword
+  // kScaleDw * (tile within the group) + d.
+  struct Scales {
+    u32x4 a[2], b;
   };
 
   // `ua`, `ub`: the block position of the rows that mxfp6_lds_offset leaves
@@ -431,20 +456,53 @@ struct PingPongMxTile {
       for (int c = 0; c < kPieces; ++c) f.b[fn][c] = read_piece(bt, o.b[kk][c] + fn * 4096);
   }
 
-  // Scale dword d of the wave's rows; the lane's block (lane half) is shifted
-  // into the even bytes so that op-select 2c picks block 2c + h of the dword.
-  __device__ __forceinline__ static void read_scales(uint32_t (&sa)[kFM], uint32_t (&sb)[kFN],
-                                                     const char* s, int d, int g, int w4,
-                                                     int lrow, int lhalf) {
+  // buffer_load_dwordx4 into registers, not tracked by the compiler: the
+  // value may be used only after an explicit wait has covered the load and
+  // the registers have passed through settle().
+  __device__ __forceinline__ static u32x4 load_dword4(u32x4 rsrc, uint32_t voff,
+                                                      uint32_t soff) {
+    u32x4 v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen"
+                 : "=v"(v)
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory");
+    return v;
+  }
+
+  // Scale load q (0 .. 2) of the group starting at byte `soff` of every
+  // scale row: A block pair q, or the B block pair.
+  __device__ __forceinline__ static void load_scale(Scales& s, int q, u32x4 rsa, u32x4 rsb,
+                                                    const uint32_t (&va)[2], uint32_t vb,
+                                                    uint32_t soff) {
+    if (q < 2)
+      s.a[q] = load_dword4(rsa, va[q], soff);
+    else
+      s.b = load_dword4(rsb, vb, soff);
+  }
+
+  // Ties the scale registers to this point of the program (after the wait
+  // that covers their loads), so that no use is placed before it.
+  __device__ __forceinline__ static void settle(Scales& s) {
+    asm volatile("" : "+v"(s.a[0]));
+    asm volatile("" : "+v"(s.a[1]));
+    asm volatile("" : "+v"(s.b));
+  }
+
+  // Scale dword w of the wave's rows.  A lane-half swap turns a pair's
+  // register (block 2p in lanes 0-31, 2p+1 in lanes 32-63) into one per
+  // block holding it in all lanes; then the lane's block (lane half) is
+  // shifted into the even bytes so that op-select 2c picks block 2c + h.
+  __device__ __forceinline__ static void pick_scales(uint32_t (&sa)[kFM], uint32_t (&sb)[kFN],
+                                                     const Scales& s, int w, int lhalf) {
 #pragma unroll
-    for (int fm = 0; fm < kFM; ++fm)
-      sa[fm] = *reinterpret_cast<const uint32_t*>(s + 1024 * d + 4 * (128 * g + 32 * fm + lrow)) >>
-               (8 * lhalf);
-#pragma unroll
-    for (int fn = 0; fn < kFN; ++fn)
-      sb[fn] = *reinterpret_cast<const uint32_t*>(s + 1024 * (kScaleDw + d) +
-                                                  4 * (64 * w4 + 32 * fn + lrow)) >>
-               (8 * lhalf);
+    for (int p = 0; p < 2; ++p) {
+      const auto r = __builtin_amdgcn_permlane32_swap(s.a[p][w], s.a[p][w], false, false);
+      sa[2 * p] = r[0] >> (8 * lhalf);
+      sa[2 * p + 1] = r[1] >> (8 * lhalf);
+    }
+    const auto r = __builtin_amdgcn_permlane32_swap(s.b[w], s.b[w], false, false);
+    sb[0] = r[0] >> (8 * lhalf);
+    sb[1] = r[1] >> (8 * lhalf);
   }
 
   // One scaled MFMA on 8-dword operands.
@@ -471,8 +529,8 @@ struct PingPongMxTile {
     }
   }
 
-  // kMfmas MFMAs of phase kk; N loads (given by `issue(q)`) go out between
-  // them, the first after the first MFMA.
+  // kMfmas MFMAs of step kk; N loads (given by `issue(q)`) go out spread
+  // between them, the first after the first MFMA.
   template <int N, class Issue>
   __device__ __forceinline__ static void compute(f32x16 (&acc)[kFM][kFN], const Frags& f,
                                                  const uint32_t (&sa)[kFM],
@@ -488,15 +546,28 @@ struct PingPongMxTile {
       else
         acc[fm][fn] = mfma<2>(av, bv, acc[fm][fn], sa[fm], sb[fn]);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (N > 0) {
-        if (m < N) issue(m);
-        if (m + kMfmas < N) issue(m + kMfmas);
-      }
+#pragma unroll
+      for (int q = 0; q < N; ++q)
+        if (q * kMfmas / N == m) issue(q);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   __device__ __forceinline__ static void barrier() { PingPongTile<true, Swz>::barrier(); }
+
+  // The end of every phase: the wave's LDS reads have returned and all but
+  // its N newest loads (those of its last two compute phases) have landed,
+  // so every tile a later phase reads is in LDS and its scales are in
+  // registers before the barrier.
+  template <int N>
+  __device__ __forceinline__ static void end_phase() {
+    static_assert(N == 8 || N == 11, "vmcnt immediate");
+    if constexpr (N == 8)
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)" ::: "memory");
+    barrier();
+  }
 
   // The fp6 half-tile loader.  The physical slots a lane fills are those of
   // HalfLoader; slot j of logical row r receives the operand bytes
@@ -527,15 +598,17 @@ struct PingPongMxTile {
                                           uint32_t kbyte0) const {
       dma16_so<I * 4096>(rsrc, voff[I], kbyte0, half + (uint32_t)w4 * 1024u);
     }
-
-    __device__ __forceinline__ void issue_rt(int i, u32x4 rsrc, uint32_t half, int w4,
-                                             uint32_t kbyte0) const {
-      if (i == 0) issue<0>(rsrc, half, w4, kbyte0);
-      if (i == 1) issue<1>(rsrc, half, w4, kbyte0);
-      if (i == 2) issue<2>(rsrc, half, w4, kbyte0);
-      if (i == 3) issue<3>(rsrc, half, w4, kbyte0);
-    }
   };
+  using Loader = typename std::conditional<kFp6, Fp6Loader, KExactHalfLoader<Swz>>::type;
+
+  template <class L>
+  __device__ __forceinline__ static void issue_half(const L& ld, int i, u32x4 rsrc,
+                                                    uint32_t half, int w4, uint32_t kbyte0) {
+    if (i == 0) ld.template issue<0>(rsrc, half, w4, kbyte0);
+    if (i == 1) ld.template issue<1>(rsrc, half, w4, kbyte0);
+    if (i == 2) ld.template issue<2>(rsrc, half, w4, kbyte0);
+    if (i == 3) ld.template issue<3>(rsrc, half, w4, kbyte0);
+  }
 
   // ua, ub: fp6 only, see mxfp6_lds_offset.
   __device__ __forceinline__ static void run(char* smem, const TileJob& j, const char* sfa,
@@ -547,81 +620,77 @@ struct PingPongMxTile {
     const int g = wave >> 2, w4 = wave & 3;
     const int lrow = lane & 31, lhalf = lane >> 5;
 
-    const uint32_t sf_pitch = (uint32_t)(K / 32);
     const u32x4 ra = rsrc_words(j.a, j.a_bytes), rb = rsrc_words(j.b, j.b_bytes);
     const u32x4 ra0 = rsrc_words(j.a, 0), rb0 = rsrc_words(j.b, 0);
+    const uint32_t sf_pitch = (uint32_t)(K / 32);
     const u32x4 rsa = rsrc_words(sfa, (uint32_t)j.m_valid * sf_pitch);
     const u32x4 rsb = rsrc_words(sfb, (uint32_t)j.n_valid * sf_pitch);
     const int a_rows = j.m_valid - 128 * g, b_rows = j.n_valid - 128 * g;
-    HalfLoader<Swz> la, lb;
-    Fp6Loader la6, lb6;
+    Loader la, lb;
     if constexpr (kFp6) {
-      la6.init(w4, lane, j.a_pitch, a_rows, ua);
-      lb6.init(w4, lane, j.b_pitch, b_rows, ub);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (la6.voff[i] != kOutOfRange) la6.voff[i] += (uint32_t)(128 * g) * j.a_pitch;
-        if (lb6.voff[i] != kOutOfRange) lb6.voff[i] += (uint32_t)(128 * g) * j.b_pitch;
-      }
+      la.init(w4, lane, j.a_pitch, a_rows, ua);
+      lb.init(w4, lane, j.b_pitch, b_rows, ub);
     } else {
-      la.init(w4, lane, j.a_pitch);
-      lb.init(w4, lane, j.b_pitch);
-      la.base += (uint32_t)(128 * g) * j.a_pitch;
-      lb.base += (uint32_t)(128 * g) * j.b_pitch;
+      HalfLoader<Swz> ha, hb;
+      ha.init(w4, lane, j.a_pitch);
+      hb.init(w4, lane, j.b_pitch);
+      la.init(ha, a_rows);
+      lb.init(hb, b_rows);
     }
-    // Scales: wave w4 of group g loads the dwords of rows 128g + 64(w4&1)
-    // + lane of A (w4 < 2) or B (w4 >= 2).
-    const int s_row = 128 * g + 64 * (w4 & 1) + lane;
-    const bool s_is_b = w4 >= 2;
-    const u32x4 rs = s_is_b ? rsb : rsa;
-    const int s_valid = s_is_b ? j.n_valid : j.m_valid;
-    const uint32_t s_lds_off =
-        (s_is_b ? 1024u * kScaleDw : 0u) + 4u * (uint32_t)(128 * g + 64 * (w4 & 1));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (la.voff[i] != kOutOfRange) la.voff[i] += (uint32_t)(128 * g) * j.a_pitch;
+      if (lb.voff[i] != kOutOfRange) lb.voff[i] += (uint32_t)(128 * g) * j.b_pitch;
+    }
+    // Scale rows of the lane: A 128g + 32(2p + h) + lrow for pair p, B
+    // 64 w4 + 32 h + lrow.
+    uint32_t sva[2], svb;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = 128 * g + 32 * (2 * p + lhalf) + lrow;
+      sva[p] = r < j.m_valid ? (uint32_t)r * sf_pitch : kOutOfRange;
+    }
+    {
+      const int r = 64 * w4 + 32 * lhalf + lrow;
+      svb = r < j.n_valid ? (uint32_t)r * sf_pitch : kOutOfRange;
+    }
 
     const uint32_t s0 = lds_addr(smem);
-    const uint32_t a_ring = s0 + g * kHalfBytes, b_ring = s0 + kBOff + g * kHalfBytes;
-    const uint32_t s_ring = s0 + kSOff + s_lds_off;
-    const uint32_t kbytes = (uint32_t)(kFp4 ? K / 2 : K);
+    const uint32_t a_ring = s0 + g * kHalfBytes;                        // + (t%2) tiles
+    const uint32_t b_ring = s0 + kARing * kTileBytes + g * kHalfBytes;  // + (t%3) tiles
+    const char* a_rd = smem;
+    const char* b_rd = smem + kARing * kTileBytes;
     const int T = (int)(K / kBK);
 
     auto ld_a = [&](int t, int i) {
-      if constexpr (kFp6)
-        la6.issue_rt(i, t < T ? ra : ra0, a_ring + (t & 1) * kTileBytes, w4,
-                     (uint32_t)t * 96u);
-      else
-        la.issue(ra, a_ring + (t & 1) * kTileBytes, w4, i, a_rows, (uint32_t)t * 128u, kbytes);
+      issue_half(la, i, t < T ? ra : ra0, a_ring + (t & 1) * kTileBytes, w4,
+                 (uint32_t)t * (uint32_t)kTileRowBytes);
     };
-    // B half of tile t when `real`, else an out-of-range load into the sink.
-    const uint32_t sink = s0 + kSinkOff;
-    auto ld_b = [&](int t, int i, bool real) {
-      if constexpr (kFp6)
-        lb6.issue_rt(i, real && t < T ? rb : rb0, real ? b_ring + (t & 1) * kTileBytes : sink,
-                     w4, (uint32_t)t * 96u);
-      else
-        lb.issue(rb, real ? b_ring + (t & 1) * kTileBytes : sink, w4, i, real ? b_rows : 0,
-                 (uint32_t)t * 128u, kbytes);
+    auto ld_b = [&](int t, int i) {
+      issue_half(lb, i, t < T ? rb : rb0, b_ring + (t % 3) * kTileBytes, w4,
+                 (uint32_t)t * (uint32_t)kTileRowBytes);
     };
-    // Scale dword d of tile t.
-    auto ld_s = [&](int t, int d) {
-      const bool ok = t < T && s_row < s_valid;
-      dma4(rs, ok ? (uint32_t)s_row * sf_pitch + 4u * (uint32_t)(kScaleDw * t + d) : kOutOfRange,
-           s_ring + (t & 1) * kScaleBytes + 1024u * d);
+    // Scales of the group starting at tile t.
+    auto ld_s = [&](Scales& s, int t, int q) {
+      load_scale(s, q, rsa, rsb, sva, svb, (uint32_t)(t * 4 * kScaleDw));
     };
 
-    // Prologue: tile 0 whole and A(1) with its scales; group 1 also B_hi(1)
-    // (group 0 loads B_lo(1) in its first memory phase).  Per wave: kLoads
-    // loads per tile.
+    // Tiles 0 and 1 (B, A, and the scales of the first group: the order the
+    // mainloop keeps).  Scale dwords past K are read out of range (zero) or
+    // from the next row; no MFMA uses them.  `cur` holds the current scale
+    // group, `nxt` receives the next.
+    Scales cur, nxt;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int i = 0; i < 4; ++i) ld_b(0, i);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ld_a(t, i);
+    for (int i = 0; i < 4; ++i) ld_a(0, i);
 #pragma unroll
-      for (int d = 0; d < kScaleDw; ++d) ld_s(t, d);
+    for (int q = 0; q < kScaleLoads; ++q) ld_s(cur, 0, q);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ld_b(t, i, t == 0 || g);
-    }
-    wait_loads_but<kLoads>();  // tile 0 has landed
-    barrier();
+    for (int i = 0; i < 4; ++i) ld_b(1, i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ld_a(1, i);
+    end_phase<8>();
 
     const Offsets o = offsets(g, w4, lrow, lhalf, ua, ub);
     f32x16 acc[kFM][kFN];
@@ -630,53 +699,68 @@ struct PingPongMxTile {
 #pragma unroll
       for (int k = 0; k < kFN; ++k) acc[i][k] = f32x16{};
 
-    if (g) barrier();  // group 1 runs one phase behind group 0
-    for (int t = 0; t < T; ++t) {
-      const char* at = smem + (t & 1) * kTileBytes;
-      const char* bt = smem + kBOff + (t & 1) * kTileBytes;
-      const char* st = smem + kSOff + (t & 1) * kScaleBytes;
+    // Tile t, the Sub-th of its scale group.  The first tile of a group also
+    // loads the next group's scales (into `nxt`) with its A half; the waits
+    // count those loads in the phases that follow.
+    auto tile = [&](auto sub, int t) {
+      constexpr int Sub = decltype(sub)::value;
+      constexpr int kPrev = Sub == 1 ? 8 + kScaleLoads : 8;
+      constexpr int kThis = Sub == 0 ? 8 + kScaleLoads : 8;
+      const char* at = a_rd + (t & 1) * kTileBytes;
+      const char* bt = b_rd + (t % 3) * kTileBytes;
       Frags f;
       uint32_t sa[kFM], sb[kFN];
-      // First memory phase; then B_lo(t+1) (group 0).
       read(f, at, bt, o, 0);
-      read_scales(sa, sb, st, 0, g, w4, lrow, lhalf);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ld_b(t + 1, i, !g);
-      barrier();
-      compute<0>(acc, f, sa, sb, 0, [&](int) {});
-      barrier();
-      // Second memory phase.  Of the wave's loads only the 4 newest (the B
-      // loads just issued) may still be in flight: group 1's share of tile
-      // t+1 is then in LDS before the barrier that lets group 0 read it.
+      pick_scales(sa, sb, cur, kScaleDw * Sub, lhalf);
+      end_phase<kPrev>();
+      compute<4>(acc, f, sa, sb, 0, [&](int q) { ld_b(t + 2, q); });
+      end_phase<kPrev>();
       read(f, at, bt, o, 1);
-      if constexpr (kFp4) read_scales(sa, sb, st, 1, g, w4, lrow, lhalf);
-      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
-      barrier();
-      // Second compute phase, with the loads of tile t+2: A half, scales,
-      // B half (group 1).  Afterwards only those kLoads may be in flight:
-      // group 0's share of tile t+1 has landed.
-      compute<kLoads>(acc, f, sa, sb, 1, [&](int q) {
-        if (q < 4) ld_a(t + 2, q);
-        else if (q < 4 + kScaleDw) ld_s(t + 2, q - 4);
-        else ld_b(t + 2, q - 4 - kScaleDw, g != 0);
-      });
-      wait_loads_but<kLoads>();
-      barrier();
+      if constexpr (kFp4) pick_scales(sa, sb, cur, kScaleDw * Sub + 1, lhalf);
+      end_phase<kPrev>();
+      if constexpr (Sub == 0)
+        compute<4 + kScaleLoads>(acc, f, sa, sb, 1, [&](int q) {
+          if (q < 4) ld_a(t + 2, q);
+          else ld_s(nxt, t + kScaleTiles, q - 4);
+        });
+      else
+        compute<4>(acc, f, sa, sb, 1, [&](int q) { ld_a(t + 2, q); });
+      end_phase<kThis>();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+
+    if (g) barrier();  // group 1 runs one phase behind group 0
+    int t = 0;
+    settle(cur);
+    for (; t + kScaleTiles <= T; t += kScaleTiles) {
+      tile(I0{}, t);
+      tile(I1{}, t + 1);
+      if constexpr (kScaleTiles == 4) {
+        tile(I2{}, t + 2);
+        tile(I3{}, t + 3);
+      }
+      // The next group's loads were covered by the waits of the tiles since.
+      settle(nxt);
+      cur = nxt;
+    }
+    if (t < T) tile(I0{}, t);
+    if constexpr (kScaleTiles == 4) {
+      if (t + 1 < T) tile(I1{}, t + 1);
+      if (t + 2 < T) tile(I2{}, t + 2);
     }
     if (!g) barrier();
+    // All loads have landed before the scale registers (which the last
+    // loads write) may hold anything else.
+    settle(cur);
+    settle(nxt);
     wait_vmem();
+    settle(cur);
+    settle(nxt);
 
     Base::epilogue(acc, j, nullptr, SG_NONE, D, d_dtype, ldd, lane, g, w4);
-  }
-
-  template <int N>
-  __device__ __forceinline__ static void wait_loads_but() {
-    if constexpr (N == 9)
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-    static_assert(N == 9 || N == 10, "vmcnt immediate");
   }
 };
 

@@ -21,28 +21,6 @@
 
 namespace sg {
 
-// The half-tile loader for K a multiple of 64: each lane's four row offsets
-// (out of range for rows past the operand) are fixed per tile job, and the K
-// position of a load travels in the instruction's SGPR offset; a K tile past
-// the end is loaded through a descriptor with no records (zero fill).
-template <int Swz>
-struct KExactHalfLoader {
-  uint32_t voff[4];
-
-  __device__ __forceinline__ void init(const HalfLoader<Swz>& h, int rows_valid) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      voff[i] = h.row + 32 * i < rows_valid ? h.base + (uint32_t)(32 * i) * h.pitch
-                                            : kOutOfRange;
-  }
-
-  template <int I>
-  __device__ __forceinline__ void issue(u32x4 rsrc, uint32_t half, int w4,
-                                        uint32_t kbyte0) const {
-    dma16_so<I * 4096>(rsrc, voff[I], kbyte0, half + (uint32_t)w4 * 1024u);
-  }
-};
-
 template <bool IsBF16, int Swz>
 struct PingPong16Tile {
   using PP = PingPongTile<IsBF16, Swz>;
