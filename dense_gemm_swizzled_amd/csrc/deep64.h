@@ -1,0 +1,136 @@
+// deep64.h -- 64x64 tiles with an eight-stage LDS ring, for GEMMs too small
+// to give every CU more than one tile (M = N = K = 1024 is 256 such tiles).
+//
+// Why.  Such a tile does 4 MFMAs per wave per 64-wide K tile, a few hundred
+// cycles, while a K tile's loads take a load latency (around a microsecond
+// from L2) to land.  A double-buffered mainloop therefore waits one latency
+// per K tile.  Here the loads run seven K tiles ahead: LDS holds eight
+// stages of 16 KiB (A then B, 64 rows x 128 bytes each), and the wait before
+// K tile t only needs t's own loads, issued seven tiles earlier.
+//
+// Layout.  A (K-major) and a K-major B use the XOR map lds_offset<128, 16>
+// and the fragment reads of GemmTile.  An MN-major B is stored as it lies in
+// memory, one 128-byte LDS row per k (64 n values), with the 16-byte chunks
+// of rows whose bit 3 is set rotated by four chunks: the MFMA operand of a
+// lane is 8 consecutive k of one n, read with eight 2-byte LDS reads, and the
+// rotation puts the rows k and k+8 that the two lane halves read in the same
+// instruction on different banks.
+//
+// Waves.  Four waves in a 2x2 grid, one 32x32 accumulator each (the
+// GemmTile<64, 64> layout, whose epilogue this tile uses).  Every wave
+// issues four of a K tile's sixteen 1 KiB direct-to-LDS loads; a barrier
+// before each K tile makes all of them visible and frees the slot the
+// tile's successor loads go to.
+#pragma once
+
+#include "pingpong.h"
+
+namespace sg {
+
+template <bool IsBF16, bool BMn>
+struct Deep64Tile {
+  using Base = GemmTile<64, 64, IsBF16, false, BMn, kSwzDefault, 4>;
+  static constexpr int kStages = 8;
+  static constexpr int kBK = 64;
+  static constexpr int kOpBytes = 64 * 128;                // one operand's K tile
+  static constexpr int kStageBytes = 2 * kOpBytes;         // A, then B
+  static constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
+  // A wave's loads newer than those of the K tile about to be read.
+  static constexpr int kNewer = (kStages - 2) * 4;
+  static_assert(kNewer == 24, "vmcnt immediate");
+
+  // Byte offset, in an MN-major B stage, of byte `byte` of k-row k.
+  __device__ __forceinline__ static uint32_t bmn_offset(uint32_t k, uint32_t byte) {
+    return k * 128u + ((byte + 64u * ((k >> 3) & 1u)) & 127u);
+  }
+
+  __device__ __forceinline__ static void run(char* smem, const TileJob& j, int64_t K,
+                                             const void* C, int c_dtype, void* D,
+                                             int d_dtype, int64_t ldd) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+
+    const u32x4 ra = rsrc_words(j.a, j.a_bytes), rb = rsrc_words(j.b, j.b_bytes);
+    const uint32_t kbytes = (uint32_t)K * 2u;
+    const int T = (int)((K + kBK - 1) / kBK);
+    HalfLoader<kSwzDefault> la, lb;
+    la.init(wave, lane, j.a_pitch);
+    lb.init(wave, lane, j.b_pitch);
+    const uint32_t s0 = lds_addr(smem);
+
+    // Loads of K tile t into stage t mod kStages; past K every chunk is out
+    // of range (zero fill).  Regions 4i + wave of each operand (1 KiB each).
+    auto issue = [&](int t) {
+      const uint32_t stage = s0 + (uint32_t)(t % kStages) * kStageBytes;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        la.issue(ra, stage, wave, i, j.m_valid, (uint32_t)t * 128u, kbytes);
+      if constexpr (!BMn) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          lb.issue(rb, stage + kOpBytes, wave, i, j.n_valid, (uint32_t)t * 128u, kbytes);
+      } else {
+        // Lane l of region r fills k-row 8r + l/8, physical chunk l%8, which
+        // holds logical chunk (l%8 + 4 * bit 3 of the row) mod 8.
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = 4 * i + wave, krow = 8 * r + (lane >> 3);
+          const int64_t k = (int64_t)t * kBK + krow;
+          const uint32_t c = (uint32_t)((lane & 7) + 4 * ((krow >> 3) & 1)) & 7u;
+          const uint32_t off = k < K ? (uint32_t)k * j.b_pitch + 16u * c : kOutOfRange;
+          dma16(rb, off, stage + kOpBytes + (uint32_t)r * 1024u);
+        }
+      }
+    };
+
+    const typename Base::FragOffsets o = Base::frag_offsets(wm, wn, lrow, lhalf);
+    f32x16 acc[1][1];
+    acc[0][0] = f32x16{};
+
+#pragma unroll
+    for (int t = 0; t < kStages - 1; ++t) issue(t);
+
+    for (int t = 0; t < T; ++t) {
+      // K tile t has landed for this wave; after the barrier, for all waves,
+      // and every wave is done reading K tile t-1, whose stage t+7 reuses.
+      asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)" ::: "memory");
+      PingPongTile<IsBF16, kSwzDefault>::barrier();
+      issue(t + kStages - 1);
+      const char* as = smem + (t % kStages) * kStageBytes;
+      const char* bs = as + kOpBytes;
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        const u32x4 a = lds_read16(as, o.a[kk]);
+        u32x4 b;
+        if constexpr (!BMn) {
+          b = lds_read16(bs, o.b[kk]);
+        } else {
+          const uint32_t n2 = 2u * (uint32_t)(wn * 32 + lrow);
+          const uint32_t k0 = (uint32_t)(16 * kk + 8 * lhalf);
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            h[e] = *reinterpret_cast<const uint16_t*>(bs + bmn_offset(k0 + e, n2));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) b[q] = h[2 * q] | (h[2 * q + 1] << 16);
+        }
+        acc[0][0] = mfma32x32x16<IsBF16>(b, a, acc[0][0]);
+      }
+    }
+    wait_vmem();  // the loads past K
+
+    Base::epilogue(acc, j, C, c_dtype, D, d_dtype, ldd, lane, wm, wn);
+  }
+};
+
+template <bool IsBF16, bool BMn>
+__global__ void __launch_bounds__(256, 1) deep64_gemm_kernel(const DenseParams p) {
+  using Tile = Deep64Tile<IsBF16, BMn>;
+  __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+  const TileJob j = dense_tile_job<64, 64, false, BMn>(p, blockIdx.x);
+  Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.ldd);
+}
+
+}  // namespace sg
