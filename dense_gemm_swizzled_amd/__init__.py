@@ -31,7 +31,7 @@ __all__ = [
     "mxfp6_gemm_run", "gemm_layout_run", "gemm_layout128_run", "gemm_last_error",
     "gemm_version", "gemm_lds_layout", "gemm_lds_layout_mxfp6", "gemm_lds_image",
     "SG_E2M3", "SG_E3M2",
-    "gemm", "gemm_strided", "grouped_gemm", "mx_gemm", "mxfp4_gemm", "mxfp6_gemm",
+    "gemm", "gemm_plan", "gemm_strided", "grouped_gemm", "mx_gemm", "mxfp4_gemm", "mxfp6_gemm",
     "gemm_layout",
     "gemm_layout128", "SG_LAYOUT_PAD16",
     "library_path", "load",
@@ -224,6 +224,36 @@ def gemm(A, B, *, a_major: str = "k", b_major: str = "k", C=None,
                     _dt(C.dtype) if C is not None else SG_NONE, out.data_ptr(),
                     _dt(out.dtype), _stream(A.device)))
     return out
+
+
+def gemm_plan(A, B, *, a_major: str = "k", b_major: str = "k", C=None, out):
+    """gemm() with its argument marshalling done once: returns a callable
+    that launches D = A*B (+C) into `out` on the stream current now, for
+    launch-bound small problems where the per-call Python work would
+    otherwise take longer than the kernel.  The tensors must stay alive and
+    keep their storage while the callable is in use."""
+    if a_major == "k":
+        M, K = A.shape
+    else:
+        K, M = A.shape
+    if b_major == "k":
+        N, Kb = B.shape
+    else:
+        Kb, N = B.shape
+    if Kb != K or A.dtype != B.dtype or tuple(out.shape) != (M, N):
+        raise GemmError(-3, "A, B and out disagree on shapes or dtype")
+    f = load().gemm_run
+    args = (M, N, K, A.data_ptr(), 0 if a_major == "k" else 1, B.data_ptr(),
+            0 if b_major == "k" else 1, _dt(A.dtype),
+            C.data_ptr() if C is not None else None,
+            _dt(C.dtype) if C is not None else SG_NONE, out.data_ptr(), _dt(out.dtype),
+            _stream(A.device))
+
+    def run() -> None:
+        rc = f(*args)
+        if rc != SG_OK:
+            raise GemmError(rc, gemm_last_error())
+    return run
 
 
 def _ld(t, name: str) -> int:

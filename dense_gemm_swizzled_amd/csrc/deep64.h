@@ -100,12 +100,14 @@ struct Deep64Tile {
       issue(t + kStages - 1);
       const char* as = smem + (t % kStages) * kStageBytes;
       const char* bs = as + kOpBytes;
+      // All of the K tile's fragment reads first, so that the wave waits for
+      // LDS once per K tile, then its four MFMAs.
+      u32x4 a[kBK / 16], b[kBK / 16];
 #pragma unroll
       for (int kk = 0; kk < kBK / 16; ++kk) {
-        const u32x4 a = lds_read16(as, o.a[kk]);
-        u32x4 b;
+        a[kk] = lds_read16(as, o.a[kk]);
         if constexpr (!BMn) {
-          b = lds_read16(bs, o.b[kk]);
+          b[kk] = lds_read16(bs, o.b[kk]);
         } else {
           const uint32_t n2 = 2u * (uint32_t)(wn * 32 + lrow);
           const uint32_t k0 = (uint32_t)(16 * kk + 8 * lhalf);
@@ -114,10 +116,13 @@ struct Deep64Tile {
           for (int e = 0; e < 8; ++e)
             h[e] = *reinterpret_cast<const uint16_t*>(bs + bmn_offset(k0 + e, n2));
 #pragma unroll
-          for (int q = 0; q < 4; ++q) b[q] = h[2 * q] | (h[2 * q + 1] << 16);
+          for (int q = 0; q < 4; ++q) b[kk][q] = h[2 * q] | (h[2 * q + 1] << 16);
         }
-        acc[0][0] = mfma32x32x16<IsBF16>(b, a, acc[0][0]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk)
+        acc[0][0] = mfma32x32x16<IsBF16>(b[kk], a[kk], acc[0][0]);
     }
     wait_vmem();  // the loads past K
 

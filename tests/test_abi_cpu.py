@@ -284,3 +284,13 @@ def test_lds_image_rejects():
     assert sg.gemm_lds_image(P, 100, 64, 2, 0, 0, 64, P, None) == SHAPE
     assert sg.gemm_lds_image(P, 100, 64, 2, 0, 32, 128, P, None) == SHAPE
     assert sg.gemm_lds_image(None, 100, 64, 2, 0, 0, 128, P, None) == NULL
+
+
+def test_gemm_plan_rejects_mismatched_shapes():
+    import torch
+    A = torch.zeros(8, 16, dtype=torch.bfloat16)
+    B = torch.zeros(4, 16, dtype=torch.bfloat16)
+    with pytest.raises(sg.GemmError):
+        sg.gemm_plan(A, B, out=torch.zeros(8, 5))      # out is [M][N] = [8][4]
+    with pytest.raises(sg.GemmError):
+        sg.gemm_plan(A, torch.zeros(4, 12, dtype=torch.bfloat16), out=torch.zeros(8, 4))

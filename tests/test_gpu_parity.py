@@ -249,6 +249,28 @@ def test_dense_256_tiles_integer_inputs_exact(dev):
     assert np.array_equal(d.cpu().numpy().astype(np.int64), want)
 
 
+def test_gemm_plan_matches_gemm_and_oracle(dev):
+    # The prepared call launches the same kernel with the same arguments:
+    # bit-identical to gemm(), on the 1024^3 workload's shape family (64x64
+    # tiles, B [K][N]), called twice.
+    case = si.dense_case(200, 136, 264, 17, ab_dtype="bf16", a_major="k", b_major="mn",
+                         with_c=True, c_dtype="bf16", d_dtype="f32")
+    A, B, C = case.A.to(dev), case.B.to(dev), case.C.to(dev)
+    say("gemm_plan vs gemm")
+    want = sg.gemm(A, B, a_major="k", b_major="mn", C=C, out_dtype=torch.float32)
+    out = torch.full_like(want, float("nan"))
+    run = sg.gemm_plan(A, B, a_major="k", b_major="mn", C=C, out=out)
+    run()
+    torch.cuda.synchronize()
+    assert torch.equal(out, want)
+    out.fill_(float("nan"))
+    run()
+    torch.cuda.synchronize()
+    assert torch.equal(out, want)
+    ref, bound = oracle_dense(case)
+    check_close(_np(out), ref, bound, "f32", "gemm_plan")
+
+
 def test_dense_in_place_c_equals_d(dev):
     case = si.dense_case(128, 128, 96, 5, ab_dtype="bf16", with_c=True, c_dtype="f32",
                          d_dtype="f32")
