@@ -6,7 +6,8 @@
 // from L2) to land.  A double-buffered mainloop therefore waits one latency
 // per K tile.  Here the loads run seven K tiles ahead: LDS holds eight
 // stages of 16 KiB (A then B, 64 rows x 128 bytes each), and the wait before
-// K tile t only needs t's own loads, issued seven tiles earlier.
+// K tile t+1's fragments are read only needs that tile's own loads, issued
+// six tiles earlier; the reads of tile t+1 overlap the MFMAs of tile t.
 //
 // Layout.  A (K-major) and a K-major B use the XOR map lds_offset<128, 16>
 // and the fragment reads of GemmTile.  An MN-major B is stored as it lies in
@@ -35,9 +36,9 @@ struct Deep64Tile {
   static constexpr int kOpBytes = 64 * 128;                // one operand's K tile
   static constexpr int kStageBytes = 2 * kOpBytes;         // A, then B
   static constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
-  // A wave's loads newer than those of the K tile about to be read.
-  static constexpr int kNewer = (kStages - 2) * 4;
-  static_assert(kNewer == 24, "vmcnt immediate");
+  // A wave's loads newer than those of K tile t (t+1) at the first wait
+  // (in the loop).
+  static_assert((kStages - 2) * 4 == 24 && (kStages - 3) * 4 == 20, "vmcnt immediates");
 
   // Byte offset, in an MN-major B stage, of byte `byte` of k-row k.
   __device__ __forceinline__ static uint32_t bmn_offset(uint32_t k, uint32_t byte) {
@@ -89,25 +90,18 @@ struct Deep64Tile {
     f32x16 acc[1][1];
     acc[0][0] = f32x16{};
 
-#pragma unroll
-    for (int t = 0; t < kStages - 1; ++t) issue(t);
-
-    for (int t = 0; t < T; ++t) {
-      // K tile t has landed for this wave; after the barrier, for all waves,
-      // and every wave is done reading K tile t-1, whose stage t+7 reuses.
-      asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)" ::: "memory");
-      PingPongTile<IsBF16, kSwzDefault>::barrier();
-      issue(t + kStages - 1);
+    // The fragments of one K tile: four 16-wide steps of A and B.
+    struct Frags {
+      u32x4 a[kBK / 16], b[kBK / 16];
+    };
+    auto read = [&](Frags& f, int t) {
       const char* as = smem + (t % kStages) * kStageBytes;
       const char* bs = as + kOpBytes;
-      // All of the K tile's fragment reads first, so that the wave waits for
-      // LDS once per K tile, then its four MFMAs.
-      u32x4 a[kBK / 16], b[kBK / 16];
 #pragma unroll
       for (int kk = 0; kk < kBK / 16; ++kk) {
-        a[kk] = lds_read16(as, o.a[kk]);
+        f.a[kk] = lds_read16(as, o.a[kk]);
         if constexpr (!BMn) {
-          b[kk] = lds_read16(bs, o.b[kk]);
+          f.b[kk] = lds_read16(bs, o.b[kk]);
         } else {
           const uint32_t n2 = 2u * (uint32_t)(wn * 32 + lrow);
           const uint32_t k0 = (uint32_t)(16 * kk + 8 * lhalf);
@@ -116,14 +110,38 @@ struct Deep64Tile {
           for (int e = 0; e < 8; ++e)
             h[e] = *reinterpret_cast<const uint16_t*>(bs + bmn_offset(k0 + e, n2));
 #pragma unroll
-          for (int q = 0; q < 4; ++q) b[kk][q] = h[2 * q] | (h[2 * q + 1] << 16);
+          for (int q = 0; q < 4; ++q) f.b[kk][q] = h[2 * q] | (h[2 * q + 1] << 16);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
+    };
+
+#pragma unroll
+    for (int t = 0; t < kStages - 1; ++t) issue(t);
+
+    // Software pipelined: the fragments of K tile t+1 are read while the
+    // MFMAs of tile t run.  Before iteration t the wave waits for its loads
+    // of tile t+1 (the 20 newer ones may stay in flight); the barrier makes
+    // every wave's loads of t+1 visible and frees the stage of tile t-1,
+    // whose fragments were read in iteration t-2, for the loads of t+7.
+    Frags f0, f1;
+    asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    PingPongTile<IsBF16, kSwzDefault>::barrier();
+    read(f0, 0);
+    auto iteration = [&](int t, Frags& cur, Frags& nxt) {
+      asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)" ::: "memory");
+      PingPongTile<IsBF16, kSwzDefault>::barrier();
+      issue(t + kStages - 1);
+      read(nxt, t + 1);  // past the last tile: stale LDS, never used
 #pragma unroll
       for (int kk = 0; kk < kBK / 16; ++kk)
-        acc[0][0] = mfma32x32x16<IsBF16>(b[kk], a[kk], acc[0][0]);
+        acc[0][0] = mfma32x32x16<IsBF16>(cur.b[kk], cur.a[kk], acc[0][0]);
+    };
+    int t = 0;
+    for (; t + 1 < T; t += 2) {
+      iteration(t, f0, f1);
+      iteration(t + 1, f1, f0);
     }
+    if (t < T) iteration(t, f0, f1);
     wait_vmem();  // the loads past K
 
     Base::epilogue(acc, j, C, c_dtype, D, d_dtype, ldd, lane, wm, wn);
