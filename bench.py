@@ -38,17 +38,27 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments and blank lines removed (string literals in
+    these sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash() -> str:
-    """sha256 of the kernel sources and the C header: HBM traffic measured
-    with rocprofv3 is reported only while it still describes this code."""
+    """sha256 of the kernel sources and the C header, comments left out: HBM
+    traffic measured with rocprofv3 is reported only while it still
+    describes this code."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_gemm_swizzled_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
-    with open(os.path.join(ROOT, "include", "swizzled_gemm.h"), "rb") as f:
-        h.update(f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
+    with open(os.path.join(ROOT, "include", "swizzled_gemm.h"), encoding="utf-8") as f:
+        h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 

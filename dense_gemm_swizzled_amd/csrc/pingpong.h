@@ -1,5 +1,7 @@
 // pingpong.h -- the 8-wave "ping-pong" mainloop for 256x256 tiles whose A
-// and B are both K-major (16-bit elements).
+// and B are both K-major: 16-bit elements with 32x32x16 MFMAs here (the
+// 16x16x32 form is pingpong16.h), and the block-scaled MXFP8 / MXFP6 / MXFP4
+// form at the end of this file.
 //
 // Roles.  The workgroup's 8 waves form two groups of four, one wave of each
 // group per SIMD (the hardware deals a workgroup's waves to the SIMDs round
