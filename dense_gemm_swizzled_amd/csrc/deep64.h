@@ -9,13 +9,13 @@
 // K tile t+1's fragments are read only needs that tile's own loads, issued
 // six tiles earlier; the reads of tile t+1 overlap the MFMAs of tile t.
 //
-// Layout.  A (K-major) and a K-major B use the XOR map lds_offset<128, 16>
-// and the fragment reads of GemmTile.  An MN-major B is stored as it lies in
-// memory, one 128-byte LDS row per k (64 n values), with the 16-byte chunks
-// of rows whose bit 3 is set rotated by four chunks: the MFMA operand of a
-// lane is 8 consecutive k of one n, read with eight 2-byte LDS reads, and the
-// rotation puts the rows k and k+8 that the two lane halves read in the same
-// instruction on different banks.
+// Layout.  A K-major operand uses the XOR map lds_offset<128, 16> and the
+// fragment reads of GemmTile.  An MN-major operand is stored as it lies in
+// memory, one 128-byte LDS row per k (64 m or n values), with the 16-byte
+// chunks of rows whose bit 3 is set rotated by four chunks: the MFMA operand
+// of a lane is 8 consecutive k of one m or n, read with eight 2-byte LDS
+// reads, and the rotation puts the rows k and k+8 that the two lane halves
+// read in the same instruction on different banks.
 //
 // Waves.  Four waves in a 2x2 grid, one 32x32 accumulator each (the
 // GemmTile<64, 64> layout, whose epilogue this tile uses).  Every wave
@@ -28,9 +28,9 @@
 
 namespace sg {
 
-template <bool IsBF16, bool BMn>
+template <bool IsBF16, bool AMn, bool BMn>
 struct Deep64Tile {
-  using Base = GemmTile<64, 64, IsBF16, false, BMn, kSwzDefault, 4>;
+  using Base = GemmTile<64, 64, IsBF16, AMn, BMn, kSwzDefault, 4>;
   static constexpr int kStages = 8;
   static constexpr int kBK = 64;
   static constexpr int kOpBytes = 64 * 128;                // one operand's K tile
@@ -40,7 +40,7 @@ struct Deep64Tile {
   // (in the loop).
   static_assert((kStages - 2) * 4 == 24 && (kStages - 3) * 4 == 20, "vmcnt immediates");
 
-  // Byte offset, in an MN-major B stage, of byte `byte` of k-row k.
+  // Byte offset, in an MN-major operand's stage, of byte `byte` of k-row k.
   __device__ __forceinline__ static uint32_t bmn_offset(uint32_t k, uint32_t byte) {
     return k * 128u + ((byte + 64u * ((k >> 3) & 1u)) & 127u);
   }
@@ -61,29 +61,33 @@ struct Deep64Tile {
     lb.init(wave, lane, j.b_pitch);
     const uint32_t s0 = lds_addr(smem);
 
-    // Loads of K tile t into stage t mod kStages; past K every chunk is out
-    // of range (zero fill).  Regions 4i + wave of each operand (1 KiB each).
-    auto issue = [&](int t) {
-      const uint32_t stage = s0 + (uint32_t)(t % kStages) * kStageBytes;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        la.issue(ra, stage, wave, i, j.m_valid, (uint32_t)t * 128u, kbytes);
-      if constexpr (!BMn) {
+    // Loads of K tile t of one operand into `dst`; past K every chunk is
+    // out of range (zero fill).  Regions 4i + wave (1 KiB each).  MN-major:
+    // lane l of region r fills k-row 8r + l/8, physical chunk l%8, which
+    // holds logical chunk (l%8 + 4 * bit 3 of the row) mod 8.
+    auto issue_op = [&](auto mn, const HalfLoader<kSwzDefault>& ld, u32x4 rsrc, uint32_t pitch,
+                        int rows_valid, uint32_t dst, int t) {
+      if constexpr (!decltype(mn)::value) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-          lb.issue(rb, stage + kOpBytes, wave, i, j.n_valid, (uint32_t)t * 128u, kbytes);
+          ld.issue(rsrc, dst, wave, i, rows_valid, (uint32_t)t * 128u, kbytes);
       } else {
-        // Lane l of region r fills k-row 8r + l/8, physical chunk l%8, which
-        // holds logical chunk (l%8 + 4 * bit 3 of the row) mod 8.
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int r = 4 * i + wave, krow = 8 * r + (lane >> 3);
           const int64_t k = (int64_t)t * kBK + krow;
           const uint32_t c = (uint32_t)((lane & 7) + 4 * ((krow >> 3) & 1)) & 7u;
-          const uint32_t off = k < K ? (uint32_t)k * j.b_pitch + 16u * c : kOutOfRange;
-          dma16(rb, off, stage + kOpBytes + (uint32_t)r * 1024u);
+          const uint32_t off = k < K ? (uint32_t)k * pitch + 16u * c : kOutOfRange;
+          dma16(rsrc, off, dst + (uint32_t)r * 1024u);
         }
       }
+    };
+    // K tile t into stage t mod kStages.
+    auto issue = [&](int t) {
+      const uint32_t stage = s0 + (uint32_t)(t % kStages) * kStageBytes;
+      issue_op(std::integral_constant<bool, AMn>{}, la, ra, j.a_pitch, j.m_valid, stage, t);
+      issue_op(std::integral_constant<bool, BMn>{}, lb, rb, j.b_pitch, j.n_valid,
+               stage + kOpBytes, t);
     };
 
     const typename Base::FragOffsets o = Base::frag_offsets(wm, wn, lrow, lhalf);
@@ -94,24 +98,33 @@ struct Deep64Tile {
     struct Frags {
       u32x4 a[kBK / 16], b[kBK / 16];
     };
+    // An MN-major operand's fragment: k = 16 kk + 8 h + e (e = 0..7) of
+    // column `col` (m or n), two bytes at a time.
+    auto gather = [&](const char* base, int col, int kk) {
+      const uint32_t c2 = 2u * (uint32_t)col;
+      const uint32_t k0 = (uint32_t)(16 * kk + 8 * lhalf);
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        h[e] = *reinterpret_cast<const uint16_t*>(base + bmn_offset(k0 + e, c2));
+      u32x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = h[2 * q] | (h[2 * q + 1] << 16);
+      return v;
+    };
     auto read = [&](Frags& f, int t) {
       const char* as = smem + (t % kStages) * kStageBytes;
       const char* bs = as + kOpBytes;
 #pragma unroll
       for (int kk = 0; kk < kBK / 16; ++kk) {
-        f.a[kk] = lds_read16(as, o.a[kk]);
-        if constexpr (!BMn) {
+        if constexpr (!AMn)
+          f.a[kk] = lds_read16(as, o.a[kk]);
+        else
+          f.a[kk] = gather(as, wm * 32 + lrow, kk);
+        if constexpr (!BMn)
           f.b[kk] = lds_read16(bs, o.b[kk]);
-        } else {
-          const uint32_t n2 = 2u * (uint32_t)(wn * 32 + lrow);
-          const uint32_t k0 = (uint32_t)(16 * kk + 8 * lhalf);
-          uint32_t h[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            h[e] = *reinterpret_cast<const uint16_t*>(bs + bmn_offset(k0 + e, n2));
-#pragma unroll
-          for (int q = 0; q < 4; ++q) f.b[kk][q] = h[2 * q] | (h[2 * q + 1] << 16);
-        }
+        else
+          f.b[kk] = gather(bs, wn * 32 + lrow, kk);
       }
     };
 
@@ -148,11 +161,11 @@ struct Deep64Tile {
   }
 };
 
-template <bool IsBF16, bool BMn>
+template <bool IsBF16, bool AMn, bool BMn>
 __global__ void __launch_bounds__(256, 1) deep64_gemm_kernel(const DenseParams p) {
-  using Tile = Deep64Tile<IsBF16, BMn>;
+  using Tile = Deep64Tile<IsBF16, AMn, BMn>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
-  const TileJob j = dense_tile_job<64, 64, false, BMn>(p, blockIdx.x);
+  const TileJob j = dense_tile_job<64, 64, AMn, BMn>(p, blockIdx.x);
   Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.ldd);
 }
 

@@ -42,17 +42,20 @@ hipError_t go_pingpong32(const DenseParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 64x64 tiles with a K-major A run the eight-stage ring.
-template <bool BF, bool BMn>
+// 64x64 tiles run the eight-stage ring.
+template <bool BF, bool AMn, bool BMn>
 hipError_t go_deep64(const DenseParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((deep64_gemm_kernel<BF, BMn>), dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s,
-                     p);
+  hipLaunchKernelGGL((deep64_gemm_kernel<BF, AMn, BMn>), dim3(p.tiles_m * p.tiles_n), dim3(256),
+                     0, s, p);
   return hipGetLastError();
 }
 
 template <int BM, int BN, bool BF, int Swz>
 hipError_t dense_by_major(bool a_mn, bool b_mn, const DenseParams& p, hipStream_t s) {
-  if (BM == 64 && !a_mn) return b_mn ? go_deep64<BF, true>(p, s) : go_deep64<BF, false>(p, s);
+  if (BM == 64) {
+    if (a_mn) return b_mn ? go_deep64<BF, true, true>(p, s) : go_deep64<BF, true, false>(p, s);
+    return b_mn ? go_deep64<BF, false, true>(p, s) : go_deep64<BF, false, false>(p, s);
+  }
   if (!a_mn && !b_mn)
     return BM == 256 ? go_pingpong<BF, Swz>(p, s) : go_dense<BM, BN, BF, false, false, Swz>(p, s);
   if (!a_mn && b_mn) return go_dense<BM, BN, BF, false, true, Swz>(p, s);
