@@ -188,7 +188,8 @@ int mxfp4_gemm_run(int64_t M, int64_t N, int64_t K, const void* A,
  *   B    fp6 K-major [N][3K/4] bytes;  SFB  e8m0 [N][K/32].
  *   D    [M][N] of d_dtype (SG_F32 or SG_BF16).
  *   K    must be a multiple of 128 (96 bytes of every row per K tile);
- *        M and N may be ragged.  The kernel reads only bytes of A and B.
+ *        M and N may be ragged.  No read leaves the M*3K/4 bytes of A, the
+ *        N*3K/4 bytes of B or the scale arrays.
  * Errors: SG_ERR_NULL, SG_ERR_ALIGN, SG_ERR_SHAPE (K % 128 != 0 or
  * extents), SG_ERR_DTYPE (fmt or d_dtype), SG_ERR_HIP.
  */
