@@ -1,5 +1,7 @@
 // deep64.h -- 64x64 tiles with an eight-stage LDS ring, for GEMMs too small
-// to give every CU more than one tile (M = N = K = 1024 is 256 such tiles).
+// to give every CU more than one tile (M = N = K = 1024 is 256 such tiles),
+// and 128x128 tiles (K-major operands) with a five-stage ring, for GEMMs
+// with fewer than 256 tiles of 256x256 (M = N = K = 2048 is 256 such tiles).
 //
 // Why.  Such a tile does 4 MFMAs per wave per 64-wide K tile, a few hundred
 // cycles, while a K tile's loads take a load latency (around a microsecond
@@ -17,28 +19,33 @@
 // reads, and the rotation puts the rows k and k+8 that the two lane halves
 // read in the same instruction on different banks.
 //
-// Waves.  Four waves in a 2x2 grid, one 32x32 accumulator each (the
-// GemmTile<64, 64> layout, whose epilogue this tile uses).  Every wave
-// issues four of a K tile's sixteen 1 KiB direct-to-LDS loads; a barrier
-// before each K tile makes all of them visible and frees the slot the
-// tile's successor loads go to.
+// Waves.  Four waves in a 2x2 grid, one (64x64 tiles) or 2x2 (128x128) 32x32
+// accumulators each (the GemmTile layout, whose epilogue this tile uses).
+// Every wave issues a quarter of a K tile's 1 KiB direct-to-LDS loads; a
+// barrier before each K tile makes all of them visible and frees the stage
+// the next loads go to.
 #pragma once
 
 #include "pingpong.h"
 
 namespace sg {
 
-template <bool IsBF16, bool AMn, bool BMn>
-struct Deep64Tile {
-  using Base = GemmTile<64, 64, IsBF16, AMn, BMn, kSwzDefault, 4>;
-  static constexpr int kStages = 8;
+template <int BM, bool IsBF16, bool AMn, bool BMn>
+struct DeepTile {
+  static_assert(BM == 64 || (BM == 128 && !AMn && !BMn),
+                "128x128 tiles take K-major operands only");
+  using Base = GemmTile<BM, BM, IsBF16, AMn, BMn, kSwzDefault, 4>;
+  static constexpr int kFM = Base::kFM, kFN = Base::kFN;   // 32x32 blocks per wave
+  static constexpr int kStages = BM == 64 ? 8 : 5;
   static constexpr int kBK = 64;
-  static constexpr int kOpBytes = 64 * 128;                // one operand's K tile
+  static constexpr int kOpBytes = BM * 128;                // one operand's K tile
   static constexpr int kStageBytes = 2 * kOpBytes;         // A, then B
-  static constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
-  // A wave's loads newer than those of K tile t (t+1) at the first wait
-  // (in the loop).
-  static_assert((kStages - 2) * 4 == 24 && (kStages - 3) * 4 == 20, "vmcnt immediates");
+  static constexpr int kLdsBytes = kStages * kStageBytes;  // 128 or 160 KiB
+  static constexpr int kLoads = 2 * (BM / 32);             // a wave's loads per K tile
+  // A wave's loads newer than those of K tile 0 at the first wait, and than
+  // those of K tile t+1 in iteration t.
+  static constexpr int kFirst = (kStages - 2) * kLoads, kLoop = (kStages - 3) * kLoads;
+  static_assert(kFirst == 24 && (kLoop == 20 || kLoop == 16), "vmcnt immediates");
 
   // Byte offset, in an MN-major operand's stage, of byte `byte` of k-row k.
   __device__ __forceinline__ static uint32_t bmn_offset(uint32_t k, uint32_t byte) {
@@ -69,7 +76,7 @@ struct Deep64Tile {
                         int rows_valid, uint32_t dst, int t) {
       if constexpr (!decltype(mn)::value) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < BM / 32; ++i)
           ld.issue(rsrc, dst, wave, i, rows_valid, (uint32_t)t * 128u, kbytes);
       } else {
 #pragma unroll
@@ -91,12 +98,15 @@ struct Deep64Tile {
     };
 
     const typename Base::FragOffsets o = Base::frag_offsets(wm, wn, lrow, lhalf);
-    f32x16 acc[1][1];
-    acc[0][0] = f32x16{};
+    f32x16 acc[kFM][kFN];
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int k = 0; k < kFN; ++k) acc[i][k] = f32x16{};
 
     // The fragments of one K tile: four 16-wide steps of A and B.
     struct Frags {
-      u32x4 a[kBK / 16], b[kBK / 16];
+      u32x4 a[kBK / 16][kFM], b[kBK / 16][kFN];
     };
     // An MN-major operand's fragment: k = 16 kk + 8 h + e (e = 0..7) of
     // column `col` (m or n), two bytes at a time.
@@ -117,14 +127,20 @@ struct Deep64Tile {
       const char* bs = as + kOpBytes;
 #pragma unroll
       for (int kk = 0; kk < kBK / 16; ++kk) {
-        if constexpr (!AMn)
-          f.a[kk] = lds_read16(as, o.a[kk]);
-        else
-          f.a[kk] = gather(as, wm * 32 + lrow, kk);
-        if constexpr (!BMn)
-          f.b[kk] = lds_read16(bs, o.b[kk]);
-        else
-          f.b[kk] = gather(bs, wn * 32 + lrow, kk);
+#pragma unroll
+        for (int fm = 0; fm < kFM; ++fm) {
+          if constexpr (!AMn)
+            f.a[kk][fm] = lds_read16(as, o.a[kk] + fm * 32 * 128);
+          else
+            f.a[kk][fm] = gather(as, wm * 32 + lrow, kk);
+        }
+#pragma unroll
+        for (int fn = 0; fn < kFN; ++fn) {
+          if constexpr (!BMn)
+            f.b[kk][fn] = lds_read16(bs, o.b[kk] + fn * 32 * 128);
+          else
+            f.b[kk][fn] = gather(bs, wn * 32 + lrow, kk);
+        }
       }
     };
 
@@ -133,21 +149,30 @@ struct Deep64Tile {
 
     // Software pipelined: the fragments of K tile t+1 are read while the
     // MFMAs of tile t run.  Before iteration t the wave waits for its loads
-    // of tile t+1 (the 20 newer ones may stay in flight); the barrier makes
-    // every wave's loads of t+1 visible and frees the stage of tile t-1,
-    // whose fragments were read in iteration t-2, for the loads of t+7.
+    // of tile t+1 (the kLoop newer ones may stay in flight); the barrier
+    // makes every wave's loads of t+1 visible and frees the stage of tile
+    // t-1, whose fragments were read in iteration t-2, for the loads of tile
+    // t + kStages - 1.
     Frags f0, f1;
     asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
     PingPongTile<IsBF16, kSwzDefault>::barrier();
     read(f0, 0);
     auto iteration = [&](int t, Frags& cur, Frags& nxt) {
-      asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)" ::: "memory");
+      if constexpr (kLoop == 20)
+        asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
       PingPongTile<IsBF16, kSwzDefault>::barrier();
       issue(t + kStages - 1);
       read(nxt, t + 1);  // past the last tile: stale LDS, never used
 #pragma unroll
       for (int kk = 0; kk < kBK / 16; ++kk)
-        acc[0][0] = mfma32x32x16<IsBF16>(cur.b[kk], cur.a[kk], acc[0][0]);
+#pragma unroll
+        for (int m = 0; m < kFM * kFN; ++m) {
+          // snake order: consecutive MFMAs share an operand
+          const int fm = m / kFN, fn = (fm & 1) ? kFN - 1 - m % kFN : m % kFN;
+          acc[fm][fn] = mfma32x32x16<IsBF16>(cur.b[kk][fn], cur.a[kk][fm], acc[fm][fn]);
+        }
     };
     int t = 0;
     for (; t + 1 < T; t += 2) {
@@ -161,11 +186,11 @@ struct Deep64Tile {
   }
 };
 
-template <bool IsBF16, bool AMn, bool BMn>
-__global__ void __launch_bounds__(256, 1) deep64_gemm_kernel(const DenseParams p) {
-  using Tile = Deep64Tile<IsBF16, AMn, BMn>;
+template <int BM, bool IsBF16, bool AMn, bool BMn>
+__global__ void __launch_bounds__(256, 1) deep_gemm_kernel(const DenseParams p) {
+  using Tile = DeepTile<BM, IsBF16, AMn, BMn>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
-  const TileJob j = dense_tile_job<64, 64, AMn, BMn>(p, blockIdx.x);
+  const TileJob j = dense_tile_job<BM, BM, AMn, BMn>(p, blockIdx.x);
   Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.ldd);
 }
 

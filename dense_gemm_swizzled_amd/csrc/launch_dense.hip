@@ -42,22 +42,43 @@ hipError_t go_pingpong32(const DenseParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 64x64 tiles run the eight-stage ring.
-template <bool BF, bool AMn, bool BMn>
-hipError_t go_deep64(const DenseParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((deep64_gemm_kernel<BF, AMn, BMn>), dim3(p.tiles_m * p.tiles_n), dim3(256),
-                     0, s, p);
+// 64x64 tiles run the eight-stage ring, 128x128 tiles with K-major operands
+// the five-stage one.
+template <int BM, bool BF, bool AMn, bool BMn>
+hipError_t go_deep(const DenseParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((deep_gemm_kernel<BM, BF, AMn, BMn>), dim3(p.tiles_m * p.tiles_n),
+                     dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device; a race only
+// repeats the query).
+int device_cus() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cache[dev] = cus;
+  }
+  return cache[dev];
 }
 
 template <int BM, int BN, bool BF, int Swz>
 hipError_t dense_by_major(bool a_mn, bool b_mn, const DenseParams& p, hipStream_t s) {
   if (BM == 64) {
-    if (a_mn) return b_mn ? go_deep64<BF, true, true>(p, s) : go_deep64<BF, true, false>(p, s);
-    return b_mn ? go_deep64<BF, false, true>(p, s) : go_deep64<BF, false, false>(p, s);
+    if (a_mn) return b_mn ? go_deep<64, BF, true, true>(p, s) : go_deep<64, BF, true, false>(p, s);
+    return b_mn ? go_deep<64, BF, false, true>(p, s) : go_deep<64, BF, false, false>(p, s);
   }
-  if (!a_mn && !b_mn)
-    return BM == 256 ? go_pingpong<BF, Swz>(p, s) : go_dense<BM, BN, BF, false, false, Swz>(p, s);
+  if (!a_mn && !b_mn) {
+    if (BM == 256) return go_pingpong<BF, Swz>(p, s);
+    // 128x128: the five-stage ring (160 KiB, one workgroup per CU) while the
+    // tiles fit in one round of the CUs; beyond that the two-stage kernel
+    // (64 KiB, two workgroups per CU) keeps more of them in flight.
+    if ((int64_t)p.tiles_m * p.tiles_n <= device_cus()) return go_deep<128, BF, false, false>(p, s);
+    return go_dense<BM, BN, BF, false, false, Swz>(p, s);
+  }
   if (!a_mn && b_mn) return go_dense<BM, BN, BF, false, true, Swz>(p, s);
   if (a_mn && !b_mn) return go_dense<BM, BN, BF, true, false, Swz>(p, s);
   return go_dense<BM, BN, BF, true, true, Swz>(p, s);

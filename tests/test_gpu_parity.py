@@ -146,6 +146,25 @@ def test_dense_128_tiles_ragged(dev, a_major, b_major):
     check_close(_np(d), ref, bound, "f32", "128 tiles")
 
 
+@pytest.mark.parametrize("tiles", ["64", "128", "128x2"])
+def test_dense_deep_ring_integer_exact(dev, tiles):
+    # Integer values in [-4, 4] over K = 1000 (16 K tiles, the last partial):
+    # every partial sum is exact in fp32, so the result must be bit-exact.
+    # The K tiles go round the 64x64 kernel's eight stages twice and the
+    # 128x128 kernel's five stages three times; with more 128x128 tiles than
+    # one round of CUs ("128x2": 552 tiles) the two-stage kernel runs.
+    M, N = {"64": (520, 392), "128": (1800, 1800), "128x2": (3000, 2900)}[tiles]
+    K = 1000
+    a = si.integer_valued((M, K), 95)
+    b = si.integer_valued((N, K), 96)
+    A, B = si.to_bf16(a), si.to_bf16(b)
+    say(f"integer-valued exact, {tiles}-tile deep ring {M}x{N}x{K}")
+    d = sg.gemm(A.to(dev), B.to(dev), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = a.astype(np.int64) @ b.astype(np.int64).T
+    assert np.array_equal(d.cpu().numpy().astype(np.int64), want)
+
+
 @pytest.mark.parametrize("c_dtype,d_dtype", [(None, "bf16"), ("bf16", "bf16"),
                                              ("f16", "f16"), ("f32", "bf16"),
                                              ("bf16", "f32")])
