@@ -9,8 +9,9 @@ Two layers:
 * ``gemm_run``, ``gemm_strided_run``, ``grouped_gemm_run``, ``mx_gemm_run``,
   ``mxfp4_gemm_run``, ``mxfp6_gemm_run``, ``gemm_layout_run``,
   ``gemm_layout128_run``, ``gemm_last_error``, ``gemm_version``,
-  ``gemm_lds_layout``, ``gemm_lds_layout_mxfp6``, ``gemm_lds_image``: the C
-  entry points under the same names, taking integer device pointers.
+  ``gemm_lds_layout``, ``gemm_lds_layout_mxfp6``, ``gemm_lds_layout_cblock``,
+  ``gemm_lds_image``: the C entry points under the same names, taking integer
+  device pointers.
 * ``gemm``, ``gemm_strided``, ``grouped_gemm``, ``mx_gemm``, ``mxfp4_gemm``,
   ``mxfp6_gemm``, ``gemm_layout``, ``gemm_layout128``: the same calls on torch CUDA
   tensors (shapes read from the tensors, output allocated by torch, launched
@@ -29,7 +30,8 @@ __all__ = [
     "SG_K_MAJOR", "SG_MN_MAJOR", "SG_MAX_GROUPS", "GemmError",
     "gemm_run", "gemm_strided_run", "grouped_gemm_run", "mx_gemm_run", "mxfp4_gemm_run",
     "mxfp6_gemm_run", "gemm_layout_run", "gemm_layout128_run", "gemm_last_error",
-    "gemm_version", "gemm_lds_layout", "gemm_lds_layout_mxfp6", "gemm_lds_image",
+    "gemm_version", "gemm_lds_layout", "gemm_lds_layout_mxfp6", "gemm_lds_layout_cblock",
+    "gemm_lds_image",
     "SG_E2M3", "SG_E3M2",
     "gemm", "gemm_plan", "gemm_strided", "grouped_gemm", "mx_gemm", "mxfp4_gemm", "mxfp6_gemm",
     "gemm_layout",
@@ -86,11 +88,13 @@ def load():
     lib.gemm_layout128_run.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, vp, i32, vp]
     lib.gemm_lds_layout.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int32)]
     lib.gemm_lds_layout_mxfp6.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int32)]
+    lib.gemm_lds_layout_cblock.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     lib.gemm_lds_image.argtypes = [vp, i64, i64, i32, i64, i64, i32, vp, vp]
     for f in (lib.gemm_run, lib.gemm_strided_run, lib.grouped_gemm_run, lib.mx_gemm_run,
               lib.mxfp4_gemm_run, lib.mxfp6_gemm_run,
               lib.gemm_layout_run, lib.gemm_layout128_run,
-              lib.gemm_lds_layout, lib.gemm_lds_layout_mxfp6, lib.gemm_lds_image):
+              lib.gemm_lds_layout, lib.gemm_lds_layout_mxfp6, lib.gemm_lds_layout_cblock,
+              lib.gemm_lds_image):
         f.restype = ctypes.c_int
     lib.gemm_last_error.argtypes = []
     lib.gemm_last_error.restype = ctypes.c_char_p
@@ -170,6 +174,17 @@ def gemm_lds_layout_mxfp6(rows: int, unshifted: int = 32) -> np.ndarray:
     if rc != SG_OK:
         raise GemmError(rc, gemm_last_error())
     return out[:-1].reshape(rows, 12)
+
+
+def gemm_lds_layout_cblock() -> np.ndarray:
+    """[4][128][8] LDS places of a 16-bit C in the 256x256 kernel's epilogue:
+    wave, row and 16-byte chunk of the wave's 128 x 64 block -> quarter *
+    16384 + byte offset inside that quarter's 16 KiB half slot."""
+    out = np.zeros(4 * 128 * 8, dtype=np.int32)
+    rc = load().gemm_lds_layout_cblock(out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    if rc != SG_OK:
+        raise GemmError(rc, gemm_last_error())
+    return out.reshape(4, 128, 8)
 
 
 def gemm_lds_image(X, rows_total, K, elem_bytes, row0, k0, tile_rows, out,

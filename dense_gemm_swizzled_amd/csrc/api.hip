@@ -119,6 +119,9 @@ int dense_run(const char* who, DenseMode mode, int swz, int64_t M, int64_t N, in
                 "%s: a leading dimension is below its minimum (lda %lld, ldb %lld, ldc %lld, "
                 "ldd %lld)", who, (long long)lda, (long long)ldb, (long long)ldc,
                 (long long)ldd);
+  if (N % 4)
+    return fail(SG_ERR_SHAPE, "%s: N=%lld is not a multiple of 4 (D is written 4 columns at "
+                              "a time)", who, (long long)N);
   if (M == 0 || N == 0) return ok();
   if (!D) return fail(SG_ERR_NULL, "%s: D is NULL", who);
   // alpha == 0: A and B are not read; beta == 0: C is not read.
@@ -438,6 +441,15 @@ int gemm_lds_layout_mxfp6(int rows, int unshifted, int32_t* out) {
   for (int r = 0; r < rows; ++r)
     for (int q = 0; q < 12; ++q)
       out[r * 12 + q] = (int32_t)sg::mxfp6_lds_offset(r, 8u * q, (uint32_t)unshifted);
+  return ok();
+}
+
+int gemm_lds_layout_cblock(int32_t* out) {
+  if (!out) return fail(SG_ERR_NULL, "gemm_lds_layout_cblock: out is NULL");
+  for (int w = 0; w < 4; ++w)
+    for (int r = 0; r < 128; ++r)
+      for (int c = 0; c < 8; ++c)
+        out[(w * 128 + r) * 8 + c] = (int32_t)sg::cblock_lds_offset(w, r, c);
   return ok();
 }
 

@@ -99,4 +99,20 @@ SG_HD uint32_t mxfp6_lds_offset(uint32_t row, uint32_t byte, uint32_t unshifted)
   return lds_offset<128, kSwzDefault>(row, b >> 4) + (b & 15u);
 }
 
+// The C block that the 256x256 kernel of 16x16x32 MFMAs brings into LDS
+// through the loads of its last two K tiles (a 16-bit C): wave w4 of a
+// group owns 128 output rows x 64 columns, and row r, 16-byte chunk c (8
+// columns) of that block lies in quarter r / 32, one 16 KiB half slot of the
+// operand rings, in the wave's 1 KiB region 4((r / 8) mod 4) + w4, where a
+// direct-to-LDS load puts lane l's 16 bytes at byte 16 l: row r mod 8 (128
+// bytes), chunk c XOR cblock_key(r).  The key spreads the 16 rows that one
+// 8-byte epilogue read covers (rows R..R+15, one chunk half) over the 16
+// chunk positions of a 256-byte bank line, so 32 lanes touch 64 banks once.
+// Returns quarter * 16384 + the offset inside the quarter's half slot.
+SG_HD constexpr uint32_t cblock_key(uint32_t r) { return (r >> 1) & 7u; }
+SG_HD constexpr uint32_t cblock_lds_offset(uint32_t w4, uint32_t r, uint32_t c) {
+  return (r >> 5) * 16384u + (4u * ((r >> 3) & 3u) + w4) * 1024u + (r & 7u) * 128u +
+         16u * (c ^ cblock_key(r));
+}
+
 }  // namespace sg

@@ -111,37 +111,174 @@ struct PingPong16Tile {
     }
   }
 
-  // Mainloop for K a multiple of 64: the K tiles t+2 >= T load through the
-  // empty descriptors `ra0`, `rb0`.
-  template <bool Active>
-  __device__ __forceinline__ static void mainloop_x(f32x4 (&acc)[kI][kJ],
-                                                    const KExactHalfLoader<Swz>& la,
-                                                    const KExactHalfLoader<Swz>& lb, u32x4 ra,
-                                                    u32x4 rb, u32x4 ra0, u32x4 rb0,
-                                                    uint32_t a_ring, uint32_t b_ring,
-                                                    const char* a_rd, const char* b_rd,
-                                                    const Offsets& o, int g, int w4, int T) {
+  // The wait and barrier that end a phase: the wave's loads older than its
+  // newest N have landed in LDS and its fragment reads are done.
+  template <int N>
+  __device__ __forceinline__ static void end_phase() {
+    static_assert(N == 8 || N == 12 || N == 16, "vmcnt immediate");
+    if constexpr (N == 8)
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    else if constexpr (N == 12)
+      asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+    PP::barrier();
+  }
+
+  // One K tile t of the mainloop: the loads of phase 2 go through `xb`,
+  // `rbt` with SGPR offset `sb` into B slot (t+2) mod 3, those of phase 4
+  // through `xa`, `rat`, `sa` into A slot t mod 2 (which held tile t).
+  // W1..W4: the vmcnt of the four phase-ending waits.
+  template <bool Active, int W1, int W2, int W3, int W4>
+  __device__ __forceinline__ static void ktile(f32x4 (&acc)[kI][kJ], int t, int bs,
+                                               const KExactHalfLoader<Swz>& xb, u32x4 rbt,
+                                               uint32_t sb, const KExactHalfLoader<Swz>& xa,
+                                               u32x4 rat, uint32_t sa, uint32_t a_ring,
+                                               uint32_t b_ring, const char* a_rd,
+                                               const char* b_rd, const Offsets& o, int w4) {
+    const int as = t & 1, bs2 = bs == 0 ? 2 : bs - 1;  // (t+2) mod 2, (t+2) mod 3
+    const char* at = a_rd + as * kTileBytes;
+    const char* bt = b_rd + bs * kTileBytes;
+    Frags f;
+    if constexpr (Active) read(f, at, bt, o, 0);
+    end_phase<W1>();
+    compute_x<Active>(acc, f, xb, rbt, b_ring + bs2 * kTileBytes, w4, sb);
+    end_phase<W2>();
+    if constexpr (Active) read(f, at, bt, o, 1);
+    end_phase<W3>();
+    compute_x<Active>(acc, f, xa, rat, a_ring + as * kTileBytes, w4, sa);
+    end_phase<W4>();
+  }
+
+  // Where the last two K tiles' loads put a 16-bit C.  Those loads would
+  // fetch the zero tiles T and T+1; instead, wave w4 of group g brings the C
+  // block of its own outputs (128 rows x 64 columns, 16 KiB) into the four
+  // half slots they fill, quarter Q (rows 32Q..32Q+31 of the block) into B
+  // slot T mod 3, A slot T mod 2, B slot (T+1) mod 3, A slot (T+1) mod 2 for
+  // Q = 0..3, half g, laid out by cblock_lds_offset: load q of the quarter
+  // fills region 4q + w4 with rows 32Q + 8q .. +7, lane l taking row l / 8
+  // of them and the chunk whose place is l mod 8.
+  struct CBlock {
+    u32x4 rsrc;      // C from row d_row0 + 128g, column n0 of the tile
+    uint32_t pitch;  // bytes per C row
+    int rows;        // C rows of the block that exist
+    int lrow;        // this lane's row inside a 1 KiB region (0..7)
+    uint32_t col[4]; // this lane's byte offset in a row, for region 4q + w4
+
+    __device__ __forceinline__ void init(const TileJob& j, const void* C, int g, int w4,
+                                         int lane) {
+      const int64_t row0 = j.d_row0 + 128 * g;
+      rows = min(j.m_valid - 128 * g, 128);
+      pitch = (uint32_t)j.ldc * 2u;
+      // Records up to the 16-byte chunk holding the tile's last valid element
+      // of its last valid row (the base is 16-byte aligned, so that chunk
+      // never crosses a page C does not touch); chunks past it read as zero.
+      const uint32_t bytes =
+          rows > 0 ? (uint32_t)(rows - 1) * pitch + (((uint32_t)j.n_valid * 2u + 15u) & ~15u)
+                   : 0u;
+      rsrc = rsrc_words(static_cast<const char*>(C) + (row0 * j.ldc + j.n0) * 2, bytes);
+      lrow = lane >> 3;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)  // (the key of row 32Q + r is that of r)
+        col[q] = 128u * (uint32_t)w4 +
+                 16u * ((uint32_t)(lane & 7) ^ cblock_key((uint32_t)(8 * q + lrow)));
+    }
+    // The loader of quarter Q: rows past the block read as zero.
+    __device__ __forceinline__ KExactHalfLoader<Swz> quarter(int Q) const {
+      KExactHalfLoader<Swz> x;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 32 * Q + 8 * q + lrow;
+        x.voff[q] = r < rows ? (uint32_t)r * pitch + col[q] : kOutOfRange;
+      }
+      return x;
+    }
+  };
+
+  // Mainloop for K a multiple of 64.  The K tiles t+2 >= T load zeros through
+  // the empty descriptors `ra0`, `rb0`, or (LdsC, T >= 2) the wave's C block.
+  // Once K tile T-1's operands have landed (the wait ending K tile T-2), only
+  // C loads are in flight, so the waits of the last K tile leave them be.
+  template <bool Active, bool LdsC>
+  __device__ __forceinline__ static void mainloop_x(
+      f32x4 (&acc)[kI][kJ], const KExactHalfLoader<Swz>& la, const KExactHalfLoader<Swz>& lb,
+      u32x4 ra, u32x4 rb, u32x4 ra0, u32x4 rb0, uint32_t a_ring, uint32_t b_ring,
+      const char* a_rd, const char* b_rd, const Offsets& o, int g, int w4, int T,
+      const TileJob& j, const void* C, int lane) {
     if (g) PP::barrier();  // group 1 runs one phase behind group 0
     int bs = 0;            // t mod 3
-    for (int t = 0; t < T; ++t) {
-      const int as = t & 1, bs2 = bs == 0 ? 2 : bs - 1;  // (t+2) mod 2, (t+2) mod 3
-      const char* at = a_rd + as * kTileBytes;
-      const char* bt = b_rd + bs * kTileBytes;
+    int t = 0;
+    for (; t + 2 < T; ++t) {
       const uint32_t k2 = (uint32_t)(t + 2) * 128u;
-      const bool in_k = t + 2 < T;
-      const u32x4 rat = in_k ? ra : ra0, rbt = in_k ? rb : rb0;
-      Frags f;
-      if constexpr (Active) read(f, at, bt, o, 0);
-      PP::end_phase();
-      compute_x<Active>(acc, f, lb, rbt, b_ring + bs2 * kTileBytes, w4, k2);
-      PP::end_phase();
-      if constexpr (Active) read(f, at, bt, o, 1);
-      PP::end_phase();
-      compute_x<Active>(acc, f, la, rat, a_ring + as * kTileBytes, w4, k2);
-      PP::end_phase();
+      ktile<Active, 8, 8, 8, 8>(acc, t, bs, lb, rb, k2, la, ra, k2, a_ring, b_ring, a_rd, b_rd,
+                                o, w4);
       bs = bs == 2 ? 0 : bs + 1;
     }
+    if constexpr (LdsC) {
+      CBlock cb;
+      cb.init(j, C, g, w4, lane);
+      ktile<Active, 8, 8, 8, 8>(acc, t, bs, cb.quarter(0), cb.rsrc, 0u, cb.quarter(1), cb.rsrc,
+                                0u, a_ring, b_ring, a_rd, b_rd, o, w4);
+      bs = bs == 2 ? 0 : bs + 1;
+      ktile<Active, 8, 12, 12, 16>(acc, t + 1, bs, cb.quarter(2), cb.rsrc, 0u, cb.quarter(3),
+                                   cb.rsrc, 0u, a_ring, b_ring, a_rd, b_rd, o, w4);
+    } else {
+      for (; t < T; ++t) {
+        const uint32_t k2 = (uint32_t)(t + 2) * 128u;
+        ktile<Active, 8, 8, 8, 8>(acc, t, bs, lb, rb0, k2, la, ra0, k2, a_ring, b_ring, a_rd,
+                                  b_rd, o, w4);
+        bs = bs == 2 ? 0 : bs + 1;
+      }
+    }
     if (!g) PP::barrier();
+  }
+
+  // The epilogue with the C block in LDS (16-bit C): lane l of accumulator
+  // block (i, jn) reads C row 16i + l%16 of the block, columns 16jn +
+  // 4(l/16) .. +3: half (l/16) mod 2 of chunk 2jn + l/32.
+  template <int CD, int DD>
+  __device__ __forceinline__ static void epilogue_ldsc_t(const f32x4 (&acc)[kI][kJ],
+                                                         const TileJob& j,
+                                                         const char* const (&cq)[4], void* D,
+                                                         int64_t ldd, int lane, int g, int w4) {
+    u32x2 c[kI][kJ];
+#pragma unroll
+    for (int i = 0; i < kI; ++i)
+#pragma unroll
+      for (int jn = 0; jn < kJ; ++jn) {
+        const uint32_t r = (uint32_t)(16 * i + (lane & 15));
+        const uint32_t off = cblock_lds_offset((uint32_t)w4, r, (uint32_t)(2 * jn + (lane >> 5)));
+        c[i][jn] = lds_read8(cq[i >> 1], (off & 16383u) + 8u * (uint32_t)((lane >> 4) & 1));
+      }
+#pragma unroll
+    for (int i = 0; i < kI; ++i) {
+      const int ml = 128 * g + 16 * i + (lane & 15);
+      if (ml >= j.m_valid) continue;
+      const int64_t row = (j.d_row0 + ml) * ldd + j.n0;
+#pragma unroll
+      for (int jn = 0; jn < kJ; ++jn) {
+        const int nl = 64 * w4 + 16 * jn + 4 * (lane >> 4);
+        if (nl >= j.n_valid) continue;
+        store_d_chunk<CD, DD>(acc[i][jn], c[i][jn], D, row + nl, j.alpha, j.beta);
+      }
+    }
+  }
+
+  __device__ __forceinline__ static void epilogue_ldsc(const f32x4 (&acc)[kI][kJ],
+                                                       const TileJob& j,
+                                                       const char* const (&cq)[4], int c_dtype,
+                                                       void* D, int d_dtype, int64_t ldd,
+                                                       int lane, int g, int w4) {
+#define SG_EPI(CD, DD) return epilogue_ldsc_t<CD, DD>(acc, j, cq, D, ldd, lane, g, w4)
+    if (c_dtype == SG_BF16) {
+      if (d_dtype == SG_F32) SG_EPI(SG_BF16, SG_F32);
+      if (d_dtype == SG_BF16) SG_EPI(SG_BF16, SG_BF16);
+      SG_EPI(SG_BF16, SG_F16);
+    }
+    if (d_dtype == SG_F32) SG_EPI(SG_F16, SG_F32);
+    if (d_dtype == SG_BF16) SG_EPI(SG_F16, SG_BF16);
+    SG_EPI(SG_F16, SG_F16);
+#undef SG_EPI
   }
 
   template <bool Active>
@@ -220,16 +357,25 @@ struct PingPong16Tile {
 
     // A wave whose 128 output rows all lie past M (the second group of a tile
     // with at most 128 valid rows) runs the mainloop without its MFMAs.
-    if ((K & (kBK - 1)) == 0) {
+    // A 16-bit C comes in through the last two K tiles' loads when K is a
+    // multiple of 64 and 128 C rows stay within 32-bit buffer offsets.
+    const bool kexact = (K & (kBK - 1)) == 0;
+    const bool ldsc = kexact && T >= 2 && C != nullptr &&
+                      (c_dtype == SG_BF16 || c_dtype == SG_F16) && j.ldc <= (int64_t{1} << 22);
+    if (kexact) {
       KExactHalfLoader<Swz> xa, xb;
       xa.init(la, a_rows);
       xb.init(lb, b_rows);
       const u32x4 ra0 = rsrc_words(j.a, 0), rb0 = rsrc_words(j.b, 0);
-      if (a_rows > 0)
-        mainloop_x<true>(acc, xa, xb, ra, rb, ra0, rb0, a_ring, b_ring, a_rd, b_rd, o, g, w4, T);
+      if (a_rows > 0 && ldsc)
+        mainloop_x<true, true>(acc, xa, xb, ra, rb, ra0, rb0, a_ring, b_ring, a_rd, b_rd, o, g,
+                               w4, T, j, C, lane);
+      else if (a_rows > 0)
+        mainloop_x<true, false>(acc, xa, xb, ra, rb, ra0, rb0, a_ring, b_ring, a_rd, b_rd, o, g,
+                                w4, T, j, C, lane);
       else
-        mainloop_x<false>(acc, xa, xb, ra, rb, ra0, rb0, a_ring, b_ring, a_rd, b_rd, o, g, w4,
-                          T);
+        mainloop_x<false, false>(acc, xa, xb, ra, rb, ra0, rb0, a_ring, b_ring, a_rd, b_rd, o,
+                                 g, w4, T, j, C, lane);
     } else if (a_rows > 0) {
       mainloop<true>(acc, la, lb, ra, rb, a_rows, b_rows, a_ring, b_ring, a_rd, b_rd, o, g, w4,
                      T, kbytes);
@@ -237,9 +383,19 @@ struct PingPong16Tile {
       mainloop<false>(acc, la, lb, ra, rb, a_rows, b_rows, a_ring, b_ring, a_rd, b_rd, o, g,
                       w4, T, kbytes);
     }
-    wait_vmem();  // the zero-filled loads past K
+    wait_vmem();  // the C block, or the zero-filled loads past K
 
-    epilogue16<kI, kJ>(acc, j, C, c_dtype, D, d_dtype, ldd, lane, 128 * g, 64 * w4);
+    if (ldsc) {
+      PP::barrier();
+      const int tb = T % 3, ta = T & 1;
+      const char* const cq[4] = {b_rd + tb * kTileBytes + g * kHalfBytes,
+                                 a_rd + ta * kTileBytes + g * kHalfBytes,
+                                 b_rd + (tb == 2 ? 0 : tb + 1) * kTileBytes + g * kHalfBytes,
+                                 a_rd + (ta ^ 1) * kTileBytes + g * kHalfBytes};
+      if (a_rows > 0) epilogue_ldsc(acc, j, cq, c_dtype, D, d_dtype, ldd, lane, g, w4);
+    } else {
+      epilogue16<kI, kJ>(acc, j, C, c_dtype, D, d_dtype, ldd, lane, 128 * g, 64 * w4);
+    }
   }
 };
 

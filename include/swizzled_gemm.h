@@ -107,7 +107,8 @@ int gemm_run(int64_t M, int64_t N, int64_t K, const void* A, int a_major,
  *   must be a multiple of 16 bytes and every pointer 16-byte aligned.  C may
  *   equal D when c_dtype == d_dtype and ldc == ldd.  The other arguments and
  *   the errors are gemm_run's, plus SG_ERR_SHAPE for a leading dimension below
- *   its minimum.
+ *   its minimum or an N that is not a multiple of 4 (the epilogue writes D
+ *   four columns at a time; gemm_run's packed rows already imply it).
  */
 int gemm_strided_run(int64_t M, int64_t N, int64_t K, float alpha, const void* A,
                      int64_t lda, int a_major, const void* B, int64_t ldb, int b_major,
@@ -263,6 +264,21 @@ int gemm_lds_layout(int rows, int row_bytes, int32_t* out);
  * Returns SG_OK, SG_ERR_NULL or SG_ERR_SHAPE.
  */
 int gemm_lds_layout_mxfp6(int rows, int unshifted, int32_t* out);
+
+/*
+ * gemm_lds_layout_cblock -- where the 256x256 bf16/fp16 kernel keeps a
+ * 16-bit C in LDS for its epilogue (host-side, no GPU needed).  That kernel
+ * reads C (the "+C" of the GEMM) through the loads of its last two K tiles,
+ * which would otherwise fetch zeros past K, into the four half-tile ring
+ * slots those loads fill.  Writes out[(w * 128 + r) * 8 + c], for wave
+ * w < 4 of a 128-row group, row r < 128 and 16-byte chunk c < 8 of that
+ * wave's 128 x 64 block of C: quarter r / 32 (which slot) times 16384 plus
+ * the byte offset inside the slot's 16 KiB half.  The placement is an XOR
+ * of the chunk index with a row key, the same construction as the operand
+ * swizzle ("Swizzling explained properly", section "What does swizzling
+ * do?"), chosen for 8-byte epilogue reads.  Returns SG_OK or SG_ERR_NULL.
+ */
+int gemm_lds_layout_cblock(int32_t* out);
 
 /*
  * gemm_lds_image -- runs the kernels' global->LDS loader once for one operand

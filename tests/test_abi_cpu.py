@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     assert {"gemm_run", "gemm_strided_run", "grouped_gemm_run", "mx_gemm_run", "mxfp4_gemm_run",
             "mxfp6_gemm_run", "gemm_layout_run", "gemm_layout128_run",
             "gemm_last_error", "gemm_version", "gemm_lds_layout", "gemm_lds_layout_mxfp6",
-            "gemm_lds_image"} <= set(names)
+            "gemm_lds_layout_cblock", "gemm_lds_image"} <= set(names)
     lib = ctypes.CDLL(sg.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -71,6 +71,7 @@ def _strided(**kw):
     (dict(C=P + 8192, c_dtype=sg.SG_BF16, ldc=268), ALIGN),
     (dict(C=P, c_dtype=sg.SG_F32, ldc=272), DTYPE),  # in place needs ldc == ldd
     (dict(A=None), NULL), (dict(M=-1), SHAPE), (dict(a_major=7), MAJOR),
+    (dict(N=262), SHAPE), (dict(N=261, M=0), SHAPE),  # D is written 4 columns at a time
 ])
 def test_gemm_strided_run_rejects(kw, code):
     rc = _strided(**kw)

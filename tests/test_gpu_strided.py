@@ -72,11 +72,13 @@ def _run(dev, M, N, K, a_major, b_major, ab, Abuf, lda, Bbuf, ldb, Cbuf, ldc, ld
 
 @pytest.mark.parametrize("a_major,b_major,ab", [("k", "k", "bf16"), ("mn", "k", "bf16"),
                                                 ("k", "mn", "f16"), ("mn", "mn", "bf16")])
-@pytest.mark.parametrize("M,N,K", [(300, 264, 136), (4100, 4104, 136), (4100, 4104, 192)])
+@pytest.mark.parametrize("M,N,K", [(300, 264, 136), (4100, 4104, 136), (4100, 4104, 192),
+                                   (300, 252, 136), (4100, 4108, 192)])
 def test_strided_scaled_parity(dev, a_major, b_major, ab, M, N, K):
     # 300 x 264: 128x128 tiles; 4100 x 4104 with K-major operands: the
     # 256x256 ping-pong, K = 136 on its checked loader, K = 192 on the
     # loader for K a multiple of 64 (MN-major operands use 128x128 tiles).
+    # N = 252 and 4108 leave 252 and 12 columns in the last tile column.
     Abuf, lda, Bbuf, ldb, Cbuf, ldc, ldd = _operands(M, N, K, a_major, b_major, ab, M + K)
     alpha, beta = 1.5, -0.75
     say(f"strided {M}x{N}x{K} {a_major}/{b_major} {ab} lda={lda} ldb={ldb} ldc={ldc} ldd={ldd}")
@@ -104,6 +106,36 @@ def test_strided_scaled_integer_exact(dev):
              "f32")
     want = 2 * (a @ b.T) - 3 * c
     assert np.array_equal(d.cpu().numpy().astype(np.int64), want)
+
+
+@pytest.mark.parametrize("K,c_dtype,d_dtype,alpha,beta", [
+    (128, "bf16", "f32", 1.0, 1.0),    # two K tiles: both carry C, no steady state
+    (192, "f16", "f32", 2.0, -3.0),
+    (512, "bf16", "bf16", 1.0, 1.0),
+    (256, "f16", "f16", 1.0, 0.5),
+    (64, "bf16", "f32", 1.0, 1.0),     # one K tile: C is read by the epilogue
+])
+def test_256_tiles_16bit_c_integer_exact(dev, K, c_dtype, d_dtype, alpha, beta):
+    # The 256x256 kernel brings a 16-bit C into LDS with the loads of its last
+    # two K tiles.  Ragged M (the last tile row has 4 rows, so its second wave
+    # group is idle) and N = 4108 (the last tile column has 12 columns, C rows
+    # padded with NaN past N): integers in [-4, 4] and C in [-8, 8] keep every
+    # sum and scaling exact in fp32, so D is the exact value rounded once.
+    M, N = 4100, 4108
+    rng = np.random.default_rng(K)
+    a = rng.integers(-4, 5, (M, K))
+    b = rng.integers(-4, 5, (N, K))
+    c = rng.integers(-8, 9, (M, N))
+    ldc, ldd = N + 20, N + 4   # 16-byte row pitches
+    Abuf = torch.from_numpy(a).to(torch.bfloat16)
+    Bbuf = torch.from_numpy(b).to(torch.bfloat16)
+    Cbuf = _padded(torch.from_numpy(c).to(DT[c_dtype]), ldc, float("nan"))
+    say(f"256 tiles, {c_dtype} C in LDS, {M}x{N}x{K} D={d_dtype} alpha={alpha} beta={beta}")
+    d = _run(dev, M, N, K, "k", "k", "bf16", Abuf, K, Bbuf, K, Cbuf, ldc, ldd, alpha, beta,
+             d_dtype)
+    exact = alpha * (a.astype(np.float64) @ b.astype(np.float64).T) + beta * c
+    want = torch.from_numpy(exact).to(torch.float32).to(DT[d_dtype])
+    assert torch.equal(d.cpu(), want)
 
 
 def test_alpha_zero_and_beta_zero_read_nothing(dev):

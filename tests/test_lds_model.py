@@ -194,6 +194,49 @@ def test_mxfp6_reads_without_the_shift_would_conflict(model):
     assert _degree(model, "r64", a) == 2
 
 
+def test_cblock_map_fits_the_loads_it_rides_on():
+    # The 256x256 kernel's C block: each wave's 128 x 8 chunks fill exactly
+    # its own 1 KiB regions 4q + w of the four 16 KiB quarters, and load q of
+    # quarter Q (lane l -> byte 16 l of region 4q + w) carries row 32Q + 8q +
+    # l/8 -- the rows the load's lanes are given.
+    m = sg.gemm_lds_layout_cblock()
+    flat = m.reshape(-1)
+    assert len(set(flat.tolist())) == flat.size and flat.min() >= 0 and flat.max() < 65536
+    assert (flat % 16 == 0).all()
+    for w in range(4):
+        for r in range(128):
+            for c in range(8):
+                off = int(m[w, r, c])
+                Q, inq = divmod(off, 16384)
+                region, byte = divmod(inq, 1024)
+                assert Q == r // 32 and region == 4 * ((r // 8) % 4) + w
+                assert byte // 128 == r % 8   # lane l = byte / 16 covers row l / 8
+    # every lane's 16 bytes receive exactly one chunk of the row it loads
+    for w in range(4):
+        for Q in range(4):
+            for q in range(4):
+                got = sorted(int(m[w, 32 * Q + 8 * q + l // 8, c]) % 1024
+                             for l in range(0, 64, 8) for c in range(8))
+                assert got == list(range(0, 1024, 16))
+
+
+def test_cblock_epilogue_reads_conflict_free(model):
+    # Lane l of accumulator block (i, jn) reads C row 16i + l%16, columns
+    # 16jn + 4(l/16) .. +3: 8 bytes at half (l/16)%2 of chunk 2jn + l/32.
+    m = sg.gemm_lds_layout_cblock()
+    worst = 0
+    for w in range(4):
+        for i in range(8):
+            for jn in range(4):
+                a = [int(m[w, 16 * i + l % 16, 2 * jn + l // 32]) + 8 * ((l // 16) % 2)
+                     for l in range(64)]
+                worst = max(worst, _degree(model, "r64", a))
+    assert worst == 1
+    # the same reads with the chunks left in place would conflict
+    a = [(l % 16) * 128 + 16 * (l // 32) + 8 * ((l // 16) % 2) for l in range(64)]
+    assert _degree(model, "r64", a) > 1
+
+
 def test_padded_layout_is_conflict_free(model):
     # The padded layout of the layout ablation (144-byte rows, no XOR): the
     # 32x32x16 fragment reads and the register-staged ds_write_b128 stores
