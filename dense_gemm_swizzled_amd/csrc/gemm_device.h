@@ -58,6 +58,9 @@ __device__ __forceinline__ u32x2 lds_read8(const char* lds, uint32_t off) {
   typedef const volatile __attribute__((address_space(3))) u32x2 lds_u32x2;
   return *(lds_u32x2*)(lds + off);
 }
+__device__ __forceinline__ void lds_write8(char* lds, uint32_t off, u32x2 v) {
+  *reinterpret_cast<u32x2*>(lds + off) = v;
+}
 __device__ __forceinline__ void lds_write16(char* lds, uint32_t off, u32x4 v) {
   *reinterpret_cast<u32x4*>(lds + off) = v;
 }

@@ -107,9 +107,10 @@ __device__ __forceinline__ c_chunk_t<CD> load_c_chunk(const void* C, int64_t idx
     return *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(C) + idx);
 }
 
-template <int CD, int DD>
-__device__ __forceinline__ void store_d_chunk(f32x4 v, const c_chunk_t<CD>& c, void* D,
-                                              int64_t idx, float alpha, float beta) {
+// alpha * acc + beta * C of one chunk, in fp32.
+template <int CD>
+__device__ __forceinline__ f32x4 epi_value(f32x4 v, const c_chunk_t<CD>& c, float alpha,
+                                           float beta) {
   if constexpr (CD != SG_NONE) {
     f32x4 cf;
     if constexpr (CD == SG_F32) {
@@ -128,19 +129,27 @@ __device__ __forceinline__ void store_d_chunk(f32x4 v, const c_chunk_t<CD>& c, v
   } else {
     v *= alpha;
   }
-  if constexpr (DD == SG_F32) {
+  return v;
+}
+
+// A chunk rounded to a 16-bit D type (round to nearest even).
+template <int DD>
+__device__ __forceinline__ u32x2 pack_d16(f32x4 v) {
+  static_assert(DD == SG_BF16 || DD == SG_F16, "16-bit D");
+  if constexpr (DD == SG_BF16)
+    return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  else
+    return u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+}
+
+template <int CD, int DD>
+__device__ __forceinline__ void store_d_chunk(f32x4 v, const c_chunk_t<CD>& c, void* D,
+                                              int64_t idx, float alpha, float beta) {
+  v = epi_value<CD>(v, c, alpha, beta);
+  if constexpr (DD == SG_F32)
     *reinterpret_cast<f32x4*>(static_cast<float*>(D) + idx) = v;
-  } else {
-    u32x2 o;
-    if constexpr (DD == SG_BF16) {
-      o[0] = pack_bf16x2(v[0], v[1]);
-      o[1] = pack_bf16x2(v[2], v[3]);
-    } else {
-      o[0] = pack_f16x2(v[0], v[1]);
-      o[1] = pack_f16x2(v[2], v[3]);
-    }
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(D) + idx) = o;
-  }
+  else
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(D) + idx) = pack_d16<DD>(v);
 }
 
 // Epilogue of a wave's NI x NJ blocks of 16x16 accumulators (v_mfma_f32_

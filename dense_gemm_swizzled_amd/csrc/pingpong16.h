@@ -233,51 +233,87 @@ struct PingPong16Tile {
     if (!g) PP::barrier();
   }
 
-  // The epilogue with the C block in LDS (16-bit C): lane l of accumulator
-  // block (i, jn) reads C row 16i + l%16 of the block, columns 16jn +
-  // 4(l/16) .. +3: half (l/16) mod 2 of chunk 2jn + l/32.
+  // The epilogue through the wave's C block area (cblock_lds_offset): lane l
+  // of accumulator block (i, jn) holds row 16i + l%16 of the block, columns
+  // 16jn + 4(l/16) .. +3, i.e. half (l/16) mod 2 of chunk 2jn + l/32.  A
+  // 16-bit C (CD) is read from there; a 16-bit D is written back there and
+  // then stored a whole 128-byte row segment per 8 lanes (row 8s + l/8,
+  // chunk l%8), 16 stores of 16 bytes instead of 32 of 8.  An fp32 D is
+  // stored from registers.
   template <int CD, int DD>
-  __device__ __forceinline__ static void epilogue_ldsc_t(const f32x4 (&acc)[kI][kJ],
-                                                         const TileJob& j,
-                                                         const char* const (&cq)[4], void* D,
-                                                         int64_t ldd, int lane, int g, int w4) {
+  __device__ __forceinline__ static void epilogue_lds_t(const f32x4 (&acc)[kI][kJ],
+                                                        const TileJob& j, char* const (&cq)[4],
+                                                        void* D, int64_t ldd, int lane, int g,
+                                                        int w4) {
+    auto place = [&](int i, int jn) {
+      const uint32_t r = (uint32_t)(16 * i + (lane & 15));
+      const uint32_t off = cblock_lds_offset((uint32_t)w4, r, (uint32_t)(2 * jn + (lane >> 5)));
+      return (off & 16383u) + 8u * (uint32_t)((lane >> 4) & 1);
+    };
     u32x2 c[kI][kJ];
+    if constexpr (CD != SG_NONE) {
 #pragma unroll
-    for (int i = 0; i < kI; ++i)
+      for (int i = 0; i < kI; ++i)
 #pragma unroll
-      for (int jn = 0; jn < kJ; ++jn) {
-        const uint32_t r = (uint32_t)(16 * i + (lane & 15));
-        const uint32_t off = cblock_lds_offset((uint32_t)w4, r, (uint32_t)(2 * jn + (lane >> 5)));
-        c[i][jn] = lds_read8(cq[i >> 1], (off & 16383u) + 8u * (uint32_t)((lane >> 4) & 1));
+        for (int jn = 0; jn < kJ; ++jn) c[i][jn] = lds_read8(cq[i >> 1], place(i, jn));
+    }
+    if constexpr (DD == SG_F32) {
+#pragma unroll
+      for (int i = 0; i < kI; ++i) {
+        const int ml = 128 * g + 16 * i + (lane & 15);
+        if (ml >= j.m_valid) continue;
+        const int64_t row = (j.d_row0 + ml) * ldd + j.n0;
+#pragma unroll
+        for (int jn = 0; jn < kJ; ++jn) {
+          const int nl = 64 * w4 + 16 * jn + 4 * (lane >> 4);
+          if (nl >= j.n_valid) continue;
+          store_d_chunk<CD, DD>(acc[i][jn], c[i][jn], D, row + nl, j.alpha, j.beta);
+        }
       }
+    } else {
+      // A wave's LDS accesses complete in order: each write follows the read
+      // of the same bytes, each row read follows the writes.
 #pragma unroll
-    for (int i = 0; i < kI; ++i) {
-      const int ml = 128 * g + 16 * i + (lane & 15);
-      if (ml >= j.m_valid) continue;
-      const int64_t row = (j.d_row0 + ml) * ldd + j.n0;
+      for (int i = 0; i < kI; ++i)
 #pragma unroll
-      for (int jn = 0; jn < kJ; ++jn) {
-        const int nl = 64 * w4 + 16 * jn + 4 * (lane >> 4);
-        if (nl >= j.n_valid) continue;
-        store_d_chunk<CD, DD>(acc[i][jn], c[i][jn], D, row + nl, j.alpha, j.beta);
+        for (int jn = 0; jn < kJ; ++jn)
+          lds_write8(cq[i >> 1], place(i, jn),
+                     pack_d16<DD>(epi_value<CD>(acc[i][jn], c[i][jn], j.alpha, j.beta)));
+      const int cc = lane & 7;
+      const int nl = 64 * w4 + 8 * cc;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const uint32_t r = (uint32_t)(8 * s + (lane >> 3));
+        const u32x4 d = lds_read16(cq[s >> 2], cblock_lds_offset((uint32_t)w4, r, cc) & 16383u);
+        const int ml = 128 * g + (int)r;
+        if (ml >= j.m_valid || nl >= j.n_valid) continue;
+        uint16_t* p = static_cast<uint16_t*>(D) + (j.d_row0 + ml) * ldd + j.n0 + nl;
+        if (j.n_valid - nl >= 8)
+          *reinterpret_cast<u32x4*>(p) = d;
+        else  // 4 columns left (N is a multiple of 4)
+          *reinterpret_cast<u32x2*>(p) = u32x2{d[0], d[1]};
       }
     }
   }
 
-  __device__ __forceinline__ static void epilogue_ldsc(const f32x4 (&acc)[kI][kJ],
-                                                       const TileJob& j,
-                                                       const char* const (&cq)[4], int c_dtype,
-                                                       void* D, int d_dtype, int64_t ldd,
-                                                       int lane, int g, int w4) {
-#define SG_EPI(CD, DD) return epilogue_ldsc_t<CD, DD>(acc, j, cq, D, ldd, lane, g, w4)
-    if (c_dtype == SG_BF16) {
-      if (d_dtype == SG_F32) SG_EPI(SG_BF16, SG_F32);
-      if (d_dtype == SG_BF16) SG_EPI(SG_BF16, SG_BF16);
-      SG_EPI(SG_BF16, SG_F16);
+  // cd: the C type in LDS, SG_NONE for none.  Takes 16-bit C or 16-bit D.
+  __device__ __forceinline__ static void epilogue_lds(const f32x4 (&acc)[kI][kJ],
+                                                      const TileJob& j, char* const (&cq)[4],
+                                                      int cd, void* D, int d_dtype, int64_t ldd,
+                                                      int lane, int g, int w4) {
+#define SG_EPI(CD, DD) return epilogue_lds_t<CD, DD>(acc, j, cq, D, ldd, lane, g, w4)
+    if (d_dtype == SG_F32) {
+      if (cd == SG_BF16) SG_EPI(SG_BF16, SG_F32);
+      SG_EPI(SG_F16, SG_F32);
     }
-    if (d_dtype == SG_F32) SG_EPI(SG_F16, SG_F32);
-    if (d_dtype == SG_BF16) SG_EPI(SG_F16, SG_BF16);
-    SG_EPI(SG_F16, SG_F16);
+    if (d_dtype == SG_BF16) {
+      if (cd == SG_BF16) SG_EPI(SG_BF16, SG_BF16);
+      if (cd == SG_F16) SG_EPI(SG_F16, SG_BF16);
+      SG_EPI(SG_NONE, SG_BF16);
+    }
+    if (cd == SG_BF16) SG_EPI(SG_BF16, SG_F16);
+    if (cd == SG_F16) SG_EPI(SG_F16, SG_F16);
+    SG_EPI(SG_NONE, SG_F16);
 #undef SG_EPI
   }
 
@@ -385,14 +421,20 @@ struct PingPong16Tile {
     }
     wait_vmem();  // the C block, or the zero-filled loads past K
 
-    if (ldsc) {
+    // Through LDS: a 16-bit C that came in with the last loads, and a 16-bit
+    // D.  Every fragment read is done once all waves pass the barrier, and
+    // the wave's C block area is written by its own loads only.
+    const bool d16 = d_dtype == SG_BF16 || d_dtype == SG_F16;
+    if (ldsc || (d16 && C == nullptr)) {
       PP::barrier();
       const int tb = T % 3, ta = T & 1;
-      const char* const cq[4] = {b_rd + tb * kTileBytes + g * kHalfBytes,
-                                 a_rd + ta * kTileBytes + g * kHalfBytes,
-                                 b_rd + (tb == 2 ? 0 : tb + 1) * kTileBytes + g * kHalfBytes,
-                                 a_rd + (ta ^ 1) * kTileBytes + g * kHalfBytes};
-      if (a_rows > 0) epilogue_ldsc(acc, j, cq, c_dtype, D, d_dtype, ldd, lane, g, w4);
+      char* const b_slots = smem + kARing * kTileBytes + g * kHalfBytes;
+      char* const a_slots = smem + g * kHalfBytes;
+      char* const cq[4] = {b_slots + tb * kTileBytes, a_slots + ta * kTileBytes,
+                           b_slots + (tb == 2 ? 0 : tb + 1) * kTileBytes,
+                           a_slots + (ta ^ 1) * kTileBytes};
+      if (a_rows > 0)
+        epilogue_lds(acc, j, cq, ldsc ? c_dtype : SG_NONE, D, d_dtype, ldd, lane, g, w4);
     } else {
       epilogue16<kI, kJ>(acc, j, C, c_dtype, D, d_dtype, ldd, lane, 128 * g, 64 * w4);
     }
