@@ -145,6 +145,43 @@ struct KExactHalfLoader {
   }
 };
 
+// The four 16 KiB half slots of group g that hold a wave's block of C or D
+// at the end of a 256x256 tile (cblock_lds_offset's quarters): the slots
+// the loads of K tiles T and T+1 fill, B ring (after A's two slots) and A
+// ring alternating.
+__device__ __forceinline__ void cblock_quarters(char* (&cq)[4], char* smem, int T, int g,
+                                                int tile_bytes, int half_bytes) {
+  const int tb = T % 3, ta = T & 1;
+  char* const b_slots = smem + 2 * tile_bytes + g * half_bytes;
+  char* const a_slots = smem + g * half_bytes;
+  cq[0] = b_slots + tb * tile_bytes;
+  cq[1] = a_slots + ta * tile_bytes;
+  cq[2] = b_slots + (tb == 2 ? 0 : tb + 1) * tile_bytes;
+  cq[3] = a_slots + (ta ^ 1) * tile_bytes;
+}
+
+// Stores wave w4's 128 x 64 block of a 16-bit D, already rounded and written
+// to its C block area: lane l takes 16-byte chunk l%8 of row 8s + l/8, so 8
+// lanes store one 128-byte row segment (16 stores per wave).  N is a
+// multiple of 4: a chunk with 4 valid columns stores its first 8 bytes.
+__device__ __forceinline__ void store_d16_block(char* const (&cq)[4], const TileJob& j, void* D,
+                                                int64_t ldd, int lane, int g, int w4) {
+  const int cc = lane & 7;
+  const int nl = 64 * w4 + 8 * cc;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const uint32_t r = (uint32_t)(8 * s + (lane >> 3));
+    const u32x4 d = lds_read16(cq[s >> 2], cblock_lds_offset((uint32_t)w4, r, cc) & 16383u);
+    const int ml = 128 * g + (int)r;
+    if (ml >= j.m_valid || nl >= j.n_valid) continue;
+    uint16_t* p = static_cast<uint16_t*>(D) + (j.d_row0 + ml) * ldd + j.n0 + nl;
+    if (j.n_valid - nl >= 8)
+      *reinterpret_cast<u32x4*>(p) = d;
+    else
+      *reinterpret_cast<u32x2*>(p) = u32x2{d[0], d[1]};
+  }
+}
+
 template <bool IsBF16, int Swz>
 struct PingPongTile {
   using Base = GemmTile<256, 256, IsBF16, false, false, Swz, 8>;
@@ -762,7 +799,42 @@ struct PingPongMxTile {
     settle(cur);
     settle(nxt);
 
-    Base::epilogue(acc, j, nullptr, SG_NONE, D, d_dtype, ldd, lane, g, w4);
+    if (d_dtype == SG_F32) {
+      Base::epilogue(acc, j, nullptr, SG_NONE, D, d_dtype, ldd, lane, g, w4);
+    } else {
+      // A 16-bit D goes out through the wave's C block area (lane l of
+      // accumulator block (fm, fn) holds row 32fm + l%32 of the block,
+      // columns 32fn + 8q + 4(l/32) .. +3 in registers 4q .. 4q+3); every
+      // fragment read is done once all waves pass the barrier.
+      barrier();
+      char* cq[4];
+      cblock_quarters(cq, smem, T, g, kTileBytes, kHalfBytes);
+      if (d_dtype == SG_BF16)
+        stage_d16<SG_BF16>(acc, cq, j.alpha, lane, w4);
+      else
+        stage_d16<SG_F16>(acc, cq, j.alpha, lane, w4);
+      store_d16_block(cq, j, D, ldd, lane, g, w4);
+    }
+  }
+
+  template <int DD>
+  __device__ __forceinline__ static void stage_d16(const f32x16 (&acc)[kFM][kFN],
+                                                   char* const (&cq)[4], float alpha, int lane,
+                                                   int w4) {
+    const u32x2 none{};
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < kFN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
+                           acc[fm][fn][4 * q + 3]};
+          const uint32_t r = (uint32_t)(32 * fm + (lane & 31));
+          const uint32_t off = (cblock_lds_offset((uint32_t)w4, r, (uint32_t)(4 * fn + q)) &
+                                16383u) + 8u * (uint32_t)(lane >> 5);
+          lds_write8(cq[fm], off, pack_d16<DD>(epi_value<SG_NONE>(v, none, alpha, 0.0f)));
+        }
   }
 };
 

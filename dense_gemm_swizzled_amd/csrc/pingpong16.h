@@ -279,20 +279,7 @@ struct PingPong16Tile {
         for (int jn = 0; jn < kJ; ++jn)
           lds_write8(cq[i >> 1], place(i, jn),
                      pack_d16<DD>(epi_value<CD>(acc[i][jn], c[i][jn], j.alpha, j.beta)));
-      const int cc = lane & 7;
-      const int nl = 64 * w4 + 8 * cc;
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const uint32_t r = (uint32_t)(8 * s + (lane >> 3));
-        const u32x4 d = lds_read16(cq[s >> 2], cblock_lds_offset((uint32_t)w4, r, cc) & 16383u);
-        const int ml = 128 * g + (int)r;
-        if (ml >= j.m_valid || nl >= j.n_valid) continue;
-        uint16_t* p = static_cast<uint16_t*>(D) + (j.d_row0 + ml) * ldd + j.n0 + nl;
-        if (j.n_valid - nl >= 8)
-          *reinterpret_cast<u32x4*>(p) = d;
-        else  // 4 columns left (N is a multiple of 4)
-          *reinterpret_cast<u32x2*>(p) = u32x2{d[0], d[1]};
-      }
+      store_d16_block(cq, j, D, ldd, lane, g, w4);
     }
   }
 
@@ -427,12 +414,8 @@ struct PingPong16Tile {
     const bool d16 = d_dtype == SG_BF16 || d_dtype == SG_F16;
     if (ldsc || (d16 && C == nullptr)) {
       PP::barrier();
-      const int tb = T % 3, ta = T & 1;
-      char* const b_slots = smem + kARing * kTileBytes + g * kHalfBytes;
-      char* const a_slots = smem + g * kHalfBytes;
-      char* const cq[4] = {b_slots + tb * kTileBytes, a_slots + ta * kTileBytes,
-                           b_slots + (tb == 2 ? 0 : tb + 1) * kTileBytes,
-                           a_slots + (ta ^ 1) * kTileBytes};
+      char* cq[4];
+      cblock_quarters(cq, smem, T, g, kTileBytes, kHalfBytes);
       if (a_rows > 0)
         epilogue_lds(acc, j, cq, ldsc ? c_dtype : SG_NONE, D, d_dtype, ldd, lane, g, w4);
     } else {
