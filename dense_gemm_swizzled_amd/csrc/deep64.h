@@ -182,7 +182,57 @@ struct DeepTile {
     if (t < T) iteration(t, f0, f1);
     wait_vmem();  // the loads past K
 
-    Base::epilogue(acc, j, C, c_dtype, D, d_dtype, ldd, lane, wm, wn);
+    if (d_dtype == SG_F32 && C == nullptr) {
+      PingPongTile<IsBF16, kSwzDefault>::barrier();  // every wave's reads are done
+      store_f32_via_lds(acc, j, smem + wave * kWaveBytes, D, ldd, lane, wm, wn);
+    } else {
+      Base::epilogue(acc, j, C, c_dtype, D, d_dtype, ldd, lane, wm, wn);
+    }
+  }
+
+  // An fp32 D (no C) through LDS.  Lane l of accumulator block (fm, fn) holds
+  // row 32fm + l%32 of the wave's block, columns 32fn + 8q + 4(l/32) .. +3 in
+  // registers 4q .. 4q+3: 16-byte chunk 8fn + 2q + l/32 of a kRowBytes row.
+  // The wave writes its block into its own area, chunk c of row r at chunk
+  // c XOR (r mod 8), which gives the 8 rows of one ds_write_b128 phase (8
+  // lanes, one 128-byte bank line) 8 distinct places in the line, then
+  // reads it back one contiguous KiB per instruction
+  // and stores whole rows: kRowBytes / 16 lanes per row, where the register
+  // layout gave each store instruction 32 bytes per row.
+  static constexpr int kRowBytes = 128 * kFN;                 // fp32 row of a wave
+  static constexpr int kWaveBytes = 32 * kFM * kRowBytes;     // 4 or 16 KiB
+  static_assert(4 * kWaveBytes <= kLdsBytes, "staging fits the ring");
+  __device__ __forceinline__ static uint32_t row_key(uint32_t r) { return r & 7u; }
+  __device__ __forceinline__ static void store_f32_via_lds(const f32x16 (&acc)[kFM][kFN],
+                                                           const TileJob& j, char* area,
+                                                           void* D, int64_t ldd, int lane,
+                                                           int wm, int wn) {
+    const u32x2 none{};
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < kFN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = epi_value<SG_NONE>(
+              f32x4{acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
+                    acc[fm][fn][4 * q + 3]},
+              none, j.alpha, 0.0f);
+          const uint32_t r = (uint32_t)(32 * fm + (lane & 31));
+          const uint32_t c = (uint32_t)(8 * fn + 2 * q + (lane >> 5));
+          lds_write16(area, r * kRowBytes + 16u * (c ^ row_key(r)), __builtin_bit_cast(u32x4, v));
+        }
+    constexpr int kLanesPerRow = kRowBytes / 16, kRowsPerStep = 64 / kLanesPerRow;
+    const uint32_t cc = (uint32_t)(lane % kLanesPerRow);
+    const int nl = wn * Base::kWN + 4 * (int)cc;
+#pragma unroll
+    for (int s = 0; s < kWaveBytes / 1024; ++s) {
+      const uint32_t r = (uint32_t)(kRowsPerStep * s + lane / kLanesPerRow);
+      const u32x4 d = lds_read16(area, r * kRowBytes + 16u * (cc ^ row_key(r)));
+      const int ml = wm * Base::kWM + (int)r;
+      if (ml >= j.m_valid || nl >= j.n_valid) continue;
+      *reinterpret_cast<u32x4*>(static_cast<float*>(D) + (j.d_row0 + ml) * ldd + j.n0 + nl) = d;
+    }
   }
 };
 

@@ -802,38 +802,60 @@ struct PingPongMxTile {
     if (d_dtype == SG_F32) {
       Base::epilogue(acc, j, nullptr, SG_NONE, D, d_dtype, ldd, lane, g, w4);
     } else {
-      // A 16-bit D goes out through the wave's C block area (lane l of
-      // accumulator block (fm, fn) holds row 32fm + l%32 of the block,
-      // columns 32fn + 8q + 4(l/32) .. +3 in registers 4q .. 4q+3); every
-      // fragment read is done once all waves pass the barrier.
+      // A 16-bit D goes out through LDS: once all waves pass the barrier no
+      // fragment read or load is pending, and wave (g, w4) takes 16 KiB of
+      // its own.
       barrier();
-      char* cq[4];
-      cblock_quarters(cq, smem, T, g, kTileBytes, kHalfBytes);
+      char* area = smem + (4 * g + w4) * 16384;
       if (d_dtype == SG_BF16)
-        stage_d16<SG_BF16>(acc, cq, j.alpha, lane, w4);
+        stage_d16<SG_BF16>(acc, area, j.alpha, lane);
       else
-        stage_d16<SG_F16>(acc, cq, j.alpha, lane, w4);
-      store_d16_block(cq, j, D, ldd, lane, g, w4);
+        stage_d16<SG_F16>(acc, area, j.alpha, lane);
+      const int cc = lane & 7;
+      const int nl = 64 * w4 + 8 * cc;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const uint32_t r = (uint32_t)(8 * s + (lane >> 3));
+        const u32x4 d = lds_read16(area, r * 128u + 16u * ((uint32_t)cc ^ (r & 7u)));
+        const int ml = 128 * g + (int)r;
+        if (ml >= j.m_valid || nl >= j.n_valid) continue;
+        uint16_t* p = static_cast<uint16_t*>(D) + (j.d_row0 + ml) * ldd + j.n0 + nl;
+        *reinterpret_cast<u32x4*>(p) = d;  // N * 2 is a multiple of 16 bytes
+      }
     }
   }
 
+  // The wave's 128 x 64 block of a 16-bit D into `area`: row r (128 bytes),
+  // 16-byte chunk c (8 columns) at chunk c XOR (r mod 8), so the 8 rows of
+  // a ds_write_b128 phase fill one 128-byte bank line.  Lane l of
+  // accumulator block (fm, fn) holds row 32fm + l%32 of the block, columns
+  // 32fn + 8q + 4(l/32) .. +3 in registers 4q .. 4q+3; for each pair of q a
+  // v_permlane32_swap trades halves between lanes l and l+32, leaving lane l
+  // the whole chunk 4fn + 2p + l/32.
   template <int DD>
-  __device__ __forceinline__ static void stage_d16(const f32x16 (&acc)[kFM][kFN],
-                                                   char* const (&cq)[4], float alpha, int lane,
-                                                   int w4) {
+  __device__ __forceinline__ static void stage_d16(const f32x16 (&acc)[kFM][kFN], char* area,
+                                                   float alpha, int lane) {
     const u32x2 none{};
+    auto half = [&](int fm, int fn, int q) {
+      const f32x4 v = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
+                       acc[fm][fn][4 * q + 3]};
+      return pack_d16<DD>(epi_value<SG_NONE>(v, none, alpha, 0.0f));
+    };
+    const uint32_t r0 = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
 #pragma unroll
     for (int fm = 0; fm < kFM; ++fm)
 #pragma unroll
       for (int fn = 0; fn < kFN; ++fn)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
-                           acc[fm][fn][4 * q + 3]};
-          const uint32_t r = (uint32_t)(32 * fm + (lane & 31));
-          const uint32_t off = (cblock_lds_offset((uint32_t)w4, r, (uint32_t)(4 * fn + q)) &
-                                16383u) + 8u * (uint32_t)(lane >> 5);
-          lds_write8(cq[fm], off, pack_d16<DD>(epi_value<SG_NONE>(v, none, alpha, 0.0f)));
+        for (int p = 0; p < 2; ++p) {
+          const u32x2 lo = half(fm, fn, 2 * p), hi = half(fm, fn, 2 * p + 1);
+          // lanes 0-31 end with (own lo, partner's lo), lanes 32-63 with
+          // (partner's hi, own hi): columns in order either way.
+          const auto x = __builtin_amdgcn_permlane32_swap(lo[0], hi[0], false, false);
+          const auto y = __builtin_amdgcn_permlane32_swap(lo[1], hi[1], false, false);
+          const uint32_t r = 32u * (uint32_t)fm + r0;
+          const uint32_t c = 4u * (uint32_t)fn + 2u * (uint32_t)p + h;
+          lds_write16(area, r * 128u + 16u * (c ^ (r & 7u)), u32x4{x[0], y[0], x[1], y[1]});
         }
   }
 };
