@@ -237,6 +237,45 @@ def test_cblock_epilogue_reads_conflict_free(model):
     assert _degree(model, "r64", a) > 1
 
 
+@pytest.mark.parametrize("kfm,kfn", [(1, 1), (2, 2)])
+def test_fp32_d_staging_conflict_free(model, kfm, kfn):
+    # The deep-ring kernels' fp32 D (64x64 tiles: a 32x32 block per wave;
+    # 128x128: 64x64): lane l of accumulator block (fm, fn) writes 16 bytes
+    # of row 32fm + l%32, chunk 8fn + 2q + l/32, to row * 128kfn + 16 (chunk
+    # XOR row%8) with ds_write_b128; the store pass reads one contiguous KiB
+    # per instruction (row 8s/kfn + l/(8kfn), chunk l%(8kfn)).
+    rb = 128 * kfn
+    place = lambda r, c: r * rb + 16 * (c ^ (r & 7))
+    assert len({place(r, c) for r in range(32 * kfm) for c in range(8 * kfn)}) == 32 * kfm * 8 * kfn
+    w = max(_degree(model, "w128", [place(32 * fm + l % 32, 8 * fn + 2 * q + l // 32)
+                                    for l in range(64)])
+            for fm in range(kfm) for fn in range(kfn) for q in range(4))
+    lpr = rb // 16
+    r = max(_degree(model, "r128", [place((64 // lpr) * s + l // lpr, l % lpr) for l in range(64)])
+            for s in range(32 * kfm * rb // 1024))
+    assert (w, r) == (1, 1)
+
+
+def test_mx_d_staging_conflict_free(model):
+    # The MX kernels' 16-bit D: after v_permlane32_swap, lane l holds chunk
+    # 4fn + 2p + l/32 of row 32fm + l%32 of its 128 x 64 block (128-byte
+    # rows), written at chunk XOR row%8; the store pass reads row 8s + l/8,
+    # chunk l%8.
+    place = lambda r, c: r * 128 + 16 * (c ^ (r & 7))
+    w = max(_degree(model, "w128", [place(32 * fm + l % 32, 4 * fn + 2 * p + l // 32)
+                                    for l in range(64)])
+            for fm in range(4) for fn in range(2) for p in range(2))
+    r = max(_degree(model, "r128", [place(8 * s + l // 8, l % 8) for l in range(64)])
+            for s in range(16))
+    assert (w, r) == (1, 1)
+    # 8-byte halves written straight from the accumulator layout (32 rows,
+    # one half each per 32 lanes) find only 16 places in a 256-byte line:
+    # even the C block map, built for 8-byte accesses, leaves them 2-way.
+    m = sg.gemm_lds_layout_cblock()
+    a = [int(m[0, l % 32, 0]) % 16384 + 8 * (l // 32) for l in range(64)]
+    assert _degree(model, "r64", a) == 2
+
+
 def test_padded_layout_is_conflict_free(model):
     # The padded layout of the layout ablation (144-byte rows, no XOR): the
     # 32x32x16 fragment reads and the register-staged ds_write_b128 stores
