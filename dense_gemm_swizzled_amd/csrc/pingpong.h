@@ -160,10 +160,20 @@ __device__ __forceinline__ void cblock_quarters(char* (&cq)[4], char* smem, int 
   cq[3] = a_slots + (ta ^ 1) * tile_bytes;
 }
 
-// Stores wave w4's 128 x 64 block of a 16-bit D, already rounded and written
-// to its C block area: lane l takes 16-byte chunk l%8 of row 8s + l/8, so 8
-// lanes store one 128-byte row segment (16 stores per wave).  N is a
-// multiple of 4: a chunk with 4 valid columns stores its first 8 bytes.
+// Where the 256x256 kernel of 16x16x32 MFMAs stages a 16-bit D: wave w4's
+// own 1 KiB regions of the four quarters (as the C block: row r of its 128 x
+// 64 block in quarter r / 32, region 4((r / 8) mod 4) + w4, 128-byte row r
+// mod 8), 16-byte chunk c at chunk c XOR (r mod 8), so that the 8 rows of a
+// ds_write_b128 phase fill one 128-byte bank line.  Offset inside the
+// quarter's 16 KiB half slot.
+__device__ __forceinline__ uint32_t dstage_offset(uint32_t w4, uint32_t r, uint32_t c) {
+  return (4u * ((r >> 3) & 3u) + w4) * 1024u + (r & 7u) * 128u + 16u * (c ^ (r & 7u));
+}
+
+// Stores wave w4's staged 128 x 64 block of a 16-bit D: lane l takes 16-byte
+// chunk l%8 of row 8s + l/8 (one contiguous KiB per read), so 8 lanes store
+// one 128-byte row segment (16 stores per wave).  N is a multiple of 4: a
+// chunk with 4 valid columns stores its first 8 bytes.
 __device__ __forceinline__ void store_d16_block(char* const (&cq)[4], const TileJob& j, void* D,
                                                 int64_t ldd, int lane, int g, int w4) {
   const int cc = lane & 7;
@@ -171,7 +181,7 @@ __device__ __forceinline__ void store_d16_block(char* const (&cq)[4], const Tile
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
     const uint32_t r = (uint32_t)(8 * s + (lane >> 3));
-    const u32x4 d = lds_read16(cq[s >> 2], cblock_lds_offset((uint32_t)w4, r, cc) & 16383u);
+    const u32x4 d = lds_read16(cq[s >> 2], dstage_offset((uint32_t)w4, r, (uint32_t)cc));
     const int ml = 128 * g + (int)r;
     if (ml >= j.m_valid || nl >= j.n_valid) continue;
     uint16_t* p = static_cast<uint16_t*>(D) + (j.d_row0 + ml) * ldd + j.n0 + nl;

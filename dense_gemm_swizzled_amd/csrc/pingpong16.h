@@ -236,10 +236,10 @@ struct PingPong16Tile {
   // The epilogue through the wave's C block area (cblock_lds_offset): lane l
   // of accumulator block (i, jn) holds row 16i + l%16 of the block, columns
   // 16jn + 4(l/16) .. +3, i.e. half (l/16) mod 2 of chunk 2jn + l/32.  A
-  // 16-bit C (CD) is read from there; a 16-bit D is written back there and
-  // then stored a whole 128-byte row segment per 8 lanes (row 8s + l/8,
-  // chunk l%8), 16 stores of 16 bytes instead of 32 of 8.  An fp32 D is
-  // stored from registers.
+  // 16-bit C (CD) is read from there; a 16-bit D is staged in the same
+  // regions (dstage_offset) and stored a whole 128-byte row segment per 8
+  // lanes (row 8s + l/8, chunk l%8), 16 stores of 16 bytes instead of 32 of
+  // 8.  An fp32 D is stored from registers.
   template <int CD, int DD>
   __device__ __forceinline__ static void epilogue_lds_t(const f32x4 (&acc)[kI][kJ],
                                                         const TileJob& j, char* const (&cq)[4],
@@ -271,14 +271,28 @@ struct PingPong16Tile {
         }
       }
     } else {
-      // A wave's LDS accesses complete in order: each write follows the read
-      // of the same bytes, each row read follows the writes.
+      // Lane l holds 4 columns of row 16i + l%16: with ρ = l/16, columns
+      // 16jn + 4ρ .. +3.  For each pair of blocks (2jp, 2jp+1) a
+      // v_permlane16_swap trades them between lane rows ρ = 0, 1 and ρ = 2,
+      // 3, leaving lane l the whole 16-byte chunk 2(2jp + ρ%2) + ρ/2 of the
+      // row (columns in order), written to dstage_offset with
+      // ds_write_b128.  A wave's LDS accesses complete in order: the writes
+      // follow every read of C, the row reads follow the writes.
+      const int rho = lane >> 4;
 #pragma unroll
       for (int i = 0; i < kI; ++i)
 #pragma unroll
-        for (int jn = 0; jn < kJ; ++jn)
-          lds_write8(cq[i >> 1], place(i, jn),
-                     pack_d16<DD>(epi_value<CD>(acc[i][jn], c[i][jn], j.alpha, j.beta)));
+        for (int jp = 0; jp < kJ / 2; ++jp) {
+          const u32x2 x0 = pack_d16<DD>(epi_value<CD>(acc[i][2 * jp], c[i][2 * jp], j.alpha,
+                                                      j.beta));
+          const u32x2 x1 = pack_d16<DD>(epi_value<CD>(acc[i][2 * jp + 1], c[i][2 * jp + 1],
+                                                      j.alpha, j.beta));
+          const auto a = __builtin_amdgcn_permlane16_swap(x0[0], x1[0], false, false);
+          const auto b = __builtin_amdgcn_permlane16_swap(x0[1], x1[1], false, false);
+          const uint32_t r = (uint32_t)(16 * i + (lane & 15));
+          const uint32_t ch = (uint32_t)(4 * jp + 2 * (rho & 1) + (rho >> 1));
+          lds_write16(cq[i >> 1], dstage_offset((uint32_t)w4, r, ch), u32x4{a[0], b[0], a[1], b[1]});
+        }
       store_d16_block(cq, j, D, ldd, lane, g, w4);
     }
   }

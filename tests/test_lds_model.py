@@ -237,6 +237,28 @@ def test_cblock_epilogue_reads_conflict_free(model):
     assert _degree(model, "r64", a) > 1
 
 
+def test_16x16_d_staging_conflict_free(model):
+    # The 256x256 kernel of 16x16x32 MFMAs stages a 16-bit D in the wave's C
+    # block regions: row r of its 128 x 64 block in quarter r/32, region
+    # 4((r/8)%4) + w, 128-byte row r%8, chunk c at c XOR r%8.  After
+    # v_permlane16_swap, lane l (rho = l/16) of block row i and block pair jp
+    # writes chunk 4jp + 2(rho%2) + rho/2 of row 16i + l%16 (ds_write_b128);
+    # the store pass reads row 8s + l/8, chunk l%8.
+    place = lambda w, r, c: ((r // 32) * 16384 + (4 * ((r // 8) % 4) + w) * 1024
+                             + (r % 8) * 128 + 16 * (c ^ (r % 8)))
+    m = sg.gemm_lds_layout_cblock()
+    for w in range(4):   # the same bytes as the wave's C block
+        assert ({place(w, r, c) for r in range(128) for c in range(8)}
+                == set(m[w].reshape(-1).tolist()))
+    wr = max(_degree(model, "w128", [place(w, 16 * i + l % 16,
+                                           4 * jp + 2 * ((l // 16) % 2) + l // 32)
+                                     for l in range(64)])
+             for w in range(4) for i in range(8) for jp in range(2))
+    rd = max(_degree(model, "r128", [place(w, 8 * s + l // 8, l % 8) for l in range(64)])
+             for w in range(4) for s in range(16))
+    assert (wr, rd) == (1, 1)
+
+
 @pytest.mark.parametrize("kfm,kfn", [(1, 1), (2, 2)])
 def test_fp32_d_staging_conflict_free(model, kfm, kfn):
     # The deep-ring kernels' fp32 D (64x64 tiles: a 32x32 block per wave;
