@@ -325,6 +325,31 @@ def test_dense_degenerate_shapes(dev):
     check_close(_np(d), ref, bound, "bf16", "1x8x8")
 
 
+@pytest.mark.parametrize("K", [0, 8, 64])
+@pytest.mark.parametrize("with_c", [False, True])
+def test_dense_256_tiles_16bit_d_short_k(dev, K, with_c):
+    # The 256x256 kernel writes a 16-bit D through LDS after any mainloop:
+    # none (K = 0: D = C exactly, or zero), one partial K tile, one whole K
+    # tile (a C is then read by the epilogue, not by the last loads).  N =
+    # 4104 leaves 8 columns in the last tile column.
+    M, N = 4096, 4104
+    say(f"256 tiles, bf16 D through LDS, K={K} C={with_c}")
+    if K == 0:
+        g = torch.Generator().manual_seed(5)
+        C = torch.randn(M, N, generator=g).to(torch.bfloat16).to(dev) if with_c else None
+        A = torch.empty(M, 0, dtype=torch.bfloat16, device=dev)
+        B = torch.empty(N, 0, dtype=torch.bfloat16, device=dev)
+        d = sg.gemm(A, B, C=C, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(d, C) if with_c else torch.count_nonzero(d) == 0
+        return
+    case = si.dense_case(M, N, K, 60 + K, ab_dtype="bf16", with_c=with_c, c_dtype="bf16",
+                         d_dtype="bf16", scale=1.0 / np.sqrt(K))
+    d = run_dense(case, dev)
+    ref, bound = oracle_dense(case)
+    check_close(_np(d), ref, bound, "bf16", f"256 tiles K={K}")
+
+
 def test_dense_8192_full_size_sampled(dev):
     case = si.dense_8192(seed=3)
     say(f"{case.name} (sampled)")
