@@ -301,6 +301,20 @@ def test_dense_in_place_c_equals_d(dev):
     check_close(_np(CD), ref, bound, "f32", "in-place")
 
 
+def test_dense_256_tiles_in_place_bf16(dev):
+    # C == D on the 256x256 kernel with a bf16 C: each wave's C block comes
+    # into LDS with the last K tiles' loads, before any of its D is written.
+    M, N, K = 4100, 4104, 192
+    case = si.dense_case(M, N, K, 21, ab_dtype="bf16", with_c=True, c_dtype="bf16",
+                         d_dtype="bf16", scale=1.0 / np.sqrt(K))
+    say("in-place C == D, 256 tiles, bf16")
+    CD = case.C.to(dev).clone()
+    sg.gemm(case.A.to(dev), case.B.to(dev), C=CD, out=CD)
+    torch.cuda.synchronize()
+    ref, bound = oracle_dense(case)
+    check_close(_np(CD), ref, bound, "bf16", "in-place 256")
+
+
 def test_dense_degenerate_shapes(dev):
     say("degenerate shapes")
     # K = 0: D = C exactly; and D = 0 without C.
