@@ -15,6 +15,10 @@
 // fragment reads (lane l: row l%16 of a 16-row block, 16-byte chunk 4kh +
 // l/16 of the row, conflict-free under the swizzle) and 32 MFMAs with the
 // four loads of a half tile between them, one per eight MFMAs.
+//
+// The epilogue goes through LDS: a 16-bit C arrives with the loads of the
+// last two K tiles (which would otherwise fetch zeros past K), and a 16-bit
+// D is staged there and stored as whole 128-byte row segments.
 #pragma once
 
 #include "pingpong.h"
