@@ -14,10 +14,12 @@
 // Layout.  A K-major operand uses the XOR map lds_offset<128, 16> and the
 // fragment reads of GemmTile.  An MN-major operand is stored as it lies in
 // memory, one 128-byte LDS row per k (64 m or n values), with the 16-byte
-// chunks of rows whose bit 3 is set rotated by four chunks: the MFMA operand
-// of a lane is 8 consecutive k of one m or n, read with eight 2-byte LDS
-// reads, and the rotation puts the rows k and k+8 that the two lane halves
-// read in the same instruction on different banks.
+// chunks of rows whose bit 1 is set rotated by four chunks.  The MFMA
+// operand of a lane is 8 consecutive k of one m or n; two transposing reads
+// (ds_read_b64_tr_b16) fetch it: in each group of 16 lanes, lane i reads 4
+// consecutive m or n of row k0 + i/4, and the read hands lane j the 4 k of
+// column j.  One read covers rows k0..k0+3 at 64 bytes each per 32 lanes,
+// and the rotation puts those four rows on the four quarters of the banks.
 //
 // Waves.  Four waves in a 2x2 grid, one (64x64 tiles) or 2x2 (128x128) 32x32
 // accumulators each (the GemmTile layout, whose epilogue this tile uses).
@@ -49,7 +51,7 @@ struct DeepTile {
 
   // Byte offset, in an MN-major operand's stage, of byte `byte` of k-row k.
   __device__ __forceinline__ static uint32_t bmn_offset(uint32_t k, uint32_t byte) {
-    return k * 128u + ((byte + 64u * ((k >> 3) & 1u)) & 127u);
+    return k * 128u + ((byte + 64u * ((k >> 1) & 1u)) & 127u);
   }
 
   __device__ __forceinline__ static void run(char* smem, const TileJob& j, int64_t K,
@@ -71,7 +73,7 @@ struct DeepTile {
     // Loads of K tile t of one operand into `dst`; past K every chunk is
     // out of range (zero fill).  Regions 4i + wave (1 KiB each).  MN-major:
     // lane l of region r fills k-row 8r + l/8, physical chunk l%8, which
-    // holds logical chunk (l%8 + 4 * bit 3 of the row) mod 8.
+    // holds logical chunk (l%8 + 4 * bit 1 of the row) mod 8.
     auto issue_op = [&](auto mn, const HalfLoader<kSwzDefault>& ld, u32x4 rsrc, uint32_t pitch,
                         int rows_valid, uint32_t dst, int t) {
       if constexpr (!decltype(mn)::value) {
@@ -83,7 +85,7 @@ struct DeepTile {
         for (int i = 0; i < 2; ++i) {
           const int r = 4 * i + wave, krow = 8 * r + (lane >> 3);
           const int64_t k = (int64_t)t * kBK + krow;
-          const uint32_t c = (uint32_t)((lane & 7) + 4 * ((krow >> 3) & 1)) & 7u;
+          const uint32_t c = (uint32_t)((lane & 7) + 4 * ((krow >> 1) & 1)) & 7u;
           const uint32_t off = k < K ? (uint32_t)k * pitch + 16u * c : kOutOfRange;
           dma16(rsrc, off, dst + (uint32_t)r * 1024u);
         }
@@ -108,18 +110,26 @@ struct DeepTile {
     struct Frags {
       u32x4 a[kBK / 16][kFM], b[kBK / 16][kFN];
     };
-    // An MN-major operand's fragment: k = 16 kk + 8 h + e (e = 0..7) of
-    // column `col` (m or n), two bytes at a time.
-    auto gather = [&](const char* base, int col, int kk) {
-      const uint32_t c2 = 2u * (uint32_t)col;
-      const uint32_t k0 = (uint32_t)(16 * kk + 8 * lhalf);
-      uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        h[e] = *reinterpret_cast<const uint16_t*>(base + bmn_offset(k0 + e, c2));
+    // An MN-major operand's fragment for columns col0 .. col0+31 (m or n):
+    // lane l gets k = 16 kk + 8 (l/32) + e (e = 0..7) of column col0 + l%32.
+    // Lane group G = l/16 covers columns col0 + 16 (G%2) + 0..15 and, for
+    // read r, k0 = 16 kk + 8 (G/2) + 4r; its lane i supplies row k0 + i/4,
+    // columns +4 (i%4) .. +3, and receives the 4 k of its own column.
+    const int tr_g = lane >> 4, tr_i = lane & 15;
+    auto gather = [&](const char* base, int col0, int kk) {
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+      const uint32_t c2 = 2u * (uint32_t)(col0 + 16 * (tr_g & 1) + 4 * (tr_i & 3));
       u32x4 v;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = h[2 * q] | (h[2 * q + 1] << 16);
+      for (int r = 0; r < 2; ++r) {
+        const uint32_t k = (uint32_t)(16 * kk + 8 * (tr_g >> 1) + 4 * r + (tr_i >> 2));
+        const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)((__attribute__((address_space(3))) char*)base + bmn_offset(k, c2)));
+        const u32x2 w = __builtin_bit_cast(u32x2, t);
+        v[2 * r] = w[0];
+        v[2 * r + 1] = w[1];
+      }
       return v;
     };
     auto read = [&](Frags& f, int t) {
@@ -132,14 +142,14 @@ struct DeepTile {
           if constexpr (!AMn)
             f.a[kk][fm] = lds_read16(as, o.a[kk] + fm * 32 * 128);
           else
-            f.a[kk][fm] = gather(as, wm * 32 + lrow, kk);
+            f.a[kk][fm] = gather(as, wm * 32, kk);
         }
 #pragma unroll
         for (int fn = 0; fn < kFN; ++fn) {
           if constexpr (!BMn)
             f.b[kk][fn] = lds_read16(bs, o.b[kk] + fn * 32 * 128);
           else
-            f.b[kk][fn] = gather(bs, wn * 32 + lrow, kk);
+            f.b[kk][fn] = gather(bs, wn * 32, kk);
         }
       }
     };

@@ -259,6 +259,29 @@ def test_16x16_d_staging_conflict_free(model):
     assert (wr, rd) == (1, 1)
 
 
+def test_mn_major_transposing_reads_conflict_free(model):
+    # The 64x64 deep-ring kernel keeps an MN-major operand one 128-byte row
+    # per k, chunks of rows with bit 1 set rotated by 64 bytes.  A fragment
+    # (columns c0..c0+31, 16 wide K step kk) is two ds_read_b64_tr_b16: lane
+    # l (group G = l/16, i = l%16) reads 8 bytes of row 16kk + 8(G/2) + 4r +
+    # i/4 at column c0 + 16(G%2) + 4(i%4).
+    off = lambda k, byte: k * 128 + ((byte + 64 * ((k >> 1) & 1)) % 128)
+    worst = 0
+    for c0 in (0, 32):
+        for kk in range(4):
+            for r in range(2):
+                a = [off(16 * kk + 8 * ((l // 16) // 2) + 4 * r + (l % 16) // 4,
+                         2 * (c0 + 16 * ((l // 16) % 2) + 4 * ((l % 16) % 4)))
+                     for l in range(64)]
+                worst = max(worst, _degree(model, "r64", a))
+    assert worst == 1
+    # with the rotation on bit 3 instead, rows k0 and k0+2 share their banks
+    off3 = lambda k, byte: k * 128 + ((byte + 64 * ((k >> 3) & 1)) % 128)
+    a = [off3(8 * ((l // 16) // 2) + (l % 16) // 4, 2 * (16 * ((l // 16) % 2) + 4 * (l % 4)))
+         for l in range(64)]
+    assert _degree(model, "r64", a) == 2
+
+
 @pytest.mark.parametrize("kfm,kfn", [(1, 1), (2, 2)])
 def test_fp32_d_staging_conflict_free(model, kfm, kfn):
     # The deep-ring kernels' fp32 D (64x64 tiles: a 32x32 block per wave;
