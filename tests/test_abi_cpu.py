@@ -79,6 +79,11 @@ def test_gemm_strided_run_rejects(kw, code):
     assert sg.gemm_last_error().startswith("gemm_strided_run")
 
 
+def test_cblock_layout_rejects_null():
+    assert sg.load().gemm_lds_layout_cblock(None) == NULL
+    assert sg.gemm_last_error().startswith("gemm_lds_layout_cblock")
+
+
 def test_gemm_strided_run_unread_operands_may_be_null():
     # alpha == 0 reads neither A nor B, beta == 0 does not read C: no
     # launch happens for M = 0, and the checks that remain pass.
