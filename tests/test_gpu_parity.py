@@ -165,6 +165,26 @@ def test_dense_deep_ring_integer_exact(dev, tiles):
     assert np.array_equal(d.cpu().numpy().astype(np.int64), want)
 
 
+@pytest.mark.parametrize("a_major,b_major", [("k", "k"), ("mn", "k"), ("k", "mn"), ("mn", "mn")])
+@pytest.mark.parametrize("K", [448, 512, 576, 640])
+def test_dense_64_tiles_majorness_integer_exact(dev, a_major, b_major, K):
+    # 64x64 tiles (520 x 392: 81 tiles) with 7..10 K tiles: from 8 K tiles on
+    # (unless both operands are MN-major) the kernel reads fragments two K
+    # tiles ahead, with every remainder of its three-way unrolled loop; with 7
+    # the one-ahead loop runs.  Integer values keep every sum exact in fp32.
+    M, N = 520, 392
+    a = si.integer_valued((M, K), 97 + K)
+    b = si.integer_valued((N, K), 98 + K)
+    A, B = si.to_bf16(a), si.to_bf16(b)
+    A = A if a_major == "k" else A.t().contiguous()
+    B = B if b_major == "k" else B.t().contiguous()
+    say(f"integer-valued exact, 64-tile {M}x{N}x{K} {a_major}/{b_major}")
+    d = sg.gemm(A.to(dev), B.to(dev), a_major=a_major, b_major=b_major, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = a.astype(np.int64) @ b.astype(np.int64).T
+    assert np.array_equal(d.cpu().numpy().astype(np.int64), want)
+
+
 @pytest.mark.parametrize("c_dtype,d_dtype", [(None, "bf16"), ("bf16", "bf16"),
                                              ("f16", "f16"), ("f32", "bf16"),
                                              ("bf16", "f32")])
