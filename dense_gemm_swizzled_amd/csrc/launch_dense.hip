@@ -26,10 +26,10 @@ hipError_t go_dense(const DenseParams& p, hipStream_t s) {
 
 // 256x256 tiles with both operands K-major run the ping-pong mainloop with
 // 16x16x32 MFMAs.
-template <bool BF, int Swz>
+template <bool BF, int Swz, bool BMn = false>
 hipError_t go_pingpong(const DenseParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((pingpong16_gemm_kernel<BF, Swz>), dim3(p.tiles_m * p.tiles_n), dim3(512),
-                     0, s, p);
+  hipLaunchKernelGGL((pingpong16_gemm_kernel<BF, Swz, BMn>), dim3(p.tiles_m * p.tiles_n),
+                     dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
@@ -79,6 +79,10 @@ hipError_t dense_by_major(bool a_mn, bool b_mn, const DenseParams& p, hipStream_
     if ((int64_t)p.tiles_m * p.tiles_n <= device_cus()) return go_deep<128, BF, false, false>(p, s);
     return go_dense<BM, BN, BF, false, false, Swz>(p, s);
   }
+  // An MN-major B on 256x256 tiles takes the ping-pong when K is a multiple
+  // of 64 with at least two K tiles (its loader and ring start assume both).
+  if (BM == 256 && !a_mn && b_mn && p.K % 64 == 0 && p.K >= 128)
+    return go_pingpong<BF, Swz, true>(p, s);
   if (!a_mn && b_mn) return go_dense<BM, BN, BF, false, true, Swz>(p, s);
   if (a_mn && !b_mn) return go_dense<BM, BN, BF, true, false, Swz>(p, s);
   return go_dense<BM, BN, BF, true, true, Swz>(p, s);

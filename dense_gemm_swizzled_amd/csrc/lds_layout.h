@@ -99,6 +99,17 @@ SG_HD uint32_t mxfp6_lds_offset(uint32_t row, uint32_t byte, uint32_t unshifted)
   return lds_offset<128, kSwzDefault>(row, b >> 4) + (b & 15u);
 }
 
+// An MN-major B half tile of the 256x256 kernel of 16x16x32 MFMAs: one
+// 256-byte LDS row per k (128 n values), its 32-byte units (16 n) placed at
+// unit XOR mn256_key(k).  A fragment read (ds_read_b64_tr_b16) covers, per
+// 32 lanes, rows k0..k0+3 and k0+8..k0+11 at one 32-byte unit; the key
+// gives those eight rows eight different units, so the read meets the 64
+// banks once.  Returns the byte offset of byte `byte` of row k.
+SG_HD constexpr uint32_t mn256_key(uint32_t k) { return (k & 3u) | (((k >> 3) & 1u) << 2); }
+SG_HD constexpr uint32_t mn256_lds_offset(uint32_t k, uint32_t byte) {
+  return k * 256u + 32u * ((byte >> 5) ^ mn256_key(k)) + (byte & 31u);
+}
+
 // The C block that the 256x256 kernel of 16x16x32 MFMAs brings into LDS
 // through the loads of its last two K tiles (a 16-bit C): wave w4 of a
 // group owns 128 output rows x 64 columns, and row r, 16-byte chunk c (8

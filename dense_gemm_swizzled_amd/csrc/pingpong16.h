@@ -25,7 +25,10 @@
 
 namespace sg {
 
-template <bool IsBF16, int Swz>
+// BMn: B is MN-major ([K][N]); its half tiles hold one 256-byte row per k
+// (mn256_lds_offset) and its fragments come from transposing reads.  Only
+// for K a multiple of 64 with at least two K tiles.
+template <bool IsBF16, int Swz, bool BMn = false>
 struct PingPong16Tile {
   using PP = PingPongTile<IsBF16, Swz>;
   static constexpr int kHalfBytes = PP::kHalfBytes;
@@ -45,6 +48,7 @@ struct PingPong16Tile {
   // share the XOR key).
   struct Offsets {
     uint32_t a[2][2], b[2][2];
+    uint32_t bt[kJ];  // MN-major B: block j, K half 0, read 0 (see read)
   };
 
   __device__ __forceinline__ static Offsets offsets(int g, int w4, int lane) {
@@ -58,7 +62,48 @@ struct PingPong16Tile {
         o.b[kh][q] = (w4 >> 1) * kHalfBytes +
                      lds_offset<128, Swz>((w4 & 1) * 64 + 16 * q + r, 4 * kh + c);
       }
+    if constexpr (BMn) {
+      // Lane group c = l/16 takes k rows 8c + 4r + 32kh .. +3 (read r, K half
+      // kh), lane r = l%16 supplies row (l%16)/4 of them at columns
+      // 64(w4%2) + 16j + 4(l%4) of its half; the key is the same for every r
+      // and kh (they add 4r + 32kh to k).
+#pragma unroll
+      for (int jb = 0; jb < kJ; ++jb)
+        o.bt[jb] = (w4 >> 1) * kHalfBytes +
+                   mn256_lds_offset((uint32_t)(8 * c + (r >> 2)),
+                                    2u * (uint32_t)(64 * (w4 & 1) + 16 * jb + 4 * (r & 3)));
+    }
     return o;
+  }
+
+  // Two transposing reads give lane l the 8 k (32kh + 8(l/16) .. +7) of the
+  // column l%16 of block j: in each 16-lane group, lane i reads 4 columns of
+  // one k row and receives the 4 k of its own column.
+  __device__ __forceinline__ static u32x4 read_bt(const char* bt, uint32_t off) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    typedef __attribute__((address_space(3))) char lds_char;
+    const v4i16 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)bt + off));
+    const v4i16 t1 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)bt + off + 1024u));
+    const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
+    return u32x4{w0[0], w0[1], w1[0], w1[1]};
+  }
+
+  // The K-exact loader of an MN-major B half (group g: columns 128g .. +128
+  // of the tile): load q of wave w4 fills region 4q + w4 with k rows 4(4q +
+  // w4) .. +3, lane l taking row l/16 and the 16 bytes whose place is
+  // 16(l%16) (the unit XOR is its own inverse); columns past the tile read
+  // as zero.  The K position (64 rows a tile) travels in the SGPR offset.
+  __device__ __forceinline__ static void init_bmn(KExactHalfLoader<Swz>& x, int g, int w4,
+                                                  int lane, uint32_t pitch, int cols) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t k = (uint32_t)(4 * (4 * q + w4) + (lane >> 4));
+      const uint32_t lbyte = mn256_lds_offset(k, 16u * (uint32_t)(lane & 15)) - k * 256u;
+      const int col = (int)(lbyte >> 1);
+      x.voff[q] = col < cols ? k * pitch + 2u * (uint32_t)(128 * g + col) : kOutOfRange;
+    }
   }
 
   __device__ __forceinline__ static void read(Frags& f, const char* at, const char* bt,
@@ -66,7 +111,12 @@ struct PingPong16Tile {
 #pragma unroll
     for (int i = 0; i < kI; ++i) f.a[i] = lds_read16(at, o.a[kh][i & 1] + (i >> 1) * 4096);
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) f.b[j] = lds_read16(bt, o.b[kh][j & 1] + (j >> 1) * 4096);
+    for (int j = 0; j < kJ; ++j) {
+      if constexpr (BMn)
+        f.b[j] = read_bt(bt, o.bt[j] + 8192u * (uint32_t)kh);
+      else
+        f.b[j] = lds_read16(bt, o.b[kh][j & 1] + (j >> 1) * 4096);
+    }
   }
 
   // 32 MFMAs with the four loads of one half tile between them, one per
@@ -208,14 +258,14 @@ struct PingPong16Tile {
       f32x4 (&acc)[kI][kJ], const KExactHalfLoader<Swz>& la, const KExactHalfLoader<Swz>& lb,
       u32x4 ra, u32x4 rb, u32x4 ra0, u32x4 rb0, uint32_t a_ring, uint32_t b_ring,
       const char* a_rd, const char* b_rd, const Offsets& o, int g, int w4, int T,
-      const TileJob& j, const void* C, int lane) {
+      const TileJob& j, const void* C, int lane, uint32_t kstep_b) {
     if (g) PP::barrier();  // group 1 runs one phase behind group 0
     int bs = 0;            // t mod 3
     int t = 0;
     for (; t + 2 < T; ++t) {
-      const uint32_t k2 = (uint32_t)(t + 2) * 128u;
-      ktile<Active, 8, 8, 8, 8>(acc, t, bs, lb, rb, k2, la, ra, k2, a_ring, b_ring, a_rd, b_rd,
-                                o, w4);
+      const uint32_t k2 = (uint32_t)(t + 2) * 128u, kb2 = (uint32_t)(t + 2) * kstep_b;
+      ktile<Active, 8, 8, 8, 8>(acc, t, bs, lb, rb, kb2, la, ra, k2, a_ring, b_ring, a_rd,
+                                b_rd, o, w4);
       bs = bs == 2 ? 0 : bs + 1;
     }
     if constexpr (LdsC) {
@@ -376,13 +426,25 @@ struct PingPong16Tile {
 
     const uint32_t kbytes = (uint32_t)K * 2u;
     const int T = (int)((K + kBK - 1) / kBK);
+    // Bytes of B's descriptor per K tile: 64 k of a K-major row, or 64 rows
+    // of an MN-major B.
+    const uint32_t kstep_b = BMn ? 64u * j.b_pitch : 128u;
+    KExactHalfLoader<Swz> xbm;
+    if constexpr (BMn) init_bmn(xbm, g, w4, lane, j.b_pitch, b_rows);
 
     // Tiles 0 and 1 (B before A, the order the mainloop keeps).
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      if constexpr (BMn) {
+        xbm.template issue<0>(rb, b_ring + t * kTileBytes, w4, t * kstep_b);
+        xbm.template issue<1>(rb, b_ring + t * kTileBytes, w4, t * kstep_b);
+        xbm.template issue<2>(rb, b_ring + t * kTileBytes, w4, t * kstep_b);
+        xbm.template issue<3>(rb, b_ring + t * kTileBytes, w4, t * kstep_b);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        lb.issue(rb, b_ring + t * kTileBytes, w4, i, b_rows, t * 128u, kbytes);
+        for (int i = 0; i < 4; ++i)
+          lb.issue(rb, b_ring + t * kTileBytes, w4, i, b_rows, t * 128u, kbytes);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         la.issue(ra, a_ring + t * kTileBytes, w4, i, a_rows, t * 128u, kbytes);
@@ -400,23 +462,26 @@ struct PingPong16Tile {
     // with at most 128 valid rows) runs the mainloop without its MFMAs.
     // A 16-bit C comes in through the last two K tiles' loads when K is a
     // multiple of 64 and 128 C rows stay within 32-bit buffer offsets.
-    const bool kexact = (K & (kBK - 1)) == 0;
+    const bool kexact = BMn || (K & (kBK - 1)) == 0;
     const bool ldsc = kexact && T >= 2 && C != nullptr &&
                       (c_dtype == SG_BF16 || c_dtype == SG_F16) && j.ldc <= (int64_t{1} << 22);
     if (kexact) {
       KExactHalfLoader<Swz> xa, xb;
       xa.init(la, a_rows);
-      xb.init(lb, b_rows);
+      if constexpr (BMn)
+        xb = xbm;
+      else
+        xb.init(lb, b_rows);
       const u32x4 ra0 = rsrc_words(j.a, 0), rb0 = rsrc_words(j.b, 0);
       if (a_rows > 0 && ldsc)
         mainloop_x<true, true>(acc, xa, xb, ra, rb, ra0, rb0, a_ring, b_ring, a_rd, b_rd, o, g,
-                               w4, T, j, C, lane);
+                               w4, T, j, C, lane, kstep_b);
       else if (a_rows > 0)
         mainloop_x<true, false>(acc, xa, xb, ra, rb, ra0, rb0, a_ring, b_ring, a_rd, b_rd, o, g,
-                                w4, T, j, C, lane);
+                                w4, T, j, C, lane, kstep_b);
       else
         mainloop_x<false, false>(acc, xa, xb, ra, rb, ra0, rb0, a_ring, b_ring, a_rd, b_rd, o,
-                                 g, w4, T, j, C, lane);
+                                 g, w4, T, j, C, lane, kstep_b);
     } else if (a_rows > 0) {
       mainloop<true>(acc, la, lb, ra, rb, a_rows, b_rows, a_ring, b_ring, a_rd, b_rd, o, g, w4,
                      T, kbytes);
@@ -442,11 +507,11 @@ struct PingPong16Tile {
   }
 };
 
-template <bool IsBF16, int Swz>
+template <bool IsBF16, int Swz, bool BMn = false>
 __global__ void __launch_bounds__(512, 1) pingpong16_gemm_kernel(const DenseParams p) {
-  using Tile = PingPong16Tile<IsBF16, Swz>;
+  using Tile = PingPong16Tile<IsBF16, Swz, BMn>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
-  const TileJob j = dense_tile_job<256, 256, false, false>(p, blockIdx.x);
+  const TileJob j = dense_tile_job<256, 256, false, BMn>(p, blockIdx.x);
   Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.ldd);
 }
 

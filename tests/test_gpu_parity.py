@@ -321,6 +321,34 @@ def test_dense_in_place_c_equals_d(dev):
     check_close(_np(CD), ref, bound, "f32", "in-place")
 
 
+@pytest.mark.parametrize("K", [128, 320, 1024])
+def test_dense_256_tiles_mn_major_b_integer_exact(dev, K):
+    # B stored [K][N] on 256x256 tiles: the ping-pong keeps it one 256-byte
+    # LDS row per k and reads fragments with transposing reads.  Ragged M and
+    # N (4 rows, 8 columns in the last tiles); two, five and sixteen K tiles.
+    M, N = 4100, 4104
+    a = si.integer_valued((M, K), 131 + K)
+    b = si.integer_valued((N, K), 132 + K)
+    A = si.to_bf16(a)
+    B = si.to_bf16(b).t().contiguous()
+    say(f"integer-valued exact, 256 tiles, MN-major B {M}x{N}x{K}")
+    d = sg.gemm(A.to(dev), B.to(dev), b_major="mn", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = a.astype(np.int64) @ b.astype(np.int64).T
+    assert np.array_equal(d.cpu().numpy().astype(np.int64), want)
+
+
+def test_dense_256_tiles_mn_major_b_with_c(dev):
+    # The same path with a bf16 C brought in by the last loads and bf16 D.
+    M, N, K = 4100, 4104, 192
+    case = si.dense_case(M, N, K, 133, ab_dtype="bf16", b_major="mn", with_c=True,
+                         c_dtype="bf16", d_dtype="bf16", scale=1.0 / np.sqrt(K))
+    say(f"256 tiles, MN-major B, bf16 C {M}x{N}x{K}")
+    d = run_dense(case, dev)
+    ref, bound = oracle_dense(case)
+    check_close(_np(d), ref, bound, "bf16", "256 tiles MN-major B")
+
+
 def test_dense_256_tiles_in_place_bf16(dev):
     # C == D on the 256x256 kernel with a bf16 C: each wave's C block comes
     # into LDS with the last K tiles' loads, before any of its D is written.

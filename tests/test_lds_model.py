@@ -282,6 +282,26 @@ def test_mn_major_transposing_reads_conflict_free(model):
     assert _degree(model, "r64", a) == 2
 
 
+def test_mn_major_b_256_tiles_conflict_free(model):
+    # The 256x256 kernel's MN-major B half: one 256-byte row per k, 32-byte
+    # unit u of row k at u XOR ((k % 4) + 4 ((k / 8) % 2)).  Lane l (group c =
+    # l/16, i = l%16) of wave w4 reads 8 bytes of row 32kh + 8c + 4r + i/4 at
+    # column 64(w4%2) + 16j + 4(i%4) (ds_read_b64_tr_b16).
+    key = lambda k: (k % 4) | (((k >> 3) & 1) << 2)
+    off = lambda k, byte: k * 256 + 32 * ((byte >> 5) ^ key(k)) + byte % 32
+    assert sorted(off(k, b) for k in range(64) for b in range(0, 256, 16)) == \
+        list(range(0, 16384, 16))
+    worst = 0
+    for w4 in range(4):
+        for j in range(4):
+            for kh in range(2):
+                for r in range(2):
+                    a = [off(32 * kh + 8 * (l // 16) + 4 * r + (l % 16) // 4,
+                             2 * (64 * (w4 % 2) + 16 * j + 4 * (l % 4))) for l in range(64)]
+                    worst = max(worst, _degree(model, "r64", a))
+    assert worst == 1
+
+
 @pytest.mark.parametrize("kfm,kfn", [(1, 1), (2, 2)])
 def test_fp32_d_staging_conflict_free(model, kfm, kfn):
     # The deep-ring kernels' fp32 D (64x64 tiles: a 32x32 block per wave;
