@@ -26,9 +26,9 @@ hipError_t go_dense(const DenseParams& p, hipStream_t s) {
 
 // 256x256 tiles with both operands K-major run the ping-pong mainloop with
 // 16x16x32 MFMAs.
-template <bool BF, int Swz, bool BMn = false>
+template <bool BF, int Swz, bool AMn = false, bool BMn = false>
 hipError_t go_pingpong(const DenseParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((pingpong16_gemm_kernel<BF, Swz, BMn>), dim3(p.tiles_m * p.tiles_n),
+  hipLaunchKernelGGL((pingpong16_gemm_kernel<BF, Swz, AMn, BMn>), dim3(p.tiles_m * p.tiles_n),
                      dim3(512), 0, s, p);
   return hipGetLastError();
 }
@@ -79,10 +79,14 @@ hipError_t dense_by_major(bool a_mn, bool b_mn, const DenseParams& p, hipStream_
     if ((int64_t)p.tiles_m * p.tiles_n <= device_cus()) return go_deep<128, BF, false, false>(p, s);
     return go_dense<BM, BN, BF, false, false, Swz>(p, s);
   }
-  // An MN-major B on 256x256 tiles takes the ping-pong when K is a multiple
-  // of 64 with at least two K tiles (its loader and ring start assume both).
-  if (BM == 256 && !a_mn && b_mn && p.K % 64 == 0 && p.K >= 128)
-    return go_pingpong<BF, Swz, true>(p, s);
+  // MN-major operands on 256x256 tiles take the ping-pong when K is a
+  // multiple of 64 with at least two K tiles (its loader and ring start
+  // assume both).
+  if (BM == 256 && p.K % 64 == 0 && p.K >= 128) {
+    if (!a_mn && b_mn) return go_pingpong<BF, Swz, false, true>(p, s);
+    if (a_mn && !b_mn) return go_pingpong<BF, Swz, true, false>(p, s);
+    if (a_mn && b_mn) return go_pingpong<BF, Swz, true, true>(p, s);
+  }
   if (!a_mn && b_mn) return go_dense<BM, BN, BF, false, true, Swz>(p, s);
   if (a_mn && !b_mn) return go_dense<BM, BN, BF, true, false, Swz>(p, s);
   return go_dense<BM, BN, BF, true, true, Swz>(p, s);

@@ -25,10 +25,11 @@
 
 namespace sg {
 
-// BMn: B is MN-major ([K][N]); its half tiles hold one 256-byte row per k
-// (mn256_lds_offset) and its fragments come from transposing reads.  Only
-// for K a multiple of 64 with at least two K tiles.
-template <bool IsBF16, int Swz, bool BMn = false>
+// AMn / BMn: A is [K][M] / B is [K][N] (MN-major); such an operand's half
+// tiles hold one 256-byte row per k (mn256_lds_offset) and its fragments
+// come from transposing reads.  Only for K a multiple of 64 with at least
+// two K tiles.
+template <bool IsBF16, int Swz, bool AMn = false, bool BMn = false>
 struct PingPong16Tile {
   using PP = PingPongTile<IsBF16, Swz>;
   static constexpr int kHalfBytes = PP::kHalfBytes;
@@ -49,6 +50,7 @@ struct PingPong16Tile {
   struct Offsets {
     uint32_t a[2][2], b[2][2];
     uint32_t bt[kJ];  // MN-major B: block j, K half 0, read 0 (see read)
+    uint32_t at[kI];  // MN-major A: block i, the same
   };
 
   __device__ __forceinline__ static Offsets offsets(int g, int w4, int lane) {
@@ -73,6 +75,12 @@ struct PingPong16Tile {
                    mn256_lds_offset((uint32_t)(8 * c + (r >> 2)),
                                     2u * (uint32_t)(64 * (w4 & 1) + 16 * jb + 4 * (r & 3)));
     }
+    if constexpr (AMn) {  // the group's own half, all 128 m
+#pragma unroll
+      for (int ib = 0; ib < kI; ++ib)
+        o.at[ib] = g * kHalfBytes + mn256_lds_offset((uint32_t)(8 * c + (r >> 2)),
+                                                     2u * (uint32_t)(16 * ib + 4 * (r & 3)));
+    }
     return o;
   }
 
@@ -90,7 +98,7 @@ struct PingPong16Tile {
     return u32x4{w0[0], w0[1], w1[0], w1[1]};
   }
 
-  // The K-exact loader of an MN-major B half (group g: columns 128g .. +128
+  // The K-exact loader of an MN-major half (group g: columns 128g .. +128
   // of the tile): load q of wave w4 fills region 4q + w4 with k rows 4(4q +
   // w4) .. +3, lane l taking row l/16 and the 16 bytes whose place is
   // 16(l%16) (the unit XOR is its own inverse); columns past the tile read
@@ -109,7 +117,12 @@ struct PingPong16Tile {
   __device__ __forceinline__ static void read(Frags& f, const char* at, const char* bt,
                                               const Offsets& o, int kh) {
 #pragma unroll
-    for (int i = 0; i < kI; ++i) f.a[i] = lds_read16(at, o.a[kh][i & 1] + (i >> 1) * 4096);
+    for (int i = 0; i < kI; ++i) {
+      if constexpr (AMn)
+        f.a[i] = read_bt(at, o.at[i] + 8192u * (uint32_t)kh);
+      else
+        f.a[i] = lds_read16(at, o.a[kh][i & 1] + (i >> 1) * 4096);
+    }
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       if constexpr (BMn)
@@ -258,13 +271,13 @@ struct PingPong16Tile {
       f32x4 (&acc)[kI][kJ], const KExactHalfLoader<Swz>& la, const KExactHalfLoader<Swz>& lb,
       u32x4 ra, u32x4 rb, u32x4 ra0, u32x4 rb0, uint32_t a_ring, uint32_t b_ring,
       const char* a_rd, const char* b_rd, const Offsets& o, int g, int w4, int T,
-      const TileJob& j, const void* C, int lane, uint32_t kstep_b) {
+      const TileJob& j, const void* C, int lane, uint32_t kstep_a, uint32_t kstep_b) {
     if (g) PP::barrier();  // group 1 runs one phase behind group 0
     int bs = 0;            // t mod 3
     int t = 0;
     for (; t + 2 < T; ++t) {
-      const uint32_t k2 = (uint32_t)(t + 2) * 128u, kb2 = (uint32_t)(t + 2) * kstep_b;
-      ktile<Active, 8, 8, 8, 8>(acc, t, bs, lb, rb, kb2, la, ra, k2, a_ring, b_ring, a_rd,
+      const uint32_t ka2 = (uint32_t)(t + 2) * kstep_a, kb2 = (uint32_t)(t + 2) * kstep_b;
+      ktile<Active, 8, 8, 8, 8>(acc, t, bs, lb, rb, kb2, la, ra, ka2, a_ring, b_ring, a_rd,
                                 b_rd, o, w4);
       bs = bs == 2 ? 0 : bs + 1;
     }
@@ -428,8 +441,10 @@ struct PingPong16Tile {
     const int T = (int)((K + kBK - 1) / kBK);
     // Bytes of B's descriptor per K tile: 64 k of a K-major row, or 64 rows
     // of an MN-major B.
+    const uint32_t kstep_a = AMn ? 64u * j.a_pitch : 128u;
     const uint32_t kstep_b = BMn ? 64u * j.b_pitch : 128u;
-    KExactHalfLoader<Swz> xbm;
+    KExactHalfLoader<Swz> xam, xbm;
+    if constexpr (AMn) init_bmn(xam, g, w4, lane, j.a_pitch, a_rows);
     if constexpr (BMn) init_bmn(xbm, g, w4, lane, j.b_pitch, b_rows);
 
     // Tiles 0 and 1 (B before A, the order the mainloop keeps).
@@ -445,9 +460,16 @@ struct PingPong16Tile {
         for (int i = 0; i < 4; ++i)
           lb.issue(rb, b_ring + t * kTileBytes, w4, i, b_rows, t * 128u, kbytes);
       }
+      if constexpr (AMn) {
+        xam.template issue<0>(ra, a_ring + t * kTileBytes, w4, t * kstep_a);
+        xam.template issue<1>(ra, a_ring + t * kTileBytes, w4, t * kstep_a);
+        xam.template issue<2>(ra, a_ring + t * kTileBytes, w4, t * kstep_a);
+        xam.template issue<3>(ra, a_ring + t * kTileBytes, w4, t * kstep_a);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        la.issue(ra, a_ring + t * kTileBytes, w4, i, a_rows, t * 128u, kbytes);
+        for (int i = 0; i < 4; ++i)
+          la.issue(ra, a_ring + t * kTileBytes, w4, i, a_rows, t * 128u, kbytes);
+      }
     }
     PP::end_phase();
 
@@ -462,12 +484,15 @@ struct PingPong16Tile {
     // with at most 128 valid rows) runs the mainloop without its MFMAs.
     // A 16-bit C comes in through the last two K tiles' loads when K is a
     // multiple of 64 and 128 C rows stay within 32-bit buffer offsets.
-    const bool kexact = BMn || (K & (kBK - 1)) == 0;
+    const bool kexact = AMn || BMn || (K & (kBK - 1)) == 0;
     const bool ldsc = kexact && T >= 2 && C != nullptr &&
                       (c_dtype == SG_BF16 || c_dtype == SG_F16) && j.ldc <= (int64_t{1} << 22);
     if (kexact) {
       KExactHalfLoader<Swz> xa, xb;
-      xa.init(la, a_rows);
+      if constexpr (AMn)
+        xa = xam;
+      else
+        xa.init(la, a_rows);
       if constexpr (BMn)
         xb = xbm;
       else
@@ -475,13 +500,13 @@ struct PingPong16Tile {
       const u32x4 ra0 = rsrc_words(j.a, 0), rb0 = rsrc_words(j.b, 0);
       if (a_rows > 0 && ldsc)
         mainloop_x<true, true>(acc, xa, xb, ra, rb, ra0, rb0, a_ring, b_ring, a_rd, b_rd, o, g,
-                               w4, T, j, C, lane, kstep_b);
+                               w4, T, j, C, lane, kstep_a, kstep_b);
       else if (a_rows > 0)
         mainloop_x<true, false>(acc, xa, xb, ra, rb, ra0, rb0, a_ring, b_ring, a_rd, b_rd, o, g,
-                                w4, T, j, C, lane, kstep_b);
+                                w4, T, j, C, lane, kstep_a, kstep_b);
       else
         mainloop_x<false, false>(acc, xa, xb, ra, rb, ra0, rb0, a_ring, b_ring, a_rd, b_rd, o,
-                                 g, w4, T, j, C, lane, kstep_b);
+                                 g, w4, T, j, C, lane, kstep_a, kstep_b);
     } else if (a_rows > 0) {
       mainloop<true>(acc, la, lb, ra, rb, a_rows, b_rows, a_ring, b_ring, a_rd, b_rd, o, g, w4,
                      T, kbytes);
@@ -507,11 +532,11 @@ struct PingPong16Tile {
   }
 };
 
-template <bool IsBF16, int Swz, bool BMn = false>
+template <bool IsBF16, int Swz, bool AMn = false, bool BMn = false>
 __global__ void __launch_bounds__(512, 1) pingpong16_gemm_kernel(const DenseParams p) {
-  using Tile = PingPong16Tile<IsBF16, Swz, BMn>;
+  using Tile = PingPong16Tile<IsBF16, Swz, AMn, BMn>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
-  const TileJob j = dense_tile_job<256, 256, false, BMn>(p, blockIdx.x);
+  const TileJob j = dense_tile_job<256, 256, AMn, BMn>(p, blockIdx.x);
   Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.ldd);
 }
 

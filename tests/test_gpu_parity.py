@@ -321,28 +321,33 @@ def test_dense_in_place_c_equals_d(dev):
     check_close(_np(CD), ref, bound, "f32", "in-place")
 
 
+@pytest.mark.parametrize("a_major,b_major", [("k", "mn"), ("mn", "k"), ("mn", "mn")])
 @pytest.mark.parametrize("K", [128, 320, 1024])
-def test_dense_256_tiles_mn_major_b_integer_exact(dev, K):
-    # B stored [K][N] on 256x256 tiles: the ping-pong keeps it one 256-byte
-    # LDS row per k and reads fragments with transposing reads.  Ragged M and
-    # N (4 rows, 8 columns in the last tiles); two, five and sixteen K tiles.
-    M, N = 4100, 4104
+def test_dense_256_tiles_mn_major_integer_exact(dev, a_major, b_major, K):
+    # A stored [K][M] and/or B stored [K][N] on 256x256 tiles: the ping-pong
+    # keeps such an operand one 256-byte LDS row per k and reads fragments
+    # with transposing reads.  Ragged M and N (8 rows and columns in the last
+    # tiles: MN-major rows need a multiple of 8 elements); two, five and
+    # sixteen K tiles.
+    M, N = 4104, 4104
     a = si.integer_valued((M, K), 131 + K)
     b = si.integer_valued((N, K), 132 + K)
-    A = si.to_bf16(a)
-    B = si.to_bf16(b).t().contiguous()
-    say(f"integer-valued exact, 256 tiles, MN-major B {M}x{N}x{K}")
-    d = sg.gemm(A.to(dev), B.to(dev), b_major="mn", out_dtype=torch.float32)
+    A = si.to_bf16(a) if a_major == "k" else si.to_bf16(a).t().contiguous()
+    B = si.to_bf16(b) if b_major == "k" else si.to_bf16(b).t().contiguous()
+    say(f"integer-valued exact, 256 tiles, {a_major}/{b_major} {M}x{N}x{K}")
+    d = sg.gemm(A.to(dev), B.to(dev), a_major=a_major, b_major=b_major,
+                out_dtype=torch.float32)
     torch.cuda.synchronize()
     want = a.astype(np.int64) @ b.astype(np.int64).T
     assert np.array_equal(d.cpu().numpy().astype(np.int64), want)
 
 
-def test_dense_256_tiles_mn_major_b_with_c(dev):
-    # The same path with a bf16 C brought in by the last loads and bf16 D.
-    M, N, K = 4100, 4104, 192
-    case = si.dense_case(M, N, K, 133, ab_dtype="bf16", b_major="mn", with_c=True,
-                         c_dtype="bf16", d_dtype="bf16", scale=1.0 / np.sqrt(K))
+def test_dense_256_tiles_mn_major_with_c(dev):
+    # Both operands MN-major with a bf16 C brought in by the last loads and
+    # bf16 D.
+    M, N, K = 4104, 4104, 192
+    case = si.dense_case(M, N, K, 133, ab_dtype="bf16", a_major="mn", b_major="mn",
+                         with_c=True, c_dtype="bf16", d_dtype="bf16", scale=1.0 / np.sqrt(K))
     say(f"256 tiles, MN-major B, bf16 C {M}x{N}x{K}")
     d = run_dense(case, dev)
     ref, bound = oracle_dense(case)
