@@ -75,9 +75,10 @@ def _run(dev, M, N, K, a_major, b_major, ab, Abuf, lda, Bbuf, ldb, Cbuf, ldc, ld
 @pytest.mark.parametrize("M,N,K", [(300, 264, 136), (4100, 4104, 136), (4100, 4104, 192),
                                    (300, 252, 136), (4100, 4108, 192)])
 def test_strided_scaled_parity(dev, a_major, b_major, ab, M, N, K):
-    # 300 x 264: 128x128 tiles; 4100 x 4104 with K-major operands: the
-    # 256x256 ping-pong, K = 136 on its checked loader, K = 192 on the
-    # loader for K a multiple of 64 (MN-major operands use 128x128 tiles).
+    # 300 x 264: 128x128 tiles; 4100 x 4104: 256x256 tiles, K = 136 on the
+    # ping-pong's checked loader (K-major operands) or the two-stage kernel
+    # (MN-major ones), K = 192 on the ping-pong's loader for K a multiple of
+    # 64 (MN-major operands through transposing reads).
     # N = 252 and 4108 leave 252 and 12 columns in the last tile column.
     Abuf, lda, Bbuf, ldb, Cbuf, ldc, ldd = _operands(M, N, K, a_major, b_major, ab, M + K)
     alpha, beta = 1.5, -0.75
