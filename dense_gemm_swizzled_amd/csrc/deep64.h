@@ -34,8 +34,7 @@ namespace sg {
 
 template <int BM, bool IsBF16, bool AMn, bool BMn>
 struct DeepTile {
-  static_assert(BM == 64 || (BM == 128 && !AMn && !BMn),
-                "128x128 tiles take K-major operands only");
+  static_assert(BM == 64 || BM == 128, "64x64 or 128x128 tiles");
   using Base = GemmTile<BM, BM, IsBF16, AMn, BMn, kSwzDefault, 4>;
   static constexpr int kFM = Base::kFM, kFN = Base::kFN;   // 32x32 blocks per wave
   static constexpr int kStages = BM == 64 ? 8 : 5;
@@ -50,8 +49,16 @@ struct DeepTile {
   static_assert(kFirst == 24 && (kLoop == 20 || kLoop == 16), "vmcnt immediates");
 
   // Byte offset, in an MN-major operand's stage, of byte `byte` of k-row k.
+  // 64x64 tiles: 128-byte rows, rows with bit 1 of k rotated by 64 bytes.
+  // 128x128 tiles: 256-byte rows, 32-byte unit u at u XOR 2(k mod 4): one
+  // transposing read covers 4 rows x 64 bytes (two units) per 32 lanes,
+  // which the key spreads over the 8 units of the bank line.
+  static constexpr uint32_t kMnRow = BM * 2;
   __device__ __forceinline__ static uint32_t bmn_offset(uint32_t k, uint32_t byte) {
-    return k * 128u + ((byte + 64u * ((k >> 1) & 1u)) & 127u);
+    if constexpr (BM == 64)
+      return k * 128u + ((byte + 64u * ((k >> 1) & 1u)) & 127u);
+    else
+      return k * 256u + 32u * ((byte >> 5) ^ (2u * (k & 3u))) + (byte & 31u);
   }
 
   __device__ __forceinline__ static void run(char* smem, const TileJob& j, int64_t K,
@@ -80,13 +87,26 @@ struct DeepTile {
 #pragma unroll
         for (int i = 0; i < BM / 32; ++i)
           ld.issue(rsrc, dst, wave, i, rows_valid, (uint32_t)t * 128u, kbytes);
-      } else {
+      } else if constexpr (BM == 64) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int r = 4 * i + wave, krow = 8 * r + (lane >> 3);
           const int64_t k = (int64_t)t * kBK + krow;
           const uint32_t c = (uint32_t)((lane & 7) + 4 * ((krow >> 1) & 1)) & 7u;
           const uint32_t off = k < K ? (uint32_t)k * pitch + 16u * c : kOutOfRange;
+          dma16(rsrc, off, dst + (uint32_t)r * 1024u);
+        }
+      } else {
+        // 128x128: region r holds k-rows 4r .. 4r+3; lane l fills physical
+        // bytes 16(l%16) of row 4r + l/16, which hold the logical bytes the
+        // (self-inverse) unit XOR maps there.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * i + wave, krow = 4 * r + (lane >> 4);
+          const int64_t k = (int64_t)t * kBK + krow;
+          const uint32_t lb = bmn_offset((uint32_t)krow, 16u * (uint32_t)(lane & 15)) -
+                              (uint32_t)krow * kMnRow;
+          const uint32_t off = k < K ? (uint32_t)k * pitch + lb : kOutOfRange;
           dma16(rsrc, off, dst + (uint32_t)r * 1024u);
         }
       }
@@ -142,14 +162,14 @@ struct DeepTile {
           if constexpr (!AMn)
             f.a[kk][fm] = lds_read16(as, o.a[kk] + fm * 32 * 128);
           else
-            f.a[kk][fm] = gather(as, wm * 32, kk);
+            f.a[kk][fm] = gather(as, wm * 32 * kFM + 32 * fm, kk);
         }
 #pragma unroll
         for (int fn = 0; fn < kFN; ++fn) {
           if constexpr (!BMn)
             f.b[kk][fn] = lds_read16(bs, o.b[kk] + fn * 32 * 128);
           else
-            f.b[kk][fn] = gather(bs, wn * 32, kk);
+            f.b[kk][fn] = gather(bs, wn * 32 * kFN + 32 * fn, kk);
         }
       }
     };

@@ -87,6 +87,13 @@ hipError_t dense_by_major(bool a_mn, bool b_mn, const DenseParams& p, hipStream_
     if (a_mn && !b_mn) return go_pingpong<BF, Swz, true, false>(p, s);
     if (a_mn && b_mn) return go_pingpong<BF, Swz, true, true>(p, s);
   }
+  // 128x128 tiles with an MN-major operand: the five-stage ring while the
+  // tiles fit in one round of the CUs.
+  if (BM == 128 && (int64_t)p.tiles_m * p.tiles_n <= device_cus()) {
+    if (!a_mn && b_mn) return go_deep<128, BF, false, true>(p, s);
+    if (a_mn && !b_mn) return go_deep<128, BF, true, false>(p, s);
+    if (a_mn && b_mn) return go_deep<128, BF, true, true>(p, s);
+  }
   if (!a_mn && b_mn) return go_dense<BM, BN, BF, false, true, Swz>(p, s);
   if (a_mn && !b_mn) return go_dense<BM, BN, BF, true, false, Swz>(p, s);
   return go_dense<BM, BN, BF, true, true, Swz>(p, s);

@@ -165,6 +165,24 @@ def test_dense_deep_ring_integer_exact(dev, tiles):
     assert np.array_equal(d.cpu().numpy().astype(np.int64), want)
 
 
+@pytest.mark.parametrize("a_major,b_major", [("mn", "k"), ("k", "mn"), ("mn", "mn")])
+def test_dense_128_tiles_deep_ring_mn_major_integer_exact(dev, a_major, b_major):
+    # 1800 x 1800: 225 tiles of 128x128, one round of CUs, so the five-stage
+    # ring runs; an MN-major operand keeps 256-byte LDS rows per k and is read
+    # with transposing reads.  K = 1000: 16 K tiles, the last partial.
+    M, N, K = 1800, 1800, 1000
+    a = si.integer_valued((M, K), 141)
+    b = si.integer_valued((N, K), 142)
+    A = si.to_bf16(a) if a_major == "k" else si.to_bf16(a).t().contiguous()
+    B = si.to_bf16(b) if b_major == "k" else si.to_bf16(b).t().contiguous()
+    say(f"integer-valued exact, 128-tile deep ring {a_major}/{b_major} {M}x{N}x{K}")
+    d = sg.gemm(A.to(dev), B.to(dev), a_major=a_major, b_major=b_major,
+                out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = a.astype(np.int64) @ b.astype(np.int64).T
+    assert np.array_equal(d.cpu().numpy().astype(np.int64), want)
+
+
 @pytest.mark.parametrize("a_major,b_major", [("k", "k"), ("mn", "k"), ("k", "mn"), ("mn", "mn")])
 @pytest.mark.parametrize("K", [448, 512, 576, 640])
 def test_dense_64_tiles_majorness_integer_exact(dev, a_major, b_major, K):

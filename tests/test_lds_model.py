@@ -282,6 +282,24 @@ def test_mn_major_transposing_reads_conflict_free(model):
     assert _degree(model, "r64", a) == 2
 
 
+def test_mn_major_128_tiles_deep_ring_conflict_free(model):
+    # The 128x128 deep ring's MN-major operand: 256-byte rows, 32-byte unit u
+    # of row k at u XOR 2(k % 4).  Lane l (group c = l/16, i = l%16) reads 8
+    # bytes of row 16kk + 8(c/2) + 4r + i/4 at column col0 + 16(c%2) + 4(i%4),
+    # col0 = 32 x (wave block) (ds_read_b64_tr_b16).
+    off = lambda k, byte: k * 256 + 32 * ((byte >> 5) ^ (2 * (k % 4))) + byte % 32
+    assert sorted(off(k, b) for k in range(64) for b in range(0, 256, 16)) == \
+        list(range(0, 16384, 16))
+    worst = 0
+    for col0 in range(0, 128, 32):
+        for kk in range(4):
+            for r in range(2):
+                a = [off(16 * kk + 8 * ((l // 16) // 2) + 4 * r + (l % 16) // 4,
+                         2 * (col0 + 16 * ((l // 16) % 2) + 4 * (l % 4))) for l in range(64)]
+                worst = max(worst, _degree(model, "r64", a))
+    assert worst == 1
+
+
 def test_mn_major_b_256_tiles_conflict_free(model):
     # The 256x256 kernel's MN-major B half: one 256-byte row per k, 32-byte
     # unit u of row k at u XOR ((k % 4) + 4 ((k / 8) % 2)).  Lane l (group c =
