@@ -1,6 +1,6 @@
 // deep64.h -- 64x64 tiles with an eight-stage LDS ring, for GEMMs too small
 // to give every CU more than one tile (M = N = K = 1024 is 256 such tiles),
-// and 128x128 tiles (K-major operands) with a five-stage ring, for GEMMs
+// and 128x128 tiles with a five-stage ring, for GEMMs
 // with fewer than 256 tiles of 256x256 (M = N = K = 2048 is 256 such tiles).
 //
 // Why.  Such a tile does 4 MFMAs per wave per 64-wide K tile, a few hundred
@@ -13,8 +13,9 @@
 //
 // Layout.  A K-major operand uses the XOR map lds_offset<128, 16> and the
 // fragment reads of GemmTile.  An MN-major operand is stored as it lies in
-// memory, one 128-byte LDS row per k (64 m or n values), with the 16-byte
-// chunks of rows whose bit 1 is set rotated by four chunks.  The MFMA
+// memory, one LDS row per k: for 64x64 tiles 128 bytes (64 m or n values),
+// the 16-byte chunks of rows whose bit 1 is set rotated by four chunks; for
+// 128x128 tiles 256 bytes, see bmn_offset.  The MFMA
 // operand of a lane is 8 consecutive k of one m or n; two transposing reads
 // (ds_read_b64_tr_b16) fetch it: in each group of 16 lanes, lane i reads 4
 // consecutive m or n of row k0 + i/4, and the read hands lane j the 4 k of
