@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.4,
                "e2m3": 10066.4, "e3m2": 10066.4}
 HBM_PEAK_GBS = 8000.0
+SPEC_GHZ = 2.4   # the clock MI355X's published MFMA peaks are quoted at
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -234,6 +235,98 @@ def build_workload(name: str, dev, layout=None):
     raise SystemExit(f"unknown workload {name}")
 
 
+def prewarm(run, stream, min_s=0.5, max_s=4.0, tol=0.01):
+    """Launches the step until the GPU has run it for at least min_s seconds
+    and two successive windows of launches agree on the mean launch time
+    within tol (or max_s seconds have passed).  The MI355X's clock takes
+    tens of launches of a long GEMM to settle (at 8192^3 the early launches
+    run 10-35% slower than the settled ones), so a short warmup alone would
+    time the ramp.  Returns (launches, GPU seconds, last window's mean ms)."""
+    import torch
+    total_s, launches, prev, window = 0.0, 0, None, 8
+    while True:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(window):
+            run()
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / window
+        total_s += ms * window / 1e3
+        launches += window
+        if total_s >= max_s or (total_s >= min_s and prev is not None
+                                and abs(ms - prev) <= tol * prev):
+            return launches, total_s, ms
+        prev = ms
+        # windows of about 20 ms of GPU time
+        window = int(min(5000, max(8, 20.0 / max(ms, 1e-3))))
+
+
+def measure_clock(run, dev, launches=3):
+    """The clock the dominant kernel ran at: the library's per-workgroup
+    clock trace (shader-clock and real-time counters at the start and end of
+    every workgroup) over `launches` more launches.  Returns (GHz, number of
+    workgroups the launch ran), or (None, 0) if none was recorded."""
+    import numpy as np
+    import torch
+
+    import dense_gemm_swizzled_amd as sg
+    sentinel = -1
+    slots = 1 << 16
+    buf = torch.full((4 * slots,), sentinel, dtype=torch.int64, device=dev)
+    khz = sg.gemm_clock_trace(buf.data_ptr(), slots)
+    try:
+        for _ in range(launches):
+            run()
+        torch.cuda.synchronize()
+    finally:
+        sg.gemm_clock_trace(None, 0)
+    raw = buf.view(-1, 4).cpu().numpy()
+    written = (raw != sentinel).any(axis=1)
+    v = raw[written].astype(np.float64)
+    ok = (v[:, 1] > v[:, 0]) & (v[:, 3] > v[:, 2])
+    log(f"[bench] clock trace: {int(written.sum())} workgroup slots written, "
+        f"{int(ok.sum())} with increasing counters")
+    if not ok.any() or khz <= 0:
+        return None, 0
+    v = v[ok]
+    return (float((v[:, 1] - v[:, 0]).sum() / (v[:, 3] - v[:, 2]).sum() * khz / 1e6),
+            int(ok.sum()))
+
+
+def probe_clock(dev, iters=10000):
+    """The MFMA clock probe: the two waves on every SIMD each issue 8 * iters
+    independent 16-cycle bf16 MFMAs.  Per CU (eight waves), the clock from
+    the MFMA count is 16 * 2 * 8 * iters cycles over the real-time span of
+    its waves, and the shader-clock counter's span over the same real-time
+    span is the counter's rate; they agree when the counter counts core
+    clocks and the MFMA pipes were kept busy.  Returns both, in GHz,
+    averaged over the CUs."""
+    import numpy as np
+    import torch
+
+    import dense_gemm_swizzled_amd as sg
+    khz = sg.gemm_clock_trace(None, 0)
+    waves = sg.gemm_clock_probe_waves()
+    out = torch.zeros(5 * waves, dtype=torch.int64, device=dev)
+    rc = sg.gemm_clock_probe(iters, out.data_ptr(), torch.cuda.current_stream(dev).cuda_stream)
+    if rc != sg.SG_OK:
+        raise sg.GemmError(rc, sg.gemm_last_error())
+    torch.cuda.synchronize()
+    return probe_ghz(out[:4 * waves].view(-1, 8, 4).cpu().numpy(), iters, khz)
+
+
+def probe_ghz(v, iters, khz):
+    """(MFMA-count GHz, counter GHz) from the probe's [CU][wave][4] counters."""
+    import numpy as np
+    v = v.astype(np.float64)
+    span_rt = (v[:, :, 3].max(axis=1) - v[:, :, 2].min(axis=1)) / (khz * 1e3)
+    span_t = v[:, :, 1].max(axis=1) - v[:, :, 0].min(axis=1)
+    mfma_cycles = 16.0 * 2 * 8 * iters
+    return float(np.mean(mfma_cycles / span_rt) / 1e9), float(np.mean(span_t / span_rt) / 1e9)
+
+
 def cpu_baseline(oracle_sample, rows_total, target_s=12.0):
     """Times the oracle on a row sample sized for about target_s seconds."""
     import oracle
@@ -264,6 +357,9 @@ def main():
                              "dense_1024",
                              "single_tile", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prewarm", action="store_true",
+                    help="time right after the --warmup launches, without running until "
+                         "the launch time has settled")
     ap.add_argument("--layout", type=int, choices=[16, 8, 0], default=None,
                     help="run the dense workload through gemm_layout_run with this LDS "
                          "layout (16 = the library's XOR swizzle over 256-byte lines, "
@@ -293,6 +389,9 @@ def main():
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
+    pw_launches, pw_s, pw_ms = (0, 0.0, None) if args.no_prewarm else prewarm(run, stream)
+    log(f"[bench] prewarm: {pw_launches} more launches, {pw_s:.2f} s of GPU time, last "
+        f"window {pw_ms} ms per launch")
 
     # Two HIP events on the launch stream (the library launches on torch's
     # current stream) bracket the K timed steps: their elapsed time over K is
@@ -318,6 +417,16 @@ def main():
     log(f"[bench] {cfg['workload']}: {ms_per_step:.4f} ms/step wall, kernel mean "
         f"{mean_ms:.4f} ms -> {achieved:.1f} TFLOP/s "
         f"({100 * achieved / peak:.1f}% of {peak} TFLOP/s)")
+
+    clock, workgroups = None, 0
+    if flops > 0:
+        gemm_ghz, workgroups = measure_clock(run, dev)
+        probe_mfma, probe_ctr = probe_clock(dev)
+        clock = {"gemm_ghz": None if gemm_ghz is None else round(gemm_ghz, 4),
+                 "workgroups": workgroups,
+                 "probe_mfma_ghz": round(probe_mfma, 4),
+                 "probe_counter_ghz": round(probe_ctr, 4), "spec_ghz": SPEC_GHZ}
+        log(f"[bench] clock: {clock}")
 
     cpu = None
     if not args.no_cpu_baseline and oracle_sample is not None:
@@ -346,7 +455,16 @@ def main():
                      "traffic_unit": "bytes per launch (HBM side)",
                      "kernel_ms_mean": round(mean_ms, 5)},
         "cpu_baseline": cpu,
+        "prewarm_launches": pw_launches,
+        "prewarm_s": round(pw_s, 3),
+        "clock": clock,
     }
+    if clock is not None and clock["gemm_ghz"]:
+        # The MFMA peak at the clock the kernel held (the published peak is
+        # quoted at 2.4 GHz).
+        adj = peak * clock["gemm_ghz"] / SPEC_GHZ
+        out["roofline"]["clock_adjusted_peak"] = round(adj, 1)
+        out["roofline"]["frac_of_clock_adjusted_peak"] = round(achieved / adj, 4)
     if args.workload == "grouped":
         # Per group the kernel can go no faster than its MFMA time or the HBM
         # time of its own bytes (A_g, B_g, D_g), whichever is longer.
@@ -357,11 +475,13 @@ def main():
             floor_s += max(f_g / (peak * 1e12), b_g / (HBM_PEAK_GBS * 1e9))
         out["roofline"]["attainable_ms"] = round(floor_s * 1e3, 5)
         out["roofline"]["frac_of_attainable"] = round(floor_s * 1e3 / mean_ms, 4)
-    if args.workload == "single_tile":
-        # One workgroup on one CU: the share of the peak a single CU holds.
-        cu_peak = peak / 256
-        out["roofline"]["one_cu_peak"] = round(cu_peak, 3)
-        out["roofline"]["frac_of_one_cu"] = round(achieved / cu_peak, 4)
+    if args.workload == "single_tile" and workgroups > 0:
+        # A handful of workgroups, each on a CU of its own: the share of the
+        # peak of the CUs the launch occupied.
+        cu_peak = peak / 256 * workgroups
+        out["roofline"]["occupied_cus"] = workgroups
+        out["roofline"]["occupied_cu_peak"] = round(cu_peak, 3)
+        out["roofline"]["frac_of_occupied_cus"] = round(achieved / cu_peak, 4)
     print(json.dumps(out), flush=True)
 
 

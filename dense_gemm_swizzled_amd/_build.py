@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libswizzled_gemm.so")
-SOURCES = ["api.hip", "launch_dense.hip", "launch_mx.hip"]
+SOURCES = ["api.hip", "launch_dense.hip", "launch_mx.hip", "diag.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

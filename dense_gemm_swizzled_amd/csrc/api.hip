@@ -16,6 +16,8 @@
 namespace {
 
 thread_local std::string g_last_error;
+// The clock trace of this thread's launches (gemm_clock_trace); off by default.
+thread_local sg::ClockTrace g_clk{nullptr, 0};
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -136,6 +138,12 @@ int dense_run(const char* who, DenseMode mode, int swz, int64_t M, int64_t N, in
     return fail(SG_ERR_ALIGN,
                 "%s: row pitches must be multiples of 16 bytes (A %lld, B %lld, D %lld bytes)",
                 who, (long long)(lda * eb), (long long)(ldb * eb), (long long)(ldd * db));
+  // The loaders move whole 16-byte chunks of a K-major row: with K % 8 != 0
+  // the elements past K in the last chunk would come from the row padding.
+  // (Packed rows cannot get here: their pitch 2K is then not a multiple of 16.)
+  if (K > 0 && K % 8 && (a_major == SG_K_MAJOR || b_major == SG_K_MAJOR))
+    return fail(SG_ERR_SHAPE, "%s: K=%lld is not a multiple of 8 with a K-major operand",
+                who, (long long)K);
   const sg::TileShape tile = mode == kAblation256   ? sg::kTile256
                             : mode == kAblation128 ? sg::kTile128
                                                    : pick_dense_tile(M, N);
@@ -167,6 +175,7 @@ int dense_run(const char* who, DenseMode mode, int swz, int64_t M, int64_t N, in
   p.tiles_m = (int)tiles_m;
   p.tiles_n = (int)tiles_n;
   p.group_m = kGroupM;
+  p.clk = g_clk;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = mode == kAblation256   ? sg::launch_layout(swz, p, s)
                        : mode == kAblation128 ? sg::launch_layout128(swz, p, s)
@@ -179,7 +188,16 @@ int dense_run(const char* who, DenseMode mode, int swz, int64_t M, int64_t N, in
 
 }  // namespace
 
+namespace sg {
+const char*& last_kernel() {
+  thread_local const char* name = "";
+  return name;
+}
+}  // namespace sg
+
 extern "C" {
+
+const char* gemm_last_kernel(void) { return sg::last_kernel(); }
 
 const char* gemm_last_error(void) { return g_last_error.c_str(); }
 
@@ -272,6 +290,7 @@ int grouped_gemm_run(int G, const int64_t* m_offsets, int64_t N, int64_t K,
   p.G = G;
   p.tiles_n = (int)cdiv(N, T);
   p.group_m = kGroupM;
+  p.clk = g_clk;
   int64_t acc = 0;
   for (int g = 0; g <= G; ++g) {
     p.m_off[g] = m_offsets[g];
@@ -327,6 +346,7 @@ int mxfp4_gemm_run(int64_t M, int64_t N, int64_t K, const void* A, const void* S
   p.tiles_m = (int)tiles_m;
   p.tiles_n = (int)tiles_n;
   p.group_m = kGroupM;
+  p.clk = g_clk;
   hipError_t e = sg::launch_mxfp4(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mxfp4_gemm_run launch");
   return ok();
@@ -372,6 +392,7 @@ int mxfp6_gemm_run(int fmt, int64_t M, int64_t N, int64_t K, const void* A, cons
   p.tiles_m = (int)tiles_m;
   p.tiles_n = (int)tiles_n;
   p.group_m = kGroupM;
+  p.clk = g_clk;
   hipError_t e = sg::launch_mxfp6(fmt == SG_E3M2, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mxfp6_gemm_run launch");
   return ok();
@@ -416,10 +437,41 @@ int mx_gemm_run(int64_t M, int64_t N, int64_t K, const void* A, const void* SFA,
   p.tiles_m = (int)tiles_m;
   p.tiles_n = (int)tiles_n;
   p.group_m = kGroupM;
+  p.clk = g_clk;
   hipError_t e = sg::launch_mx(tile, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mx_gemm_run launch");
   return ok();
 }
+
+int gemm_clock_trace(void* buf, int64_t slots, int* wall_khz) {
+  if (slots < 0) return fail(SG_ERR_SHAPE, "gemm_clock_trace: slots=%lld < 0", (long long)slots);
+  if (buf && (reinterpret_cast<uintptr_t>(buf) & 7u))
+    return fail(SG_ERR_ALIGN, "gemm_clock_trace: buf must be 8-byte aligned");
+  if (wall_khz) {
+    int dev = 0, khz = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (e != hipSuccess) return hip_fail(e, "gemm_clock_trace: wall clock rate");
+    *wall_khz = khz;
+  }
+  g_clk.buf = static_cast<uint64_t*>(buf);
+  g_clk.slots = buf ? slots : 0;
+  return ok();
+}
+
+int gemm_clock_probe(int64_t iters, void* out, void* stream) {
+  if (!out) return fail(SG_ERR_NULL, "gemm_clock_probe: out is NULL");
+  if (reinterpret_cast<uintptr_t>(out) & 7u)
+    return fail(SG_ERR_ALIGN, "gemm_clock_probe: out must be 8-byte aligned");
+  if (iters < 1 || iters > (int64_t{1} << 24))
+    return fail(SG_ERR_SHAPE, "gemm_clock_probe: iters=%lld outside [1, 2^24]",
+                (long long)iters);
+  hipError_t e = sg::launch_clock_probe(iters, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemm_clock_probe launch");
+  return ok();
+}
+
+int gemm_clock_probe_waves(void) { return sg::clock_probe_waves(); }
 
 int gemm_lds_layout(int rows, int row_bytes, int32_t* out) {
   if (!out) return fail(SG_ERR_NULL, "gemm_lds_layout: out is NULL");
@@ -450,6 +502,79 @@ int gemm_lds_layout_cblock(int32_t* out) {
     for (int r = 0; r < 128; ++r)
       for (int c = 0; c < 8; ++c)
         out[(w * 128 + r) * 8 + c] = (int32_t)sg::cblock_lds_offset(w, r, c);
+  return ok();
+}
+
+int gemm_lds_image_tile(int kind, const void* X, int64_t rows, int64_t row_bytes,
+                        int64_t row0, int64_t byte0, void* out, void* stream) {
+  const char* who = "gemm_lds_image_tile";
+  if (kind < SG_IMG_HALF || kind > SG_IMG_CBLOCK)
+    return fail(SG_ERR_DTYPE, "%s: unknown kind %d", who, kind);
+  if (!X || !out) return fail(SG_ERR_NULL, "%s: X or out is NULL", who);
+  if (!aligned16(X) || !aligned16(out) || row_bytes % 16)
+    return fail(SG_ERR_ALIGN, "%s: X and out must be 16-byte aligned and row_bytes a "
+                              "multiple of 16", who);
+  if (rows <= 0 || row_bytes <= 0 || row0 < 0 || row0 >= rows || byte0 < 0 ||
+      byte0 >= row_bytes || rows * row_bytes >= kMaxExtent)
+    return fail(SG_ERR_SHAPE, "%s: origin (%lld, %lld) outside the %lld x %lld operand", who,
+                (long long)row0, (long long)byte0, (long long)rows, (long long)row_bytes);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* x = static_cast<const char*>(X);
+  hipError_t e = hipSuccess;
+  if (kind == SG_IMG_HALF || kind == SG_IMG_HALF_KEXACT) {
+    if (byte0 % 128 || (kind == SG_IMG_HALF_KEXACT && row_bytes % 128))
+      return fail(SG_ERR_SHAPE, "%s: byte0 %% 128 and (K-exact) row_bytes %% 128 must be 0",
+                  who);
+    const int64_t valid = rows - row0;
+    e = sg::launch_lds_image_pp(kind, x + row0 * row_bytes, (uint32_t)(valid * row_bytes),
+                                (uint32_t)row_bytes, (int)(valid < 256 ? valid : 256),
+                                (uint32_t)byte0, (uint32_t)row_bytes, 32u, 0u, out, s);
+  } else if (kind == SG_IMG_MN256) {
+    if (row0 % 64 || byte0 % 256)
+      return fail(SG_ERR_SHAPE, "%s: row0 %% 64 and byte0 %% 256 must be 0", who);
+    const int64_t cols = (row_bytes - byte0) / 2;
+    e = sg::launch_lds_image_pp(kind, x + byte0,
+                                (uint32_t)((rows - 1) * row_bytes + (row_bytes - byte0)),
+                                (uint32_t)row_bytes, (int)(cols < 256 ? cols : 256), 0u, 0u,
+                                32u, (uint32_t)(row0 / 64), out, s);
+  } else if (kind == SG_IMG_FP6) {
+    if (row0 % 256 || byte0 % 96 || row_bytes % 96)
+      return fail(SG_ERR_SHAPE, "%s: row0 %% 256, byte0 %% 96 and row_bytes %% 96 must be 0",
+                  who);
+    // As the MX kernel sets up a 256-row tile: below the operand's last tile
+    // the descriptor covers the 8 bytes its shifted rows read past the tile;
+    // in the last tile the rows at the last row's block position stay
+    // unshifted.
+    const int64_t left = rows - row0;
+    const int m_valid = (int)(left < 256 ? left : 256);
+    const uint32_t bytes = (uint32_t)(m_valid * row_bytes) + (left > 256 ? 8u : 0u);
+    const uint32_t unshifted = left > 256 ? 32u : (uint32_t)((left - 1) & 31);
+    e = sg::launch_lds_image_pp(kind, x + row0 * row_bytes, bytes, (uint32_t)row_bytes,
+                                m_valid, 0u, 0u, unshifted, (uint32_t)(byte0 / 96), out, s);
+  } else {
+    if (row0 % 256 || byte0 % 512 || row_bytes / 2 > (int64_t{1} << 22))
+      return fail(SG_ERR_SHAPE, "%s: row0 %% 256 and byte0 %% 512 must be 0 (and ldc <= "
+                  "2^22)", who);
+    const int64_t left = rows - row0, cols = (row_bytes - byte0) / 2;
+    e = sg::launch_lds_image_cblock(X, row_bytes / 2, row0, byte0 / 2,
+                                    (int)(left < 256 ? left : 256),
+                                    (int)(cols < 256 ? cols : 256), out, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, who);
+  return ok();
+}
+
+int gemm_mfma_scale_probe(int fmt, const void* a, const void* b, const void* sa,
+                          const void* sb, void* out, void* stream) {
+  if (fmt != 0 && fmt != 2 && fmt != 3 && fmt != 4)
+    return fail(SG_ERR_DTYPE, "gemm_mfma_scale_probe: fmt %d is not 0, 2, 3 or 4", fmt);
+  if (!a || !b || !sa || !sb || !out)
+    return fail(SG_ERR_NULL, "gemm_mfma_scale_probe: a NULL pointer");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(out))
+    return fail(SG_ERR_ALIGN, "gemm_mfma_scale_probe: a, b and out must be 16-byte aligned");
+  hipError_t e = sg::launch_mfma_scale_probe(fmt, a, b, sa, sb, out,
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemm_mfma_scale_probe launch");
   return ok();
 }
 

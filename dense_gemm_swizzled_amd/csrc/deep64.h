@@ -271,8 +271,10 @@ template <int BM, bool IsBF16, bool AMn, bool BMn>
 __global__ void __launch_bounds__(256, 1) deep_gemm_kernel(const DenseParams p) {
   using Tile = DeepTile<BM, IsBF16, AMn, BMn>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+  const ClockStamp cs = clock_begin(p.clk);
   const TileJob j = dense_tile_job<BM, BM, AMn, BMn>(p, blockIdx.x);
   Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.ldd);
+  clock_end(p.clk, cs);
 }
 
 }  // namespace sg

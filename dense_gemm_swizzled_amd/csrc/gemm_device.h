@@ -66,6 +66,44 @@ __device__ __forceinline__ void lds_write16(char* lds, uint32_t off, u32x4 v) {
 }
 
 // ---------------------------------------------------------------------------
+// Clock trace (measurement only).  When `buf` is non-NULL, workgroup b <
+// `slots` records the shader-clock counter (s_memtime) and the constant-rate
+// real-time counter (s_memrealtime) when it starts and when its first wave
+// has finished, as buf[4b .. 4b+3] = {t_start, t_end, rt_start, rt_end}; the
+// ratio of the two deltas, times the real-time counter's rate, is the clock
+// the workgroup ran at.  With `buf` NULL the kernels only test the pointer.
+// ---------------------------------------------------------------------------
+struct ClockTrace {
+  uint64_t* buf;
+  int64_t slots;
+};
+
+struct ClockStamp {
+  uint64_t t, rt;
+};
+
+__device__ __forceinline__ ClockStamp clock_begin(const ClockTrace& c) {
+  ClockStamp s{0, 0};
+  if (c.buf) {
+    s.t = __builtin_amdgcn_s_memtime();
+    s.rt = __builtin_amdgcn_s_memrealtime();
+  }
+  return s;
+}
+
+__device__ __forceinline__ void clock_end(const ClockTrace& c, const ClockStamp& s) {
+  if (c.buf && (int64_t)blockIdx.x < c.slots && threadIdx.x == 0) {
+    const uint64_t t = __builtin_amdgcn_s_memtime();
+    const uint64_t rt = __builtin_amdgcn_s_memrealtime();
+    uint64_t* o = c.buf + 4 * (int64_t)blockIdx.x;
+    o[0] = s.t;
+    o[1] = t;
+    o[2] = s.rt;
+    o[3] = rt;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Operand tile loaders.  A tile is `Rows` operand rows (M rows of A or N rows
 // of B) by 128 bytes of K (64 fp16/bf16 or 128 fp8 elements), stored in LDS
 // K-major as Rows x 128 B under lds_offset<128, Swz>.  Global reads are 16

@@ -42,6 +42,7 @@ struct DenseParams {
   int c_dtype, d_dtype;
   int tiles_m, tiles_n;
   int group_m;
+  ClockTrace clk;
 };
 
 struct GroupedParams {
@@ -53,6 +54,7 @@ struct GroupedParams {
   int G;
   int tiles_n;
   int group_m;
+  ClockTrace clk;
   int64_t m_off[SG_MAX_GROUPS + 1];      // row offsets of the groups
   int32_t tile_start[SG_MAX_GROUPS + 1]; // first tile id of each group
 };
@@ -631,8 +633,10 @@ __global__ void __launch_bounds__(64 * Waves, 1)
   __shared__ __attribute__((aligned(4096))) char s0[Tile::kStageBytes];
   __shared__ __attribute__((aligned(4096))) char s1[Tile::kStageBytes];
 
+  const ClockStamp cs = clock_begin(p.clk);
   const TileJob j = dense_tile_job<BM, BN, AMn, BMn>(p, blockIdx.x);
   Tile::run(s0, s1, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.ldd);
+  clock_end(p.clk, cs);
 }
 
 template <int BM, int BN, bool IsBF16, int Swz, int Waves>
@@ -642,8 +646,10 @@ __global__ void __launch_bounds__(64 * Waves, 1)
   __shared__ __attribute__((aligned(4096))) char s0[Tile::kStageBytes];
   __shared__ __attribute__((aligned(4096))) char s1[Tile::kStageBytes];
 
+  const ClockStamp cs = clock_begin(p.clk);
   const TileJob j = grouped_tile_job<BM, BN>(p, blockIdx.x);
   Tile::run(s0, s1, j, p.K, nullptr, SG_NONE, p.D, p.d_dtype, p.N);
+  clock_end(p.clk, cs);
 }
 
 }  // namespace sg

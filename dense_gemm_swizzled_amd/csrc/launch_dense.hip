@@ -15,8 +15,18 @@ namespace {
 template <int BM, bool AMn, bool BMn>
 constexpr int waves_for() { return BM == 256 && !AMn && !BMn ? 8 : 4; }
 
+constexpr const char* dt_name(bool bf) { return bf ? "bf16" : "f16"; }
+constexpr const char* mj_name(bool mn) { return mn ? "mn" : "k"; }
+constexpr const char* swz_name(int swz) {
+  return swz == 16 ? "swz16" : swz == 8 ? "swz8" : swz == 0 ? "swz0" : "pad16";
+}
+
 template <int BM, int BN, bool BF, bool AMn, bool BMn, int Swz>
 hipError_t go_dense(const DenseParams& p, hipStream_t s) {
+  static const char* const name =
+      kernel_label("dense_gemm_kernel", BM == 256 ? "256" : BM == 128 ? "128" : "64",
+                   dt_name(BF), mj_name(AMn), mj_name(BMn), swz_name(Swz));
+  last_kernel() = name;
   const int grid = p.tiles_m * p.tiles_n;
   constexpr int W = waves_for<BM, AMn, BMn>();
   hipLaunchKernelGGL((dense_gemm_kernel<BM, BN, BF, AMn, BMn, Swz, W>), dim3(grid),
@@ -28,6 +38,9 @@ hipError_t go_dense(const DenseParams& p, hipStream_t s) {
 // 16x16x32 MFMAs.
 template <bool BF, int Swz, bool AMn = false, bool BMn = false>
 hipError_t go_pingpong(const DenseParams& p, hipStream_t s) {
+  static const char* const name = kernel_label("pingpong16_gemm_kernel", dt_name(BF),
+                                               mj_name(AMn), mj_name(BMn), swz_name(Swz));
+  last_kernel() = name;
   hipLaunchKernelGGL((pingpong16_gemm_kernel<BF, Swz, AMn, BMn>), dim3(p.tiles_m * p.tiles_n),
                      dim3(512), 0, s, p);
   return hipGetLastError();
@@ -37,6 +50,8 @@ hipError_t go_pingpong(const DenseParams& p, hipStream_t s) {
 // kernel its measurements were taken with.
 template <int Swz>
 hipError_t go_pingpong32(const DenseParams& p, hipStream_t s) {
+  static const char* const name = kernel_label("pingpong_gemm_kernel", "bf16", swz_name(Swz));
+  last_kernel() = name;
   hipLaunchKernelGGL((pingpong_gemm_kernel<true, Swz>), dim3(p.tiles_m * p.tiles_n),
                      dim3(512), 0, s, p);
   return hipGetLastError();
@@ -46,6 +61,9 @@ hipError_t go_pingpong32(const DenseParams& p, hipStream_t s) {
 // the five-stage one.
 template <int BM, bool BF, bool AMn, bool BMn>
 hipError_t go_deep(const DenseParams& p, hipStream_t s) {
+  static const char* const name = kernel_label("deep_gemm_kernel", BM == 128 ? "128" : "64",
+                                               dt_name(BF), mj_name(AMn), mj_name(BMn));
+  last_kernel() = name;
   hipLaunchKernelGGL((deep_gemm_kernel<BM, BF, AMn, BMn>), dim3(p.tiles_m * p.tiles_n),
                      dim3(256), 0, s, p);
   return hipGetLastError();
@@ -133,6 +151,12 @@ hipError_t launch_layout128(int layout, const DenseParams& p, hipStream_t s) {
 hipError_t launch_grouped(TileShape tile, bool bf16, int swz, const GroupedParams& p,
                           int grid, hipStream_t s) {
   if (swz != 16) return hipErrorInvalidValue;
+  static const char* const names[2][2] = {
+      {kernel_label("pingpong16_grouped_kernel", "f16"),
+       kernel_label("pingpong16_grouped_kernel", "bf16")},
+      {kernel_label("grouped_gemm_kernel", "128", "f16"),
+       kernel_label("grouped_gemm_kernel", "128", "bf16")}};
+  last_kernel() = names[tile == kTile256 ? 0 : 1][bf16 ? 1 : 0];
   if (tile == kTile256) {
     if (bf16)
       hipLaunchKernelGGL((pingpong16_grouped_kernel<true, 16>), dim3(grid), dim3(512), 0, s, p);

@@ -5,6 +5,9 @@
 namespace sg {
 
 hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s) {
+  static const char* const names[2] = {kernel_label("pingpong_mx_kernel", "e4m3"),
+                                       kernel_label("mx_gemm_kernel", "128", "e4m3")};
+  last_kernel() = names[tile == kTile256 ? 0 : 1];
   const int grid = p.tiles_m * p.tiles_n;
   if (tile == kTile256)
     hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, 0>), dim3(grid), dim3(512), 0, s, p);
@@ -15,12 +18,17 @@ hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s) {
 }
 
 hipError_t launch_mxfp4(const MxParams& p, hipStream_t s) {
+  static const char* const name = kernel_label("pingpong_mx_kernel", "e2m1");
+  last_kernel() = name;
   hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, 4>), dim3(p.tiles_m * p.tiles_n),
                      dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_mxfp6(bool e3m2, const MxParams& p, hipStream_t s) {
+  static const char* const names[2] = {kernel_label("pingpong_mx_kernel", "e2m3"),
+                                       kernel_label("pingpong_mx_kernel", "e3m2")};
+  last_kernel() = names[e3m2 ? 1 : 0];
   if (e3m2)
     hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, 3>), dim3(p.tiles_m * p.tiles_n),
                        dim3(512), 0, s, p);

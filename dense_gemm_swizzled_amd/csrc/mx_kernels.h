@@ -32,6 +32,7 @@ struct MxParams {
   int d_dtype;
   int tiles_m, tiles_n;
   int group_m;
+  ClockTrace clk;
 };
 
 __device__ __forceinline__ f32x16 mfma_scale_f8(const u32x4 (&a)[2],
@@ -242,6 +243,7 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(const MxParams p) 
   __shared__ __attribute__((aligned(4096))) char s0[Tile::kStageBytes];
   __shared__ __attribute__((aligned(4096))) char s1[Tile::kStageBytes];
 
+  const ClockStamp cs = clock_begin(p.clk);
   const int total = p.tiles_m * p.tiles_n;
   const int t = xcd_remap(blockIdx.x, total);
   int tm, tn;
@@ -265,6 +267,7 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(const MxParams p) 
   const char* sfa = static_cast<const char*>(p.SFA) + m0 * (p.K / 32);
   const char* sfb = static_cast<const char*>(p.SFB) + n0 * (p.K / 32);
   Tile::run(s0, s1, j, sfa, sfb, p.K, p.D, p.d_dtype, p.N);
+  clock_end(p.clk, cs);
 }
 
 }  // namespace sg

@@ -376,16 +376,10 @@ template <bool IsBF16, int Swz>
 __global__ void __launch_bounds__(512, 1) pingpong_gemm_kernel(const DenseParams p) {
   using Tile = PingPongTile<IsBF16, Swz>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+  const ClockStamp cs = clock_begin(p.clk);
   const TileJob j = dense_tile_job<256, 256, false, false>(p, blockIdx.x);
   Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.ldd);
-}
-
-template <bool IsBF16, int Swz>
-__global__ void __launch_bounds__(512, 1) pingpong_grouped_kernel(const GroupedParams p) {
-  using Tile = PingPongTile<IsBF16, Swz>;
-  __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
-  const TileJob j = grouped_tile_job<256, 256>(p, blockIdx.x);
-  Tile::run(smem, j, p.K, nullptr, SG_NONE, p.D, p.d_dtype, p.N);
+  clock_end(p.clk, cs);
 }
 
 }  // namespace sg
@@ -874,6 +868,7 @@ template <int Swz, int Fmt>
 __global__ void __launch_bounds__(512, 1) pingpong_mx_kernel(const MxParams p) {
   using Tile = PingPongMxTile<Swz, Fmt>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+  const ClockStamp cs = clock_begin(p.clk);
   const int total = p.tiles_m * p.tiles_n;
   const int t = xcd_remap(blockIdx.x, total);
   int tm, tn;
@@ -907,6 +902,7 @@ __global__ void __launch_bounds__(512, 1) pingpong_mx_kernel(const MxParams p) {
   j.beta = 0.0f;
   Tile::run(smem, j, static_cast<const char*>(p.SFA) + m0 * (p.K / 32),
             static_cast<const char*>(p.SFB) + n0 * (p.K / 32), p.K, p.D, p.d_dtype, p.N, ua, ub);
+  clock_end(p.clk, cs);
 }
 
 }  // namespace sg

@@ -536,16 +536,20 @@ template <bool IsBF16, int Swz, bool AMn = false, bool BMn = false>
 __global__ void __launch_bounds__(512, 1) pingpong16_gemm_kernel(const DenseParams p) {
   using Tile = PingPong16Tile<IsBF16, Swz, AMn, BMn>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+  const ClockStamp cs = clock_begin(p.clk);
   const TileJob j = dense_tile_job<256, 256, AMn, BMn>(p, blockIdx.x);
   Tile::run(smem, j, p.K, p.C, p.c_dtype, p.D, p.d_dtype, p.ldd);
+  clock_end(p.clk, cs);
 }
 
 template <bool IsBF16, int Swz>
 __global__ void __launch_bounds__(512, 1) pingpong16_grouped_kernel(const GroupedParams p) {
   using Tile = PingPong16Tile<IsBF16, Swz>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
+  const ClockStamp cs = clock_begin(p.clk);
   const TileJob j = grouped_tile_job<256, 256>(p, blockIdx.x);
   Tile::run(smem, j, p.K, nullptr, SG_NONE, p.D, p.d_dtype, p.N);
+  clock_end(p.clk, cs);
 }
 
 }  // namespace sg

@@ -67,7 +67,7 @@ extern "C" {
 #define SG_MN_MAJOR 1 /* M (for A) or N (for B) is the contiguous dimension */
 
 /* Largest group count grouped_gemm_run accepts. */
-#define SG_MAX_GROUPS 128
+#define SG_MAX_GROUPS 256
 
 /*
  * gemm_run -- D = A*B (+C), fp32 accumulation.
@@ -107,8 +107,12 @@ int gemm_run(int64_t M, int64_t N, int64_t K, const void* A, int a_major,
  *   must be a multiple of 16 bytes and every pointer 16-byte aligned.  C may
  *   equal D when c_dtype == d_dtype and ldc == ldd.  The other arguments and
  *   the errors are gemm_run's, plus SG_ERR_SHAPE for a leading dimension below
- *   its minimum or an N that is not a multiple of 4 (the epilogue writes D
- *   four columns at a time; gemm_run's packed rows already imply it).
+ *   its minimum, an N that is not a multiple of 4 (the epilogue writes D
+ *   four columns at a time; gemm_run's packed rows already imply it), or a
+ *   K that is not a multiple of 8 while A or B is K-major (the loaders move
+ *   whole 16-byte chunks of a row, so the elements past K inside the last
+ *   chunk would be read from the row's padding; gemm_run's packed K-major
+ *   rows already imply K % 8 == 0 through the 16-byte pitch rule).
  */
 int gemm_strided_run(int64_t M, int64_t N, int64_t K, float alpha, const void* A,
                      int64_t lda, int a_major, const void* B, int64_t ldb, int b_major,
@@ -294,6 +298,114 @@ int gemm_lds_layout_cblock(int32_t* out);
 int gemm_lds_image(const void* X, int64_t rows_total, int64_t K, int elem_bytes,
                    int64_t row0, int64_t k0, int tile_rows, void* out,
                    void* stream);
+
+/*
+ * Measurement support (not part of any GEMM call).
+ *
+ * gemm_clock_trace -- turns the clock trace of this thread's later launches
+ * on (buf non-NULL) or off (buf NULL).  While on, every kernel of a gemm_run,
+ * gemm_strided_run, gemm_layout_run, gemm_layout128_run, grouped_gemm_run,
+ * mx_gemm_run, mxfp4_gemm_run or mxfp6_gemm_run call records, for each
+ * workgroup b < slots, buf[4b .. 4b+3] = {shader-clock counter at its start,
+ * the same at the end of its first wave, real-time counter at the start, the
+ * same at the end}.  The shader-clock counter (s_memtime) advances once per
+ * core clock; the real-time counter (s_memrealtime) at the constant rate
+ * written to *wall_khz (kHz, the device attribute; NULL skips it).  So
+ * (t_end - t_start) / (rt_end - rt_start) * wall_khz is the clock in kHz
+ * that workgroup ran at: the clock the GEMM itself held, which sets its
+ * clock-adjusted MFMA peak.  buf: DEVICE memory of 4 * slots uint64_t,
+ * 8-byte aligned, alive while the trace is on.  The kernels only test the
+ * pointer when the trace is off.  Errors: SG_ERR_SHAPE (slots < 0),
+ * SG_ERR_ALIGN, SG_ERR_HIP.
+ */
+int gemm_clock_trace(void* buf, int64_t slots, int* wall_khz);
+
+/*
+ * gemm_clock_probe -- a kernel of W = gemm_clock_probe_waves() waves, one
+ * workgroup of eight waves per CU of 256 CUs (two waves per SIMD, as the
+ * 256x256 GEMM runs), each issuing `iters` rounds of 8 independent
+ * v_mfma_f32_16x16x32_bf16 (16 cycles each) on random bf16 register
+ * operands.  Wave w writes out[4w .. 4w+3] = {shader-clock counter at the
+ * start of its loop, at the end, real-time counter at the start, at the end}
+ * and out[4W + w] = bits of its fp32 accumulator sum.  Over a CU's eight
+ * waves, 16 * 2 * 8 * iters cycles (the MFMAs of one SIMD) per real-time
+ * span is the clock under a full MFMA load, and the shader-clock span over
+ * the same real-time span shows whether the counter counts core clocks.
+ * out: DEVICE memory of 5 * W uint64_t.  iters in [1, 2^24].  Errors:
+ * SG_ERR_NULL, SG_ERR_ALIGN, SG_ERR_SHAPE, SG_ERR_HIP.
+ */
+int gemm_clock_probe(int64_t iters, void* out, void* stream);
+int gemm_clock_probe_waves(void);
+
+/*
+ * gemm_last_kernel -- the kernel instantiation the last call on this thread
+ * that launched one enqueued, as "name<parameters>" (for example
+ * "pingpong16_gemm_kernel<bf16,k,k,swz16>"); "" before any launch.  Calls
+ * that launch nothing (an error, an empty problem) leave it unchanged.
+ * Thread-local; never NULL.
+ */
+const char* gemm_last_kernel(void);
+
+/*
+ * gemm_lds_image_tile -- runs one loader of the 256x256 kernels once, as the
+ * first group of four waves of a workgroup issues it, and copies the LDS it
+ * filled to `out` byte for byte, so that tests can hold the loaded image
+ * against the byte map the fragment reads use ("Swizzling explained
+ * properly", section "Sample swizzled matmul": the stores into the swizzled
+ * tile and the reads out of it must use one map).
+ *   X        DEVICE rows of `row_bytes` bytes (a multiple of 16), `rows` of
+ *            them, 16-byte aligned; bytes past a row or rows past `rows`
+ *            read as zero where the loader zero-fills.
+ *   kind     SG_IMG_HALF / SG_IMG_HALF_KEXACT: a K-major 16-bit operand; the
+ *              half tile of rows [row0, row0 + 128) and bytes [byte0, byte0
+ *              + 128) (byte0 % 128 == 0) through the loader that checks K
+ *              per load / the K-exact loader (row_bytes % 128 == 0).  The
+ *              image is 16384 bytes laid out by gemm_lds_layout(128, 128).
+ *            SG_IMG_MN256: an MN-major 16-bit operand [K = rows][row_bytes/2];
+ *              k rows [row0, row0 + 64) (row0 % 64 == 0), columns [byte0/2,
+ *              byte0/2 + 128) (byte0 % 256 == 0).  16384 bytes: byte b of
+ *              k row r at 256 r + 32 ((b / 32) XOR key(r)) + b mod 32,
+ *              key(r) = (r mod 4) + 4 (bit 3 of r).
+ *            SG_IMG_FP6: an MXFP6 operand (row_bytes = 3K/4, a multiple of
+ *              96); rows [row0, row0 + 128) of the 256-row tile at row0
+ *              (row0 % 256 == 0), the K tile of bytes [byte0, byte0 + 96)
+ *              (byte0 % 96 == 0).  16384 bytes laid out by
+ *              gemm_lds_layout_mxfp6(128, u) with u the block position of
+ *              the operand's last row if that row lies in this 256-row tile,
+ *              else 32.
+ *            SG_IMG_CBLOCK: a 16-bit C [rows][row_bytes/2]; the first 128
+ *              rows of the 256 x 256 output tile at (row0, byte0/2) (row0 %
+ *              256 == 0, byte0 % 512 == 0).  65536 bytes: the four
+ *              quarters of gemm_lds_layout_cblock(), quarter Q at 16384 Q.
+ *   out      DEVICE buffer of 16384 (65536 for SG_IMG_CBLOCK) bytes.
+ * Errors: SG_ERR_NULL, SG_ERR_ALIGN, SG_ERR_SHAPE (origin not on the grid,
+ * or outside the operand), SG_ERR_DTYPE (unknown kind), SG_ERR_HIP.
+ */
+#define SG_IMG_HALF 1
+#define SG_IMG_HALF_KEXACT 2
+#define SG_IMG_MN256 3
+#define SG_IMG_FP6 4
+#define SG_IMG_CBLOCK 5
+int gemm_lds_image_tile(int kind, const void* X, int64_t rows, int64_t row_bytes,
+                        int64_t row0, int64_t byte0, void* out, void* stream);
+
+/*
+ * gemm_mfma_scale_probe -- one v_mfma_scale_f32_32x32x64_f8f6f4 of one wave
+ * with the format code fmt for both operands (0 e4m3, 2 e2m3, 3 e3m2, 4
+ * e2m1), accumulating from zero: lane l (0..63) passes a[32 l .. 32 l + 31]
+ * as its first source operand, b[32 l ..] as its second, and scale bytes
+ * sa[l], sb[l] (byte 0 of each scale register).  out[16 l + r] receives
+ * accumulator register r of lane l.  It exposes the scaled MFMA's operand
+ * and scale layout -- which K element and which 32-element block each lane
+ * and byte feed ("06 Blackwell Tensor Core - tcgen05 MMA", section
+ * "Block-Scaled MMA", defines that placement for its own hardware) -- to
+ * tests with one-hot operands.  a, b: DEVICE, 2048 bytes each; sa, sb: 64
+ * bytes each; out: 4096 bytes (fp32).
+ * Errors: SG_ERR_NULL, SG_ERR_ALIGN (a, b, out not 16-byte aligned),
+ * SG_ERR_DTYPE (fmt), SG_ERR_HIP.
+ */
+int gemm_mfma_scale_probe(int fmt, const void* a, const void* b, const void* sa,
+                          const void* sb, void* out, void* stream);
 
 #ifdef __cplusplus
 }

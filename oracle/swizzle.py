@@ -93,3 +93,36 @@ def lds_image(tile: np.ndarray, line_bytes: int) -> np.ndarray:
             o = int(m[r, c])
             out[o:o + ATOM_BYTES] = t[r, ATOM_BYTES * c:ATOM_BYTES * (c + 1)]
     return out
+
+
+# ---------------------------------------------------------------------------
+# The kernels' other LDS maps, restated from their definitions (the XOR of a
+# unit index with a row key, as above), independently of the HIP headers.
+# Each places whole units, so each is a bijection on its region; their bank
+# behaviour is checked against the measured bank model elsewhere.
+# ---------------------------------------------------------------------------
+
+def mn256_offset(k: int, byte: int) -> int:
+    """An MN-major half tile of the 16-bit 256x256 kernel: one 256-byte row
+    per k; the 32-byte unit u of row k sits at unit u XOR key(k), with
+    key(k) = (k mod 4) + 4 * (bit 3 of k)."""
+    key = (k & 3) | (((k >> 3) & 1) << 2)
+    return 256 * k + 32 * ((byte >> 5) ^ key) + (byte & 31)
+
+
+def mxfp6_offset(row: int, byte: int, unshifted: int = 32) -> int:
+    """Byte ``byte`` (< 96) of a 96-byte MXFP6 tile row in the 128-byte rows
+    of the 256-byte-line XOR map, odd rows displaced by 8 bytes except those
+    at block position ``unshifted`` (row mod 32; 32 for none)."""
+    shift = 8 if (row & 1) and (row & 31) != unshifted else 0
+    b = byte + shift
+    return lds_tile_offset(row, b >> 4, 128, 256) + (b & 15)
+
+
+def cblock_offset(w4: int, r: int, c: int) -> int:
+    """Where 16-byte chunk ``c`` (< 8) of row ``r`` (< 128) of wave ``w4``'s
+    128 x 64 block of a 16-bit C lives: quarter r // 32 (16 KiB each), the
+    wave's 1 KiB region 4 * ((r // 8) mod 4) + w4, 128-byte row r mod 8, and
+    chunk c XOR ((r // 2) mod 8)."""
+    return ((r >> 5) * 16384 + (4 * ((r >> 3) & 3) + w4) * 1024 + (r & 7) * 128
+            + 16 * (c ^ ((r >> 1) & 7)))

@@ -72,11 +72,25 @@ def _strided(**kw):
     (dict(C=P, c_dtype=sg.SG_F32, ldc=272), DTYPE),  # in place needs ldc == ldd
     (dict(A=None), NULL), (dict(M=-1), SHAPE), (dict(a_major=7), MAJOR),
     (dict(N=262), SHAPE), (dict(N=261, M=0), SHAPE),  # D is written 4 columns at a time
+    # a K-major operand needs K % 8 == 0 (the loaders move whole 16-byte
+    # chunks, so K = 100 with lda = 104 would read elements 100..103 from the
+    # row padding)
+    (dict(K=100, lda=104, ldb=104), SHAPE),
+    (dict(K=100, lda=304, a_major=1, ldb=104), SHAPE),
+    (dict(K=100, lda=104, ldb=264, b_major=1), SHAPE),
 ])
 def test_gemm_strided_run_rejects(kw, code):
     rc = _strided(**kw)
     assert rc == code, sg.gemm_last_error()
     assert sg.gemm_last_error().startswith("gemm_strided_run")
+
+
+def test_gemm_strided_run_k_not_multiple_of_8_needs_mn_major_operands():
+    # Both operands MN-major: K indexes rows, which the loaders bound row by
+    # row, so K = 100 passes validation (the call then fails only at the
+    # launch, which needs a GPU).
+    rc = _strided(K=100, lda=304, a_major=1, ldb=264, b_major=1)
+    assert rc != SHAPE, sg.gemm_last_error()
 
 
 def test_cblock_layout_rejects_null():
@@ -170,7 +184,7 @@ def _grouped(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(G=0, offs=[0]), GROUPS), (dict(G=129, offs=list(range(130))), GROUPS),
+    (dict(G=0, offs=[0]), GROUPS), (dict(G=257, offs=list(range(258))), GROUPS),
     (dict(offs=[1, 128, 256]), GROUPS), (dict(offs=[0, 200, 100]), GROUPS),
     (dict(offs=None), NULL), (dict(D=None), NULL), (dict(A=None), NULL),
     (dict(a_major=1), MAJOR), (dict(b_major=1), MAJOR),
@@ -183,6 +197,17 @@ def test_grouped_rejects(kw, code):
 
 def test_grouped_all_empty_is_noop():
     assert _grouped(offs=[0, 0, 0], A=None, B=None, D=None) == sg.SG_OK
+
+
+def test_grouped_accepts_the_largest_group_count():
+    # SG_MAX_GROUPS offsets travel by value in the kernel arguments; G = 256
+    # passes every check (all groups empty, so nothing is launched).
+    assert sg.SG_MAX_GROUPS == 256
+    G = sg.SG_MAX_GROUPS
+    assert _grouped(G=G, offs=[0] * (G + 1)) == sg.SG_OK, sg.gemm_last_error()
+    assert _grouped(G=G + 1, offs=[0] * (G + 2)) == GROUPS
+    # a decrease at the last group is still seen
+    assert _grouped(G=G, offs=[0] * G + [-1]) == GROUPS
 
 
 def _mx(**kw):

@@ -177,3 +177,44 @@ def test_lds_image_roundtrip():
     for r in range(32):
         for c in range(8):
             assert np.array_equal(img[m[r, c]:m[r, c] + 16], tile[r, 16 * c:16 * c + 16])
+
+
+# ------------------------------------------------- the kernels' other maps
+
+def test_mn256_offset_is_a_bijection_of_whole_units():
+    offs = [swizzle.mn256_offset(k, b) for k in range(64) for b in range(256)]
+    assert sorted(offs) == list(range(64 * 256))
+    for k in range(64):                       # 32-byte units stay whole
+        for u in range(8):
+            base = swizzle.mn256_offset(k, 32 * u)
+            assert base % 32 == 0
+            assert [swizzle.mn256_offset(k, 32 * u + i) for i in range(32)] == \
+                list(range(base, base + 32))
+
+
+def test_mn256_rows_of_one_transposing_read_use_distinct_units():
+    # A read covers rows k0..k0+3 and k0+8..k0+11 at one logical unit: the
+    # keys must give those eight rows eight different physical units.
+    for k0 in range(0, 64, 16):
+        for rr in (0, 4):
+            rows = [k0 + rr + d for d in (0, 1, 2, 3, 8, 9, 10, 11)]
+            for u in range(8):
+                units = {(swizzle.mn256_offset(k, 32 * u) % 256) // 32 for k in rows}
+                assert len(units) == 8
+
+
+@pytest.mark.parametrize("unshifted", [32, 0, 11, 31])
+def test_mxfp6_offset_places_every_byte_once(unshifted):
+    offs = [swizzle.mxfp6_offset(r, b, unshifted) for r in range(128) for b in range(96)]
+    assert len(set(offs)) == len(offs)
+    for r in range(128):
+        # a row's bytes stay in the 256-byte bank line of its two-row pair
+        # (the XOR moves units only within a line)
+        lines = {o // 256 for o in (swizzle.mxfp6_offset(r, b, unshifted) for b in range(96))}
+        assert lines == {r // 2}
+
+
+def test_cblock_offset_is_a_bijection_of_the_four_quarters():
+    offs = [swizzle.cblock_offset(w, r, c) for w in range(4) for r in range(128)
+            for c in range(8)]
+    assert sorted(offs) == list(range(0, 65536, 16))
