@@ -36,7 +36,8 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.4,
                "e2m3": 10066.4, "e3m2": 10066.4}
 HBM_PEAK_GBS = 8000.0
 SPEC_GHZ = 2.4   # the clock MI355X's published MFMA peaks are quoted at
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+SIMDS = 1024        # 256 CUs x 4 SIMDs
 
 
 def _code_only(text: str) -> str:
@@ -63,19 +64,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM-side bytes per launch from the committed FETCH_SIZE / WRITE_SIZE
-    passes, or None when they were taken on other kernel sources."""
-    import json
+def measured_counters(workload: str):
+    """The committed rocprofv3 counters of `workload` (profiles/counters.json,
+    written by --profile), or None when they were taken on other kernel
+    sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTERS_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
-    w = t.get("workloads", {}).get(workload)
-    return None if w is None else w["bytes"]
+    return t.get("workloads", {}).get(workload)
 
 
 def log(*a):
@@ -102,6 +102,15 @@ def build_workload(name: str, dev, layout=None):
             # The call's arguments are marshalled once: at 1024^3 and below the
             # kernel is shorter than a Python-level call.
             run = sg.gemm_plan(A, B, a_major=case.a_major, b_major=case.b_major, C=C, out=D)
+        elif layout[0] == "io":
+            if case.ab_dtype != "bf16" or case.a_major != "k" or case.b_major != "k" \
+                    or case.d_dtype != "bf16":
+                raise SystemExit("--layout-io needs a bf16 workload with K-major A and B and "
+                                 "a bf16 D")
+            _, ops, outs = layout
+
+            def run():
+                sg.gemm_layout_io(A, B, ops, outs, C=C, out=D)
         else:
             if case.ab_dtype != "bf16" or case.a_major != "k" or case.b_major != "k":
                 raise SystemExit("--layout needs a bf16 workload with K-major A and B")
@@ -118,7 +127,11 @@ def build_workload(name: str, dev, layout=None):
         cfg = {"workload": case.name, "M": case.M, "N": case.N, "K": case.K,
                "a_major": case.a_major, "b_major": case.b_major,
                "ab_dtype": case.ab_dtype, "c": case.c_dtype, "d_dtype": case.d_dtype}
-        if layout is not None:
+        if layout is not None and layout[0] == "io":
+            cfg["lds_layout"] = {16: "xor_256B_lines", 0: "none"}[layout[1]]
+            cfg["output_staging"] = "xor" if layout[2] else "none"
+            cfg["tile"] = "256x256"
+        elif layout is not None:
             cfg["lds_layout"] = {16: "xor_256B_lines", 8: "xor_128B_lines", 0: "none",
                                  sg.SG_LAYOUT_PAD16: "padded_16B"}[layout[1]]
             cfg["tile"] = f"{layout[0]}x{layout[0]}"
@@ -327,6 +340,225 @@ def probe_ghz(v, iters, khz):
     return float(np.mean(mfma_cycles / span_rt) / 1e9), float(np.mean(span_t / span_rt) / 1e9)
 
 
+# ------------------------------------------------------------------ profiling
+#
+# bench.py --profile OUTDIR runs the bench of each selected workload under
+# rocprofv3 as child processes (this process never touches the GPU), one pass
+# per counter group the hardware can collect at once, and writes
+# OUTDIR/<kernel>__<workload>.md plus OUTDIR/counters.json, the file the
+# normal run reads its traffic and counters from (copied to profiles/).
+
+PMC_PASSES = [
+    ("sq", ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES",
+            "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+            "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F6F4", "SQ_WAVES",
+            "GRBM_GUI_ACTIVE"]),
+    ("fetch", ["FETCH_SIZE"]),
+    ("write", ["WRITE_SIZE"]),
+]
+MOPS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+        "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F6F4"]
+
+
+def profile_key(workload: str, layout) -> str:
+    """The counters.json key of a bench configuration."""
+    if layout is None:
+        return workload
+    if layout[0] == "io":
+        return f"{workload}@io{layout[1]}_{layout[2]}"
+    return f"{workload}@layout{layout[0]}_{layout[1]}"
+
+
+def _csv_rows(outdir: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(outdir, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _rocprof(tool_args, bench_args, outdir, tag, timeout_s=300):
+    """One rocprofv3 pass over `bench.py bench_args`; returns (stdout, outdir
+    of the pass)."""
+    import subprocess
+    d = os.path.join(outdir, "raw", tag)
+    os.makedirs(d, exist_ok=True)
+    cmd = ["rocprofv3", *tool_args, "-d", d, "-o", tag, "--output-format", "csv", "--",
+           sys.executable, os.path.join(ROOT, "bench.py"), *bench_args]
+    log(f"[profile] {tag}: {' '.join(cmd)}")
+    r = subprocess.run(cmd, cwd="/tmp", env={**os.environ, "TMPDIR": "/tmp"},
+                       capture_output=True, text=True, timeout=timeout_s)
+    with open(os.path.join(d, "bench.err"), "w") as f:
+        f.write(r.stderr)
+    if r.returncode != 0 and not r.stdout.strip():
+        raise SystemExit(f"[profile] {tag} failed ({r.returncode}):\n{r.stderr[-2000:]}")
+    log(f"[profile] {tag}: done")
+    return r.stdout, d, cmd
+
+
+def _dominant(trace_rows):
+    """(name, [durations ns in launch order]) of the kernel with the most GPU
+    time."""
+    by = {}
+    for r in trace_rows:
+        name = r["Kernel_Name"]
+        by.setdefault(name, []).append(
+            (int(r.get("Dispatch_Id") or 0), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    name = max(by, key=lambda n: sum(d for _, d in by[n]))
+    return name, [d for _, d in sorted(by[name])]
+
+
+def _counter_means(rows, kernel, first, count):
+    """Per counter, the mean over dispatches [first, first + count) of
+    `kernel` (values of one dispatch summed over their dimensions)."""
+    per = {}
+    for r in rows:
+        if r["Kernel_Name"] != kernel:
+            continue
+        did = int(r["Dispatch_Id"])
+        per.setdefault(did, {})
+        name = r["Counter_Name"]
+        per[did][name] = per[did].get(name, 0.0) + float(r["Counter_Value"])
+    ids = sorted(per)[first:first + count]
+    out = {}
+    for did in ids:
+        for k, v in per[did].items():
+            out[k] = out.get(k, 0.0) + v / len(ids)
+    return out
+
+
+def _short(kernel: str) -> str:
+    """'void sg::deep_gemm_kernel<64, ...>(...)' -> 'deep_gemm_kernel'."""
+    k = kernel.split("(")[0]
+    k = k.split("<")[0]
+    return k.split("::")[-1].replace("void ", "").strip() or "kernel"
+
+
+def profile(args, layout_args):
+    outdir = os.path.abspath(args.profile)
+    os.makedirs(outdir, exist_ok=True)
+    try:
+        with open(COUNTERS_FILE) as f:
+            base = json.load(f)
+        if base.get("kernel_source_hash") != kernel_source_hash():
+            base = {}
+    except (OSError, ValueError):
+        base = {}
+    result = {"kernel_source_hash": kernel_source_hash(),
+              "note": "per launch: kernel_ns (mean of the timed launches, kernel trace), "
+                      "clock_ghz (the kernel's own clock trace), counters (mean of the timed "
+                      "launches of a --pmc pass); bytes = FETCH_SIZE[KiB]*1024*fetch_factor + "
+                      "WRITE_SIZE[KiB]*1024*write_factor, factors from a 1 GiB device copy",
+              "fetch_factor": base.get("fetch_factor"), "write_factor": base.get("write_factor"),
+              "workloads": dict(base.get("workloads", {}))}
+    workloads = args.workload.split(",")
+    if "copy" in workloads:
+        workloads = ["copy"] + [w for w in workloads if w != "copy"]
+    for w in workloads:
+        key = profile_key(w, _layout_tuple(args))
+        common = ["--workload", w, "--no-cpu-baseline", *layout_args]
+        trace_args = common + ["--steps", str(args.steps), "--warmup", str(args.warmup)]
+        pmc_args = common + ["--steps", "10", "--warmup", "3", "--no-prewarm", "--no-clock"]
+        stdout, d, cmd_trace = _rocprof(["--kernel-trace", "--stats"], trace_args, outdir,
+                                        f"{w}_trace")
+        line = json.loads(stdout.strip().splitlines()[-1])
+        name, durs = _dominant(_csv_rows(d, "kernel_trace.csv"))
+        first = args.warmup + int(line.get("prewarm_launches") or 0)
+        timed = durs[first:first + args.steps] or durs
+        kernel_ns = sum(timed) / len(timed)
+        clock = (line.get("clock") or {}).get("gemm_ghz")
+        counters, cmds = {}, [cmd_trace]
+        passes = PMC_PASSES if w != "copy" else [p for p in PMC_PASSES if p[0] != "sq"]
+        for tag, names in passes:
+            _, d2, cmd = _rocprof(["--pmc", *names], pmc_args, outdir, f"{w}_{tag}")
+            cmds.append(cmd)
+            rows = _csv_rows(d2, "counter_collection.csv")
+            counters.update(_counter_means(rows, name, 3, 10))
+        flops = _flops_of(line)
+        entry = {"kernel": name, "kernel_ns": round(kernel_ns, 1), "launches_averaged": len(timed),
+                 "clock_ghz": clock, "counters": {k: round(v, 3) for k, v in counters.items()}}
+        if w == "copy":
+            n = line["config"]["bytes_read"]
+            result["fetch_factor"] = n / (counters["FETCH_SIZE"] * 1024)
+            result["write_factor"] = line["config"]["bytes_written"] / (counters["WRITE_SIZE"] * 1024)
+        if "FETCH_SIZE" in counters and result["fetch_factor"]:
+            entry["fetch_kib"] = counters["FETCH_SIZE"]
+            entry["write_kib"] = counters["WRITE_SIZE"]
+            entry["bytes"] = (counters["FETCH_SIZE"] * 1024 * result["fetch_factor"]
+                              + counters["WRITE_SIZE"] * 1024 * result["write_factor"])
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
+            mops = sum(counters.get(m, 0.0) for m in MOPS)
+            entry["mops_x512"] = mops * 512
+            entry["flops"] = flops
+            entry["mops_x512_equals_2mnk"] = abs(mops * 512 - flops) < 0.5
+            entry["lds_bank_conflict_cycles"] = counters["SQ_LDS_BANK_CONFLICT"]
+            entry["lds_idx_active_cycles"] = counters["SQ_LDS_IDX_ACTIVE"]
+            if clock:
+                entry["mfma_busy"] = round(counters["SQ_VALU_MFMA_BUSY_CYCLES"]
+                                           / (SIMDS * clock * kernel_ns), 4)
+        result["workloads"][key] = entry
+        _write_summary(outdir, w, key, line, entry, cmds, result)
+        with open(os.path.join(outdir, "counters.json"), "w") as f:
+            json.dump(result, f, indent=1, sort_keys=True)
+        log(f"[profile] {key}: {json.dumps(entry)}")
+
+
+def _flops_of(line) -> float:
+    c = line["config"]
+    if "m_sizes" in c:
+        return 2.0 * sum(c["m_sizes"]) * c["N"] * c["K"]
+    if "M" in c:
+        return 2.0 * c["M"] * c["N"] * c["K"]
+    return 0.0
+
+
+def _layout_tuple(args):
+    if args.layout is not None:
+        return (256, args.layout)
+    if args.layout_io is not None:
+        ops, outs = (int(x) for x in args.layout_io.split(","))
+        return ("io", ops, outs)
+    if args.layout128 is not None:
+        return (128, -1 if args.layout128 == "pad" else int(args.layout128))
+    return None
+
+
+def _write_summary(outdir, w, key, line, e, cmds, result):
+    name = f"{_short(e['kernel'])}__{key.replace('@', '_')}.md"
+    peak = PEAK_TFLOPS.get(line.get("dtype"), 0)
+    L = [f"# {_short(e['kernel'])} -- {key}", "",
+         f"Workload: `{json.dumps(line['config'])}`.", f"Kernel: `{e['kernel']}`.", "",
+         "Made by `python bench.py --profile <outdir> --workload " + w + "` (from the repository "
+         "root), which ran these passes (each its own process):", ""]
+    L += ["    " + " ".join(c).replace(ROOT, "$REPO") for c in cmds]
+    L += ["", "| quantity | value |", "|---|---|",
+          f"| kernel time (mean of {e['launches_averaged']} timed launches, kernel trace) | "
+          f"{e['kernel_ns'] / 1e3:.3f} us |",
+          f"| clock the kernel held (its own clock trace) | {e['clock_ghz']} GHz |"]
+    for k, v in sorted(e["counters"].items()):
+        L.append(f"| {k} (mean per timed launch) | {v:g} |")
+    if "flops" in e and e["flops"]:
+        t = e["kernel_ns"] * 1e-9
+        ach = e["flops"] / t / 1e12
+        L += [f"| algorithmic FLOP per launch | {e['flops']:.6g} |",
+              f"| MFMA MOPS x 512 | {e['mops_x512']:.6g} "
+              f"({'equal' if e['mops_x512_equals_2mnk'] else 'DIFFERENT'}) |",
+              f"| achieved | {ach:.1f} TFLOP/s = {100 * ach / peak:.1f}% of {peak} |"
+              if peak else ""]
+        if e.get("mfma_busy") is not None:
+            L.append(f"| MFMA busy = BUSY_CYCLES / (1024 SIMDs x clock x time) | "
+                     f"{100 * e['mfma_busy']:.1f}% |")
+        L.append(f"| LDS bank-conflict cycles | {e['lds_bank_conflict_cycles']:g} |")
+    if "bytes" in e:
+        L.append(f"| HBM-side bytes (FETCH x {result['fetch_factor']:.4f} + WRITE x "
+                 f"{result['write_factor']:.4f}) | {e['bytes'] / 1e6:.1f} MB |")
+    L += ["", "Bench line of the kernel-trace pass:", "", "    " + json.dumps(line)]
+    with open(os.path.join(outdir, name), "w") as f:
+        f.write("\n".join(x for x in L if x is not None) + "\n")
+
+
 def cpu_baseline(oracle_sample, rows_total, target_s=12.0):
     """Times the oracle on a row sample sized for about target_s seconds."""
     import oracle
@@ -353,9 +585,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="dense_8192",
-                    choices=["dense_8192", "grouped", "mxfp8", "mxfp4", "mxfp6", "mxfp6_e3m2",
-                             "dense_1024",
-                             "single_tile", "copy"])
+                    help="dense_8192 (default), grouped, mxfp8, mxfp4, mxfp6, mxfp6_e3m2, "
+                         "dense_1024, single_tile or copy (traffic calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prewarm", action="store_true",
                     help="time right after the --warmup launches, without running until "
@@ -364,10 +595,29 @@ def main():
                     help="run the dense workload through gemm_layout_run with this LDS "
                          "layout (16 = the library's XOR swizzle over 256-byte lines, "
                          "8 = over 128-byte lines, 0 = none) on the 256x256 ping-pong kernel")
+    ap.add_argument("--layout-io", choices=["16,1", "16,0", "0,1", "0,0"], default=None,
+                    help="run the dense workload through gemm_layout_io_run on the library's "
+                         "256x256 kernel: operand layout (16 = XOR swizzle, 0 = none), then "
+                         "the epilogue's C/D staging (1 = swizzled, 0 = not)")
     ap.add_argument("--layout128", choices=["16", "8", "0", "pad"], default=None,
                     help="the same through gemm_layout128_run on 128x128 tiles, where 'pad' "
                          "(rows padded by 16 bytes) also fits")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock trace and the MFMA clock probe after the timed region")
+    ap.add_argument("--profile", metavar="OUTDIR", default=None,
+                    help="run rocprofv3 passes (kernel trace, SQ counters, FETCH_SIZE, "
+                         "WRITE_SIZE) over this bench for the --workload list (comma "
+                         "separated; include 'copy' for the byte calibration) and write "
+                         "summaries and counters.json to OUTDIR")
     args = ap.parse_args()
+    if args.profile:
+        layout_args = []
+        for flag in ("layout", "layout_io", "layout128"):
+            v = getattr(args, flag)
+            if v is not None:
+                layout_args += ["--" + flag.replace("_", "-"), str(v)]
+        profile(args, layout_args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -379,6 +629,9 @@ def main():
     layout = None
     if args.layout is not None:
         layout = (256, args.layout)
+    elif args.layout_io is not None:
+        ops, outs = (int(x) for x in args.layout_io.split(","))
+        layout = ("io", ops, outs)
     elif args.layout128 is not None:
         import dense_gemm_swizzled_amd as sg
         layout = (128, sg.SG_LAYOUT_PAD16 if args.layout128 == "pad" else int(args.layout128))
@@ -419,7 +672,7 @@ def main():
         f"({100 * achieved / peak:.1f}% of {peak} TFLOP/s)")
 
     clock, workgroups = None, 0
-    if flops > 0:
+    if flops > 0 and not args.no_clock:
         gemm_ghz, workgroups = measure_clock(run, dev)
         probe_mfma, probe_ctr = probe_clock(dev)
         clock = {"gemm_ghz": None if gemm_ghz is None else round(gemm_ghz, 4),
@@ -427,6 +680,8 @@ def main():
                  "probe_mfma_ghz": round(probe_mfma, 4),
                  "probe_counter_ghz": round(probe_ctr, 4), "spec_ghz": SPEC_GHZ}
         log(f"[bench] clock: {clock}")
+
+    counters = measured_counters(profile_key(args.workload, layout))
 
     cpu = None
     if not args.no_cpu_baseline and oracle_sample is not None:
@@ -451,7 +706,7 @@ def main():
         "pct_of_bf16_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(args.workload) if layout is None else None,
+                     "traffic": (counters or {}).get("bytes"),
                      "traffic_unit": "bytes per launch (HBM side)",
                      "kernel_ms_mean": round(mean_ms, 5)},
         "cpu_baseline": cpu,
@@ -459,6 +714,14 @@ def main():
         "prewarm_s": round(pw_s, 3),
         "clock": clock,
     }
+    if counters is not None:
+        # From the committed rocprofv3 passes over this same code (bench.py
+        # --profile): MFMA utilisation against the clock the kernel held, the
+        # LDS bank-conflict cycles, and whether the MFMAs did exactly 2MNK.
+        out["counters"] = {k: counters.get(k) for k in (
+            "mfma_busy", "lds_bank_conflict_cycles", "lds_idx_active_cycles",
+            "mops_x512_equals_2mnk", "kernel_ns", "clock_ghz")}
+        out["counters"]["source"] = "profiles/counters.json"
     if clock is not None and clock["gemm_ghz"]:
         # The MFMA peak at the clock the kernel held (the published peak is
         # quoted at 2.4 GHz).

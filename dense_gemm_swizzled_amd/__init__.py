@@ -35,7 +35,7 @@ __all__ = [
     "SG_IMG_HALF_KEXACT", "SG_IMG_MN256", "SG_IMG_FP6", "SG_IMG_CBLOCK", "gemm_last_kernel", "gemm_clock_trace", "gemm_clock_probe", "gemm_clock_probe_waves",
     "SG_E2M3", "SG_E3M2",
     "gemm", "gemm_plan", "gemm_strided", "grouped_gemm", "mx_gemm", "mxfp4_gemm", "mxfp6_gemm",
-    "gemm_layout",
+    "gemm_layout", "gemm_layout_io", "gemm_layout_io_run",
     "gemm_layout128", "SG_LAYOUT_PAD16",
     "library_path", "load",
 ]
@@ -87,6 +87,7 @@ def load():
     lib.mxfp6_gemm_run.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
     lib.gemm_layout_run.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, vp, i32, vp]
     lib.gemm_layout128_run.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, vp, i32, vp]
+    lib.gemm_layout_io_run.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, i32, vp, i32, vp]
     lib.gemm_lds_layout.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int32)]
     lib.gemm_lds_layout_mxfp6.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int32)]
     lib.gemm_lds_layout_cblock.argtypes = [ctypes.POINTER(ctypes.c_int32)]
@@ -98,7 +99,7 @@ def load():
     lib.gemm_clock_probe_waves.argtypes = []
     for f in (lib.gemm_run, lib.gemm_strided_run, lib.grouped_gemm_run, lib.mx_gemm_run,
               lib.mxfp4_gemm_run, lib.mxfp6_gemm_run,
-              lib.gemm_layout_run, lib.gemm_layout128_run,
+              lib.gemm_layout_run, lib.gemm_layout128_run, lib.gemm_layout_io_run,
               lib.gemm_lds_layout, lib.gemm_lds_layout_mxfp6, lib.gemm_lds_layout_cblock,
               lib.gemm_lds_image, lib.gemm_lds_image_tile, lib.gemm_mfma_scale_probe,
               lib.gemm_clock_trace, lib.gemm_clock_probe,
@@ -151,6 +152,12 @@ def mxfp6_gemm_run(fmt, M, N, K, A, SFA, B, SFB, D, d_dtype, stream) -> int:
 
 def gemm_layout_run(swz_units, M, N, K, A, B, C, c_dtype, D, d_dtype, stream) -> int:
     return load().gemm_layout_run(swz_units, M, N, K, A, B, C, c_dtype, D, d_dtype, stream)
+
+
+def gemm_layout_io_run(operand_swz, output_swz, M, N, K, A, B, C, c_dtype, D, d_dtype,
+                       stream) -> int:
+    return load().gemm_layout_io_run(operand_swz, output_swz, M, N, K, A, B, C, c_dtype, D,
+                                     d_dtype, stream)
 
 
 def gemm_layout128_run(layout, M, N, K, A, B, C, c_dtype, D, d_dtype, stream) -> int:
@@ -451,6 +458,21 @@ def gemm_layout(A, B, swz_units: int, *, C=None, out_dtype=None, out=None):
                            C.data_ptr() if C is not None else None,
                            _dt(C.dtype) if C is not None else SG_NONE, out.data_ptr(),
                            _dt(out.dtype), _stream(A.device)))
+    return out
+
+
+def gemm_layout_io(A, B, operand_swz: int, output_swz: int, *, C=None, out_dtype=None,
+                   out=None):
+    """gemm() for bf16 K-major A [M][K] and B [N][K] on the library's 256x256
+    kernel with the operand layout operand_swz (16 or 0) and the epilogue's
+    C/D staging swizzled (output_swz 1) or not (0); D is 16-bit (default
+    bf16), C None or 16-bit."""
+    import torch
+    M, N, K, out = _layout_args(A, B, C, out, out_dtype or torch.bfloat16)
+    _check(gemm_layout_io_run(operand_swz, output_swz, M, N, K, A.data_ptr(), B.data_ptr(),
+                              C.data_ptr() if C is not None else None,
+                              _dt(C.dtype) if C is not None else SG_NONE, out.data_ptr(),
+                              _dt(out.dtype), _stream(A.device)))
     return out
 
 

@@ -88,7 +88,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 // Which kernels dense_run launches.
-enum DenseMode { kLibrary, kAblation256, kAblation128 };
+enum DenseMode { kLibrary, kAblation256, kAblation128, kAblationIO };
 
 // gemm_run, gemm_strided_run, gemm_layout_run and gemm_layout128_run:
 // validation, plan and launch.  kLibrary runs the library's kernels; the
@@ -144,7 +144,7 @@ int dense_run(const char* who, DenseMode mode, int swz, int64_t M, int64_t N, in
   if (K > 0 && K % 8 && (a_major == SG_K_MAJOR || b_major == SG_K_MAJOR))
     return fail(SG_ERR_SHAPE, "%s: K=%lld is not a multiple of 8 with a K-major operand",
                 who, (long long)K);
-  const sg::TileShape tile = mode == kAblation256   ? sg::kTile256
+  const sg::TileShape tile = mode == kAblation256 || mode == kAblationIO ? sg::kTile256
                             : mode == kAblation128 ? sg::kTile128
                                                    : pick_dense_tile(M, N);
   const int64_t T = tile_rows(tile);
@@ -177,7 +177,8 @@ int dense_run(const char* who, DenseMode mode, int swz, int64_t M, int64_t N, in
   p.group_m = kGroupM;
   p.clk = g_clk;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = mode == kAblation256   ? sg::launch_layout(swz, p, s)
+  const hipError_t e = mode == kAblationIO    ? sg::launch_layout_io(swz & 0xff, swz >> 8, p, s)
+                       : mode == kAblation256 ? sg::launch_layout(swz, p, s)
                        : mode == kAblation128 ? sg::launch_layout128(swz, p, s)
                                               : sg::launch_dense(tile, ab_dtype == SG_BF16,
                                                                  a_major == SG_MN_MAJOR,
@@ -230,6 +231,23 @@ int gemm_layout_run(int swz_units, int64_t M, int64_t N, int64_t K, const void* 
   return dense_run("gemm_layout_run", kAblation256, swz_units, M, N, K, 1.0f, A, K,
                    SG_K_MAJOR, B, K, SG_K_MAJOR, SG_BF16, 1.0f, C, N, c_dtype, D, N, d_dtype,
                    stream);
+}
+
+int gemm_layout_io_run(int operand_swz, int output_swz, int64_t M, int64_t N, int64_t K,
+                       const void* A, const void* B, const void* C, int c_dtype, void* D,
+                       int d_dtype, void* stream) {
+  if (operand_swz != 0 && operand_swz != 16)
+    return fail(SG_ERR_SHAPE, "gemm_layout_io_run: operand_swz %d is not 0 or 16", operand_swz);
+  if (output_swz != 0 && output_swz != 1)
+    return fail(SG_ERR_SHAPE, "gemm_layout_io_run: output_swz %d is not 0 or 1", output_swz);
+  if (d_dtype != SG_BF16 && d_dtype != SG_F16)
+    return fail(SG_ERR_DTYPE, "gemm_layout_io_run: d_dtype %d is not 16-bit (a 16-bit D is "
+                              "what the epilogue stages in LDS)", d_dtype);
+  if (C && c_dtype != SG_BF16 && c_dtype != SG_F16)
+    return fail(SG_ERR_DTYPE, "gemm_layout_io_run: c_dtype %d is not 16-bit", c_dtype);
+  return dense_run("gemm_layout_io_run", kAblationIO, operand_swz | (output_swz << 8), M, N, K,
+                   1.0f, A, K, SG_K_MAJOR, B, K, SG_K_MAJOR, SG_BF16, 1.0f, C, N, c_dtype, D,
+                   N, d_dtype, stream);
 }
 
 int gemm_layout128_run(int layout, int64_t M, int64_t N, int64_t K, const void* A,

@@ -188,7 +188,9 @@ struct DeepTile {
     asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
     PingPongTile<IsBF16, kSwzDefault>::barrier();
     read(f0, 0);
-    auto iteration = [&](int t, Frags& cur, Frags& nxt) {
+    // `steps`: the 16-wide K steps of the tile that hold any of K (4 but in
+    // the last tile), so no MFMA multiplies only the zero fill past K.
+    auto iteration = [&](int t, Frags& cur, Frags& nxt, int steps) {
       if constexpr (kLoop == 20)
         asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)" ::: "memory");
       else
@@ -197,20 +199,28 @@ struct DeepTile {
       issue(t + kStages - 1);
       read(nxt, t + 1);  // past the last tile: stale LDS, never used
 #pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk)
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        if (kk >= steps) break;
 #pragma unroll
         for (int m = 0; m < kFM * kFN; ++m) {
           // snake order: consecutive MFMAs share an operand
           const int fm = m / kFN, fn = (fm & 1) ? kFN - 1 - m % kFN : m % kFN;
           acc[fm][fn] = mfma32x32x16<IsBF16>(cur.b[kk][fn], cur.a[kk][fm], acc[fm][fn]);
         }
+      }
     };
+    const int last_steps = (int)((K - (int64_t)(T - 1) * kBK + 15) / 16);  // 1..4 (T > 0)
     int t = 0;
-    for (; t + 1 < T; t += 2) {
-      iteration(t, f0, f1);
-      iteration(t + 1, f1, f0);
+    for (; t + 2 < T; t += 2) {
+      iteration(t, f0, f1, kBK / 16);
+      iteration(t + 1, f1, f0, kBK / 16);
     }
-    if (t < T) iteration(t, f0, f1);
+    if (t + 1 < T) {
+      iteration(t, f0, f1, kBK / 16);
+      iteration(t + 1, f1, f0, last_steps);
+    } else if (t < T) {
+      iteration(t, f0, f1, last_steps);
+    }
     wait_vmem();  // the loads past K
 
     if (d_dtype == SG_F32 && C == nullptr) {

@@ -38,6 +38,10 @@ hipError_t launch_dense(TileShape tile, bool bf16, bool a_mn, bool b_mn,
 // The layout ablation: bf16, K-major operands, 256x256 tiles on the 32x32x16
 // ping-pong kernel with the LDS layout swz (0, 8 or 16 units per line).
 hipError_t launch_layout(int swz, const DenseParams& p, hipStream_t s);
+// The input/output ablation on the library's 256x256 kernel (16x16x32
+// MFMAs, 16-bit D staged in LDS): operand layout swz (16 or 0) and the
+// epilogue's C/D staging swizzled (out_swz) or in logical order.
+hipError_t launch_layout_io(int swz, bool out_swz, const DenseParams& p, hipStream_t s);
 // The same on 128x128 tiles of the 4-wave GemmTile kernel, where the padded
 // layout (kSwzPad) also fits: layout 16, 8, 0 or kSwzPad.
 hipError_t launch_layout128(int layout, const DenseParams& p, hipStream_t s);

@@ -36,13 +36,16 @@ hipError_t go_dense(const DenseParams& p, hipStream_t s) {
 
 // 256x256 tiles with both operands K-major run the ping-pong mainloop with
 // 16x16x32 MFMAs.
-template <bool BF, int Swz, bool AMn = false, bool BMn = false>
+template <bool BF, int Swz, bool AMn = false, bool BMn = false, bool OutSwz = true>
 hipError_t go_pingpong(const DenseParams& p, hipStream_t s) {
-  static const char* const name = kernel_label("pingpong16_gemm_kernel", dt_name(BF),
-                                               mj_name(AMn), mj_name(BMn), swz_name(Swz));
+  static const char* const name =
+      OutSwz ? kernel_label("pingpong16_gemm_kernel", dt_name(BF), mj_name(AMn), mj_name(BMn),
+                            swz_name(Swz))
+             : kernel_label("pingpong16_gemm_kernel", dt_name(BF), mj_name(AMn), mj_name(BMn),
+                            swz_name(Swz), "out_swz0");
   last_kernel() = name;
-  hipLaunchKernelGGL((pingpong16_gemm_kernel<BF, Swz, AMn, BMn>), dim3(p.tiles_m * p.tiles_n),
-                     dim3(512), 0, s, p);
+  hipLaunchKernelGGL((pingpong16_gemm_kernel<BF, Swz, AMn, BMn, OutSwz>),
+                     dim3(p.tiles_m * p.tiles_n), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
@@ -137,6 +140,16 @@ hipError_t launch_layout(int swz, const DenseParams& p, hipStream_t s) {
   if (swz == 16) return go_pingpong32<16>(p, s);
   if (swz == 8) return go_pingpong32<8>(p, s);
   if (swz == 0) return go_pingpong32<0>(p, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_layout_io(int swz, bool out_swz, const DenseParams& p, hipStream_t s) {
+  if (swz == 16)
+    return out_swz ? go_pingpong<true, 16, false, false, true>(p, s)
+                   : go_pingpong<true, 16, false, false, false>(p, s);
+  if (swz == 0)
+    return out_swz ? go_pingpong<true, 0, false, false, true>(p, s)
+                   : go_pingpong<true, 0, false, false, false>(p, s);
   return hipErrorInvalidValue;
 }
 

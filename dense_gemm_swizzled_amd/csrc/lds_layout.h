@@ -120,10 +120,13 @@ SG_HD constexpr uint32_t mn256_lds_offset(uint32_t k, uint32_t byte) {
 // 8-byte epilogue read covers (rows R..R+15, one chunk half) over the 16
 // chunk positions of a 256-byte bank line, so 32 lanes touch 64 banks once.
 // Returns quarter * 16384 + the offset inside the quarter's half slot.
+// With swz = false the chunk keeps its logical place (the output half of the
+// layout ablation).
 SG_HD constexpr uint32_t cblock_key(uint32_t r) { return (r >> 1) & 7u; }
-SG_HD constexpr uint32_t cblock_lds_offset(uint32_t w4, uint32_t r, uint32_t c) {
+SG_HD constexpr uint32_t cblock_lds_offset(uint32_t w4, uint32_t r, uint32_t c,
+                                           bool swz = true) {
   return (r >> 5) * 16384u + (4u * ((r >> 3) & 3u) + w4) * 1024u + (r & 7u) * 128u +
-         16u * (c ^ cblock_key(r));
+         16u * (c ^ (swz ? cblock_key(r) : 0u));
 }
 
 }  // namespace sg

@@ -165,15 +165,19 @@ __device__ __forceinline__ void cblock_quarters(char* (&cq)[4], char* smem, int 
 // 64 block in quarter r / 32, region 4((r / 8) mod 4) + w4, 128-byte row r
 // mod 8), 16-byte chunk c at chunk c XOR (r mod 8), so that the 8 rows of a
 // ds_write_b128 phase fill one 128-byte bank line.  Offset inside the
-// quarter's 16 KiB half slot.
+// quarter's 16 KiB half slot.  With Swz false the chunk keeps its logical
+// place (the output half of the layout ablation).
+template <bool Swz = true>
 __device__ __forceinline__ uint32_t dstage_offset(uint32_t w4, uint32_t r, uint32_t c) {
-  return (4u * ((r >> 3) & 3u) + w4) * 1024u + (r & 7u) * 128u + 16u * (c ^ (r & 7u));
+  return (4u * ((r >> 3) & 3u) + w4) * 1024u + (r & 7u) * 128u +
+         16u * (c ^ (Swz ? (r & 7u) : 0u));
 }
 
 // Stores wave w4's staged 128 x 64 block of a 16-bit D: lane l takes 16-byte
 // chunk l%8 of row 8s + l/8 (one contiguous KiB per read), so 8 lanes store
 // one 128-byte row segment (16 stores per wave).  N is a multiple of 4: a
 // chunk with 4 valid columns stores its first 8 bytes.
+template <bool OutSwz = true>
 __device__ __forceinline__ void store_d16_block(char* const (&cq)[4], const TileJob& j, void* D,
                                                 int64_t ldd, int lane, int g, int w4) {
   const int cc = lane & 7;
@@ -181,7 +185,7 @@ __device__ __forceinline__ void store_d16_block(char* const (&cq)[4], const Tile
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
     const uint32_t r = (uint32_t)(8 * s + (lane >> 3));
-    const u32x4 d = lds_read16(cq[s >> 2], dstage_offset((uint32_t)w4, r, (uint32_t)cc));
+    const u32x4 d = lds_read16(cq[s >> 2], dstage_offset<OutSwz>((uint32_t)w4, r, (uint32_t)cc));
     const int ml = 128 * g + (int)r;
     if (ml >= j.m_valid || nl >= j.n_valid) continue;
     uint16_t* p = static_cast<uint16_t*>(D) + (j.d_row0 + ml) * ldd + j.n0 + nl;

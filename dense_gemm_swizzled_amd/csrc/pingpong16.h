@@ -28,8 +28,10 @@ namespace sg {
 // AMn / BMn: A is [K][M] / B is [K][N] (MN-major); such an operand's half
 // tiles hold one 256-byte row per k (mn256_lds_offset) and its fragments
 // come from transposing reads.  Only for K a multiple of 64 with at least
-// two K tiles.
-template <bool IsBF16, int Swz, bool AMn = false, bool BMn = false>
+// two K tiles.  OutSwz: whether the epilogue's C and D staging in LDS use
+// their XOR keys (the library) or the logical chunk order (the output half
+// of the layout ablation); Swz is the operands' layout.
+template <bool IsBF16, int Swz, bool AMn = false, bool BMn = false, bool OutSwz = true>
 struct PingPong16Tile {
   using PP = PingPongTile<IsBF16, Swz>;
   static constexpr int kHalfBytes = PP::kHalfBytes;
@@ -248,7 +250,8 @@ struct PingPong16Tile {
 #pragma unroll
       for (int q = 0; q < 4; ++q)  // (the key of row 32Q + r is that of r)
         col[q] = 128u * (uint32_t)w4 +
-                 16u * ((uint32_t)(lane & 7) ^ cblock_key((uint32_t)(8 * q + lrow)));
+                 16u * ((uint32_t)(lane & 7) ^
+                        (OutSwz ? cblock_key((uint32_t)(8 * q + lrow)) : 0u));
     }
     // The loader of quarter Q: rows past the block read as zero.
     __device__ __forceinline__ KExactHalfLoader<Swz> quarter(int Q) const {
@@ -314,7 +317,8 @@ struct PingPong16Tile {
                                                         int w4) {
     auto place = [&](int i, int jn) {
       const uint32_t r = (uint32_t)(16 * i + (lane & 15));
-      const uint32_t off = cblock_lds_offset((uint32_t)w4, r, (uint32_t)(2 * jn + (lane >> 5)));
+      const uint32_t off =
+          cblock_lds_offset((uint32_t)w4, r, (uint32_t)(2 * jn + (lane >> 5)), OutSwz);
       return (off & 16383u) + 8u * (uint32_t)((lane >> 4) & 1);
     };
     u32x2 c[kI][kJ];
@@ -358,9 +362,10 @@ struct PingPong16Tile {
           const auto b = __builtin_amdgcn_permlane16_swap(x0[1], x1[1], false, false);
           const uint32_t r = (uint32_t)(16 * i + (lane & 15));
           const uint32_t ch = (uint32_t)(4 * jp + 2 * (rho & 1) + (rho >> 1));
-          lds_write16(cq[i >> 1], dstage_offset((uint32_t)w4, r, ch), u32x4{a[0], b[0], a[1], b[1]});
+          lds_write16(cq[i >> 1], dstage_offset<OutSwz>((uint32_t)w4, r, ch),
+                      u32x4{a[0], b[0], a[1], b[1]});
         }
-      store_d16_block(cq, j, D, ldd, lane, g, w4);
+      store_d16_block<OutSwz>(cq, j, D, ldd, lane, g, w4);
     }
   }
 
@@ -532,9 +537,9 @@ struct PingPong16Tile {
   }
 };
 
-template <bool IsBF16, int Swz, bool AMn = false, bool BMn = false>
+template <bool IsBF16, int Swz, bool AMn = false, bool BMn = false, bool OutSwz = true>
 __global__ void __launch_bounds__(512, 1) pingpong16_gemm_kernel(const DenseParams p) {
-  using Tile = PingPong16Tile<IsBF16, Swz, AMn, BMn>;
+  using Tile = PingPong16Tile<IsBF16, Swz, AMn, BMn, OutSwz>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
   const ClockStamp cs = clock_begin(p.clk);
   const TileJob j = dense_tile_job<256, 256, AMn, BMn>(p, blockIdx.x);

@@ -221,6 +221,25 @@ int gemm_layout_run(int swz_units, int64_t M, int64_t N, int64_t K, const void* 
                     void* stream);
 
 /*
+ * gemm_layout_io_run -- the input/output half of the layout experiment of
+ * "Swizzling explained properly" (section "Results": swizzling the input
+ * tiles against swizzling only the output tile), on gemm_run's own 256x256
+ * kernel (8 waves, 16x16x32 MFMAs) for bf16 K-major A and B and a 16-bit D,
+ * which that kernel stages in LDS (with a 16-bit C brought in by its last
+ * loads).  operand_swz: 16 = the library's operand layout (16-byte units
+ * XORed with the 256-byte bank-line index), 0 = no swizzle.  output_swz: 1 =
+ * the C and D staging areas use their XOR keys (the library), 0 = logical
+ * chunk order.  Every combination gives the same D bit for bit; only LDS
+ * bank conflicts and speed differ.  The other arguments are gemm_run's, with
+ * C NULL or 16-bit and d_dtype SG_BF16 or SG_F16.  Errors: as gemm_run, and
+ * SG_ERR_SHAPE for another operand_swz or output_swz, SG_ERR_DTYPE for a
+ * 32-bit C or D.
+ */
+int gemm_layout_io_run(int operand_swz, int output_swz, int64_t M, int64_t N, int64_t K,
+                       const void* A, const void* B, const void* C, int c_dtype, void* D,
+                       int d_dtype, void* stream);
+
+/*
  * gemm_layout128_run -- gemm_layout_run on 128x128 tiles of the 4-wave
  * kernel (the 32x32x16 MFMA), where a padded layout also fits in LDS: the
  * padding alternative to swizzling weighed in "Swizzling explained properly"

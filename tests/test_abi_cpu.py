@@ -28,7 +28,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"gemm_run", "gemm_strided_run", "grouped_gemm_run", "mx_gemm_run", "mxfp4_gemm_run",
-            "mxfp6_gemm_run", "gemm_layout_run", "gemm_layout128_run",
+            "mxfp6_gemm_run", "gemm_layout_run", "gemm_layout128_run", "gemm_layout_io_run",
             "gemm_last_error", "gemm_version", "gemm_lds_layout", "gemm_lds_layout_mxfp6",
             "gemm_lds_layout_cblock", "gemm_lds_image"} <= set(names)
     lib = ctypes.CDLL(sg.library_path())
@@ -91,6 +91,21 @@ def test_gemm_strided_run_k_not_multiple_of_8_needs_mn_major_operands():
     # launch, which needs a GPU).
     rc = _strided(K=100, lda=304, a_major=1, ldb=264, b_major=1)
     assert rc != SHAPE, sg.gemm_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ops=8), SHAPE), (dict(ops=-1), SHAPE), (dict(out=2), SHAPE),
+    (dict(d_dtype=sg.SG_F32), DTYPE), (dict(C=P + 4096, c_dtype=sg.SG_F32), DTYPE),
+    (dict(M=-1), SHAPE), (dict(A=None), NULL), (dict(K=60), ALIGN),
+])
+def test_gemm_layout_io_run_rejects(kw, code):
+    a = dict(ops=16, out=1, M=256, N=256, K=64, A=P, B=P, C=None, c_dtype=0, D=P,
+             d_dtype=sg.SG_BF16)
+    a.update(kw)
+    rc = sg.gemm_layout_io_run(a["ops"], a["out"], a["M"], a["N"], a["K"], a["A"], a["B"],
+                               a["C"], a["c_dtype"], a["D"], a["d_dtype"], None)
+    assert rc == code, sg.gemm_last_error()
+    assert sg.gemm_last_error().startswith("gemm_layout_io_run")
 
 
 def test_cblock_layout_rejects_null():

@@ -263,6 +263,36 @@ def test_layout_variants_bit_identical(dev):
     assert torch.equal(outs[16], outs[0])
 
 
+@pytest.mark.parametrize("with_c", [False, True])
+def test_layout_io_variants_bit_identical(dev, with_c):
+    # The input/output ablation on the library's 256x256 kernel: swizzled or
+    # plain operand tiles x swizzled or plain C/D staging.  Layouts move
+    # bytes in LDS, not the order of any sum: all four give the same bits,
+    # and the library's combination matches the oracle.
+    M, N, K = 4100, 4104, 192
+    case = si.dense_case(M, N, K, 23, ab_dtype="bf16", with_c=with_c, c_dtype="bf16",
+                         d_dtype="bf16", scale=1.0 / np.sqrt(K))
+    A, B = case.A.to(dev), case.B.to(dev)
+    C = case.C.to(dev) if with_c else None
+    say(f"layout io variants {M}x{N}x{K} C={with_c}")
+    outs = {}
+    for ops in (16, 0):
+        for out in (1, 0):
+            outs[ops, out] = sg.gemm_layout_io(A, B, ops, out, C=C, out_dtype=torch.bfloat16)
+            torch.cuda.synchronize()
+            name = sg.gemm_last_kernel()
+            assert name.startswith(f"pingpong16_gemm_kernel<bf16,k,k,swz{ops}"), name
+            assert ("out_swz0" in name) == (out == 0), name
+    ref, bound = oracle_dense(case)
+    check_close(_np(outs[16, 1]), ref, bound, "bf16", "layout io 16/1")
+    for key, d in outs.items():
+        assert torch.equal(d, outs[16, 1]), key
+    # the library's own call runs the swizzled/swizzled kernel
+    d = sg.gemm(A, B, C=C, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(d, outs[16, 1])
+
+
 def test_layout128_variants_bit_identical(dev):
     # The 128x128 kernel with the swizzles, no layout change and the padded
     # rows: same bits, and the library's layout matches the oracle.
