@@ -439,13 +439,20 @@ def _short(kernel: str) -> str:
 def profile(args, layout_args):
     outdir = os.path.abspath(args.profile)
     os.makedirs(outdir, exist_ok=True)
-    try:
-        with open(COUNTERS_FILE) as f:
-            base = json.load(f)
-        if base.get("kernel_source_hash") != kernel_source_hash():
-            base = {}
-    except (OSError, ValueError):
-        base = {}
+    # Start from what is already measured on these sources: the committed
+    # file, then earlier runs into the same OUTDIR.
+    base = {"workloads": {}}
+    for path in (COUNTERS_FILE, os.path.join(outdir, "counters.json")):
+        try:
+            with open(path) as f:
+                t = json.load(f)
+        except (OSError, ValueError):
+            continue
+        if t.get("kernel_source_hash") == kernel_source_hash():
+            base["workloads"].update(t.get("workloads", {}))
+            for k in ("fetch_factor", "write_factor"):
+                if t.get(k):
+                    base[k] = t[k]
     result = {"kernel_source_hash": kernel_source_hash(),
               "note": "per launch: kernel_ns (mean of the timed launches, kernel trace), "
                       "clock_ghz (the kernel's own clock trace), counters (mean of the timed "
