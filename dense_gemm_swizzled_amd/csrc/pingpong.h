@@ -73,6 +73,26 @@ __device__ __forceinline__ void dma16_so(u32x4 rsrc, uint32_t voff, uint32_t sof
       : "memory", "m0", "scc");
 }
 
+// The same load split in two: set_m0 writes m0 = lds_base + Imm, and
+// dma16_so_m0 issues the load with whatever m0 holds.  A kernel that places
+// the m0 write an MFMA ahead of its load (nothing in between may write m0)
+// keeps the wave's MFMA stream moving: measured on MI355X, an LDS-DMA load
+// right after its m0 write and wait state delays the wave's next MFMA by
+// about 14 cycles, one issued an MFMA after the write by about 7.
+template <int Imm>
+__device__ __forceinline__ void set_m0(uint32_t lds_base) {
+  asm volatile("s_add_u32 m0, %0, %1"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "i"(Imm)
+               : "m0", "scc");
+}
+__device__ __forceinline__ void dma16_so_m0(u32x4 rsrc, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory");
+}
+
 // buffer_load_dword ... lds: lane l's 4 bytes at byte `voff` go to LDS
 // address m0 + 4 l.
 __device__ __forceinline__ void dma4(u32x4 rsrc, uint32_t voff, uint32_t lds) {
@@ -121,6 +141,16 @@ struct HalfLoader {
     const uint32_t off = ok ? base + (uint32_t)(32 * i) * pitch + kbyte0 : kOutOfRange;
     dma16(rsrc, off, half + (uint32_t)(4 * i + w4) * 1024u);
   }
+  // issue in two steps (set_m0): the m0 write, then the load.
+  __device__ __forceinline__ void prep(uint32_t half, int w4, int i) const {
+    set_m0<0>(half + (uint32_t)(4 * i + w4) * 1024u);
+  }
+  __device__ __forceinline__ void go(u32x4 rsrc, int i, int rows_valid, uint32_t kbyte0,
+                                     uint32_t kbytes_total) const {
+    const bool ok = kbyte0 + chunk < kbytes_total && row + 32 * i < rows_valid;
+    const uint32_t off = ok ? base + (uint32_t)(32 * i) * pitch + kbyte0 : kOutOfRange;
+    dma16_so_m0(rsrc, off, 0u);
+  }
 };
 
 // The half-tile loader for K a multiple of 64: each lane's four row offsets
@@ -142,6 +172,15 @@ struct KExactHalfLoader {
   __device__ __forceinline__ void issue(u32x4 rsrc, uint32_t half, int w4,
                                         uint32_t kbyte0) const {
     dma16_so<I * 4096>(rsrc, voff[I], kbyte0, half + (uint32_t)w4 * 1024u);
+  }
+  // issue<I> in two steps, m0 first (see set_m0).
+  template <int I>
+  __device__ __forceinline__ void prep(uint32_t half, int w4) const {
+    set_m0<I * 4096>(half + (uint32_t)w4 * 1024u);
+  }
+  template <int I>
+  __device__ __forceinline__ void go(u32x4 rsrc, uint32_t kbyte0) const {
+    dma16_so_m0(rsrc, voff[I], kbyte0);
   }
 };
 
@@ -576,17 +615,25 @@ struct PingPongMxTile {
     }
   }
 
-  // kMfmas MFMAs of step kk; N loads (given by `issue(q)`) go out spread
-  // between them, the first after the first MFMA.
-  template <int N, class Issue>
+  // kMfmas MFMAs of step kk; N loads go out spread between them, the first
+  // after the first MFMA, at most one after each MFMA.  `prep(q)` (the m0
+  // write of a direct-to-LDS load, see set_m0) runs before the MFMA that
+  // load q follows, `go(q)` issues the load after it.
+  template <int N, class Prep, class Go>
   __device__ __forceinline__ static void compute(f32x16 (&acc)[kFM][kFN], const Frags& f,
                                                  const uint32_t (&sa)[kFM],
                                                  const uint32_t (&sb)[kFN], int kk,
-                                                 const Issue& issue) {
+                                                 const Prep& prep, const Go& go) {
+    static_assert(N <= kMfmas, "one load per MFMA");
 #pragma unroll
     for (int m = 0; m < kMfmas; ++m) {
       const int c = m / (kFM * kFN), fm = (m >> 1) % kFM, fn = m & 1;
       const i32x8 av = operand(f.a[fm], c), bv = operand(f.b[fn], c);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < N; ++q)
+        if (q * kMfmas / N == m) prep(q);
+      __builtin_amdgcn_sched_barrier(0);
       // op-select: block pair 2kk (e4m3, fp6) or 2c (e2m1) of the scale dword
       if ((kFp4 ? c : kk) == 0)
         acc[fm][fn] = mfma<0>(av, bv, acc[fm][fn], sa[fm], sb[fn]);
@@ -595,7 +642,7 @@ struct PingPongMxTile {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < N; ++q)
-        if (q * kMfmas / N == m) issue(q);
+        if (q * kMfmas / N == m) go(q);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -645,6 +692,14 @@ struct PingPongMxTile {
                                           uint32_t kbyte0) const {
       dma16_so<I * 4096>(rsrc, voff[I], kbyte0, half + (uint32_t)w4 * 1024u);
     }
+    template <int I>
+    __device__ __forceinline__ void prep(uint32_t half, int w4) const {
+      set_m0<I * 4096>(half + (uint32_t)w4 * 1024u);
+    }
+    template <int I>
+    __device__ __forceinline__ void go(u32x4 rsrc, uint32_t kbyte0) const {
+      dma16_so_m0(rsrc, voff[I], kbyte0);
+    }
   };
   using Loader = typename std::conditional<kFp6, Fp6Loader, KExactHalfLoader<Swz>>::type;
 
@@ -655,6 +710,21 @@ struct PingPongMxTile {
     if (i == 1) ld.template issue<1>(rsrc, half, w4, kbyte0);
     if (i == 2) ld.template issue<2>(rsrc, half, w4, kbyte0);
     if (i == 3) ld.template issue<3>(rsrc, half, w4, kbyte0);
+  }
+  // issue_half in two steps (set_m0): the m0 write, then the load.
+  template <class L>
+  __device__ __forceinline__ static void prep_half(const L& ld, int i, uint32_t half, int w4) {
+    if (i == 0) ld.template prep<0>(half, w4);
+    if (i == 1) ld.template prep<1>(half, w4);
+    if (i == 2) ld.template prep<2>(half, w4);
+    if (i == 3) ld.template prep<3>(half, w4);
+  }
+  template <class L>
+  __device__ __forceinline__ static void go_half(const L& ld, int i, u32x4 rsrc, uint32_t kbyte0) {
+    if (i == 0) ld.template go<0>(rsrc, kbyte0);
+    if (i == 1) ld.template go<1>(rsrc, kbyte0);
+    if (i == 2) ld.template go<2>(rsrc, kbyte0);
+    if (i == 3) ld.template go<3>(rsrc, kbyte0);
   }
 
   // ua, ub: fp6 only, see mxfp6_lds_offset.
@@ -717,6 +787,15 @@ struct PingPongMxTile {
       issue_half(lb, i, t < T ? rb : rb0, b_ring + (t % 3) * kTileBytes, w4,
                  (uint32_t)t * (uint32_t)kTileRowBytes);
     };
+    // The same loads in two steps, for the compute phases.
+    auto prep_a = [&](int t, int i) { prep_half(la, i, a_ring + (t & 1) * kTileBytes, w4); };
+    auto go_a = [&](int t, int i) {
+      go_half(la, i, t < T ? ra : ra0, (uint32_t)t * (uint32_t)kTileRowBytes);
+    };
+    auto prep_b = [&](int t, int i) { prep_half(lb, i, b_ring + (t % 3) * kTileBytes, w4); };
+    auto go_b = [&](int t, int i) {
+      go_half(lb, i, t < T ? rb : rb0, (uint32_t)t * (uint32_t)kTileRowBytes);
+    };
     // Scales of the group starting at tile t.
     auto ld_s = [&](Scales& s, int t, int q) {
       load_scale(s, q, rsa, rsb, sva, svb, (uint32_t)(t * 4 * kScaleDw));
@@ -760,18 +839,25 @@ struct PingPongMxTile {
       read(f, at, bt, o, 0);
       pick_scales(sa, sb, cur, kScaleDw * Sub, lhalf);
       end_phase<kPrev>();
-      compute<4>(acc, f, sa, sb, 0, [&](int q) { ld_b(t + 2, q); });
+      compute<4>(acc, f, sa, sb, 0, [&](int q) { prep_b(t + 2, q); },
+                 [&](int q) { go_b(t + 2, q); });
       end_phase<kPrev>();
       read(f, at, bt, o, 1);
       if constexpr (kFp4) pick_scales(sa, sb, cur, kScaleDw * Sub + 1, lhalf);
       end_phase<kPrev>();
       if constexpr (Sub == 0)
-        compute<4 + kScaleLoads>(acc, f, sa, sb, 1, [&](int q) {
-          if (q < 4) ld_a(t + 2, q);
-          else ld_s(nxt, t + kScaleTiles, q - 4);
-        });
+        compute<4 + kScaleLoads>(
+            acc, f, sa, sb, 1,
+            [&](int q) {
+              if (q < 4) prep_a(t + 2, q);
+            },
+            [&](int q) {
+              if (q < 4) go_a(t + 2, q);
+              else ld_s(nxt, t + kScaleTiles, q - 4);
+            });
       else
-        compute<4>(acc, f, sa, sb, 1, [&](int q) { ld_a(t + 2, q); });
+        compute<4>(acc, f, sa, sb, 1, [&](int q) { prep_a(t + 2, q); },
+                   [&](int q) { go_a(t + 2, q); });
       end_phase<kThis>();
     };
     using I0 = std::integral_constant<int, 0>;

@@ -151,15 +151,24 @@ struct PingPong16Tile {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int mm = 8 * q + m, i = mm >> 2, j = (i & 1) ? 3 - (mm & 3) : (mm & 3);
+        if (Active && m == 7) {  // the load's m0 write, one MFMA ahead (set_m0)
+          __builtin_amdgcn_sched_barrier(0);
+          ld.prep(half, w4, q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (Active) acc[i][j] = mfma16x16x32<IsBF16>(f.b[j], f.a[i], acc[i][j]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      ld.issue(rsrc, half, w4, q, rows_valid, kbyte0, kbytes);
+      if constexpr (Active)
+        ld.go(rsrc, q, rows_valid, kbyte0, kbytes);
+      else
+        ld.issue(rsrc, half, w4, q, rows_valid, kbyte0, kbytes);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // The same with the K-exact loader.
+  // The same with the K-exact loader, whose m0 write goes one MFMA ahead of
+  // its load (set_m0) when the wave has MFMAs to put between them.
   template <bool Active>
   __device__ __forceinline__ static void compute_x(f32x4 (&acc)[kI][kJ], const Frags& f,
                                                    const KExactHalfLoader<Swz>& ld, u32x4 rsrc,
@@ -169,13 +178,28 @@ struct PingPong16Tile {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int mm = 8 * q + m, i = mm >> 2, j = (i & 1) ? 3 - (mm & 3) : (mm & 3);
+        if (Active && m == 7) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (q == 0) ld.template prep<0>(half, w4);
+          if (q == 1) ld.template prep<1>(half, w4);
+          if (q == 2) ld.template prep<2>(half, w4);
+          if (q == 3) ld.template prep<3>(half, w4);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (Active) acc[i][j] = mfma16x16x32<IsBF16>(f.b[j], f.a[i], acc[i][j]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (q == 0) ld.template issue<0>(rsrc, half, w4, kbyte0);
-      if (q == 1) ld.template issue<1>(rsrc, half, w4, kbyte0);
-      if (q == 2) ld.template issue<2>(rsrc, half, w4, kbyte0);
-      if (q == 3) ld.template issue<3>(rsrc, half, w4, kbyte0);
+      if constexpr (Active) {
+        if (q == 0) ld.template go<0>(rsrc, kbyte0);
+        if (q == 1) ld.template go<1>(rsrc, kbyte0);
+        if (q == 2) ld.template go<2>(rsrc, kbyte0);
+        if (q == 3) ld.template go<3>(rsrc, kbyte0);
+      } else {  // no MFMA between an m0 write and its load: the joint form
+        if (q == 0) ld.template issue<0>(rsrc, half, w4, kbyte0);
+        if (q == 1) ld.template issue<1>(rsrc, half, w4, kbyte0);
+        if (q == 2) ld.template issue<2>(rsrc, half, w4, kbyte0);
+        if (q == 3) ld.template issue<3>(rsrc, half, w4, kbyte0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
