@@ -42,6 +42,14 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r,
                             __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// The same with an SGPR byte offset added to the address.
+__device__ __forceinline__ u32x4 buffer_load16_so(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                  uint32_t soff) {
+  return __builtin_bit_cast(
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                 r, off, (int)__builtin_amdgcn_readfirstlane(soff), 0));
+}
+
 __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r,
                                                  uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);

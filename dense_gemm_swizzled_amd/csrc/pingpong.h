@@ -456,8 +456,8 @@ namespace sg {
 // phases to land and both groups run the same instruction stream.  The
 // e8m0 scales do not fit in LDS beside the rings: each wave loads the
 // scale dwords of its own rows (four A rows and two B rows per lane, one or
-// two dwords each) straight into registers, with the A half of the same
-// tile, into one of three register sets (tile t mod 3).
+// two dwords each) straight into registers, with the A half of the first
+// tile of a group, for the next group.
 //
 // Fmt is the MFMA's operand format code: 0 e4m3, 2 e2m3, 3 e3m2, 4 e2m1.
 template <int Swz, int Fmt>
@@ -542,32 +542,31 @@ struct PingPongMxTile {
       for (int c = 0; c < kPieces; ++c) f.b[fn][c] = read_piece(bt, o.b[kk][c] + fn * 4096);
   }
 
-  // buffer_load_dwordx4 into registers, not tracked by the compiler: the
-  // value may be used only after an explicit wait has covered the load and
-  // the registers have passed through settle().
-  __device__ __forceinline__ static u32x4 load_dword4(u32x4 rsrc, uint32_t voff,
-                                                      uint32_t soff) {
-    u32x4 v;
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen"
-                 : "=v"(v)
-                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff))
-                 : "memory");
-    return v;
-  }
-
   // Scale load q (0 .. 2) of the group starting at byte `soff` of every
-  // scale row: A block pair q, or the B block pair.
-  __device__ __forceinline__ static void load_scale(Scales& s, int q, u32x4 rsa, u32x4 rsb,
+  // scale row: A block pair q, or the B block pair.  Compiler-tracked
+  // buffer loads: the first use of the registers waits for them.
+  __device__ __forceinline__ static void load_scale(Scales& s, int q,
+                                                    __amdgpu_buffer_rsrc_t rsa,
+                                                    __amdgpu_buffer_rsrc_t rsb,
                                                     const uint32_t (&va)[2], uint32_t vb,
                                                     uint32_t soff) {
     if (q < 2)
-      s.a[q] = load_dword4(rsa, va[q], soff);
+      s.a[q] = buffer_load16_so(rsa, va[q], soff);
     else
-      s.b = load_dword4(rsb, vb, soff);
+      s.b = buffer_load16_so(rsb, vb, soff);
   }
 
-  // Ties the scale registers to this point of the program (after the wait
-  // that covers their loads), so that no use is placed before it.
+  // cur = nxt as an ordered step: each register set passes through an
+  // empty statement tied to its own registers, which no LDS read or load
+  // may cross, so the copy (and any wait the compiler puts before its
+  // first use of `nxt`) comes where it is written.
+  __device__ __forceinline__ static void take(Scales& cur, Scales& nxt) {
+    asm volatile("" : "=v"(cur.a[0]) : "0"(nxt.a[0]) : "memory");
+    asm volatile("" : "=v"(cur.a[1]) : "0"(nxt.a[1]) : "memory");
+    asm volatile("" : "=v"(cur.b) : "0"(nxt.b) : "memory");
+  }
+
+  // A use of the scale registers at this point of the program.
   __device__ __forceinline__ static void settle(Scales& s) {
     asm volatile("" : "+v"(s.a[0]));
     asm volatile("" : "+v"(s.a[1]));
@@ -740,8 +739,8 @@ struct PingPongMxTile {
     const u32x4 ra = rsrc_words(j.a, j.a_bytes), rb = rsrc_words(j.b, j.b_bytes);
     const u32x4 ra0 = rsrc_words(j.a, 0), rb0 = rsrc_words(j.b, 0);
     const uint32_t sf_pitch = (uint32_t)(K / 32);
-    const u32x4 rsa = rsrc_words(sfa, (uint32_t)j.m_valid * sf_pitch);
-    const u32x4 rsb = rsrc_words(sfb, (uint32_t)j.n_valid * sf_pitch);
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sfa, (uint32_t)j.m_valid * sf_pitch);
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sfb, (uint32_t)j.n_valid * sf_pitch);
     const int a_rows = j.m_valid - 128 * g, b_rows = j.n_valid - 128 * g;
     Loader la, lb;
     if constexpr (kFp6) {
@@ -803,15 +802,15 @@ struct PingPongMxTile {
 
     // Tiles 0 and 1 (B, A, and the scales of the first group: the order the
     // mainloop keeps).  Scale dwords past K are read out of range (zero) or
-    // from the next row; no MFMA uses them.  `cur` holds the current scale
-    // group, `nxt` receives the next.
+    // from the next row; no MFMA uses them.  `nxt` receives a group's
+    // scales; the group's first memory phase takes them over into `cur`.
     Scales cur, nxt;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ld_b(0, i);
 #pragma unroll
     for (int i = 0; i < 4; ++i) ld_a(0, i);
 #pragma unroll
-    for (int q = 0; q < kScaleLoads; ++q) ld_s(cur, 0, q);
+    for (int q = 0; q < kScaleLoads; ++q) ld_s(nxt, 0, q);
 #pragma unroll
     for (int i = 0; i < 4; ++i) ld_b(1, i);
 #pragma unroll
@@ -825,9 +824,10 @@ struct PingPongMxTile {
 #pragma unroll
       for (int k = 0; k < kFN; ++k) acc[i][k] = f32x16{};
 
-    // Tile t, the Sub-th of its scale group.  The first tile of a group also
-    // loads the next group's scales (into `nxt`) with its A half; the waits
-    // count those loads in the phases that follow.
+    // Tile t, the Sub-th of its scale group.  The first tile of a group
+    // takes the group's scales over from `nxt` and loads the next group's
+    // into `nxt` with its A half; the waits count those loads in the phases
+    // that follow.
     auto tile = [&](auto sub, int t) {
       constexpr int Sub = decltype(sub)::value;
       constexpr int kPrev = Sub == 1 ? 8 + kScaleLoads : 8;
@@ -837,6 +837,13 @@ struct PingPongMxTile {
       Frags f;
       uint32_t sa[kFM], sb[kFN];
       read(f, at, bt, o, 0);
+      if constexpr (Sub == 0) {
+        // The group's first use of its scale registers, where the compiler
+        // waits for their loads (and, as it does not count the direct-to-LDS
+        // loads, for every load of the wave in flight): after this memory
+        // phase's reads are issued, while the other group computes.
+        take(cur, nxt);
+      }
       pick_scales(sa, sb, cur, kScaleDw * Sub, lhalf);
       end_phase<kPrev>();
       compute<4>(acc, f, sa, sb, 0, [&](int q) { prep_b(t + 2, q); },
@@ -864,10 +871,8 @@ struct PingPongMxTile {
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
-
     if (g) barrier();  // group 1 runs one phase behind group 0
     int t = 0;
-    settle(cur);
     for (; t + kScaleTiles <= T; t += kScaleTiles) {
       tile(I0{}, t);
       tile(I1{}, t + 1);
@@ -875,9 +880,6 @@ struct PingPongMxTile {
         tile(I2{}, t + 2);
         tile(I3{}, t + 3);
       }
-      // The next group's loads were covered by the waits of the tiles since.
-      settle(nxt);
-      cur = nxt;
     }
     if (t < T) tile(I0{}, t);
     if constexpr (kScaleTiles == 4) {
@@ -885,13 +887,12 @@ struct PingPongMxTile {
       if (t + 2 < T) tile(I2{}, t + 2);
     }
     if (!g) barrier();
-    // All loads have landed before the scale registers (which the last
-    // loads write) may hold anything else.
+    // The scale loads of the last group stay in the program (a load whose
+    // result went unused could be removed, and the explicit waits count
+    // them), and every load has landed before the epilogue.
     settle(cur);
     settle(nxt);
     wait_vmem();
-    settle(cur);
-    settle(nxt);
 
     if (d_dtype == SG_F32) {
       Base::epilogue(acc, j, nullptr, SG_NONE, D, d_dtype, ldd, lane, g, w4);
