@@ -8,13 +8,19 @@
 // cannot issue its fragment reads and loads between them; the ping-pong's
 // second wave per SIMD does that work.
 //
-// Everything but the MFMA shape is the ping-pong of pingpong.h: the roles,
-// phases, LDS rings, loads, waits and barriers.  Wave w4 of group g owns
-// output rows [128g, +128) and columns [64 w4, +64) as 8x4 blocks of 16x16
-// accumulators (128 accumulator registers).  A phase covers 32 of K: 12
-// fragment reads (lane l: row l%16 of a 16-row block, 16-byte chunk 4kh +
-// l/16 of the row, conflict-free under the swizzle) and 32 MFMAs with the
-// four loads of a half tile between them, one per eight MFMAs.
+// The roles, phases and LDS rings are those of pingpong.h.  Wave w4 of group
+// g owns output rows [128g, +128) and columns [64 w4, +64) as 8x4 blocks of
+// 16x16 accumulators (128 accumulator registers).  A phase covers 32 of K:
+// 12 fragment reads (lane l: row l%16 of a 16-row block, 16-byte chunk 4kh +
+// l/16 of the row, conflict-free under the swizzle), or 32 MFMAs.  For K a
+// multiple of 64 the memory phases also issue the group's loads (A of tile
+// t+1 in the first of tile t, B of tile t+2 in the second), so the compute
+// phases are MFMAs only: a direct-to-LDS load among a wave's MFMAs delays its
+// next MFMA by about 7 cycles even with m0 written ahead, while a memory
+// phase has room to spare (measured: 2-3% faster than issuing them between
+// the MFMAs, 4% slower with all eight in the first memory phase).  Otherwise
+// each compute phase issues the four loads of a half tile, one per eight
+// MFMAs, as in pingpong.h.
 //
 // The epilogue goes through LDS: a 16-bit C arrives with the loads of the
 // last two K tiles (which would otherwise fetch zeros past K), and a 16-bit
@@ -204,43 +210,79 @@ struct PingPong16Tile {
     }
   }
 
-  // The wait and barrier that end a phase: the wave's loads older than its
-  // newest N have landed in LDS and its fragment reads are done.
-  template <int N>
-  __device__ __forceinline__ static void end_phase() {
-    static_assert(N == 8 || N == 12 || N == 16, "vmcnt immediate");
-    if constexpr (N == 8)
+  // 32 MFMAs over one K half's fragments and nothing else (snake order, see
+  // compute).
+  template <bool Active>
+  __device__ __forceinline__ static void mfmas(f32x4 (&acc)[kI][kJ], const Frags& f) {
+    if constexpr (Active) {
+#pragma unroll
+      for (int mm = 0; mm < 32; ++mm) {
+        const int i = mm >> 2, j = (i & 1) ? 3 - (mm & 3) : (mm & 3);
+        acc[i][j] = mfma16x16x32<IsBF16>(f.b[j], f.a[i], acc[i][j]);
+      }
+    }
+  }
+
+  // The four loads of one half tile (from a memory phase, where the joint
+  // m0 write costs nothing that matters).
+  __device__ __forceinline__ static void load_half(const KExactHalfLoader<Swz>& ld, u32x4 rsrc,
+                                                   uint32_t half, int w4, uint32_t kbyte0) {
+    ld.template issue<0>(rsrc, half, w4, kbyte0);
+    ld.template issue<1>(rsrc, half, w4, kbyte0);
+    ld.template issue<2>(rsrc, half, w4, kbyte0);
+    ld.template issue<3>(rsrc, half, w4, kbyte0);
+  }
+
+  // The waits that end the four phases of a K tile, then the barrier.
+  template <int Phase>
+  __device__ __forceinline__ static void sync() {
+    if constexpr (Phase == 0)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    else if constexpr (Phase == 2)
       asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
-    else if constexpr (N == 12)
-      asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+    else if constexpr (Phase == 3)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     PP::barrier();
   }
 
-  // One K tile t of the mainloop: the loads of phase 2 go through `xb`,
-  // `rbt` with SGPR offset `sb` into B slot (t+2) mod 3, those of phase 4
-  // through `xa`, `rat`, `sa` into A slot t mod 2 (which held tile t).
-  // W1..W4: the vmcnt of the four phase-ending waits.
-  template <bool Active, int W1, int W2, int W3, int W4>
-  __device__ __forceinline__ static void ktile(f32x4 (&acc)[kI][kJ], int t, int bs,
-                                               const KExactHalfLoader<Swz>& xb, u32x4 rbt,
-                                               uint32_t sb, const KExactHalfLoader<Swz>& xa,
-                                               u32x4 rat, uint32_t sa, uint32_t a_ring,
-                                               uint32_t b_ring, const char* a_rd,
-                                               const char* b_rd, const Offsets& o, int w4) {
-    const int as = t & 1, bs2 = bs == 0 ? 2 : bs - 1;  // (t+2) mod 2, (t+2) mod 3
+  // One K tile t of the K-exact mainloop.  Its memory phases issue the
+  // group's loads, so the compute phases are MFMAs only:
+  //   memory  (K half 0): reads the fragments, then loads A of tile t+1 into
+  //           A slot (t+1) mod 2 (group g's half: its four waves were done
+  //           with tile t-1 there by the last barrier) and B of tile t+2 into
+  //           B slot (t+2) mod 3 (both groups were done with tile t-1 there);
+  //   compute (K half 0);
+  //   memory  (K half 1): reads; then all but the wave's newest 8 loads have
+  //           landed (the other group's B of tile t+1, for this group's
+  //           next read);
+  //   compute (K half 1; the last tile also loads the C block's fourth
+  //           quarter, into A slot t mod 2); then all but the newest 4 loads
+  //           have landed (the wave's own A of tile t+1).
+  // `xa`, `rat`, `ka`: the loader, descriptor and SGPR offset of A(t+1);
+  // `xb`, `rbt`, `kb` those of B(t+2); `xq`, `rq` the fourth C quarter.
+  template <bool Active, bool LastQ3>
+  __device__ __forceinline__ static void ktile(
+      f32x4 (&acc)[kI][kJ], int t, int bs, const KExactHalfLoader<Swz>& xa, u32x4 rat,
+      uint32_t ka, const KExactHalfLoader<Swz>& xb, u32x4 rbt, uint32_t kb,
+      const KExactHalfLoader<Swz>& xq, u32x4 rq, uint32_t a_ring, uint32_t b_ring,
+      const char* a_rd, const char* b_rd, const Offsets& o, int w4) {
+    const int as = t & 1, bs2 = bs == 0 ? 2 : bs - 1;  // t mod 2, (t+2) mod 3
     const char* at = a_rd + as * kTileBytes;
     const char* bt = b_rd + bs * kTileBytes;
     Frags f;
     if constexpr (Active) read(f, at, bt, o, 0);
-    end_phase<W1>();
-    compute_x<Active>(acc, f, xb, rbt, b_ring + bs2 * kTileBytes, w4, sb);
-    end_phase<W2>();
+    load_half(xa, rat, a_ring + (as ^ 1) * kTileBytes, w4, ka);
+    sync<0>();
+    mfmas<Active>(acc, f);
+    sync<1>();
     if constexpr (Active) read(f, at, bt, o, 1);
-    end_phase<W3>();
-    compute_x<Active>(acc, f, xa, rat, a_ring + as * kTileBytes, w4, sa);
-    end_phase<W4>();
+    load_half(xb, rbt, b_ring + bs2 * kTileBytes, w4, kb);
+    sync<2>();
+    if constexpr (LastQ3)
+      compute_x<Active>(acc, f, xq, rq, a_ring + as * kTileBytes, w4, 0u);
+    else
+      mfmas<Active>(acc, f);
+    sync<3>();
   }
 
   // Where the last two K tiles' loads put a 16-bit C.  Those loads would
@@ -289,10 +331,11 @@ struct PingPong16Tile {
     }
   };
 
-  // Mainloop for K a multiple of 64.  The K tiles t+2 >= T load zeros through
-  // the empty descriptors `ra0`, `rb0`, or (LdsC, T >= 2) the wave's C block.
-  // Once K tile T-1's operands have landed (the wait ending K tile T-2), only
-  // C loads are in flight, so the waits of the last K tile leave them be.
+  // Mainloop for K a multiple of 64 (the prologue has loaded B of tiles 0
+  // and 1 and A of tile 0).  Loads past the operand go through the empty
+  // descriptors `ra0`, `rb0` (zero fill) or, with LdsC (T >= 2), bring the
+  // wave's C block: quarter 0 as B of tile T, 1 as A of tile T, 2 as B of
+  // tile T+1, 3 in the last compute phase into A slot (T-1) mod 2.
   template <bool Active, bool LdsC>
   __device__ __forceinline__ static void mainloop_x(
       f32x4 (&acc)[kI][kJ], const KExactHalfLoader<Swz>& la, const KExactHalfLoader<Swz>& lb,
@@ -303,24 +346,25 @@ struct PingPong16Tile {
     int bs = 0;            // t mod 3
     int t = 0;
     for (; t + 2 < T; ++t) {
-      const uint32_t ka2 = (uint32_t)(t + 2) * kstep_a, kb2 = (uint32_t)(t + 2) * kstep_b;
-      ktile<Active, 8, 8, 8, 8>(acc, t, bs, lb, rb, kb2, la, ra, ka2, a_ring, b_ring, a_rd,
-                                b_rd, o, w4);
+      ktile<Active, false>(acc, t, bs, la, ra, (uint32_t)(t + 1) * kstep_a, lb, rb,
+                           (uint32_t)(t + 2) * kstep_b, la, ra0, a_ring, b_ring, a_rd, b_rd, o,
+                           w4);
       bs = bs == 2 ? 0 : bs + 1;
     }
     if constexpr (LdsC) {
       CBlock cb;
       cb.init(j, C, g, w4, lane);
-      ktile<Active, 8, 8, 8, 8>(acc, t, bs, cb.quarter(0), cb.rsrc, 0u, cb.quarter(1), cb.rsrc,
-                                0u, a_ring, b_ring, a_rd, b_rd, o, w4);
+      ktile<Active, false>(acc, t, bs, la, ra, (uint32_t)(t + 1) * kstep_a, cb.quarter(0),
+                           cb.rsrc, 0u, la, ra0, a_ring, b_ring, a_rd, b_rd, o, w4);
       bs = bs == 2 ? 0 : bs + 1;
-      ktile<Active, 8, 12, 12, 16>(acc, t + 1, bs, cb.quarter(2), cb.rsrc, 0u, cb.quarter(3),
-                                   cb.rsrc, 0u, a_ring, b_ring, a_rd, b_rd, o, w4);
+      ktile<Active, true>(acc, t + 1, bs, cb.quarter(1), cb.rsrc, 0u, cb.quarter(2), cb.rsrc,
+                          0u, cb.quarter(3), cb.rsrc, a_ring, b_ring, a_rd, b_rd, o, w4);
     } else {
       for (; t < T; ++t) {
-        const uint32_t k2 = (uint32_t)(t + 2) * 128u;
-        ktile<Active, 8, 8, 8, 8>(acc, t, bs, lb, rb0, k2, la, ra0, k2, a_ring, b_ring, a_rd,
-                                  b_rd, o, w4);
+        const u32x4 rat = t + 1 < T ? ra : ra0;
+        ktile<Active, false>(acc, t, bs, la, rat, (uint32_t)(t + 1) * kstep_a, lb, rb0,
+                             (uint32_t)(t + 2) * kstep_b, la, ra0, a_ring, b_ring, a_rd, b_rd,
+                             o, w4);
         bs = bs == 2 ? 0 : bs + 1;
       }
     }
@@ -476,7 +520,9 @@ struct PingPong16Tile {
     if constexpr (AMn) init_bmn(xam, g, w4, lane, j.a_pitch, a_rows);
     if constexpr (BMn) init_bmn(xbm, g, w4, lane, j.b_pitch, b_rows);
 
-    // Tiles 0 and 1 (B before A, the order the mainloop keeps).
+    // Tiles 0 and 1 (B before A, the order the mainloop keeps); the K-exact
+    // mainloop loads A of tile 1 itself.
+    const bool kexact = AMn || BMn || (K & (kBK - 1)) == 0;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       if constexpr (BMn) {
@@ -489,6 +535,7 @@ struct PingPong16Tile {
         for (int i = 0; i < 4; ++i)
           lb.issue(rb, b_ring + t * kTileBytes, w4, i, b_rows, t * 128u, kbytes);
       }
+      if (t == 1 && kexact) break;
       if constexpr (AMn) {
         xam.template issue<0>(ra, a_ring + t * kTileBytes, w4, t * kstep_a);
         xam.template issue<1>(ra, a_ring + t * kTileBytes, w4, t * kstep_a);
@@ -500,7 +547,12 @@ struct PingPong16Tile {
           la.issue(ra, a_ring + t * kTileBytes, w4, i, a_rows, t * 128u, kbytes);
       }
     }
-    PP::end_phase();
+    if (kexact) {  // tile 0 has landed; B of tile 1 may still be in flight
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+      PP::barrier();
+    } else {
+      PP::end_phase();
+    }
 
     const Offsets o = offsets(g, w4, lane);
     f32x4 acc[kI][kJ];
@@ -513,7 +565,6 @@ struct PingPong16Tile {
     // with at most 128 valid rows) runs the mainloop without its MFMAs.
     // A 16-bit C comes in through the last two K tiles' loads when K is a
     // multiple of 64 and 128 C rows stay within 32-bit buffer offsets.
-    const bool kexact = AMn || BMn || (K & (kBK - 1)) == 0;
     const bool ldsc = kexact && T >= 2 && C != nullptr &&
                       (c_dtype == SG_BF16 || c_dtype == SG_F16) && j.ldc <= (int64_t{1} << 22);
     if (kexact) {
