@@ -276,36 +276,40 @@ def prewarm(run, stream, min_s=0.5, max_s=4.0, tol=0.01):
         window = int(min(5000, max(8, 20.0 / max(ms, 1e-3))))
 
 
-def measure_clock(run, dev, launches=3):
+def measure_clock(run, dev, launches=20):
     """The clock the dominant kernel ran at: the library's per-workgroup
     clock trace (shader-clock and real-time counters at the start and end of
-    every workgroup) over `launches` more launches.  Returns (GHz, number of
-    workgroups the launch ran), or (None, 0) if none was recorded."""
+    every workgroup) over `launches` more launches, each into its own part
+    of the trace buffer (the clock moves over a few milliseconds, so one
+    launch alone is not representative).  Returns (GHz, workgroups one launch
+    ran), or (None, 0) if none was recorded."""
     import numpy as np
     import torch
 
     import dense_gemm_swizzled_amd as sg
     sentinel = -1
-    slots = 1 << 16
-    buf = torch.full((4 * slots,), sentinel, dtype=torch.int64, device=dev)
-    khz = sg.gemm_clock_trace(buf.data_ptr(), slots)
+    slots = 1 << 13          # per launch; every grid here is smaller
+    buf = torch.full((launches, 4 * slots), sentinel, dtype=torch.int64, device=dev)
+    khz = 0
     try:
-        for _ in range(launches):
+        for i in range(launches):
+            khz = sg.gemm_clock_trace(buf[i].data_ptr(), slots)
             run()
         torch.cuda.synchronize()
     finally:
         sg.gemm_clock_trace(None, 0)
-    raw = buf.view(-1, 4).cpu().numpy()
-    written = (raw != sentinel).any(axis=1)
+    raw = buf.view(launches, slots, 4).cpu().numpy()
+    written = (raw != sentinel).any(axis=2)
+    per_launch = int(written.sum(axis=1).max())
     v = raw[written].astype(np.float64)
     ok = (v[:, 1] > v[:, 0]) & (v[:, 3] > v[:, 2])
-    log(f"[bench] clock trace: {int(written.sum())} workgroup slots written, "
-        f"{int(ok.sum())} with increasing counters")
+    log(f"[bench] clock trace: {per_launch} workgroups a launch over {launches} launches, "
+        f"{int(ok.sum())} records with increasing counters")
     if not ok.any() or khz <= 0:
         return None, 0
     v = v[ok]
     return (float((v[:, 1] - v[:, 0]).sum() / (v[:, 3] - v[:, 2]).sum() * khz / 1e6),
-            int(ok.sum()))
+            per_launch)
 
 
 def probe_clock(dev, iters=10000):
@@ -433,7 +437,8 @@ def _short(kernel: str) -> str:
     """'void sg::deep_gemm_kernel<64, ...>(...)' -> 'deep_gemm_kernel'."""
     k = kernel.split("(")[0]
     k = k.split("<")[0]
-    return k.split("::")[-1].replace("void ", "").strip() or "kernel"
+    k = k.split("::")[-1].replace("void ", "").strip()
+    return k.removeprefix("__amd_rocclr_") or "kernel"
 
 
 def profile(args, layout_args):
