@@ -449,11 +449,12 @@ namespace sg {
 // (two steps): 512 cycles of MFMA for e4m3 and e2m1, 256 for fp6 (the
 // 6-bit MFMA runs at the 4-bit rate).
 //
-// Schedule: the 16-bit ping-pong's.  LDS holds an A ring of two tiles and a
-// B ring of three (160 KiB); group g loads half g of every tile of both
-// operands, B(t+2) during its compute phase over the first K step of tile
-// t and A(t+2) during the one over the second step, so every load has five
-// phases to land and both groups run the same instruction stream.  The
+// Schedule: the 16-bit ping-pong's for K a multiple of 64 (pingpong16.h).
+// LDS holds an A ring of two tiles and a B ring of three (160 KiB); group g
+// loads half g of every tile of both operands, from its memory phases after
+// their reads: A(t+1) in the one over the first K step of tile t, B(t+2) in
+// the one over the second, so the compute phases are MFMAs only (and the
+// scale loads below); both groups run the same instruction stream.  The
 // e8m0 scales do not fit in LDS beside the rings: each wave loads the
 // scale dwords of its own rows (four A rows and two B rows per lane, one or
 // two dwords each) straight into registers, with the A half of the first
@@ -648,17 +649,23 @@ struct PingPongMxTile {
 
   __device__ __forceinline__ static void barrier() { PingPongTile<true, Swz>::barrier(); }
 
-  // The end of every phase: the wave's LDS reads have returned and all but
-  // its N newest loads (those of its last two compute phases) have landed,
-  // so every tile a later phase reads is in LDS and its scales are in
-  // registers before the barrier.
-  template <int N>
-  __device__ __forceinline__ static void end_phase() {
-    static_assert(N == 8 || N == 11, "vmcnt immediate");
-    if constexpr (N == 8)
+  // The end of a phase of the mainloop: the wave's LDS reads have returned
+  // (Lgkm) and all but its V newest loads have landed (V < 0: no load wait),
+  // then the barrier.
+  template <int V, bool Lgkm>
+  __device__ __forceinline__ static void sync() {
+    static_assert(V == -1 || V == 4 || V == 7 || V == 8 || V == 11, "vmcnt immediate");
+    if constexpr (V == 4)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if constexpr (V == 7)
+      asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+    else if constexpr (V == 8)
       asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
-    else
+    else if constexpr (V == 11)
       asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)" ::: "memory");
+    else if constexpr (Lgkm)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    static_assert(V < 8 ? (V < 0 || !Lgkm) : Lgkm, "waits as used below");
     barrier();
   }
 
@@ -691,14 +698,6 @@ struct PingPongMxTile {
                                           uint32_t kbyte0) const {
       dma16_so<I * 4096>(rsrc, voff[I], kbyte0, half + (uint32_t)w4 * 1024u);
     }
-    template <int I>
-    __device__ __forceinline__ void prep(uint32_t half, int w4) const {
-      set_m0<I * 4096>(half + (uint32_t)w4 * 1024u);
-    }
-    template <int I>
-    __device__ __forceinline__ void go(u32x4 rsrc, uint32_t kbyte0) const {
-      dma16_so_m0(rsrc, voff[I], kbyte0);
-    }
   };
   using Loader = typename std::conditional<kFp6, Fp6Loader, KExactHalfLoader<Swz>>::type;
 
@@ -709,21 +708,6 @@ struct PingPongMxTile {
     if (i == 1) ld.template issue<1>(rsrc, half, w4, kbyte0);
     if (i == 2) ld.template issue<2>(rsrc, half, w4, kbyte0);
     if (i == 3) ld.template issue<3>(rsrc, half, w4, kbyte0);
-  }
-  // issue_half in two steps (set_m0): the m0 write, then the load.
-  template <class L>
-  __device__ __forceinline__ static void prep_half(const L& ld, int i, uint32_t half, int w4) {
-    if (i == 0) ld.template prep<0>(half, w4);
-    if (i == 1) ld.template prep<1>(half, w4);
-    if (i == 2) ld.template prep<2>(half, w4);
-    if (i == 3) ld.template prep<3>(half, w4);
-  }
-  template <class L>
-  __device__ __forceinline__ static void go_half(const L& ld, int i, u32x4 rsrc, uint32_t kbyte0) {
-    if (i == 0) ld.template go<0>(rsrc, kbyte0);
-    if (i == 1) ld.template go<1>(rsrc, kbyte0);
-    if (i == 2) ld.template go<2>(rsrc, kbyte0);
-    if (i == 3) ld.template go<3>(rsrc, kbyte0);
   }
 
   // ua, ub: fp6 only, see mxfp6_lds_offset.
@@ -786,15 +770,6 @@ struct PingPongMxTile {
       issue_half(lb, i, t < T ? rb : rb0, b_ring + (t % 3) * kTileBytes, w4,
                  (uint32_t)t * (uint32_t)kTileRowBytes);
     };
-    // The same loads in two steps, for the compute phases.
-    auto prep_a = [&](int t, int i) { prep_half(la, i, a_ring + (t & 1) * kTileBytes, w4); };
-    auto go_a = [&](int t, int i) {
-      go_half(la, i, t < T ? ra : ra0, (uint32_t)t * (uint32_t)kTileRowBytes);
-    };
-    auto prep_b = [&](int t, int i) { prep_half(lb, i, b_ring + (t % 3) * kTileBytes, w4); };
-    auto go_b = [&](int t, int i) {
-      go_half(lb, i, t < T ? rb : rb0, (uint32_t)t * (uint32_t)kTileRowBytes);
-    };
     // Scales of the group starting at tile t.
     auto ld_s = [&](Scales& s, int t, int q) {
       load_scale(s, q, rsa, rsb, sva, svb, (uint32_t)(t * 4 * kScaleDw));
@@ -813,9 +788,10 @@ struct PingPongMxTile {
     for (int q = 0; q < kScaleLoads; ++q) ld_s(nxt, 0, q);
 #pragma unroll
     for (int i = 0; i < 4; ++i) ld_b(1, i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ld_a(1, i);
-    end_phase<8>();
+    // Tile 0 has landed (B of tile 1 and the scales may be in flight); A of
+    // tile 1 comes with the first memory phase.
+    asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)" ::: "memory");
+    barrier();
 
     const Offsets o = offsets(g, w4, lrow, lhalf, ua, ub);
     f32x16 acc[kFM][kFN];
@@ -825,13 +801,21 @@ struct PingPongMxTile {
       for (int k = 0; k < kFN; ++k) acc[i][k] = f32x16{};
 
     // Tile t, the Sub-th of its scale group.  The first tile of a group
-    // takes the group's scales over from `nxt` and loads the next group's
-    // into `nxt` with its A half; the waits count those loads in the phases
-    // that follow.
+    // takes the group's scales over from `nxt` and, in its second compute
+    // phase, loads the next group's into `nxt`.  The memory phases issue the
+    // tile loads after their reads, so the compute phases are MFMAs (and
+    // those scale loads) only: A(t+1) into A slot (t+1) mod 2 (its four
+    // waves were done with tile t-1 there at the barrier that opened tile t)
+    // and B(t+2) into B slot (t+2) mod 3 (both groups were done with tile
+    // t-1 there).  Waits, in loads issued after the one waited for: the
+    // second memory phase, the other group's B(t+1) for this group's next
+    // read (A(t+1), B(t+2) and the scale loads of tile t-1 if it was a
+    // group's first); the second compute phase, the wave's own A(t+1)
+    // (B(t+2) and this tile's scale loads).
     auto tile = [&](auto sub, int t) {
       constexpr int Sub = decltype(sub)::value;
-      constexpr int kPrev = Sub == 1 ? 8 + kScaleLoads : 8;
-      constexpr int kThis = Sub == 0 ? 8 + kScaleLoads : 8;
+      constexpr int kWaitM = Sub == 1 ? 8 + kScaleLoads : 8;
+      constexpr int kWaitC = Sub == 0 ? 4 + kScaleLoads : 4;
       const char* at = a_rd + (t & 1) * kTileBytes;
       const char* bt = b_rd + (t % 3) * kTileBytes;
       Frags f;
@@ -845,27 +829,22 @@ struct PingPongMxTile {
         take(cur, nxt);
       }
       pick_scales(sa, sb, cur, kScaleDw * Sub, lhalf);
-      end_phase<kPrev>();
-      compute<4>(acc, f, sa, sb, 0, [&](int q) { prep_b(t + 2, q); },
-                 [&](int q) { go_b(t + 2, q); });
-      end_phase<kPrev>();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ld_a(t + 1, i);
+      sync<-1, true>();
+      compute<0>(acc, f, sa, sb, 0, [&](int) {}, [&](int) {});
+      sync<-1, false>();
       read(f, at, bt, o, 1);
       if constexpr (kFp4) pick_scales(sa, sb, cur, kScaleDw * Sub + 1, lhalf);
-      end_phase<kPrev>();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ld_b(t + 2, i);
+      sync<kWaitM, true>();
       if constexpr (Sub == 0)
-        compute<4 + kScaleLoads>(
-            acc, f, sa, sb, 1,
-            [&](int q) {
-              if (q < 4) prep_a(t + 2, q);
-            },
-            [&](int q) {
-              if (q < 4) go_a(t + 2, q);
-              else ld_s(nxt, t + kScaleTiles, q - 4);
-            });
+        compute<kScaleLoads>(acc, f, sa, sb, 1, [&](int) {},
+                             [&](int q) { ld_s(nxt, t + kScaleTiles, q); });
       else
-        compute<4>(acc, f, sa, sb, 1, [&](int q) { prep_a(t + 2, q); },
-                   [&](int q) { go_a(t + 2, q); });
-      end_phase<kThis>();
+        compute<0>(acc, f, sa, sb, 1, [&](int) {}, [&](int) {});
+      sync<kWaitC, false>();
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
