@@ -276,13 +276,13 @@ def prewarm(run, stream, min_s=0.5, max_s=4.0, tol=0.01):
         window = int(min(5000, max(8, 20.0 / max(ms, 1e-3))))
 
 
-def measure_clock(run, dev, launches=20):
+def measure_clock(run, dev, launches=10):
     """The clock the dominant kernel ran at: the library's per-workgroup
     clock trace (shader-clock and real-time counters at the start and end of
-    every workgroup) over `launches` more launches, each into its own part
-    of the trace buffer (the clock moves over a few milliseconds, so one
-    launch alone is not representative).  Returns (GHz, workgroups one launch
-    ran), or (None, 0) if none was recorded."""
+    every workgroup) over `launches` launches, each into its own part of the
+    trace buffer (the clock moves over a few milliseconds, so one launch
+    alone is not representative).  Returns (GHz, workgroups one launch ran),
+    or (None, 0) if none was recorded."""
     import numpy as np
     import torch
 
@@ -548,7 +548,8 @@ def _write_summary(outdir, w, key, line, e, cmds, result):
     L += ["", "| quantity | value |", "|---|---|",
           f"| kernel time (mean of {e['launches_averaged']} timed launches, kernel trace) | "
           f"{e['kernel_ns'] / 1e3:.3f} us |",
-          f"| clock the kernel held (its own clock trace) | {e['clock_ghz']} GHz |"]
+          f"| clock the kernel held (its own clock trace, 10 launches before and 10 after the timed ones) | "
+          f"{e['clock_ghz']} GHz |"]
     for k, v in sorted(e["counters"].items()):
         L.append(f"| {k} (mean per timed launch) | {v:g} |")
     if "flops" in e and e["flops"]:
@@ -658,6 +659,13 @@ def main():
     log(f"[bench] prewarm: {pw_launches} more launches, {pw_s:.2f} s of GPU time, last "
         f"window {pw_ms} ms per launch")
 
+    # The clock is traced over 10 launches before the timed region and 10
+    # after it (never inside): the clock drifts slowly, and the mean of the
+    # two windows brackets the timed one.
+    clock_before = (None, 0)
+    if flops > 0 and not args.no_clock:
+        clock_before = measure_clock(run, dev, launches=10)
+
     # Two HIP events on the launch stream (the library launches on torch's
     # current stream) bracket the K timed steps: their elapsed time over K is
     # the mean launch duration.  Events around every launch would add their
@@ -685,9 +693,14 @@ def main():
 
     clock, workgroups = None, 0
     if flops > 0 and not args.no_clock:
-        gemm_ghz, workgroups = measure_clock(run, dev)
+        ghz_after, workgroups = measure_clock(run, dev, launches=10)
+        ghz_before = clock_before[0]
+        gemm_ghz = (None if ghz_after is None or ghz_before is None
+                    else 0.5 * (ghz_before + ghz_after))
         probe_mfma, probe_ctr = probe_clock(dev)
         clock = {"gemm_ghz": None if gemm_ghz is None else round(gemm_ghz, 4),
+                 "gemm_ghz_before": None if ghz_before is None else round(ghz_before, 4),
+                 "gemm_ghz_after": None if ghz_after is None else round(ghz_after, 4),
                  "workgroups": workgroups,
                  "probe_mfma_ghz": round(probe_mfma, 4),
                  "probe_counter_ghz": round(probe_ctr, 4), "spec_ghz": SPEC_GHZ}
