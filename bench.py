@@ -38,6 +38,7 @@ HBM_PEAK_GBS = 8000.0
 SPEC_GHZ = 2.4   # the clock MI355X's published MFMA peaks are quoted at
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 SIMDS = 1024        # 256 CUs x 4 SIMDs
+CLOCK_LAUNCHES = 10  # launches in each clock-trace window (before, after the timed ones)
 
 
 def _code_only(text: str) -> str:
@@ -276,40 +277,58 @@ def prewarm(run, stream, min_s=0.5, max_s=4.0, tol=0.01):
         window = int(min(5000, max(8, 20.0 / max(ms, 1e-3))))
 
 
-def measure_clock(run, dev, launches=10):
-    """The clock the dominant kernel ran at: the library's per-workgroup
-    clock trace (shader-clock and real-time counters at the start and end of
-    every workgroup) over `launches` launches, each into its own part of the
-    trace buffer (the clock moves over a few milliseconds, so one launch
-    alone is not representative).  Returns (GHz, workgroups one launch ran),
-    or (None, 0) if none was recorded."""
-    import numpy as np
-    import torch
+class ClockWindow:
+    """The clock the dominant kernel ran at over `launches` back-to-back
+    launches: the library's per-workgroup clock trace (shader-clock and
+    real-time counters at the start and end of every workgroup), each launch
+    into its own part of the trace buffer (the clock moves over a few
+    milliseconds, so one launch alone is not representative).
 
-    import dense_gemm_swizzled_amd as sg
-    sentinel = -1
-    slots = 1 << 13          # per launch; every grid here is smaller
-    buf = torch.full((launches, 4 * slots), sentinel, dtype=torch.int64, device=dev)
-    khz = 0
-    try:
-        for i in range(launches):
-            khz = sg.gemm_clock_trace(buf[i].data_ptr(), slots)
-            run()
-        torch.cuda.synchronize()
-    finally:
-        sg.gemm_clock_trace(None, 0)
-    raw = buf.view(launches, slots, 4).cpu().numpy()
-    written = (raw != sentinel).any(axis=2)
-    per_launch = int(written.sum(axis=1).max())
-    v = raw[written].astype(np.float64)
-    ok = (v[:, 1] > v[:, 0]) & (v[:, 3] > v[:, 2])
-    log(f"[bench] clock trace: {per_launch} workgroups a launch over {launches} launches, "
-        f"{int(ok.sum())} records with increasing counters")
-    if not ok.any() or khz <= 0:
-        return None, 0
-    v = v[ok]
-    return (float((v[:, 1] - v[:, 0]).sum() / (v[:, 3] - v[:, 2]).sum() * khz / 1e6),
-            per_launch)
+    The buffer is allocated when the window is made and the records are read
+    only in result(), so that running the window (enqueue only) leaves the
+    GPU no idle time: after a few milliseconds of idle the clock drops and
+    the next launches run slower while it ramps back."""
+
+    SLOTS = 1 << 13          # per launch; every grid here is smaller
+
+    def __init__(self, dev, launches):
+        import torch
+        self.launches = launches
+        self.buf = torch.full((launches, 4 * self.SLOTS), -1, dtype=torch.int64, device=dev)
+        self.khz = 0
+
+    def run(self, run):
+        import dense_gemm_swizzled_amd as sg
+        try:
+            for i in range(self.launches):
+                self.khz = sg.gemm_clock_trace(self.buf[i].data_ptr(), self.SLOTS)
+                run()
+        finally:
+            sg.gemm_clock_trace(None, 0)
+
+    def result(self):
+        """(GHz, workgroups one launch ran, mean launch span in seconds), the
+        span being first workgroup start to last workgroup end on the
+        real-time counter; or (None, 0, None) if nothing was recorded."""
+        import numpy as np
+        raw = self.buf.view(self.launches, self.SLOTS, 4).cpu().numpy()
+        written = (raw != -1).any(axis=2)
+        per_launch = int(written.sum(axis=1).max())
+        v = raw[written].astype(np.float64)
+        ok = (v[:, 1] > v[:, 0]) & (v[:, 3] > v[:, 2])
+        log(f"[bench] clock trace: {per_launch} workgroups a launch over {self.launches} "
+            f"launches, {int(ok.sum())} records with increasing counters")
+        if not ok.any() or self.khz <= 0:
+            return None, 0, None
+        spans = []
+        for i in range(self.launches):
+            r = raw[i][written[i]].astype(np.float64)
+            r = r[(r[:, 1] > r[:, 0]) & (r[:, 3] > r[:, 2])]
+            if len(r):
+                spans.append((r[:, 3].max() - r[:, 2].min()) / (self.khz * 1e3))
+        v = v[ok]
+        return (float((v[:, 1] - v[:, 0]).sum() / (v[:, 3] - v[:, 2]).sum() * self.khz / 1e6),
+                per_launch, float(np.mean(spans)) if spans else None)
 
 
 def probe_clock(dev, iters=10000):
@@ -460,8 +479,10 @@ def profile(args, layout_args):
                     base[k] = t[k]
     result = {"kernel_source_hash": kernel_source_hash(),
               "note": "per launch: kernel_ns (mean of the timed launches, kernel trace), "
-                      "clock_ghz (the kernel's own clock trace), counters (mean of the timed "
-                      "launches of a --pmc pass); bytes = FETCH_SIZE[KiB]*1024*fetch_factor + "
+                      "clock_ghz (the kernel's own clock trace, mean of the windows before "
+                      "and after the timed launches), clock_windows (each window's clock and "
+                      "its launches' mean time), mfma_busy (per window, mean), counters (mean "
+                      "of the timed launches of a --pmc pass); bytes = FETCH_SIZE[KiB]*1024*fetch_factor + "
                       "WRITE_SIZE[KiB]*1024*write_factor, factors from a 1 GiB device copy",
               "fetch_factor": base.get("fetch_factor"), "write_factor": base.get("write_factor"),
               "workloads": dict(base.get("workloads", {}))}
@@ -477,10 +498,27 @@ def profile(args, layout_args):
                                         f"{w}_trace")
         line = json.loads(stdout.strip().splitlines()[-1])
         name, durs = _dominant(_csv_rows(d, "kernel_trace.csv"))
-        first = args.warmup + int(line.get("prewarm_launches") or 0)
-        timed = durs[first:first + args.steps] or durs
+        # Launch order of the bench: warmup, prewarm, the clock window
+        # before, the timed launches, the clock window after.
+        ck = line.get("clock") or {}
+        nb, na = int(ck.get("launches_before") or 0), int(ck.get("launches_after") or 0)
+        first = args.warmup + int(line.get("prewarm_launches") or 0) + nb
+        if len(durs) != first + args.steps + na:
+            log(f"[profile] {w}: {len(durs)} launches of {name} in the trace, expected "
+                f"{first + args.steps + na}; averaging all of them")
+            first, nb, na = 0, 0, 0
+            timed = durs
+        else:
+            timed = durs[first:first + args.steps]
         kernel_ns = sum(timed) / len(timed)
-        clock = (line.get("clock") or {}).get("gemm_ghz")
+        clock = ck.get("gemm_ghz")
+        # Each clock window with its own launches' mean duration.
+        windows = []
+        for ghz, seg in ((ck.get("gemm_ghz_before"), durs[first - nb:first] if nb else []),
+                         (ck.get("gemm_ghz_after"),
+                          durs[first + args.steps:first + args.steps + na] if na else [])):
+            if ghz and seg:
+                windows.append((ghz, sum(seg) / len(seg)))
         counters, cmds = {}, [cmd_trace]
         passes = PMC_PASSES if w != "copy" else [p for p in PMC_PASSES if p[0] != "sq"]
         for tag, names in passes:
@@ -490,7 +528,9 @@ def profile(args, layout_args):
             counters.update(_counter_means(rows, name, 3, 10))
         flops = _flops_of(line)
         entry = {"kernel": name, "kernel_ns": round(kernel_ns, 1), "launches_averaged": len(timed),
-                 "clock_ghz": clock, "counters": {k: round(v, 3) for k, v in counters.items()}}
+                 "clock_ghz": clock,
+                 "clock_windows": [{"ghz": g, "kernel_ns": round(t, 1)} for g, t in windows],
+                 "counters": {k: round(v, 3) for k, v in counters.items()}}
         if w == "copy":
             n = line["config"]["bytes_read"]
             result["fetch_factor"] = n / (counters["FETCH_SIZE"] * 1024)
@@ -507,9 +547,13 @@ def profile(args, layout_args):
             entry["mops_x512_equals_2mnk"] = abs(mops * 512 - flops) < 0.5
             entry["lds_bank_conflict_cycles"] = counters["SQ_LDS_BANK_CONFLICT"]
             entry["lds_idx_active_cycles"] = counters["SQ_LDS_IDX_ACTIVE"]
-            if clock:
-                entry["mfma_busy"] = round(counters["SQ_VALU_MFMA_BUSY_CYCLES"]
-                                           / (SIMDS * clock * kernel_ns), 4)
+            if windows:
+                # Busy cycles over the SIMD cycles of a launch, each clock
+                # window's clock with that window's own launch time (the
+                # clock drifts; a clock from one window with the time of
+                # another would mix two operating points).
+                b = [counters["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * g * t) for g, t in windows]
+                entry["mfma_busy"] = round(sum(b) / len(b), 4)
         result["workloads"][key] = entry
         _write_summary(outdir, w, key, line, entry, cmds, result)
         with open(os.path.join(outdir, "counters.json"), "w") as f:
@@ -548,8 +592,11 @@ def _write_summary(outdir, w, key, line, e, cmds, result):
     L += ["", "| quantity | value |", "|---|---|",
           f"| kernel time (mean of {e['launches_averaged']} timed launches, kernel trace) | "
           f"{e['kernel_ns'] / 1e3:.3f} us |",
-          f"| clock the kernel held (its own clock trace, 10 launches before and 10 after the timed ones) | "
-          f"{e['clock_ghz']} GHz |"]
+          f"| clock the kernel held (its own clock trace, mean of the windows of "
+          f"{CLOCK_LAUNCHES} launches before and after the timed ones) | {e['clock_ghz']} GHz |"]
+    for tag, cw in zip(("before", "after"), e.get("clock_windows") or []):
+        L.append(f"| clock window {tag}: clock, mean kernel time (kernel trace) | "
+                 f"{cw['ghz']} GHz, {cw['kernel_ns'] / 1e3:.3f} us |")
     for k, v in sorted(e["counters"].items()):
         L.append(f"| {k} (mean per timed launch) | {v:g} |")
     if "flops" in e and e["flops"]:
@@ -561,7 +608,7 @@ def _write_summary(outdir, w, key, line, e, cmds, result):
               f"| achieved | {ach:.1f} TFLOP/s = {100 * ach / peak:.1f}% of {peak} |"
               if peak else ""]
         if e.get("mfma_busy") is not None:
-            L.append(f"| MFMA busy = BUSY_CYCLES / (1024 SIMDs x clock x time) | "
+            L.append(f"| MFMA busy = BUSY_CYCLES / (1024 SIMDs x clock x time), per clock window, mean | "
                      f"{100 * e['mfma_busy']:.1f}% |")
         L.append(f"| LDS bank-conflict cycles | {e['lds_bank_conflict_cycles']:g} |")
     if "bytes" in e:
@@ -616,7 +663,8 @@ def main():
                     help="the same through gemm_layout128_run on 128x128 tiles, where 'pad' "
                          "(rows padded by 16 bytes) also fits")
     ap.add_argument("--no-clock", action="store_true",
-                    help="skip the clock trace and the MFMA clock probe after the timed region")
+                    help="skip the clock-trace windows before and after the timed region and "
+                         "the MFMA clock probe")
     ap.add_argument("--profile", metavar="OUTDIR", default=None,
                     help="run rocprofv3 passes (kernel trace, SQ counters, FETCH_SIZE, "
                          "WRITE_SIZE) over this bench for the --workload list (comma "
@@ -651,20 +699,23 @@ def main():
     run, flops, dtype, cfg, oracle_sample, rows_total = build_workload(args.workload, dev, layout)
     stream = torch.cuda.current_stream(dev)
 
+    # The clock is traced over a window of launches right before the timed
+    # region and one right after it (never inside): the clock drifts slowly,
+    # and the two windows bracket the timed one.  Nothing between the prewarm,
+    # the windows and the timed region leaves the GPU idle for longer than a
+    # synchronisation.
+    traced = flops > 0 and not args.no_clock
+    if traced:
+        win_before = ClockWindow(dev, CLOCK_LAUNCHES)
+        win_after = ClockWindow(dev, CLOCK_LAUNCHES)
+
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
     pw_launches, pw_s, pw_ms = (0, 0.0, None) if args.no_prewarm else prewarm(run, stream)
-    log(f"[bench] prewarm: {pw_launches} more launches, {pw_s:.2f} s of GPU time, last "
-        f"window {pw_ms} ms per launch")
-
-    # The clock is traced over 10 launches before the timed region and 10
-    # after it (never inside): the clock drifts slowly, and the mean of the
-    # two windows brackets the timed one.
-    clock_before = (None, 0)
-    if flops > 0 and not args.no_clock:
-        clock_before = measure_clock(run, dev, launches=10)
+    if traced:
+        win_before.run(run)
 
     # Two HIP events on the launch stream (the library launches on torch's
     # current stream) bracket the K timed steps: their elapsed time over K is
@@ -682,6 +733,11 @@ def main():
     e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if traced:
+        win_after.run(run)
+        torch.cuda.synchronize()
+    log(f"[bench] prewarm: {pw_launches} more launches, {pw_s:.2f} s of GPU time, last "
+        f"window {pw_ms} ms per launch")
     mean_ms = e_start.elapsed_time(e_end) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -692,15 +748,20 @@ def main():
         f"({100 * achieved / peak:.1f}% of {peak} TFLOP/s)")
 
     clock, workgroups = None, 0
-    if flops > 0 and not args.no_clock:
-        ghz_after, workgroups = measure_clock(run, dev, launches=10)
-        ghz_before = clock_before[0]
+    if traced:
+        ghz_before, _, span_before = win_before.result()
+        ghz_after, workgroups, span_after = win_after.result()
         gemm_ghz = (None if ghz_after is None or ghz_before is None
                     else 0.5 * (ghz_before + ghz_after))
         probe_mfma, probe_ctr = probe_clock(dev)
-        clock = {"gemm_ghz": None if gemm_ghz is None else round(gemm_ghz, 4),
-                 "gemm_ghz_before": None if ghz_before is None else round(ghz_before, 4),
-                 "gemm_ghz_after": None if ghz_after is None else round(ghz_after, 4),
+
+        def r(x, n=4):
+            return None if x is None else round(x, n)
+        clock = {"gemm_ghz": r(gemm_ghz),
+                 "gemm_ghz_before": r(ghz_before), "gemm_ghz_after": r(ghz_after),
+                 "span_us_before": r(None if span_before is None else span_before * 1e6, 3),
+                 "span_us_after": r(None if span_after is None else span_after * 1e6, 3),
+                 "launches_before": CLOCK_LAUNCHES, "launches_after": CLOCK_LAUNCHES,
                  "workgroups": workgroups,
                  "probe_mfma_ghz": round(probe_mfma, 4),
                  "probe_counter_ghz": round(probe_ctr, 4), "spec_ghz": SPEC_GHZ}
@@ -749,10 +810,16 @@ def main():
         out["counters"]["source"] = "profiles/counters.json"
     if clock is not None and clock["gemm_ghz"]:
         # The MFMA peak at the clock the kernel held (the published peak is
-        # quoted at 2.4 GHz).
+        # quoted at 2.4 GHz), and the fraction of it the kernel reached.  The
+        # clock drifts between the windows, so each window's fraction takes
+        # that window's own clock and launch span; the two are averaged.
         adj = peak * clock["gemm_ghz"] / SPEC_GHZ
         out["roofline"]["clock_adjusted_peak"] = round(adj, 1)
-        out["roofline"]["frac_of_clock_adjusted_peak"] = round(achieved / adj, 4)
+        fr = [flops / span / 1e12 / (peak * ghz / SPEC_GHZ)
+              for ghz, span in ((ghz_before, span_before), (ghz_after, span_after))
+              if ghz and span]
+        if fr:
+            out["roofline"]["frac_of_clock_adjusted_peak"] = round(sum(fr) / len(fr), 4)
     if args.workload == "grouped":
         # Per group the kernel can go no faster than its MFMA time or the HBM
         # time of its own bytes (A_g, B_g, D_g), whichever is longer.
