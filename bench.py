@@ -170,59 +170,40 @@ def build_workload(name: str, dev, layout=None):
 
         return run, flops, "bf16", cfg, oracle_sample, case.m_sizes[0]
 
-    if name == "mxfp8":
-        case = si.mxfp8()
+    if name in ("mxfp8", "mxfp4", "mxfp6", "mxfp6_e3m2"):
+        case = {"mxfp8": lambda: si.mxfp8(), "mxfp4": lambda: si.mxfp4(),
+                "mxfp6": lambda: si.mxfp6(),
+                "mxfp6_e3m2": lambda: si.mxfp6(fmt="e3m2")}[name]()
         A, SFA, B, SFB = (t.to(dev) for t in (case.A, case.SFA, case.B, case.SFB))
         D = torch.empty(case.M, case.N, dtype=torch.bfloat16, device=dev)
+        # A step takes the scales as they come, [rows][K/32], and rearranges
+        # them into the 64-row blocks the GEMM reads one KiB at a time
+        # (mx_scales_to_blocks), then runs the GEMM on them.
+        sfa_b = torch.empty(sg.mx_scales_blocks_bytes(case.M, case.K), dtype=torch.uint8,
+                            device=dev)
+        sfb_b = torch.empty(sg.mx_scales_blocks_bytes(case.N, case.K), dtype=torch.uint8,
+                            device=dev)
+        code = {"e4m3": sg.SG_E4M3, "e2m1": sg.SG_E2M1, "e2m3": sg.SG_E2M3,
+                "e3m2": sg.SG_E3M2}[case.fmt]
+        st = torch.cuda.current_stream(dev).cuda_stream
+        # The closure holds the tensors themselves: their raw pointers alone
+        # would let torch's allocator hand the memory to later tensors.
+        tensors = (A, SFA, B, SFB, D, sfa_b, sfb_b)
 
         def run():
-            sg.mx_gemm(A, SFA, B, SFB, out=D)
+            a, sa, b, sb, d, sab, sbb = (t.data_ptr() for t in tensors)
+            rc = (sg.mx_scales_to_blocks(sa, case.M, case.K, sab, st)
+                  or sg.mx_scales_to_blocks(sb, case.N, case.K, sbb, st)
+                  or sg.mx_gemm_blocks_run(code, case.M, case.N, case.K, a, sab, b, sbb, d,
+                                           sg.SG_BF16, st))
+            if rc:
+                raise RuntimeError(sg.gemm_last_error())
 
         flops = 2.0 * case.M * case.N * case.K
         cfg = {"workload": case.name, "M": case.M, "N": case.N, "K": case.K,
-               "block": 32, "ab_dtype": "e4m3", "scale": "e8m0", "d_dtype": "bf16"}
-
-        def oracle_sample(rows):
-            import oracle
-            t0 = time.perf_counter()
-            oracle.mx_gemm(rows, case.N, case.K, case.A[:rows], case.SFA[:rows], case.B,
-                           case.SFB, with_bound=False)
-            return time.perf_counter() - t0, 2.0 * rows * case.N * case.K
-
-        return run, flops, "e4m3", cfg, oracle_sample, case.M
-
-    if name == "mxfp4":
-        case = si.mxfp4()
-        A, SFA, B, SFB = (t.to(dev) for t in (case.A, case.SFA, case.B, case.SFB))
-        D = torch.empty(case.M, case.N, dtype=torch.bfloat16, device=dev)
-
-        def run():
-            sg.mxfp4_gemm(A, SFA, B, SFB, out=D)
-
-        flops = 2.0 * case.M * case.N * case.K
-        cfg = {"workload": case.name, "M": case.M, "N": case.N, "K": case.K,
-               "block": 32, "ab_dtype": "e2m1", "scale": "e8m0", "d_dtype": "bf16"}
-
-        def oracle_sample(rows):
-            import oracle
-            t0 = time.perf_counter()
-            oracle.mx_gemm(rows, case.N, case.K, case.A[:rows], case.SFA[:rows], case.B,
-                           case.SFB, with_bound=False, fmt="e2m1")
-            return time.perf_counter() - t0, 2.0 * rows * case.N * case.K
-
-        return run, flops, "e2m1", cfg, oracle_sample, case.M
-
-    if name in ("mxfp6", "mxfp6_e3m2"):
-        case = si.mxfp6(fmt="e3m2") if name == "mxfp6_e3m2" else si.mxfp6()
-        A, SFA, B, SFB = (t.to(dev) for t in (case.A, case.SFA, case.B, case.SFB))
-        D = torch.empty(case.M, case.N, dtype=torch.bfloat16, device=dev)
-
-        def run():
-            sg.mxfp6_gemm(A, SFA, B, SFB, fmt=case.fmt, out=D)
-
-        flops = 2.0 * case.M * case.N * case.K
-        cfg = {"workload": case.name, "M": case.M, "N": case.N, "K": case.K,
-               "block": 32, "ab_dtype": case.fmt, "scale": "e8m0", "d_dtype": "bf16"}
+               "block": 32, "ab_dtype": case.fmt, "scale": "e8m0",
+               "scale_layout": "[rows][K/32], rearranged into 64-row blocks in the step",
+               "d_dtype": "bf16"}
 
         def oracle_sample(rows):
             import oracle

@@ -7,13 +7,15 @@ no CPU fallback: if the shared library is missing, every call raises.
 Two layers:
 
 * ``gemm_run``, ``gemm_strided_run``, ``grouped_gemm_run``, ``mx_gemm_run``,
-  ``mxfp4_gemm_run``, ``mxfp6_gemm_run``, ``gemm_layout_run``,
+  ``mxfp4_gemm_run``, ``mxfp6_gemm_run``, ``mx_scales_blocks_bytes``,
+  ``mx_scales_to_blocks``, ``mx_gemm_blocks_run``, ``gemm_layout_run``,
   ``gemm_layout128_run``, ``gemm_last_error``, ``gemm_version``,
   ``gemm_lds_layout``, ``gemm_lds_layout_mxfp6``, ``gemm_lds_layout_cblock``,
   ``gemm_lds_image``: the C entry points under the same names, taking integer
   device pointers.
 * ``gemm``, ``gemm_strided``, ``grouped_gemm``, ``mx_gemm``, ``mxfp4_gemm``,
-  ``mxfp6_gemm``, ``gemm_layout``, ``gemm_layout128``: the same calls on torch CUDA
+  ``mxfp6_gemm``, ``mx_scales_blocks``, ``mx_gemm_blocks``, ``gemm_layout``,
+  ``gemm_layout128``: the same calls on torch CUDA
   tensors (shapes read from the tensors, output allocated by torch, launched
   on torch's current stream).
 """
@@ -33,7 +35,9 @@ __all__ = [
     "gemm_version", "gemm_lds_layout", "gemm_lds_layout_mxfp6", "gemm_lds_layout_cblock",
     "gemm_lds_image", "gemm_lds_image_tile", "gemm_mfma_scale_probe", "SG_IMG_HALF",
     "SG_IMG_HALF_KEXACT", "SG_IMG_MN256", "SG_IMG_FP6", "SG_IMG_CBLOCK", "gemm_last_kernel", "gemm_clock_trace", "gemm_clock_probe", "gemm_clock_probe_waves",
-    "SG_E2M3", "SG_E3M2",
+    "SG_E2M1", "SG_E2M3", "SG_E3M2", "SG_SF_ROWS", "SG_SF_BLOCKS",
+    "mx_scales_blocks_bytes", "mx_scales_to_blocks", "mx_gemm_blocks_run", "mx_scales_blocks",
+    "mx_gemm_blocks",
     "gemm", "gemm_plan", "gemm_strided", "grouped_gemm", "mx_gemm", "mxfp4_gemm", "mxfp6_gemm",
     "gemm_layout", "gemm_layout_io", "gemm_layout_io_run",
     "gemm_layout128", "SG_LAYOUT_PAD16",
@@ -42,7 +46,8 @@ __all__ = [
 
 SG_OK = 0
 SG_NONE, SG_F16, SG_BF16, SG_F32, SG_E4M3, SG_E8M0 = 0, 1, 2, 3, 4, 5
-SG_E2M3, SG_E3M2 = 7, 8
+SG_E2M1, SG_E2M3, SG_E3M2 = 6, 7, 8
+SG_SF_ROWS, SG_SF_BLOCKS = 0, 1
 SG_K_MAJOR, SG_MN_MAJOR = 0, 1
 SG_MAX_GROUPS = 256
 SG_LAYOUT_PAD16 = -1
@@ -97,7 +102,11 @@ def load():
     lib.gemm_clock_trace.argtypes = [vp, i64, ctypes.POINTER(ctypes.c_int)]
     lib.gemm_clock_probe.argtypes = [i64, vp, vp]
     lib.gemm_clock_probe_waves.argtypes = []
-    for f in (lib.gemm_run, lib.gemm_strided_run, lib.grouped_gemm_run, lib.mx_gemm_run,
+    lib.mx_scales_blocks_bytes.argtypes = [i64, i64]
+    lib.mx_scales_blocks_bytes.restype = ctypes.c_int64
+    lib.mx_scales_to_blocks.argtypes = [vp, i64, i64, vp, vp]
+    lib.mx_gemm_blocks_run.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
+    for f in (lib.mx_scales_to_blocks, lib.mx_gemm_blocks_run, lib.gemm_run, lib.gemm_strided_run, lib.grouped_gemm_run, lib.mx_gemm_run,
               lib.mxfp4_gemm_run, lib.mxfp6_gemm_run,
               lib.gemm_layout_run, lib.gemm_layout128_run, lib.gemm_layout_io_run,
               lib.gemm_lds_layout, lib.gemm_lds_layout_mxfp6, lib.gemm_lds_layout_cblock,
@@ -148,6 +157,18 @@ def mxfp4_gemm_run(M, N, K, A, SFA, B, SFB, D, d_dtype, stream) -> int:
 
 def mxfp6_gemm_run(fmt, M, N, K, A, SFA, B, SFB, D, d_dtype, stream) -> int:
     return load().mxfp6_gemm_run(fmt, M, N, K, A, SFA, B, SFB, D, d_dtype, stream)
+
+
+def mx_scales_blocks_bytes(rows, K) -> int:
+    return load().mx_scales_blocks_bytes(rows, K)
+
+
+def mx_scales_to_blocks(SF, rows, K, out, stream) -> int:
+    return load().mx_scales_to_blocks(SF, rows, K, out, stream)
+
+
+def mx_gemm_blocks_run(fmt, M, N, K, A, SFA, B, SFB, D, d_dtype, stream) -> int:
+    return load().mx_gemm_blocks_run(fmt, M, N, K, A, SFA, B, SFB, D, d_dtype, stream)
 
 
 def gemm_layout_run(swz_units, M, N, K, A, B, C, c_dtype, D, d_dtype, stream) -> int:
@@ -537,6 +558,64 @@ def _mx_args(A, SFA, B, SFB, out, out_dtype, k_per_byte_num: int, k_per_byte_den
         _dtype_is("out", out, (torch.float32, torch.bfloat16))
     _one_device(("A", A), ("SFA", SFA), ("B", B), ("SFB", SFB), ("out", out))
     return M, N, K, _out(out, (M, N), out_dtype or torch.bfloat16, A.device)
+
+
+_MX_FMTS = {"e4m3": (SG_E4M3, 1, 1), "e2m1": (SG_E2M1, 2, 1), "e2m3": (SG_E2M3, 4, 3),
+            "e3m2": (SG_E3M2, 4, 3)}
+
+
+def mx_scales_blocks(SF, *, out=None):
+    """e8m0 scales SF [rows][K/32] (uint8) rearranged into the SG_SF_BLOCKS
+    layout: a 1-D uint8 tensor of mx_scales_blocks_bytes(rows, K) bytes
+    (allocated by torch unless `out` is given)."""
+    import torch
+    _dense("SF", SF)
+    _dtype_is("SF", SF, (torch.uint8,))
+    rows, K = int(SF.shape[0]), int(SF.shape[1]) * 32
+    n = int(mx_scales_blocks_bytes(rows, K))
+    _check(n if n < 0 else 0)
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=SF.device)
+    else:
+        _dense("out", out, 1)
+        _shape("out", out, (n,))
+        _dtype_is("out", out, (torch.uint8,))
+    _one_device(("SF", SF), ("out", out))
+    _check(mx_scales_to_blocks(SF.data_ptr(), rows, K, out.data_ptr(), _stream(SF.device)))
+    return out
+
+
+def mx_gemm_blocks(A, SFA, B, SFB, *, fmt: str = "e4m3", out_dtype=None, out=None):
+    """The block-scaled GEMM of mx_gemm / mxfp4_gemm / mxfp6_gemm (fmt
+    "e4m3", "e2m1", "e2m3" or "e3m2"; A and B as there) with SFA and SFB in
+    the SG_SF_BLOCKS layout (mx_scales_blocks)."""
+    import torch
+    _need(fmt in _MX_FMTS, -4, f"fmt must be one of {sorted(_MX_FMTS)}, got {fmt!r}")
+    code, num, den = _MX_FMTS[fmt]
+    for name, t in (("A", A), ("B", B)):
+        _dense(name, t)
+        _dtype_is(name, t, (torch.uint8,))
+    M, N = int(A.shape[0]), int(B.shape[0])
+    _need(A.shape[1] == B.shape[1], -3,
+          f"A and B rows hold different byte counts ({A.shape[1]} vs {B.shape[1]})")
+    K = int(A.shape[1]) * num // den
+    _need(K * den == int(A.shape[1]) * num, -3,
+          f"A's row of {A.shape[1]} bytes is not a whole number of elements")
+    for name, t, rows in (("SFA", SFA, M), ("SFB", SFB, N)):
+        _dense(name, t, 1)
+        _dtype_is(name, t, (torch.uint8,))
+        n = int(mx_scales_blocks_bytes(rows, K))
+        _check(n if n < 0 else 0)
+        _shape(name, t, (n,))
+    if out is not None:
+        _dense("out", out)
+        _shape("out", out, (M, N))
+        _dtype_is("out", out, (torch.float32, torch.bfloat16))
+    _one_device(("A", A), ("SFA", SFA), ("B", B), ("SFB", SFB), ("out", out))
+    out = _out(out, (M, N), out_dtype or torch.bfloat16, A.device)
+    _check(mx_gemm_blocks_run(code, M, N, K, A.data_ptr(), SFA.data_ptr(), B.data_ptr(),
+                              SFB.data_ptr(), out.data_ptr(), _dt(out.dtype), _stream(A.device)))
+    return out
 
 
 def mx_gemm(A, SFA, B, SFB, *, out_dtype=None, out=None):

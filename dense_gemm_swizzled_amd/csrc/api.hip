@@ -327,30 +327,49 @@ int grouped_gemm_run(int G, const int64_t* m_offsets, int64_t N, int64_t K,
   return ok();
 }
 
-int mxfp4_gemm_run(int64_t M, int64_t N, int64_t K, const void* A, const void* SFA,
-                   const void* B, const void* SFB, void* D, int d_dtype, void* stream) {
-  if (M < 0 || N < 0 || K < 0)
-    return fail(SG_ERR_SHAPE, "mxfp4_gemm_run: negative size");
-  if (K % 256)
-    return fail(SG_ERR_SHAPE, "mxfp4_gemm_run: K=%lld is not a multiple of 256", (long long)K);
+namespace {
+
+// The shared checks and launch of the block-scaled GEMMs: fmt SG_E4M3,
+// SG_E2M1, SG_E2M3 or SG_E3M2; scales in layout sf_layout (SG_SF_ROWS: 4-byte
+// aligned; SG_SF_BLOCKS: 16-byte aligned).
+int mx_run(const char* who, int fmt, int sf_layout, int64_t M, int64_t N, int64_t K,
+           const void* A, const void* SFA, const void* B, const void* SFB, void* D,
+           int d_dtype, void* stream) {
+  const bool fp4 = fmt == SG_E2M1, fp6 = fmt == SG_E2M3 || fmt == SG_E3M2;
+  if (fmt != SG_E4M3 && !fp4 && !fp6)
+    return fail(SG_ERR_DTYPE, "%s: fmt %d is not SG_E4M3/SG_E2M1/SG_E2M3/SG_E3M2", who, fmt);
+  if (sf_layout != SG_SF_ROWS && sf_layout != SG_SF_BLOCKS)
+    return fail(SG_ERR_SHAPE, "%s: sf_layout %d is not SG_SF_ROWS/SG_SF_BLOCKS", who, sf_layout);
+  if (M < 0 || N < 0 || K < 0) return fail(SG_ERR_SHAPE, "%s: negative size", who);
+  const int64_t kmul = fp4 ? 256 : 128;
+  if (K % kmul)
+    return fail(SG_ERR_SHAPE, "%s: K=%lld is not a multiple of %lld", who, (long long)K,
+                (long long)kmul);
   if (d_dtype != SG_F32 && d_dtype != SG_BF16)
-    return fail(SG_ERR_DTYPE, "mxfp4_gemm_run: d_dtype %d is not SG_F32/SG_BF16", d_dtype);
+    return fail(SG_ERR_DTYPE, "%s: d_dtype %d is not SG_F32/SG_BF16", who, d_dtype);
   if (M == 0 || N == 0) return ok();
-  if (!D) return fail(SG_ERR_NULL, "mxfp4_gemm_run: D is NULL");
+  if (!D) return fail(SG_ERR_NULL, "%s: D is NULL", who);
   if (K > 0 && (!A || !B || !SFA || !SFB))
-    return fail(SG_ERR_NULL, "mxfp4_gemm_run: A, B, SFA or SFB is NULL");
+    return fail(SG_ERR_NULL, "%s: A, B, SFA or SFB is NULL", who);
   const int db = elem_bytes(d_dtype);
+  const uintptr_t sf_mask = sf_layout == SG_SF_BLOCKS ? 15u : 3u;
   if ((K > 0 && (!aligned16(A) || !aligned16(B))) || !aligned16(D) ||
-      (K > 0 && ((reinterpret_cast<uintptr_t>(SFA) | reinterpret_cast<uintptr_t>(SFB)) & 3u)))
-    return fail(SG_ERR_ALIGN,
-                "mxfp4_gemm_run: A, B, D must be 16-byte aligned, SFA and SFB 4-byte aligned");
+      (K > 0 && ((reinterpret_cast<uintptr_t>(SFA) | reinterpret_cast<uintptr_t>(SFB)) & sf_mask)))
+    return fail(SG_ERR_ALIGN, "%s: A, B, D must be 16-byte aligned, SFA and SFB %d-byte aligned",
+                who, sf_layout == SG_SF_BLOCKS ? 16 : 4);
   if ((N * db) % 16)
-    return fail(SG_ERR_ALIGN, "mxfp4_gemm_run: D row pitch must be a multiple of 16 bytes");
-  if (256 * (K / 2) >= kMaxExtent)
-    return fail(SG_ERR_SHAPE, "mxfp4_gemm_run: an operand panel spans 2^31 bytes or more");
-  const int64_t tiles_m = cdiv(M, 256), tiles_n = cdiv(N, 256);
-  if (tiles_m * tiles_n > 0x7fffffffLL)
-    return fail(SG_ERR_SHAPE, "mxfp4_gemm_run: too many tiles");
+    return fail(SG_ERR_ALIGN, "%s: D row pitch must be a multiple of 16 bytes", who);
+  // MXFP8 takes 128x128 tiles for small problems; the others 256x256.
+  const sg::TileShape tile = fmt == SG_E4M3 ? pick_tile(cdiv(M, 256) * cdiv(N, 256)) : sg::kTile256;
+  const int64_t T = tile == sg::kTile256 ? 256 : 128;
+  const int64_t row_bytes = fp4 ? K / 2 : fp6 ? K / 4 * 3 : K;
+  // a tile's panel (plus, for fp6, the 8 bytes its shifted rows may read beyond it)
+  if (T * row_bytes + (fp6 ? 8 : 0) >= kMaxExtent)
+    return fail(SG_ERR_SHAPE, "%s: an operand panel spans 2^31 bytes or more", who);
+  if (sf_layout == SG_SF_BLOCKS && cdiv(T, 64) * cdiv(K, 512) * 1024 >= kMaxExtent)
+    return fail(SG_ERR_SHAPE, "%s: a tile's scales span 2^31 bytes or more", who);
+  const int64_t tiles_m = cdiv(M, T), tiles_n = cdiv(N, T);
+  if (tiles_m * tiles_n > 0x7fffffffLL) return fail(SG_ERR_SHAPE, "%s: too many tiles", who);
   sg::MxParams p;
   p.A = A;
   p.SFA = SFA;
@@ -361,103 +380,66 @@ int mxfp4_gemm_run(int64_t M, int64_t N, int64_t K, const void* A, const void* S
   p.N = N;
   p.K = K;
   p.d_dtype = d_dtype;
+  p.sf_layout = sf_layout;
   p.tiles_m = (int)tiles_m;
   p.tiles_n = (int)tiles_n;
   p.group_m = kGroupM;
   p.clk = g_clk;
-  hipError_t e = sg::launch_mxfp4(p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "mxfp4_gemm_run launch");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = fp4   ? sg::launch_mxfp4(p, s)
+                       : fp6 ? sg::launch_mxfp6(fmt == SG_E3M2, p, s)
+                             : sg::launch_mx(tile, p, s);
+  if (e != hipSuccess) return fail(SG_ERR_HIP, "%s launch: %s", who, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+int mxfp4_gemm_run(int64_t M, int64_t N, int64_t K, const void* A, const void* SFA,
+                   const void* B, const void* SFB, void* D, int d_dtype, void* stream) {
+  return mx_run("mxfp4_gemm_run", SG_E2M1, SG_SF_ROWS, M, N, K, A, SFA, B, SFB, D, d_dtype,
+                stream);
 }
 
 int mxfp6_gemm_run(int fmt, int64_t M, int64_t N, int64_t K, const void* A, const void* SFA,
                    const void* B, const void* SFB, void* D, int d_dtype, void* stream) {
   if (fmt != SG_E2M3 && fmt != SG_E3M2)
     return fail(SG_ERR_DTYPE, "mxfp6_gemm_run: fmt %d is not SG_E2M3/SG_E3M2", fmt);
-  if (M < 0 || N < 0 || K < 0)
-    return fail(SG_ERR_SHAPE, "mxfp6_gemm_run: negative size");
-  if (K % 128)
-    return fail(SG_ERR_SHAPE, "mxfp6_gemm_run: K=%lld is not a multiple of 128", (long long)K);
-  if (d_dtype != SG_F32 && d_dtype != SG_BF16)
-    return fail(SG_ERR_DTYPE, "mxfp6_gemm_run: d_dtype %d is not SG_F32/SG_BF16", d_dtype);
-  if (M == 0 || N == 0) return ok();
-  if (!D) return fail(SG_ERR_NULL, "mxfp6_gemm_run: D is NULL");
-  if (K > 0 && (!A || !B || !SFA || !SFB))
-    return fail(SG_ERR_NULL, "mxfp6_gemm_run: A, B, SFA or SFB is NULL");
-  const int db = elem_bytes(d_dtype);
-  if ((K > 0 && (!aligned16(A) || !aligned16(B))) || !aligned16(D) ||
-      (K > 0 && ((reinterpret_cast<uintptr_t>(SFA) | reinterpret_cast<uintptr_t>(SFB)) & 3u)))
-    return fail(SG_ERR_ALIGN,
-                "mxfp6_gemm_run: A, B, D must be 16-byte aligned, SFA and SFB 4-byte aligned");
-  if ((N * db) % 16)
-    return fail(SG_ERR_ALIGN, "mxfp6_gemm_run: D row pitch must be a multiple of 16 bytes");
-  // a tile's panel plus the 8 bytes its shifted rows may read beyond it
-  if (256 * (K / 4 * 3) + 8 >= kMaxExtent)
-    return fail(SG_ERR_SHAPE, "mxfp6_gemm_run: an operand panel spans 2^31 bytes or more");
-  const int64_t tiles_m = cdiv(M, 256), tiles_n = cdiv(N, 256);
-  if (tiles_m * tiles_n > 0x7fffffffLL)
-    return fail(SG_ERR_SHAPE, "mxfp6_gemm_run: too many tiles");
-  sg::MxParams p;
-  p.A = A;
-  p.SFA = SFA;
-  p.B = B;
-  p.SFB = SFB;
-  p.D = D;
-  p.M = M;
-  p.N = N;
-  p.K = K;
-  p.d_dtype = d_dtype;
-  p.tiles_m = (int)tiles_m;
-  p.tiles_n = (int)tiles_n;
-  p.group_m = kGroupM;
-  p.clk = g_clk;
-  hipError_t e = sg::launch_mxfp6(fmt == SG_E3M2, p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "mxfp6_gemm_run launch");
-  return ok();
+  return mx_run("mxfp6_gemm_run", fmt, SG_SF_ROWS, M, N, K, A, SFA, B, SFB, D, d_dtype, stream);
 }
 
 int mx_gemm_run(int64_t M, int64_t N, int64_t K, const void* A, const void* SFA,
                 const void* B, const void* SFB, void* D, int d_dtype, void* stream) {
-  if (M < 0 || N < 0 || K < 0)
-    return fail(SG_ERR_SHAPE, "mx_gemm_run: negative size");
-  if (K % 128)
-    return fail(SG_ERR_SHAPE, "mx_gemm_run: K=%lld is not a multiple of 128", (long long)K);
-  if (d_dtype != SG_F32 && d_dtype != SG_BF16)
-    return fail(SG_ERR_DTYPE, "mx_gemm_run: d_dtype %d is not SG_F32/SG_BF16", d_dtype);
-  if (M == 0 || N == 0) return ok();
-  if (!D) return fail(SG_ERR_NULL, "mx_gemm_run: D is NULL");
-  if (K > 0 && (!A || !B || !SFA || !SFB))
-    return fail(SG_ERR_NULL, "mx_gemm_run: A, B, SFA or SFB is NULL");
-  const int db = elem_bytes(d_dtype);
-  if ((K > 0 && (!aligned16(A) || !aligned16(B))) || !aligned16(D) ||
-      (K > 0 && ((reinterpret_cast<uintptr_t>(SFA) | reinterpret_cast<uintptr_t>(SFB)) & 3u)))
-    return fail(SG_ERR_ALIGN,
-                "mx_gemm_run: A, B, D must be 16-byte aligned, SFA and SFB 4-byte aligned");
-  if ((N * db) % 16)
-    return fail(SG_ERR_ALIGN, "mx_gemm_run: D row pitch must be a multiple of 16 bytes");
-  const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256);
-  const sg::TileShape tile = pick_tile(tiles256);
-  const int64_t T = tile == sg::kTile256 ? 256 : 128;
-  if (T * K >= kMaxExtent)
-    return fail(SG_ERR_SHAPE, "mx_gemm_run: an operand panel spans 2^31 bytes or more");
-  const int64_t tiles_m = cdiv(M, T), tiles_n = cdiv(N, T);
-  if (tiles_m * tiles_n > 0x7fffffffLL) return fail(SG_ERR_SHAPE, "mx_gemm_run: too many tiles");
-  sg::MxParams p;
-  p.A = A;
-  p.SFA = SFA;
-  p.B = B;
-  p.SFB = SFB;
-  p.D = D;
-  p.M = M;
-  p.N = N;
-  p.K = K;
-  p.d_dtype = d_dtype;
-  p.tiles_m = (int)tiles_m;
-  p.tiles_n = (int)tiles_n;
-  p.group_m = kGroupM;
-  p.clk = g_clk;
-  hipError_t e = sg::launch_mx(tile, p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "mx_gemm_run launch");
+  return mx_run("mx_gemm_run", SG_E4M3, SG_SF_ROWS, M, N, K, A, SFA, B, SFB, D, d_dtype,
+                stream);
+}
+
+int mx_gemm_blocks_run(int fmt, int64_t M, int64_t N, int64_t K, const void* A,
+                       const void* SFA, const void* B, const void* SFB, void* D, int d_dtype,
+                       void* stream) {
+  return mx_run("mx_gemm_blocks_run", fmt, SG_SF_BLOCKS, M, N, K, A, SFA, B, SFB, D, d_dtype,
+                stream);
+}
+
+int64_t mx_scales_blocks_bytes(int64_t rows, int64_t K) {
+  if (rows < 0 || K < 0 || K % 32)
+    return fail(SG_ERR_SHAPE, "mx_scales_blocks_bytes: rows=%lld K=%lld (K a multiple of 32)",
+                (long long)rows, (long long)K);
+  return cdiv(rows, 64) * cdiv(K, 512) * 1024;
+}
+
+int mx_scales_to_blocks(const void* SF, int64_t rows, int64_t K, void* out, void* stream) {
+  if (rows < 0 || K < 0 || K % 128)
+    return fail(SG_ERR_SHAPE, "mx_scales_to_blocks: rows=%lld K=%lld (K a multiple of 128)",
+                (long long)rows, (long long)K);
+  if (rows == 0 || K == 0) return ok();
+  if (!SF || !out) return fail(SG_ERR_NULL, "mx_scales_to_blocks: SF or out is NULL");
+  if ((reinterpret_cast<uintptr_t>(SF) & 3u) || !aligned16(out))
+    return fail(SG_ERR_ALIGN, "mx_scales_to_blocks: SF must be 4-byte, out 16-byte aligned");
+  if (cdiv(rows, 64) > 0x7fffffffLL || cdiv(cdiv(K, 512), 16) > 65535)
+    return fail(SG_ERR_SHAPE, "mx_scales_to_blocks: too many rows or K blocks");
+  hipError_t e = sg::launch_sf_blocks(SF, rows, K, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mx_scales_to_blocks launch");
   return ok();
 }
 

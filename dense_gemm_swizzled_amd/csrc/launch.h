@@ -50,6 +50,9 @@ hipError_t launch_grouped(TileShape tile, bool bf16, int swz,
 hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s);
 hipError_t launch_mxfp4(const MxParams& p, hipStream_t s);  // 256x256 tiles
 hipError_t launch_mxfp6(bool e3m2, const MxParams& p, hipStream_t s);  // 256x256 tiles
+// e8m0 scales [rows][K/32] (K a multiple of 128) into the blocks layout of
+// SfMap (mx_kernels.h).
+hipError_t launch_sf_blocks(const void* sf, int64_t rows, int64_t K, void* out, hipStream_t s);
 // The MFMA clock probe (diag.hip): one wave per SIMD of 256 CUs.
 int clock_probe_waves();
 hipError_t launch_clock_probe(int64_t iters, void* out, hipStream_t s);

@@ -38,6 +38,55 @@ hipError_t launch_mxfp6(bool e3m2, const MxParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The scale bytes of 64 rows and one group of 16 K blocks go to one KiB of
+// `out`.  A workgroup of 1024 threads takes rows [64 i, 64 i + 64) and up to
+// 16 groups (blockIdx.y), one 16-byte unit per thread: it reads the units
+// row by row (contiguous in the rows layout), transposes them through LDS
+// (groups 1040 bytes apart, so that the 16 units of one row fall in
+// different banks) and writes them a group at a time (one contiguous KiB
+// each).  Rows past `rows` and blocks past K/32 are written as zero.
+__global__ void __launch_bounds__(1024) sf_blocks_kernel(const uint32_t* sf, int64_t rows,
+                                                         int64_t pitch_dw, int64_t groups,
+                                                         u32x4* out) {
+  constexpr int kLdsRow = 1040;
+  __shared__ __attribute__((aligned(16))) char lds[16 * kLdsRow];
+  const int64_t rb = blockIdx.x, g0 = 16 * (int64_t)blockIdx.y;
+  const int ng = (int)min<int64_t>(16, groups - g0);
+  const int u = threadIdx.x;
+  if (u < 64 * ng) {
+    const int row = u / ng, g = u - row * ng;
+    const int64_t r = rb * 64 + row;
+    const int64_t n = pitch_dw - 4 * (g0 + g);  // dwords of the row from the unit's first
+    u32x4 v{0u, 0u, 0u, 0u};
+    if (r < rows) {
+      const uint32_t* src = sf + r * pitch_dw + 4 * (g0 + g);
+      if (n >= 4) {
+        __builtin_memcpy(&v, src, 16);
+      } else {
+#pragma unroll
+        for (int d = 0; d < 3; ++d)
+          if (d < n) v[d] = src[d];
+      }
+    }
+    *reinterpret_cast<u32x4*>(lds + g * kLdsRow + row * 16) = v;
+  }
+  __syncthreads();
+  if (u < 64 * ng) {
+    const int g = u >> 6, row = u & 63;
+    out[(rb * groups + g0 + g) * 64 + row] =
+        *reinterpret_cast<const u32x4*>(lds + g * kLdsRow + row * 16);
+  }
+}
+
+hipError_t launch_sf_blocks(const void* sf, int64_t rows, int64_t K, void* out, hipStream_t s) {
+  const int64_t groups = (K / 32 + 15) / 16;
+  hipLaunchKernelGGL(sf_blocks_kernel,
+                     dim3((unsigned)((rows + 63) / 64), (unsigned)((groups + 15) / 16)),
+                     dim3(1024), 0, s, static_cast<const uint32_t*>(sf), rows, K / 128, groups,
+                     static_cast<u32x4*>(out));
+  return hipGetLastError();
+}
+
 // Runs the K-major (direct-to-LDS) tile loader once (rows [row0, row0 + Rows), bytes
 // [k0*eb, k0*eb + 128) of each row) into LDS under the kernels' swizzle and
 // copies the LDS stage out linearly.

@@ -24,15 +24,52 @@ namespace sg {
 
 struct MxParams {
   const void* A;    // e4m3 [M][K]
-  const void* SFA;  // e8m0 [M][K/32]
+  const void* SFA;  // e8m0 [M][K/32] (SG_SF_ROWS) or in 64-row blocks (SG_SF_BLOCKS)
   const void* B;    // e4m3 [N][K]
-  const void* SFB;  // e8m0 [N][K/32]
+  const void* SFB;  // e8m0 [N][K/32] or in 64-row blocks
   void* D;
   int64_t M, N, K;
   int d_dtype;
+  int sf_layout;    // SG_SF_ROWS or SG_SF_BLOCKS
   int tiles_m, tiles_n;
   int group_m;
   ClockTrace clk;
+};
+
+// Where the scale byte of 32-element block b of row r lies, relative to a
+// tile's first row (tile rows start at multiples of 64).
+//   SG_SF_ROWS:   e8m0 [rows][K/32]: byte r * (K/32) + b.
+//   SG_SF_BLOCKS: the bytes of 64 rows x 16 blocks together: 1 KiB for rows
+//                 [64i, 64i+64) and blocks [16g, 16g+16), row r's 16 bytes
+//                 at 16 (r mod 64); blocks (i, g) in the order i * G + g,
+//                 G = ceil(K/512) groups a row.  A 64-lane load of one
+//                 group's 16 bytes for 64 consecutive rows reads one
+//                 contiguous KiB (8 cache lines); in the rows layout the same
+//                 load touches 64 lines, one per row.
+struct SfMap {
+  uint32_t blocked, pitch, groups;
+
+  __device__ __forceinline__ static SfMap make(int layout, int64_t K) {
+    return SfMap{layout == SG_SF_BLOCKS ? 1u : 0u, (uint32_t)(K / 32),
+                 (uint32_t)((K / 32 + 15) / 16)};
+  }
+  // The part of the offset that depends on the row.
+  __device__ __forceinline__ uint32_t row(uint32_t r) const {
+    return blocked ? (r >> 6) * groups * 1024u + (r & 63u) * 16u : r * pitch;
+  }
+  // The part that depends on the block index b (uniform in a wave).
+  __device__ __forceinline__ uint32_t block(uint32_t b) const {
+    return blocked ? (b >> 4) * 1024u + (b & 15u) : b;
+  }
+  __device__ __forceinline__ const char* tile(const void* sf, int64_t row0) const {
+    const char* p = static_cast<const char*>(sf);
+    return blocked ? p + (row0 >> 6) * (int64_t)groups * 1024 : p + row0 * (int64_t)pitch;
+  }
+  // Bytes from a tile's first row to the end of its rows_valid rows.
+  __device__ __forceinline__ uint32_t tile_bytes(int rows_valid) const {
+    return blocked ? (uint32_t)((rows_valid + 63) / 64) * groups * 1024u
+                   : (uint32_t)rows_valid * pitch;
+  }
 };
 
 __device__ __forceinline__ f32x16 mfma_scale_f8(const u32x4 (&a)[2],
@@ -72,18 +109,19 @@ struct MxTile {
   // that op-select 2*kk addresses block 4kt + 2kk + l/32.
   __device__ __forceinline__ static void load_scales(
       Scales& s, __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb,
-      uint32_t sf_pitch, int kt, int lane, int wm, int wn, int m_valid,
+      const SfMap& sf, int kt, int lane, int wm, int wn, int m_valid,
       int n_valid) {
     const int lrow = lane & 31;
+    const uint32_t kb = sf.block(4u * (uint32_t)kt);
 #pragma unroll
     for (int fm = 0; fm < kFM; ++fm) {
       const int r = wm * kWM + fm * 32 + lrow;
-      s.a[fm] = buffer_load4(rsa, r < m_valid ? r * sf_pitch + 4u * kt : kOutOfRange);
+      s.a[fm] = buffer_load4(rsa, r < m_valid ? sf.row((uint32_t)r) + kb : kOutOfRange);
     }
 #pragma unroll
     for (int fn = 0; fn < kFN; ++fn) {
       const int r = wn * kWN + fn * 32 + lrow;
-      s.b[fn] = buffer_load4(rsb, r < n_valid ? r * sf_pitch + 4u * kt : kOutOfRange);
+      s.b[fn] = buffer_load4(rsb, r < n_valid ? sf.row((uint32_t)r) + kb : kOutOfRange);
     }
   }
 
@@ -152,7 +190,7 @@ struct MxTile {
       f32x16 (&acc)[kFM][kFN], Frags& f0, Frags& f1,
       OperandLoader<BM, false, Swz, 1>& la, OperandLoader<BN, false, Swz, 1>& lb,
       Scales& sc, Scales& sc_next, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-      __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb, uint32_t sf_pitch, char* cur,
+      __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb, const SfMap& sf, char* cur,
       char* nxt, const TileJob& j, int tid, int lane, int wm, int wn, int lrow, int lhalf,
       int kt, int kt_total, int Ki) {
     constexpr int kVmem = BM / 32 + BN / 32;
@@ -163,7 +201,7 @@ struct MxTile {
     const int k1 = more ? (kt + 1) * kBK : Ki;
     la.issue(ra, nxt, tid, j.m_valid, k1, Ki);
     lb.issue(rb, nxt + kATileBytes, tid, j.n_valid, k1, Ki);
-    load_scales(sc_next, rsa, rsb, sf_pitch, more ? kt + 1 : kt, lane, wm, wn, j.m_valid,
+    load_scales(sc_next, rsa, rsb, sf, more ? kt + 1 : kt, lane, wm, wn, j.m_valid,
                 j.n_valid);
     uint32_t sa[kFM], sb[kFN];
 #pragma unroll
@@ -181,8 +219,8 @@ struct MxTile {
 
   __device__ __forceinline__ static void run(char* s0, char* s1, const TileJob& j,
                                              const char* sfa, const char* sfb,
-                                             int64_t K, void* D, int d_dtype,
-                                             int64_t ldd) {
+                                             const SfMap& sf, int64_t K, void* D,
+                                             int d_dtype, int64_t ldd) {
     const int tid = threadIdx.x;
     // The wave index is uniform across the wave; readfirstlane lets the
     // compiler keep it (and every LDS base derived from it) in SGPRs.
@@ -192,9 +230,8 @@ struct MxTile {
 
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(j.a, j.a_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(j.b, j.b_bytes);
-    const uint32_t sf_pitch = (uint32_t)(K / 32);
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sfa, (uint32_t)j.m_valid * sf_pitch);
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sfb, (uint32_t)j.n_valid * sf_pitch);
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sfa, sf.tile_bytes(j.m_valid));
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sfb, sf.tile_bytes(j.n_valid));
 
     f32x16 acc[kFM][kFN];
 #pragma unroll
@@ -212,7 +249,7 @@ struct MxTile {
     if (kt_total > 0) {
       la.issue(ra, s0, tid, j.m_valid, 0, Ki);
       lb.issue(rb, s0 + kATileBytes, tid, j.n_valid, 0, Ki);
-      load_scales(sc, rsa, rsb, sf_pitch, 0, lane, wm, wn, j.m_valid, j.n_valid);
+      load_scales(sc, rsa, rsb, sf, 0, lane, wm, wn, j.m_valid, j.n_valid);
     }
     wait_vmem();
     __syncthreads();
@@ -223,13 +260,13 @@ struct MxTile {
     // Two K tiles per trip (fixed stage objects), odd last tile peeled.
     int kt = 0;
     for (; kt + 1 < kt_total; kt += 2) {
-      k_tile(acc, f0, f1, la, lb, sc, sc_next, ra, rb, rsa, rsb, sf_pitch, s0, s1, j, tid,
+      k_tile(acc, f0, f1, la, lb, sc, sc_next, ra, rb, rsa, rsb, sf, s0, s1, j, tid,
              lane, wm, wn, lrow, lhalf, kt, kt_total, Ki);
-      k_tile(acc, f0, f1, la, lb, sc, sc_next, ra, rb, rsa, rsb, sf_pitch, s1, s0, j, tid,
+      k_tile(acc, f0, f1, la, lb, sc, sc_next, ra, rb, rsa, rsb, sf, s1, s0, j, tid,
              lane, wm, wn, lrow, lhalf, kt + 1, kt_total, Ki);
     }
     if (kt < kt_total)
-      k_tile(acc, f0, f1, la, lb, sc, sc_next, ra, rb, rsa, rsb, sf_pitch, s0, s1, j, tid,
+      k_tile(acc, f0, f1, la, lb, sc, sc_next, ra, rb, rsa, rsb, sf, s0, s1, j, tid,
              lane, wm, wn, lrow, lhalf, kt, kt_total, Ki);
 
     GemmTile<BM, BN, true, false, false, Swz>::epilogue(acc, j, nullptr, SG_NONE, D,
@@ -264,9 +301,8 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(const MxParams p) 
   j.ldc = 0;
   j.alpha = 1.0f;
   j.beta = 0.0f;
-  const char* sfa = static_cast<const char*>(p.SFA) + m0 * (p.K / 32);
-  const char* sfb = static_cast<const char*>(p.SFB) + n0 * (p.K / 32);
-  Tile::run(s0, s1, j, sfa, sfb, p.K, p.D, p.d_dtype, p.N);
+  const SfMap sf = SfMap::make(p.sf_layout, p.K);
+  Tile::run(s0, s1, j, sf.tile(p.SFA, m0), sf.tile(p.SFB, n0), sf, p.K, p.D, p.d_dtype, p.N);
   clock_end(p.clk, cs);
 }
 

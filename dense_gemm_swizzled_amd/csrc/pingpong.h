@@ -710,10 +710,11 @@ struct PingPongMxTile {
     if (i == 3) ld.template issue<3>(rsrc, half, w4, kbyte0);
   }
 
-  // ua, ub: fp6 only, see mxfp6_lds_offset.
+  // ua, ub: fp6 only, see mxfp6_lds_offset.  sfa, sfb: the scales of the
+  // tile's first rows, laid out as `sf` says.
   __device__ __forceinline__ static void run(char* smem, const TileJob& j, const char* sfa,
-                                             const char* sfb, int64_t K, void* D,
-                                             int d_dtype, int64_t ldd, uint32_t ua,
+                                             const char* sfb, const SfMap& sf, int64_t K,
+                                             void* D, int d_dtype, int64_t ldd, uint32_t ua,
                                              uint32_t ub) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -722,9 +723,8 @@ struct PingPongMxTile {
 
     const u32x4 ra = rsrc_words(j.a, j.a_bytes), rb = rsrc_words(j.b, j.b_bytes);
     const u32x4 ra0 = rsrc_words(j.a, 0), rb0 = rsrc_words(j.b, 0);
-    const uint32_t sf_pitch = (uint32_t)(K / 32);
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sfa, (uint32_t)j.m_valid * sf_pitch);
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sfb, (uint32_t)j.n_valid * sf_pitch);
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sfa, sf.tile_bytes(j.m_valid));
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sfb, sf.tile_bytes(j.n_valid));
     const int a_rows = j.m_valid - 128 * g, b_rows = j.n_valid - 128 * g;
     Loader la, lb;
     if constexpr (kFp6) {
@@ -743,16 +743,17 @@ struct PingPongMxTile {
       if (lb.voff[i] != kOutOfRange) lb.voff[i] += (uint32_t)(128 * g) * j.b_pitch;
     }
     // Scale rows of the lane: A 128g + 32(2p + h) + lrow for pair p, B
-    // 64 w4 + 32 h + lrow.
+    // 64 w4 + 32 h + lrow (64 consecutive rows per load: one KiB in the
+    // blocks layout).
     uint32_t sva[2], svb;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int r = 128 * g + 32 * (2 * p + lhalf) + lrow;
-      sva[p] = r < j.m_valid ? (uint32_t)r * sf_pitch : kOutOfRange;
+      sva[p] = r < j.m_valid ? sf.row((uint32_t)r) : kOutOfRange;
     }
     {
       const int r = 64 * w4 + 32 * lhalf + lrow;
-      svb = r < j.n_valid ? (uint32_t)r * sf_pitch : kOutOfRange;
+      svb = r < j.n_valid ? sf.row((uint32_t)r) : kOutOfRange;
     }
 
     const uint32_t s0 = lds_addr(smem);
@@ -770,9 +771,10 @@ struct PingPongMxTile {
       issue_half(lb, i, t < T ? rb : rb0, b_ring + (t % 3) * kTileBytes, w4,
                  (uint32_t)t * (uint32_t)kTileRowBytes);
     };
-    // Scales of the group starting at tile t.
+    // Scales of the group starting at tile t (its 16 bytes start at block
+    // 4 kScaleDw t, a multiple of 16).
     auto ld_s = [&](Scales& s, int t, int q) {
-      load_scale(s, q, rsa, rsb, sva, svb, (uint32_t)(t * 4 * kScaleDw));
+      load_scale(s, q, rsa, rsb, sva, svb, sf.block((uint32_t)(t * 4 * kScaleDw)));
     };
 
     // Tiles 0 and 1 (B, A, and the scales of the first group: the order the
@@ -970,8 +972,9 @@ __global__ void __launch_bounds__(512, 1) pingpong_mx_kernel(const MxParams p) {
   j.ldc = 0;
   j.alpha = 1.0f;
   j.beta = 0.0f;
-  Tile::run(smem, j, static_cast<const char*>(p.SFA) + m0 * (p.K / 32),
-            static_cast<const char*>(p.SFB) + n0 * (p.K / 32), p.K, p.D, p.d_dtype, p.N, ua, ub);
+  const SfMap sf = SfMap::make(p.sf_layout, p.K);
+  Tile::run(smem, j, sf.tile(p.SFA, m0), sf.tile(p.SFB, n0), sf, p.K, p.D, p.d_dtype, p.N, ua,
+            ub);
   clock_end(p.clk, cs);
 }
 

@@ -59,8 +59,13 @@ extern "C" {
 #define SG_F32 3  /* IEEE binary32 */
 #define SG_E4M3 4 /* OCP FP8 E4M3 (bias 7, max 448, no infinity) */
 #define SG_E8M0 5 /* OCP E8M0 scale, value 2^(e-127) */
+#define SG_E2M1 6 /* OCP FP4 E2M1 (bias 1, max 6, two elements per byte) */
 #define SG_E2M3 7 /* OCP FP6 E2M3 (bias 1, max 7.5, no infinity or NaN) */
 #define SG_E3M2 8 /* OCP FP6 E3M2 (bias 3, max 28, no infinity or NaN) */
+
+/* Layouts of the e8m0 scale arrays of the block-scaled GEMMs. */
+#define SG_SF_ROWS 0   /* [rows][K/32]: row r's byte b at r * (K/32) + b */
+#define SG_SF_BLOCKS 1 /* 1 KiB blocks of 64 rows x 16 bytes, see mx_scales_to_blocks */
 
 /* Operand majorness. */
 #define SG_K_MAJOR 0  /* K is the contiguous dimension */
@@ -201,6 +206,46 @@ int mxfp4_gemm_run(int64_t M, int64_t N, int64_t K, const void* A,
 int mxfp6_gemm_run(int fmt, int64_t M, int64_t N, int64_t K, const void* A,
                    const void* SFA, const void* B, const void* SFB, void* D,
                    int d_dtype, void* stream);
+
+/*
+ * mx_scales_blocks_bytes -- the size in bytes of an e8m0 scale array of
+ * `rows` rows and K/32 blocks in the SG_SF_BLOCKS layout (host-side, no GPU
+ * needed): ceil(rows/64) * ceil(K/512) * 1024.  Returns SG_ERR_SHAPE
+ * (negative) for rows < 0, K < 0 or K not a multiple of 32.
+ */
+int64_t mx_scales_blocks_bytes(int64_t rows, int64_t K);
+
+/*
+ * mx_scales_to_blocks -- rearranges e8m0 scales SF [rows][K/32] (SG_SF_ROWS,
+ * the layout of "06 Blackwell Tensor Core - tcgen05 MMA", section
+ * "Block-Scaled MMA": SFA(M, SFK), SFB(N, SFK)) into `out`, SG_SF_BLOCKS:
+ * row r's scale byte b (32-element block b of K) goes to byte
+ *   ((r / 64) * G + b / 16) * 1024 + (r % 64) * 16 + b % 16,  G = ceil(K/512),
+ * so that the 16 bytes of one group of 16 blocks for 64 consecutive rows are
+ * one contiguous KiB.  Bytes for rows past `rows` (up to the next multiple
+ * of 64) and blocks past K/32 are written as zero.  The block-scaled GEMMs
+ * read a row's group in one 16-byte load per lane; from SG_SF_BLOCKS a
+ * wave's load covers 8 cache lines instead of the 64 (one per row) of
+ * SG_SF_ROWS.  SF: DEVICE memory, 4-byte aligned; out: DEVICE memory of
+ * mx_scales_blocks_bytes(rows, K) bytes, 16-byte aligned (caller-owned).
+ * Asynchronous on `stream` (a hipStream_t, NULL for the default stream).
+ * Errors: SG_ERR_SHAPE (K not a multiple of 128, negative sizes, 2^31 or
+ * more blocks of 64 rows, K past 2^29), SG_ERR_NULL, SG_ERR_ALIGN,
+ * SG_ERR_HIP.
+ */
+int mx_scales_to_blocks(const void* SF, int64_t rows, int64_t K, void* out, void* stream);
+
+/*
+ * mx_gemm_blocks_run -- the block-scaled GEMM of mx_gemm_run (fmt SG_E4M3),
+ * mxfp4_gemm_run (SG_E2M1) or mxfp6_gemm_run (SG_E2M3, SG_E3M2), with SFA
+ * and SFB in the SG_SF_BLOCKS layout (mx_scales_to_blocks), 16-byte aligned.
+ * Every other argument, requirement and result is that entry point's; the
+ * D it computes is bit-identical.  Errors: theirs, and SG_ERR_DTYPE for
+ * another fmt.
+ */
+int mx_gemm_blocks_run(int fmt, int64_t M, int64_t N, int64_t K, const void* A,
+                       const void* SFA, const void* B, const void* SFB, void* D,
+                       int d_dtype, void* stream);
 
 /*
  * gemm_layout_run -- the bf16 GEMM with A and B K-major (and optional C) on

@@ -293,6 +293,73 @@ def test_mxfp6_empty_is_ok():
     assert _mx6(M=0, K=0, A=None, B=None, SFA=None, SFB=None) == 0
 
 
+def _mxb(**kw):
+    a = dict(fmt=sg.SG_E4M3, M=256, N=256, K=512, A=P, SFA=P, B=P, SFB=P, D=P,
+             d_dtype=sg.SG_BF16)
+    a.update(kw)
+    return sg.mx_gemm_blocks_run(a["fmt"], a["M"], a["N"], a["K"], a["A"], a["SFA"], a["B"],
+                                 a["SFB"], a["D"], a["d_dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(fmt=sg.SG_BF16), DTYPE), (dict(fmt=9), DTYPE), (dict(fmt=sg.SG_E8M0), DTYPE),
+    (dict(K=96), SHAPE), (dict(fmt=sg.SG_E2M1, K=384), SHAPE), (dict(M=-1), SHAPE),
+    (dict(d_dtype=sg.SG_F16), DTYPE),
+    (dict(A=None), NULL), (dict(SFA=None), NULL), (dict(SFB=None), NULL), (dict(D=None), NULL),
+    # the blocks layout is read 16 bytes at a time: 4-byte alignment is not enough
+    (dict(SFA=P + 4), ALIGN), (dict(SFB=P + 8), ALIGN), (dict(B=P + 8), ALIGN),
+    (dict(N=260), ALIGN),
+])
+def test_mx_blocks_rejects(kw, code):
+    assert _mxb(**kw) == code, sg.gemm_last_error()
+    assert sg.gemm_last_error().startswith("mx_gemm_blocks_run")
+
+
+def test_mx_blocks_empty_is_ok():
+    for fmt in (sg.SG_E4M3, sg.SG_E2M1, sg.SG_E2M3, sg.SG_E3M2):
+        assert _mxb(fmt=fmt, M=0) == 0 and _mxb(fmt=fmt, N=0) == 0
+
+
+def test_mx_rows_layout_still_takes_4_byte_aligned_scales():
+    # Only the argument checks run (no GPU).  The panel-size check comes after
+    # the alignment check: with P + 4 scales the rows layout reaches it
+    # (SHAPE), the blocks layout stops at the alignment (ALIGN).
+    assert _mx(SFA=P + 4, SFB=P + 4, K=1 << 24) == SHAPE
+    assert _mxb(SFA=P + 4, SFB=P + 4, K=1 << 24) == ALIGN
+    assert _mxb(K=1 << 24) == SHAPE
+
+
+@pytest.mark.parametrize("rows,K,nbytes", [
+    (64, 512, 1024), (65, 512, 2048), (64, 640, 2048), (0, 512, 0), (100, 128, 2048),
+    (8192, 8192, 8192 // 64 * 16 * 1024), (1, 32, 1024),
+])
+def test_mx_scales_blocks_bytes(rows, K, nbytes):
+    assert sg.mx_scales_blocks_bytes(rows, K) == nbytes
+
+
+@pytest.mark.parametrize("rows,K", [(-1, 512), (64, -32), (64, 48)])
+def test_mx_scales_blocks_bytes_rejects(rows, K):
+    assert sg.mx_scales_blocks_bytes(rows, K) == SHAPE
+    assert sg.gemm_last_error().startswith("mx_scales_blocks_bytes")
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=96), SHAPE), (dict(rows=-1), SHAPE), (dict(K=-128), SHAPE),
+    (dict(SF=None), NULL), (dict(out=None), NULL),
+    (dict(SF=P + 2), ALIGN), (dict(out=P + 8), ALIGN),
+])
+def test_mx_scales_to_blocks_rejects(kw, code):
+    a = dict(SF=P, rows=64, K=512, out=P)
+    a.update(kw)
+    assert sg.mx_scales_to_blocks(a["SF"], a["rows"], a["K"], a["out"], None) == code
+    assert sg.gemm_last_error().startswith("mx_scales_to_blocks")
+
+
+def test_mx_scales_to_blocks_empty_is_ok():
+    assert sg.mx_scales_to_blocks(None, 0, 512, None, None) == 0
+    assert sg.mx_scales_to_blocks(None, 64, 0, None, None) == 0
+
+
 def test_mxfp6_layout_is_the_xor_swizzle_with_odd_rows_shifted():
     # Restated from the definition: byte b of row r sits at byte b + 8 of the
     # row when r is odd (and not at the unshifted block position), in the

@@ -536,6 +536,62 @@ def test_grouped_full_size(dev):
 
 # ------------------------------------------------------------------ MX
 
+def run_mx_blocks(case: si.MXCase, dev, d_dtype="bf16"):
+    """The case through mx_scales_to_blocks and mx_gemm_blocks_run."""
+    sfa = sg.mx_scales_blocks(case.SFA.to(dev))
+    sfb = sg.mx_scales_blocks(case.SFB.to(dev))
+    d = sg.mx_gemm_blocks(case.A.to(dev), sfa, case.B.to(dev), sfb, fmt=case.fmt,
+                          out_dtype=DT[d_dtype])
+    torch.cuda.synchronize()
+    return d
+
+
+def blocks_reference(sf: np.ndarray) -> np.ndarray:
+    """The SG_SF_BLOCKS image of e8m0 scales [rows][K/32], written out from
+    its definition: byte b of row r at ((r // 64) * G + b // 16) * 1024 +
+    (r % 64) * 16 + b % 16, G = ceil(K/512), zeros elsewhere."""
+    rows, nb = sf.shape
+    G = (nb + 15) // 16
+    out = np.zeros(((rows + 63) // 64) * G * 1024, np.uint8)
+    for r in range(rows):
+        for b in range(nb):
+            out[((r // 64) * G + b // 16) * 1024 + (r % 64) * 16 + b % 16] = sf[r, b]
+    return out
+
+
+@pytest.mark.parametrize("rows,K", [(1, 128), (100, 640), (300, 1024), (64, 512)])
+def test_mx_scales_to_blocks_is_the_documented_permutation(dev, rows, K):
+    rng = np.random.default_rng(rows + K)
+    sf = rng.integers(0, 256, (rows, K // 32)).astype(np.uint8)
+    say(f"mx_scales_to_blocks {rows}x{K // 32}")
+    dst = torch.full((sg.mx_scales_blocks_bytes(rows, K),), 0xA5, dtype=torch.uint8,
+                     device=dev)
+    got = sg.mx_scales_blocks(torch.from_numpy(sf).to(dev), out=dst)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), blocks_reference(sf))
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [
+    ("e4m3", 300, 264, 640), ("e4m3", 4100, 4104, 640), ("e4m3", 128, 128, 128),
+    ("e2m1", 300, 264, 768), ("e2m1", 4100, 4104, 512),
+    ("e2m3", 257, 36, 640), ("e3m2", 4100, 4104, 384), ("e2m3", 1, 4, 128),
+])
+def test_mx_blocks_scales_give_the_same_d(dev, fmt, M, N, K):
+    # The same GEMM with the scales in the blocks layout: D bit-identical to
+    # the rows layout's (which the tests above compare with the oracle), on
+    # 128- and 256-wide tiles, ragged M and N, K not a multiple of 512 (a
+    # partial last scale group) and scales over 2^-17 .. 2^17.
+    case = si.mx_case(M, N, K, 31, fmt=fmt)
+    rng = np.random.default_rng(9)
+    case.SFA = torch.from_numpy(rng.integers(110, 145, (M, K // 32)).astype(np.uint8))
+    case.SFB = torch.from_numpy(rng.integers(110, 145, (N, K // 32)).astype(np.uint8))
+    say(f"mx blocks {fmt} {M}x{N}x{K}")
+    runner = {"e4m3": run_mx, "e2m1": run_mx4, "e2m3": run_mx6, "e3m2": run_mx6}[fmt]
+    for dt in ("f32", "bf16") if N % 8 == 0 else ("f32",):  # D rows of 16-byte multiples
+        ref = runner(case, dev, dt)
+        assert torch.equal(run_mx_blocks(case, dev, dt), ref), (fmt, dt)
+
+
 def run_mx(case: si.MXCase, dev, d_dtype="bf16"):
     d = sg.mx_gemm(case.A.to(dev), case.SFA.to(dev), case.B.to(dev), case.SFB.to(dev),
                    out_dtype=DT[d_dtype])
@@ -625,6 +681,7 @@ def test_mxfp4_8192_full_size_sampled(dev):
     say(f"{case.name} (sampled)")
     d = run_mx4(case, dev, "bf16")
     assert bool(torch.isfinite(d).all())
+    assert torch.equal(run_mx_blocks(case, dev, "bf16"), d)
     rows, cols = sample_points(case.M, case.N, 3000, 56)
     ref, bound = oracle.mx_gemm_points(case.M, case.N, case.K, case.A, case.SFA, case.B,
                                        case.SFB, rows, cols, fmt="e2m1")
@@ -702,6 +759,7 @@ def test_mxfp6_8192_full_size_sampled(dev):
     say(f"{case.name} (sampled)")
     d = run_mx6(case, dev, "bf16")
     assert bool(torch.isfinite(d).all())
+    assert torch.equal(run_mx_blocks(case, dev, "bf16"), d)
     rows, cols = sample_points(case.M, case.N, 3000, 57)
     ref, bound = oracle.mx_gemm_points(case.M, case.N, case.K, case.A, case.SFA, case.B,
                                        case.SFB, rows, cols, fmt=case.fmt)
@@ -715,6 +773,7 @@ def test_mx_8192_full_size(dev):
     say(f"{case.name} (every output)")
     d = run_mx(case, dev, "bf16")
     assert sg.gemm_last_kernel().startswith("pingpong_mx_kernel<e4m3")
+    assert torch.equal(run_mx_blocks(case, dev, "bf16"), d)
     got = _np(d)
     del d
     ref, bound = oracle.mx_gemm(case.M, case.N, case.K, case.A, case.SFA, case.B, case.SFB)
