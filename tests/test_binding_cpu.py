@@ -105,3 +105,35 @@ def test_block_scaled_checks(fn, row_bytes, kw):
 
 def test_mxfp6_rejects_unknown_format():
     assert _code(sg.mxfp6_gemm, u8(8, 192), u8(8, 8), u8(4, 192), u8(4, 8), fmt="e4m3") == DTYPE
+
+
+def u8(*shape):
+    return torch.zeros(*shape, dtype=torch.uint8)
+
+
+def test_mx_scales_blocks_checks():
+    assert _code(sg.mx_scales_blocks, torch.zeros(64, 16)) == DTYPE
+    assert _code(sg.mx_scales_blocks, u8(64)) == SHAPE
+    assert _code(sg.mx_scales_blocks, u8(16, 64).t()) == ALIGN
+    assert _code(sg.mx_scales_blocks, u8(64, 16), out=u8(1000)) == SHAPE
+    assert _code(sg.mx_scales_blocks, u8(64, 16), out=u8(1024, 1)) == SHAPE
+    # every other check passes: only the device is wrong
+    assert _code(sg.mx_scales_blocks, u8(64, 16), out=u8(1024)) == NULL
+
+
+def test_mx_gemm_blocks_checks():
+    M, N, K = 64, 32, 512
+    A, B = u8(M, K), u8(N, K)
+    sfa, sfb = u8(sg.mx_scales_blocks_bytes(M, K)), u8(sg.mx_scales_blocks_bytes(N, K))
+    assert _code(sg.mx_gemm_blocks, A, sfa, B, sfb, fmt="e5m2") == DTYPE
+    assert _code(sg.mx_gemm_blocks, A, u8(M, K // 32), B, sfb) == SHAPE  # rows layout
+    assert _code(sg.mx_gemm_blocks, A, u8(1000), B, sfb) == SHAPE
+    assert _code(sg.mx_gemm_blocks, A, sfa, u8(N, K - 16), sfb) == SHAPE
+    assert _code(sg.mx_gemm_blocks, A.float(), sfa, B, sfb) == DTYPE
+    assert _code(sg.mx_gemm_blocks, A, sfa, B, sfb, out=torch.zeros(M, N + 1)) == SHAPE
+    # e2m1: two elements a byte, so the same bytes hold K = 1024
+    sfa4 = u8(sg.mx_scales_blocks_bytes(M, 2 * K))
+    sfb4 = u8(sg.mx_scales_blocks_bytes(N, 2 * K))
+    assert _code(sg.mx_gemm_blocks, A, sfa, B, sfb, fmt="e2m1") == SHAPE
+    assert _code(sg.mx_gemm_blocks, A, sfa4, B, sfb4, fmt="e2m1") == NULL
+    assert _code(sg.mx_gemm_blocks, A, sfa, B, sfb) == NULL
