@@ -171,7 +171,7 @@ __global__ void __launch_bounds__(kImgThreads, 1)
     img_fp6_kernel(const char* X, uint32_t x_bytes, uint32_t pitch, int rows_valid,
                    uint32_t unshifted, uint32_t t, char* out) {
   __shared__ __attribute__((aligned(4096))) char smem[16384];
-  using Tile = PingPongMxTile<kSwzDefault, 2>;
+  using Tile = PingPongMxTile<kSwzDefault, 2, false>;
   const int lane = threadIdx.x & 63, w4 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const u32x4 rsrc = rsrc_words(X, x_bytes);
   const uint32_t half = lds_addr(smem);

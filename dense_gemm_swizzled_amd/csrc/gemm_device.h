@@ -42,7 +42,8 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r,
                             __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// The same with an SGPR byte offset added to the address.
+// The same with an SGPR byte offset added to the address.  The range check
+// may leave the SGPR offset out: off + soff must lie inside the buffer.
 __device__ __forceinline__ u32x4 buffer_load16_so(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                                   uint32_t soff) {
   return __builtin_bit_cast(
@@ -53,6 +54,11 @@ __device__ __forceinline__ u32x4 buffer_load16_so(__amdgpu_buffer_rsrc_t r, uint
 __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r,
                                                  uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t r,
+                                                 uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
 // LDS access in 16-byte units (the swizzle never splits a 16-byte atom).

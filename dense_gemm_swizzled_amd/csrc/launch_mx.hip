@@ -4,47 +4,68 @@
 
 namespace sg {
 
-hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s) {
-  static const char* const names[2] = {kernel_label("pingpong_mx_kernel", "e4m3"),
-                                       kernel_label("mx_gemm_kernel", "128", "e4m3")};
-  last_kernel() = names[tile == kTile256 ? 0 : 1];
-  const int grid = p.tiles_m * p.tiles_n;
-  if (tile == kTile256)
-    hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, 0>), dim3(grid), dim3(512), 0, s, p);
+namespace {
+
+// The 256x256 ping-pong for operand format Fmt, with the scale layout p
+// names; `labels` = {rows, blocks}.
+template <int Fmt>
+hipError_t launch_pingpong_mx(const MxParams& p, hipStream_t s, const char* const (&labels)[2]) {
+  const bool blocks = p.sf_layout == SG_SF_BLOCKS;
+  last_kernel() = labels[blocks ? 1 : 0];
+  const dim3 grid(p.tiles_m * p.tiles_n);
+  if (blocks)
+    hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, Fmt, true>), grid, dim3(512), 0, s, p);
   else
-    hipLaunchKernelGGL((mx_gemm_kernel<128, 128, kSwzDefault>), dim3(grid),
-                       dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, Fmt, false>), grid, dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mx(TileShape tile, const MxParams& p, hipStream_t s) {
+  static const char* const labels[2] = {kernel_label("pingpong_mx_kernel", "e4m3", "rows"),
+                                        kernel_label("pingpong_mx_kernel", "e4m3", "blocks")};
+  static const char* const name128 = kernel_label("mx_gemm_kernel", "128", "e4m3");
+  if (tile == kTile256) return launch_pingpong_mx<0>(p, s, labels);
+  last_kernel() = name128;
+  hipLaunchKernelGGL((mx_gemm_kernel<128, 128, kSwzDefault>), dim3(p.tiles_m * p.tiles_n),
+                     dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_mxfp4(const MxParams& p, hipStream_t s) {
-  static const char* const name = kernel_label("pingpong_mx_kernel", "e2m1");
-  last_kernel() = name;
-  hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, 4>), dim3(p.tiles_m * p.tiles_n),
-                     dim3(512), 0, s, p);
-  return hipGetLastError();
+  static const char* const labels[2] = {kernel_label("pingpong_mx_kernel", "e2m1", "rows"),
+                                        kernel_label("pingpong_mx_kernel", "e2m1", "blocks")};
+  return launch_pingpong_mx<4>(p, s, labels);
 }
 
 hipError_t launch_mxfp6(bool e3m2, const MxParams& p, hipStream_t s) {
-  static const char* const names[2] = {kernel_label("pingpong_mx_kernel", "e2m3"),
-                                       kernel_label("pingpong_mx_kernel", "e3m2")};
-  last_kernel() = names[e3m2 ? 1 : 0];
-  if (e3m2)
-    hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, 3>), dim3(p.tiles_m * p.tiles_n),
-                       dim3(512), 0, s, p);
-  else
-    hipLaunchKernelGGL((pingpong_mx_kernel<kSwzDefault, 2>), dim3(p.tiles_m * p.tiles_n),
-                       dim3(512), 0, s, p);
-  return hipGetLastError();
+  static const char* const e2m3[2] = {kernel_label("pingpong_mx_kernel", "e2m3", "rows"),
+                                      kernel_label("pingpong_mx_kernel", "e2m3", "blocks")};
+  static const char* const e3m2_[2] = {kernel_label("pingpong_mx_kernel", "e3m2", "rows"),
+                                       kernel_label("pingpong_mx_kernel", "e3m2", "blocks")};
+  return e3m2 ? launch_pingpong_mx<3>(p, s, e3m2_) : launch_pingpong_mx<2>(p, s, e2m3);
+}
+
+// One row's 16 scale bytes of a group, blocks 0..15 in order, to the block
+// layout's order: the even blocks, then the odd ones (block b at byte
+// 8 (b mod 2) + b / 2).  v_perm's selector bytes 0-3 pick the bytes of its
+// second operand, 4-7 those of its first.
+__device__ __forceinline__ u32x4 even_then_odd(u32x4 v) {
+  return u32x4{__builtin_amdgcn_perm(v[1], v[0], 0x06040200u),
+               __builtin_amdgcn_perm(v[3], v[2], 0x06040200u),
+               __builtin_amdgcn_perm(v[1], v[0], 0x07050301u),
+               __builtin_amdgcn_perm(v[3], v[2], 0x07050301u)};
 }
 
 // The scale bytes of 64 rows and one group of 16 K blocks go to one KiB of
 // `out`.  A workgroup of 1024 threads takes rows [64 i, 64 i + 64) and up to
 // 16 groups (blockIdx.y), one 16-byte unit per thread: it reads the units
-// row by row (contiguous in the rows layout), transposes them through LDS
-// (groups 1040 bytes apart, so that the 16 units of one row fall in
-// different banks) and writes them a group at a time (one contiguous KiB
-// each).  Rows past `rows` and blocks past K/32 are written as zero.
+// row by row (contiguous in the rows layout), reorders each (even_then_odd),
+// transposes them through LDS (groups 1040 bytes apart, so that the 16
+// units of one row fall in different banks) and writes them a group at a
+// time (one contiguous KiB each).  Rows past `rows` and blocks past K/32 are
+// written as zero.
 __global__ void __launch_bounds__(1024) sf_blocks_kernel(const uint32_t* sf, int64_t rows,
                                                          int64_t pitch_dw, int64_t groups,
                                                          u32x4* out) {
@@ -68,7 +89,7 @@ __global__ void __launch_bounds__(1024) sf_blocks_kernel(const uint32_t* sf, int
           if (d < n) v[d] = src[d];
       }
     }
-    *reinterpret_cast<u32x4*>(lds + g * kLdsRow + row * 16) = v;
+    *reinterpret_cast<u32x4*>(lds + g * kLdsRow + row * 16) = even_then_odd(v);
   }
   __syncthreads();
   if (u < 64 * ng) {

@@ -41,11 +41,14 @@ struct MxParams {
 //   SG_SF_ROWS:   e8m0 [rows][K/32]: byte r * (K/32) + b.
 //   SG_SF_BLOCKS: the bytes of 64 rows x 16 blocks together: 1 KiB for rows
 //                 [64i, 64i+64) and blocks [16g, 16g+16), row r's 16 bytes
-//                 at 16 (r mod 64); blocks (i, g) in the order i * G + g,
-//                 G = ceil(K/512) groups a row.  A 64-lane load of one
-//                 group's 16 bytes for 64 consecutive rows reads one
-//                 contiguous KiB (8 cache lines); in the rows layout the same
-//                 load touches 64 lines, one per row.
+//                 at 16 (r mod 64), the even blocks of the group first
+//                 (block b at 8 (b mod 2) + (b mod 16) / 2); blocks (i, g)
+//                 in the order i * G + g, G = ceil(K/512) groups a row.  A
+//                 load of one group's bytes for 32 or 64 consecutive rows
+//                 reads contiguous bytes (4 or 8 cache lines); in the rows
+//                 layout the same load touches a line per row.  The lane
+//                 halves of the scaled MFMA scale the even and the odd
+//                 blocks of a step: each finds its bytes in one 8-byte half.
 struct SfMap {
   uint32_t blocked, pitch, groups;
 
@@ -59,7 +62,11 @@ struct SfMap {
   }
   // The part that depends on the block index b (uniform in a wave).
   __device__ __forceinline__ uint32_t block(uint32_t b) const {
-    return blocked ? (b >> 4) * 1024u + (b & 15u) : b;
+    return blocked ? (b >> 4) * 1024u + in_unit(b) : b;
+  }
+  // Block layout: block b's byte inside its row's 16 bytes.
+  __device__ __forceinline__ static uint32_t in_unit(uint32_t b) {
+    return 8u * (b & 1u) + ((b & 15u) >> 1);
   }
   __device__ __forceinline__ const char* tile(const void* sf, int64_t row0) const {
     const char* p = static_cast<const char*>(sf);
@@ -81,7 +88,7 @@ __device__ __forceinline__ f32x16 mfma_scale_f8(const u32x4 (&a)[2],
   const i32x8 bv = {(int)b[0][0], (int)b[0][1], (int)b[0][2], (int)b[0][3],
                     (int)b[1][0], (int)b[1][1], (int)b[1][2], (int)b[1][3]};
   // Format codes 0/0: both operands OCP fp8 E4M3.  The op-select immediate
-  // picks byte 2*kk of the scale register (see the caller's pre-shift).
+  // picks byte 2*kk of the scale register (see MxTile::spread).
   if (kk == 0)
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0,
                                                            (int)sa, 0, (int)sb);
@@ -104,25 +111,40 @@ struct MxTile {
     uint32_t a[kFM], b[kFN];
   };
 
-  // One dword = the 4 scale bytes of K blocks [4kt, 4kt+4) of a row; the
-  // lane then shifts its own block (l/32) into the even byte positions so
-  // that op-select 2*kk addresses block 4kt + 2kk + l/32.
+  // Rows layout: one dword = the 4 scale bytes of K blocks [4kt, 4kt+4) of
+  // a row.  Block layout: the 2 bytes of blocks 4kt + h and 4kt + 2 + h
+  // (h = l/32: the lane's half of the row's 16 bytes).  `spread` then puts
+  // the lane's block of step kk at byte 2kk, where op-select 2kk reads it.
   __device__ __forceinline__ static void load_scales(
       Scales& s, __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb,
       const SfMap& sf, int kt, int lane, int wm, int wn, int m_valid,
       int n_valid) {
     const int lrow = lane & 31;
-    const uint32_t kb = sf.block(4u * (uint32_t)kt);
+    const uint32_t b = 4u * (uint32_t)kt + (uint32_t)(lane >> 5);
+    const uint32_t kb = sf.blocked ? sf.block(b) : sf.block(4u * (uint32_t)kt);
 #pragma unroll
     for (int fm = 0; fm < kFM; ++fm) {
       const int r = wm * kWM + fm * 32 + lrow;
-      s.a[fm] = buffer_load4(rsa, r < m_valid ? sf.row((uint32_t)r) + kb : kOutOfRange);
+      const uint32_t off = r < m_valid ? sf.row((uint32_t)r) + kb : kOutOfRange;
+      s.a[fm] = sf.blocked ? buffer_load2(rsa, off) : buffer_load4(rsa, off);
     }
 #pragma unroll
     for (int fn = 0; fn < kFN; ++fn) {
       const int r = wn * kWN + fn * 32 + lrow;
-      s.b[fn] = buffer_load4(rsb, r < n_valid ? sf.row((uint32_t)r) + kb : kOutOfRange);
+      const uint32_t off = r < n_valid ? sf.row((uint32_t)r) + kb : kOutOfRange;
+      s.b[fn] = sf.blocked ? buffer_load2(rsb, off) : buffer_load4(rsb, off);
     }
+  }
+
+  // The v_perm selector of `spread`: rows layout, bytes h and 2 + h of the
+  // dword to bytes 0 and 2; block layout, bytes 0 and 1 (selector 12 gives
+  // a zero byte).
+  __device__ __forceinline__ static uint32_t spread_sel(const SfMap& sf, int lane) {
+    const uint32_t h = (uint32_t)(lane >> 5);
+    return sf.blocked ? 0x0c010c00u : 0x0c000c00u | h | ((2u + h) << 16);
+  }
+  __device__ __forceinline__ static uint32_t spread(uint32_t v, uint32_t sel) {
+    return __builtin_amdgcn_perm(0u, v, sel);
   }
 
   struct Frags {
@@ -204,10 +226,11 @@ struct MxTile {
     load_scales(sc_next, rsa, rsb, sf, more ? kt + 1 : kt, lane, wm, wn, j.m_valid,
                 j.n_valid);
     uint32_t sa[kFM], sb[kFN];
+    const uint32_t sel = spread_sel(sf, lane);
 #pragma unroll
-    for (int fm = 0; fm < kFM; ++fm) sa[fm] = sc.a[fm] >> (8 * lhalf);
+    for (int fm = 0; fm < kFM; ++fm) sa[fm] = spread(sc.a[fm], sel);
 #pragma unroll
-    for (int fn = 0; fn < kFN; ++fn) sb[fn] = sc.b[fn] >> (8 * lhalf);
+    for (int fn = 0; fn < kFN; ++fn) sb[fn] = spread(sc.b[fn], sel);
     step<kVmem>(acc, f0, f1, cur, cur + kATileBytes, wm, wn, lrow, lhalf, 1, sa, sb, 0);
     wait_vmem();
     __syncthreads();

@@ -461,7 +461,13 @@ namespace sg {
 // tile of a group, for the next group.
 //
 // Fmt is the MFMA's operand format code: 0 e4m3, 2 e2m3, 3 e3m2, 4 e2m1.
-template <int Swz, int Fmt>
+// Blocks: the scales come in the 64-row block layout (SG_SF_BLOCKS), whose
+// 16 bytes for a row and a group of 16 blocks hold the 8 even blocks, then
+// the 8 odd ones.  Lane half h of the MFMA scales block 2s + h of step s, so
+// one lane-half swap per group (take) leaves each lane the 8 bytes it needs
+// and the MFMA gets the dword as it stands, the op-select naming the byte;
+// in the rows layout every phase swaps and shifts (pick_scales).
+template <int Swz, int Fmt, bool Blocks>
 struct PingPongMxTile {
   static_assert(Fmt == 0 || Fmt == 2 || Fmt == 3 || Fmt == 4, "operand format");
   static constexpr bool kFp4 = Fmt == 4, kFp6 = Fmt == 2 || Fmt == 3;
@@ -481,7 +487,9 @@ struct PingPongMxTile {
   // fp6, two for e2m1 with its two dwords a tile) of 64 scale rows: lanes
   // 0-31 take the rows of one 32-row fragment block, lanes 32-63 those of
   // the next (A blocks 0|1 and 2|3, B blocks 0|1), and a swap of the lane
-  // halves gives every lane both.
+  // halves gives every lane both (once per group in the block layout, where
+  // each lane keeps only its own half of the 16 bytes; per phase in the rows
+  // layout).
   static constexpr int kScaleTiles = kFp4 ? 2 : 4;
   static constexpr int kScaleLoads = 3;  // per wave and scale group
 
@@ -496,11 +504,21 @@ struct PingPongMxTile {
     uint32_t a[2][kPieces], b[2][kPieces];  // [kk][c or q]
   };
 
-  // The raw scale dwords of one scale group: [block pair], dword
-  // kScaleDw * (tile within the group) + d.
+  // The raw scale dwords of one scale group as loaded: [block pair], dword
+  // kScaleDw * (tile within the group) + d in the rows layout; in the block
+  // layout dwords 0-1 hold the even blocks, 2-3 the odd ones.
   struct Scales {
     u32x4 a[2], b;
   };
+  // The block layout's group once its lane halves are swapped: [fragment
+  // block], dword (tile within the group) / 2 for e4m3 and fp6, tile within
+  // the group for e2m1, of the lane's half (even blocks in lanes 0-31, odd
+  // ones in lanes 32-63).
+  struct BlockScales {
+    u32x2 a[kFM], b[kFN];
+  };
+  // The group the compute phases use.
+  using Cur = typename std::conditional<Blocks, BlockScales, Scales>::type;
 
   // `ua`, `ub`: the block position of the rows that mxfp6_lds_offset leaves
   // unshifted (fp6 only).
@@ -543,52 +561,104 @@ struct PingPongMxTile {
       for (int c = 0; c < kPieces; ++c) f.b[fn][c] = read_piece(bt, o.b[kk][c] + fn * 4096);
   }
 
-  // Scale load q (0 .. 2) of the group starting at byte `soff` of every
-  // scale row: A block pair q, or the B block pair.  Compiler-tracked
-  // buffer loads: the first use of the registers waits for them.
+  // Scale load q (0 .. 2) of the group at byte offset `soff` (from a row's
+  // first scale byte): A block pair q, or the B block pair.  Rows layout:
+  // the offset goes into the range-checked VGPR offset, as a group's last 16
+  // bytes may run past the end of the operand's last row.  Block layout: a
+  // group's 16 bytes lie inside the array for every row the descriptor
+  // covers, so the offset travels in an SGPR.  Compiler-tracked buffer
+  // loads: the first use of the registers waits for them.
   __device__ __forceinline__ static void load_scale(Scales& s, int q,
                                                     __amdgpu_buffer_rsrc_t rsa,
                                                     __amdgpu_buffer_rsrc_t rsb,
                                                     const uint32_t (&va)[2], uint32_t vb,
                                                     uint32_t soff) {
-    if (q < 2)
-      s.a[q] = buffer_load16_so(rsa, va[q], soff);
-    else
-      s.b = buffer_load16_so(rsb, vb, soff);
+    if constexpr (Blocks) {
+      if (q < 2)
+        s.a[q] = buffer_load16_so(rsa, va[q], soff);
+      else
+        s.b = buffer_load16_so(rsb, vb, soff);
+    } else {
+      if (q < 2)
+        s.a[q] = buffer_load16(rsa, va[q] + soff);
+      else
+        s.b = buffer_load16(rsb, vb + soff);
+    }
   }
 
   // cur = nxt as an ordered step: each register set passes through an
   // empty statement tied to its own registers, which no LDS read or load
   // may cross, so the copy (and any wait the compiler puts before its
-  // first use of `nxt`) comes where it is written.
-  __device__ __forceinline__ static void take(Scales& cur, Scales& nxt) {
-    asm volatile("" : "=v"(cur.a[0]) : "0"(nxt.a[0]) : "memory");
-    asm volatile("" : "=v"(cur.a[1]) : "0"(nxt.a[1]) : "memory");
-    asm volatile("" : "=v"(cur.b) : "0"(nxt.b) : "memory");
+  // first use of `nxt`) comes where it is written.  Block layout: lane l
+  // holds a row of block 2p (l < 32) or 2p + 1 (l >= 32), even blocks in
+  // dwords 0-1 and odd ones in 2-3; swapping the odd dwords of lanes 0-31
+  // with the even dwords of lanes 32-63 leaves in every lane the half that
+  // lane half scales, of block 2p in one register and of 2p + 1 in the other.
+  __device__ __forceinline__ static void take(Cur& cur, Scales& nxt) {
+    asm volatile("" : "+v"(nxt.a[0]) : : "memory");
+    asm volatile("" : "+v"(nxt.a[1]) : : "memory");
+    asm volatile("" : "+v"(nxt.b) : : "memory");
+    if constexpr (Blocks) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const auto r = __builtin_amdgcn_permlane32_swap(nxt.a[p][k], nxt.a[p][k + 2], false,
+                                                          false);
+          cur.a[2 * p][k] = r[0];
+          cur.a[2 * p + 1][k] = r[1];
+        }
+        const auto r = __builtin_amdgcn_permlane32_swap(nxt.b[k], nxt.b[k + 2], false, false);
+        cur.b[0][k] = r[0];
+        cur.b[1][k] = r[1];
+      }
+    } else {
+      cur = nxt;
+    }
+    settle(cur);
   }
 
   // A use of the scale registers at this point of the program.
   __device__ __forceinline__ static void settle(Scales& s) {
-    asm volatile("" : "+v"(s.a[0]));
-    asm volatile("" : "+v"(s.a[1]));
-    asm volatile("" : "+v"(s.b));
+    asm volatile("" : "+v"(s.a[0]) : : "memory");
+    asm volatile("" : "+v"(s.a[1]) : : "memory");
+    asm volatile("" : "+v"(s.b) : : "memory");
+  }
+  __device__ __forceinline__ static void settle(BlockScales& s) {
+#pragma unroll
+    for (int i = 0; i < kFM; ++i) asm volatile("" : "+v"(s.a[i]) : : "memory");
+#pragma unroll
+    for (int i = 0; i < kFN; ++i) asm volatile("" : "+v"(s.b[i]) : : "memory");
   }
 
-  // Scale dword w of the wave's rows.  A lane-half swap turns a pair's
-  // register (block 2p in lanes 0-31, 2p+1 in lanes 32-63) into one per
-  // block holding it in all lanes; then the lane's block (lane half) is
-  // shifted into the even bytes so that op-select 2c picks block 2c + h.
+  // The scale registers of compute phase `ph` (0, 1) of tile `sub` of the
+  // group.  Rows layout: dword w = kScaleDw sub (+ ph for e2m1) of the
+  // wave's rows; a lane-half swap turns a pair's register (block 2p in
+  // lanes 0-31, 2p+1 in lanes 32-63) into one per block holding it in all
+  // lanes; then the lane's block (lane half) is shifted into the even bytes
+  // so that op-select 2c picks block 2c + h.  Block layout: the loaded
+  // dword (see sel0).
   __device__ __forceinline__ static void pick_scales(uint32_t (&sa)[kFM], uint32_t (&sb)[kFN],
-                                                     const Scales& s, int w, int lhalf) {
+                                                     const Cur& s, int sub, int ph,
+                                                     int lhalf) {
+    if constexpr (Blocks) {
+      const int w = kFp4 ? sub : sub >> 1;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const auto r = __builtin_amdgcn_permlane32_swap(s.a[p][w], s.a[p][w], false, false);
-      sa[2 * p] = r[0] >> (8 * lhalf);
-      sa[2 * p + 1] = r[1] >> (8 * lhalf);
+      for (int fm = 0; fm < kFM; ++fm) sa[fm] = s.a[fm][w];
+#pragma unroll
+      for (int fn = 0; fn < kFN; ++fn) sb[fn] = s.b[fn][w];
+    } else {
+      const int w = kScaleDw * sub + (kFp4 ? ph : 0);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const auto r = __builtin_amdgcn_permlane32_swap(s.a[p][w], s.a[p][w], false, false);
+        sa[2 * p] = r[0] >> (8 * lhalf);
+        sa[2 * p + 1] = r[1] >> (8 * lhalf);
+      }
+      const auto r = __builtin_amdgcn_permlane32_swap(s.b[w], s.b[w], false, false);
+      sb[0] = r[0] >> (8 * lhalf);
+      sb[1] = r[1] >> (8 * lhalf);
     }
-    const auto r = __builtin_amdgcn_permlane32_swap(s.b[w], s.b[w], false, false);
-    sb[0] = r[0] >> (8 * lhalf);
-    sb[1] = r[1] >> (8 * lhalf);
   }
 
   // One scaled MFMA on 8-dword operands.
@@ -615,14 +685,25 @@ struct PingPongMxTile {
     }
   }
 
-  // kMfmas MFMAs of step kk; N loads go out spread between them, the first
-  // after the first MFMA, at most one after each MFMA.  `prep(q)` (the m0
-  // write of a direct-to-LDS load, see set_m0) runs before the MFMA that
-  // load q follows, `go(q)` issues the load after it.
+  // The op-select (scale byte) of the MFMAs of compute phase `ph` of tile
+  // `sub` of the group: rows layout, byte 2 ph (e4m3, fp6: the phase's
+  // step) or byte 2c (e2m1: chunk c, added in compute) of the shifted
+  // dword; block layout, where block 2s + h of the phase's step s sits in
+  // the lane's half: byte 2 (sub mod 2) + ph (e4m3, fp6) or 2 ph + c (e2m1).
+  __device__ __forceinline__ static constexpr int sel0(int sub, int ph) {
+    return Blocks ? (kFp4 ? 2 * ph : 2 * (sub & 1) + ph) : (kFp4 ? 0 : 2 * ph);
+  }
+  static constexpr int kSelPerChunk = Blocks ? 1 : 2;  // e2m1
+
+  // kMfmas MFMAs of one compute phase, op-select sel0 (+ the chunk's share
+  // for e2m1); N loads go out spread between them, the first after the
+  // first MFMA, at most one after each MFMA.  `prep(q)` (the m0 write of a
+  // direct-to-LDS load, see set_m0) runs before the MFMA that load q
+  // follows, `go(q)` issues the load after it.
   template <int N, class Prep, class Go>
   __device__ __forceinline__ static void compute(f32x16 (&acc)[kFM][kFN], const Frags& f,
                                                  const uint32_t (&sa)[kFM],
-                                                 const uint32_t (&sb)[kFN], int kk,
+                                                 const uint32_t (&sb)[kFN], int sel0,
                                                  const Prep& prep, const Go& go) {
     static_assert(N <= kMfmas, "one load per MFMA");
 #pragma unroll
@@ -634,11 +715,15 @@ struct PingPongMxTile {
       for (int q = 0; q < N; ++q)
         if (q * kMfmas / N == m) prep(q);
       __builtin_amdgcn_sched_barrier(0);
-      // op-select: block pair 2kk (e4m3, fp6) or 2c (e2m1) of the scale dword
-      if ((kFp4 ? c : kk) == 0)
+      const int sel = sel0 + (kFp4 ? kSelPerChunk * c : 0);
+      if (sel == 0)
         acc[fm][fn] = mfma<0>(av, bv, acc[fm][fn], sa[fm], sb[fn]);
-      else
+      else if (sel == 1)
+        acc[fm][fn] = mfma<1>(av, bv, acc[fm][fn], sa[fm], sb[fn]);
+      else if (sel == 2)
         acc[fm][fn] = mfma<2>(av, bv, acc[fm][fn], sa[fm], sb[fn]);
+      else
+        acc[fm][fn] = mfma<3>(av, bv, acc[fm][fn], sa[fm], sb[fn]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < N; ++q)
@@ -654,18 +739,13 @@ struct PingPongMxTile {
   // then the barrier.
   template <int V, bool Lgkm>
   __device__ __forceinline__ static void sync() {
-    static_assert(V == -1 || V == 4 || V == 7 || V == 8 || V == 11, "vmcnt immediate");
-    if constexpr (V == 4)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else if constexpr (V == 7)
-      asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
-    else if constexpr (V == 8)
-      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
-    else if constexpr (V == 11)
-      asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)" ::: "memory");
+    static_assert(V >= -1 && V < 64, "vmcnt immediate");
+    if constexpr (V >= 0 && Lgkm)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(V) : "memory");
+    else if constexpr (V >= 0)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(V) : "memory");
     else if constexpr (Lgkm)
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    static_assert(V < 8 ? (V < 0 || !Lgkm) : Lgkm, "waits as used below");
     barrier();
   }
 
@@ -744,7 +824,7 @@ struct PingPongMxTile {
     }
     // Scale rows of the lane: A 128g + 32(2p + h) + lrow for pair p, B
     // 64 w4 + 32 h + lrow (64 consecutive rows per load: one KiB in the
-    // blocks layout).
+    // block layout).
     uint32_t sva[2], svb;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -772,16 +852,22 @@ struct PingPongMxTile {
                  (uint32_t)t * (uint32_t)kTileRowBytes);
     };
     // Scales of the group starting at tile t (its 16 bytes start at block
-    // 4 kScaleDw t, a multiple of 16).
+    // 4 kScaleDw t, a multiple of 16).  The group after the last (t >= T,
+    // loaded but never used) re-reads the last one, so that no offset
+    // leaves the array.
+    const int t_last = T > 0 ? (T - 1) / kScaleTiles * kScaleTiles : 0;
     auto ld_s = [&](Scales& s, int t, int q) {
-      load_scale(s, q, rsa, rsb, sva, svb, sf.block((uint32_t)(t * 4 * kScaleDw)));
+      load_scale(s, q, rsa, rsb, sva, svb,
+                 sf.block((uint32_t)(min(t, t_last) * 4 * kScaleDw)));
     };
 
     // Tiles 0 and 1 (B, A, and the scales of the first group: the order the
-    // mainloop keeps).  Scale dwords past K are read out of range (zero) or
-    // from the next row; no MFMA uses them.  `nxt` receives a group's
+    // mainloop keeps).  In the rows layout, scale bytes of a group's blocks
+    // past K/32 come from the next row or, past the operand, read as zero;
+    // no MFMA uses them.  `nxt` receives a group's
     // scales; the group's first memory phase takes them over into `cur`.
-    Scales cur, nxt;
+    Cur cur;
+    Scales nxt;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ld_b(0, i);
 #pragma unroll
@@ -792,7 +878,7 @@ struct PingPongMxTile {
     for (int i = 0; i < 4; ++i) ld_b(1, i);
     // Tile 0 has landed (B of tile 1 and the scales may be in flight); A of
     // tile 1 comes with the first memory phase.
-    asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(4 + kScaleLoads) : "memory");
     barrier();
 
     const Offsets o = offsets(g, w4, lrow, lhalf, ua, ub);
@@ -830,22 +916,22 @@ struct PingPongMxTile {
         // phase's reads are issued, while the other group computes.
         take(cur, nxt);
       }
-      pick_scales(sa, sb, cur, kScaleDw * Sub, lhalf);
+      pick_scales(sa, sb, cur, Sub, 0, lhalf);
 #pragma unroll
       for (int i = 0; i < 4; ++i) ld_a(t + 1, i);
       sync<-1, true>();
-      compute<0>(acc, f, sa, sb, 0, [&](int) {}, [&](int) {});
+      compute<0>(acc, f, sa, sb, sel0(Sub, 0), [&](int) {}, [&](int) {});
       sync<-1, false>();
       read(f, at, bt, o, 1);
-      if constexpr (kFp4) pick_scales(sa, sb, cur, kScaleDw * Sub + 1, lhalf);
+      if constexpr (kFp4 && !Blocks) pick_scales(sa, sb, cur, Sub, 1, lhalf);
 #pragma unroll
       for (int i = 0; i < 4; ++i) ld_b(t + 2, i);
       sync<kWaitM, true>();
       if constexpr (Sub == 0)
-        compute<kScaleLoads>(acc, f, sa, sb, 1, [&](int) {},
+        compute<kScaleLoads>(acc, f, sa, sb, sel0(Sub, 1), [&](int) {},
                              [&](int q) { ld_s(nxt, t + kScaleTiles, q); });
       else
-        compute<0>(acc, f, sa, sb, 1, [&](int) {}, [&](int) {});
+        compute<0>(acc, f, sa, sb, sel0(Sub, 1), [&](int) {}, [&](int) {});
       sync<kWaitC, false>();
     };
     using I0 = std::integral_constant<int, 0>;
@@ -936,9 +1022,10 @@ struct PingPongMxTile {
   }
 };
 
-template <int Swz, int Fmt>
+// Blocks: p.sf_layout is SG_SF_BLOCKS (else SG_SF_ROWS).
+template <int Swz, int Fmt, bool Blocks>
 __global__ void __launch_bounds__(512, 1) pingpong_mx_kernel(const MxParams p) {
-  using Tile = PingPongMxTile<Swz, Fmt>;
+  using Tile = PingPongMxTile<Swz, Fmt, Blocks>;
   __shared__ __attribute__((aligned(4096))) char smem[Tile::kLdsBytes];
   const ClockStamp cs = clock_begin(p.clk);
   const int total = p.tiles_m * p.tiles_n;

@@ -220,12 +220,15 @@ int64_t mx_scales_blocks_bytes(int64_t rows, int64_t K);
  * the layout of "06 Blackwell Tensor Core - tcgen05 MMA", section
  * "Block-Scaled MMA": SFA(M, SFK), SFB(N, SFK)) into `out`, SG_SF_BLOCKS:
  * row r's scale byte b (32-element block b of K) goes to byte
- *   ((r / 64) * G + b / 16) * 1024 + (r % 64) * 16 + b % 16,  G = ceil(K/512),
- * so that the 16 bytes of one group of 16 blocks for 64 consecutive rows are
- * one contiguous KiB.  Bytes for rows past `rows` (up to the next multiple
- * of 64) and blocks past K/32 are written as zero.  The block-scaled GEMMs
- * read a row's group in one 16-byte load per lane; from SG_SF_BLOCKS a
- * wave's load covers 8 cache lines instead of the 64 (one per row) of
+ *   ((r / 64) * G + b / 16) * 1024 + (r % 64) * 16 + 8 * (b % 2) + (b % 16) / 2,
+ * G = ceil(K/512): the 16 bytes of one group of 16 blocks for 64 consecutive
+ * rows are one contiguous KiB, and a row's 16 bytes hold the group's 8 even
+ * blocks, then its 8 odd ones.  Bytes for rows past `rows` (up to the next
+ * multiple of 64) and blocks past K/32 are written as zero.  The scaled
+ * MFMA's two lane halves scale the even and the odd blocks of a 64-wide K
+ * step, so the block-scaled GEMMs load a row's group as one 8-byte half per
+ * lane, with no rearranging after the load; from SG_SF_BLOCKS a wave's load
+ * of 32 rows covers 4 cache lines instead of the 32 (one per row) of
  * SG_SF_ROWS.  SF: DEVICE memory, 4-byte aligned; out: DEVICE memory of
  * mx_scales_blocks_bytes(rows, K) bytes, 16-byte aligned (caller-owned).
  * Asynchronous on `stream` (a hipStream_t, NULL for the default stream).

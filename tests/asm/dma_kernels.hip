@@ -7,7 +7,10 @@ namespace sg {
 template __global__ void pingpong16_gemm_kernel<true, 16, false, false, true>(const DenseParams);
 template __global__ void pingpong16_gemm_kernel<false, 16, false, true, true>(const DenseParams);
 template __global__ void pingpong16_grouped_kernel<true, 16>(const GroupedParams);
-template __global__ void pingpong_mx_kernel<16, 0>(const MxParams);
-template __global__ void pingpong_mx_kernel<16, 2>(const MxParams);
-template __global__ void pingpong_mx_kernel<16, 4>(const MxParams);
+template __global__ void pingpong_mx_kernel<16, 0, false>(const MxParams);
+template __global__ void pingpong_mx_kernel<16, 0, true>(const MxParams);
+template __global__ void pingpong_mx_kernel<16, 2, false>(const MxParams);
+template __global__ void pingpong_mx_kernel<16, 2, true>(const MxParams);
+template __global__ void pingpong_mx_kernel<16, 4, false>(const MxParams);
+template __global__ void pingpong_mx_kernel<16, 4, true>(const MxParams);
 }  // namespace sg

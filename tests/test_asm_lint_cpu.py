@@ -97,7 +97,7 @@ def test_split_m0_kernels_keep_their_m0(tmp_path):
     assert r.returncode == 0, r.stderr[-3000:]
     with open(out) as f:
         found = dict(kernels(f.read()))
-    assert len(found) == 6, sorted(found)
+    assert len(found) == 9, sorted(found)
     for name, body in found.items():
         bad, n = lint(body)
         assert n > 0, f"{name}: no direct-to-LDS loads found"

@@ -549,13 +549,15 @@ def run_mx_blocks(case: si.MXCase, dev, d_dtype="bf16"):
 def blocks_reference(sf: np.ndarray) -> np.ndarray:
     """The SG_SF_BLOCKS image of e8m0 scales [rows][K/32], written out from
     its definition: byte b of row r at ((r // 64) * G + b // 16) * 1024 +
-    (r % 64) * 16 + b % 16, G = ceil(K/512), zeros elsewhere."""
+    (r % 64) * 16 + 8 * (b % 2) + (b % 16) // 2, G = ceil(K/512), zeros
+    elsewhere."""
     rows, nb = sf.shape
     G = (nb + 15) // 16
     out = np.zeros(((rows + 63) // 64) * G * 1024, np.uint8)
     for r in range(rows):
         for b in range(nb):
-            out[((r // 64) * G + b // 16) * 1024 + (r % 64) * 16 + b % 16] = sf[r, b]
+            out[((r // 64) * G + b // 16) * 1024 + (r % 64) * 16 + 8 * (b % 2)
+                + (b % 16) // 2] = sf[r, b]
     return out
 
 
