@@ -242,8 +242,10 @@ int mx_scales_to_blocks(const void* SF, int64_t rows, int64_t K, void* out, void
  * mx_gemm_blocks_run -- the block-scaled GEMM of mx_gemm_run (fmt SG_E4M3),
  * mxfp4_gemm_run (SG_E2M1) or mxfp6_gemm_run (SG_E2M3, SG_E3M2), with SFA
  * and SFB in the SG_SF_BLOCKS layout (mx_scales_to_blocks), 16-byte aligned.
- * Every other argument, requirement and result is that entry point's; the
- * D it computes is bit-identical.  Errors: theirs, and SG_ERR_DTYPE for
+ * The layout's padding (rows past M or N in the last 64 rows, blocks past
+ * K/32 in the last group) is never used and may hold anything.  Every other
+ * argument, requirement and result is that entry point's; the D it computes
+ * is bit-identical.  Errors: theirs, and SG_ERR_DTYPE for
  * another fmt.
  */
 int mx_gemm_blocks_run(int fmt, int64_t M, int64_t N, int64_t K, const void* A,

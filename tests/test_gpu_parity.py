@@ -594,6 +594,39 @@ def test_mx_blocks_scales_give_the_same_d(dev, fmt, M, N, K):
         assert torch.equal(run_mx_blocks(case, dev, dt), ref), (fmt, dt)
 
 
+def blocks_padding_mask(rows: int, K: int) -> np.ndarray:
+    """The bytes of an SG_SF_BLOCKS array that hold no scale: rows past
+    `rows` in the last 64-row block and blocks past K/32 in the last group."""
+    used = blocks_reference(np.ones((rows, K // 32), np.uint8))
+    return used == 0
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [
+    ("e4m3", 300, 264, 640), ("e4m3", 100, 72, 384), ("e2m1", 300, 264, 768),
+    ("e2m3", 257, 40, 640), ("e3m2", 260, 200, 384),
+])
+def test_mx_blocks_padding_is_never_used(dev, fmt, M, N, K):
+    # The block layout pads rows to a multiple of 64 and blocks to a multiple
+    # of 16; a caller that builds the array itself may leave anything there.
+    # With every padding byte 255 (NaN scales) D stays bit-identical to the
+    # zero-padded array's, on 128- and 256-wide tiles.
+    case = si.mx_case(M, N, K, 41, fmt=fmt)
+    say(f"mx blocks padding {fmt} {M}x{N}x{K}")
+    sfa = sg.mx_scales_blocks(case.SFA.to(dev))
+    sfb = sg.mx_scales_blocks(case.SFB.to(dev))
+    A, B = case.A.to(dev), case.B.to(dev)
+    ref = sg.mx_gemm_blocks(A, sfa, B, sfb, fmt=case.fmt, out_dtype=torch.float32)
+    pa = torch.from_numpy(blocks_padding_mask(M, K)).to(dev)
+    pb = torch.from_numpy(blocks_padding_mask(N, K)).to(dev)
+    assert pa.any() and pb.any()
+    sfa[pa] = 255
+    sfb[pb] = 255
+    got = sg.mx_gemm_blocks(A, sfa, B, sfb, fmt=case.fmt, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(ref).all()
+    assert torch.equal(got, ref), fmt
+
+
 def run_mx(case: si.MXCase, dev, d_dtype="bf16"):
     d = sg.mx_gemm(case.A.to(dev), case.SFA.to(dev), case.B.to(dev), case.SFB.to(dev),
                    out_dtype=DT[d_dtype])
