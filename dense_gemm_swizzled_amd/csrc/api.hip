@@ -74,10 +74,21 @@ sg::TileShape pick_tile(int64_t tiles256) {
 
 // Dense GEMM: 256x256 tiles when they fill the CUs, else 128x128 tiles when
 // they fill half of them, else 64x64 tiles (small problems: 1024^3 has 64
-// tiles of 128 but 256 of 64).
-sg::TileShape pick_dense_tile(int64_t M, int64_t N) {
+// tiles of 128 but 256 of 64).  Between those, when the 256x256 tiles would
+// run on the ping-pong (K-major operands, or K a multiple of 64 with two or
+// more K tiles) and the 128x128 tiles would need three or more rounds of the
+// CUs, one partial round of the ping-pong is faster (bf16 on MI355X, TFLOP/s
+// 256 vs 128 tiles: 3072^3 1056 vs 694, 3584^3 1337 vs 911, 3072x3072x1024
+// 846 vs 585), though not against one or two rounds of 128x128 tiles
+// (2560^3 753 vs 847, 2048x4096x4096 934 vs 1041).
+// `fits256`: 256-row panels stay within 32-bit buffer offsets.
+sg::TileShape pick_dense_tile(int64_t M, int64_t N, int64_t K, bool a_mn, bool b_mn,
+                              bool fits256) {
   if (cdiv(M, 256) * cdiv(N, 256) >= kCUs) return sg::kTile256;
-  if (cdiv(M, 128) * cdiv(N, 128) >= kCUs / 2) return sg::kTile128;
+  const int64_t tiles128 = cdiv(M, 128) * cdiv(N, 128);
+  const bool pingpong = (!a_mn && !b_mn) || (K % 64 == 0 && K >= 128);
+  if (pingpong && fits256 && cdiv(tiles128, kCUs) >= 3) return sg::kTile256;
+  if (tiles128 >= kCUs / 2) return sg::kTile128;
   return sg::kTile64;
 }
 
@@ -144,9 +155,13 @@ int dense_run(const char* who, DenseMode mode, int swz, int64_t M, int64_t N, in
   if (K > 0 && K % 8 && (a_major == SG_K_MAJOR || b_major == SG_K_MAJOR))
     return fail(SG_ERR_SHAPE, "%s: K=%lld is not a multiple of 8 with a K-major operand",
                 who, (long long)K);
+  const bool fits256 = panel_extent(a_major, M, K, lda, 256, eb) < kMaxExtent &&
+                       panel_extent(b_major, N, K, ldb, 256, eb) < kMaxExtent;
   const sg::TileShape tile = mode == kAblation256 || mode == kAblationIO ? sg::kTile256
                             : mode == kAblation128 ? sg::kTile128
-                                                   : pick_dense_tile(M, N);
+                                                   : pick_dense_tile(M, N, K, a_major == SG_MN_MAJOR,
+                                                                     b_major == SG_MN_MAJOR,
+                                                                     fits256);
   const int64_t T = tile_rows(tile);
   if (panel_extent(a_major, M, K, lda, T, eb) >= kMaxExtent ||
       panel_extent(b_major, N, K, ldb, T, eb) >= kMaxExtent ||

@@ -101,10 +101,24 @@ def test_pingpong16_f16_mn_major_exact(dev, a_major, b_major):
 
 @pytest.mark.parametrize("a_major,b_major", [("k", "k"), ("mn", "k"), ("k", "mn"), ("mn", "mn")])
 def test_two_stage_128_f16_exact(dev, a_major, b_major):
-    # 24 x 23 tiles of 128 (more than one round of CUs): the two-stage kernel.
-    say(f"dense_gemm_kernel<128,f16,{a_major},{b_major}> 3000x2904x1000")
-    _exact(dev, 3000, 2904, 1000, "f16", a_major, b_major, 221,
+    # 17 x 16 tiles of 128 (two rounds of the CUs): the two-stage kernel.
+    say(f"dense_gemm_kernel<128,f16,{a_major},{b_major}> 2104x2000x1000")
+    _exact(dev, 2104, 2000, 1000, "f16", a_major, b_major, 221,
            f"dense_gemm_kernel<128,f16,{a_major},{b_major}")
+
+
+@pytest.mark.parametrize("a_major,b_major,K,kern", [
+    ("k", "k", 1000, "pingpong16_gemm_kernel<f16,k,k"),
+    ("mn", "k", 1024, "pingpong16_gemm_kernel<f16,mn,k"),
+    ("k", "mn", 1024, "pingpong16_gemm_kernel<f16,k,mn"),
+    ("mn", "mn", 1000, "dense_gemm_kernel<128,f16,mn,mn"),
+])
+def test_partial_round_of_256_tiles_f16_exact(dev, a_major, b_major, K, kern):
+    # 12 x 12 tiles of 256 (fewer than the CUs) but 24 x 23 of 128 (three
+    # rounds): the ping-pong when its loaders take the operands (K-major, or
+    # K a multiple of 64), else the two-stage 128x128 kernel.
+    say(f"{kern}> 3000x2904x{K}")
+    _exact(dev, 3000, 2904, K, "f16", a_major, b_major, 241, kern)
 
 
 @pytest.mark.parametrize("a_major,b_major", [("k", "k"), ("mn", "k"), ("k", "mn"), ("mn", "mn")])

@@ -153,9 +153,9 @@ def test_dense_deep_ring_integer_exact(dev, tiles):
     # Integer values in [-4, 4] over K = 1000 (16 K tiles, the last partial):
     # every partial sum is exact in fp32, so the result must be bit-exact.
     # The K tiles go round the 64x64 kernel's eight stages twice and the
-    # 128x128 kernel's five stages three times; with more 128x128 tiles than
-    # one round of CUs ("128x2": 552 tiles) the two-stage kernel runs.
-    M, N = {"64": (520, 392), "128": (1800, 1800), "128x2": (3000, 2900)}[tiles]
+    # 128x128 kernel's five stages three times; with two rounds of 128x128
+    # tiles ("128x2": 272 tiles) the two-stage kernel runs.
+    M, N = {"64": (520, 392), "128": (1800, 1800), "128x2": (2100, 2000)}[tiles]
     K = 1000
     a = si.integer_valued((M, K), 95)
     b = si.integer_valued((N, K), 96)
