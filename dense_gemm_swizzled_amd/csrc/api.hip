@@ -68,8 +68,18 @@ int64_t panel_extent(int major, int64_t rows, int64_t K, int64_t ld, int64_t til
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-sg::TileShape pick_tile(int64_t tiles256) {
-  return tiles256 >= kCUs ? sg::kTile256 : sg::kTile128;
+// Grouped GEMM and MXFP8: 256x256 tiles when they fill the CUs, or when
+// 128x128 tiles would need two or more rounds of the CUs and 256-row panels
+// stay within 32-bit buffer offsets (`fits256`); else 128x128 tiles.  Their
+// 128x128 kernels trail the 256x256 ping-pongs further than the dense one
+// does (MI355X, TFLOP/s 256 vs 128 tiles: MXFP8 2560^3 1176 vs 1014, 3072^3
+// 1738 vs 803, 3840^3 2263 vs 1316; grouped bf16 4 x 512 x 4096 x 4096 1055
+// vs 1015, 4 x 768 x 4096 x 4096 1345 vs 913), but not one round of them
+// (MXFP8 2048^3 755 vs 796).
+sg::TileShape pick_tile(int64_t tiles256, int64_t tiles128, bool fits256) {
+  if (tiles256 >= kCUs) return sg::kTile256;
+  if (fits256 && cdiv(tiles128, kCUs) >= 2) return sg::kTile256;
+  return sg::kTile128;
 }
 
 // Dense GEMM: 256x256 tiles when they fill the CUs, else 128x128 tiles when
@@ -306,10 +316,14 @@ int grouped_gemm_run(int G, const int64_t* m_offsets, int64_t N, int64_t K,
     return fail(SG_ERR_ALIGN, "grouped_gemm_run: every pointer must be 16-byte aligned");
   if ((K * eb) % 16 || (N * db) % 16)
     return fail(SG_ERR_ALIGN, "grouped_gemm_run: row pitches must be multiples of 16 bytes");
-  int64_t tiles256 = 0;
-  for (int g = 0; g < G; ++g) tiles256 += cdiv(m_offsets[g + 1] - m_offsets[g], 256);
+  int64_t tiles256 = 0, tiles128 = 0;
+  for (int g = 0; g < G; ++g) {
+    tiles256 += cdiv(m_offsets[g + 1] - m_offsets[g], 256);
+    tiles128 += cdiv(m_offsets[g + 1] - m_offsets[g], 128);
+  }
   tiles256 *= cdiv(N, 256);
-  const sg::TileShape tile = pick_tile(tiles256);
+  tiles128 *= cdiv(N, 128);
+  const sg::TileShape tile = pick_tile(tiles256, tiles128, 256 * K * eb < kMaxExtent);
   const int64_t T = tile == sg::kTile256 ? 256 : 128;
   if (T * K * eb >= kMaxExtent)
     return fail(SG_ERR_SHAPE, "grouped_gemm_run: an operand panel spans 2^31 bytes or more");
@@ -375,9 +389,13 @@ int mx_run(const char* who, int fmt, int sf_layout, int64_t M, int64_t N, int64_
   if ((N * db) % 16)
     return fail(SG_ERR_ALIGN, "%s: D row pitch must be a multiple of 16 bytes", who);
   // MXFP8 takes 128x128 tiles for small problems; the others 256x256.
-  const sg::TileShape tile = fmt == SG_E4M3 ? pick_tile(cdiv(M, 256) * cdiv(N, 256)) : sg::kTile256;
-  const int64_t T = tile == sg::kTile256 ? 256 : 128;
   const int64_t row_bytes = fp4 ? K / 2 : fp6 ? K / 4 * 3 : K;
+  const bool fits256 = 256 * row_bytes < kMaxExtent &&
+                       (sf_layout != SG_SF_BLOCKS || 4 * cdiv(K, 512) * 1024 < kMaxExtent);
+  const sg::TileShape tile =
+      fmt == SG_E4M3 ? pick_tile(cdiv(M, 256) * cdiv(N, 256), cdiv(M, 128) * cdiv(N, 128), fits256)
+                     : sg::kTile256;
+  const int64_t T = tile == sg::kTile256 ? 256 : 128;
   // a tile's panel (plus, for fp6, the 8 bytes its shifted rows may read beyond it)
   if (T * row_bytes + (fp6 ? 8 : 0) >= kMaxExtent)
     return fail(SG_ERR_SHAPE, "%s: an operand panel spans 2^31 bytes or more", who);

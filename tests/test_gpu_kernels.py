@@ -174,7 +174,7 @@ def test_grouped_kernels_dtypes(dev, ab, path):
 
 
 @pytest.mark.parametrize("G,N,kern", [(256, 1024, "pingpong16_grouped_kernel<bf16"),
-                                      (256, 136, "grouped_gemm_kernel<128,bf16"),
+                                      (256, 120, "grouped_gemm_kernel<128,bf16"),
                                       (200, 520, "pingpong16_grouped_kernel<bf16")])
 def test_grouped_more_than_128_groups(dev, G, N, kern):
     # Up to SG_MAX_GROUPS = 256 groups, a quarter of them empty, sizes off
@@ -184,7 +184,9 @@ def test_grouped_more_than_128_groups(dev, G, N, kern):
     choices = [0, 0, 1, 5, 37, 100, 128, 200] + ([300] if "pingpong" in kern else [])
     sizes = [int(x) for x in rng.choice(choices, size=G)]
     tiles256 = sum((m + 255) // 256 for m in sizes) * ((N + 255) // 256)
-    assert (tiles256 >= 256) == ("pingpong" in kern), tiles256   # the planner's rule
+    tiles128 = sum((m + 127) // 128 for m in sizes) * ((N + 127) // 128)
+    # the planner's rule: 256x256 tiles fill the CUs, or 128x128 ones need two rounds
+    assert (tiles256 >= 256 or tiles128 > 256) == ("pingpong" in kern), (tiles256, tiles128)
     case = si.grouped_case(sizes, N, 128, 271, d_dtype="bf16")
     say(f"{kern}> G={G} N={N} K=128 sum M={case.m_offsets[-1]}")
     d = sg.grouped_gemm(case.A.to(dev), case.B.to(dev), case.m_offsets,
@@ -193,6 +195,21 @@ def test_grouped_more_than_128_groups(dev, G, N, kern):
     assert sg.gemm_last_kernel().startswith(kern), sg.gemm_last_kernel()
     ref, bound = oracle.grouped_gemm(case.m_offsets, case.N, case.K, case.A, case.B, "bf16")
     check_close(_np(d), ref, bound, "bf16", f"G={G}")
+
+
+def test_grouped_partial_round_of_256_tiles(dev):
+    # 10 x 8 tiles of 256 (fewer than the CUs) but 19 x 16 of 128 (two
+    # rounds): the grouped ping-pong, with an empty group and ragged sizes.
+    m_sizes, N, K = [700, 650, 0, 800], 2048, 192
+    kern = "pingpong16_grouped_kernel<bf16"
+    case = si.grouped_case(m_sizes, N, K, 291, d_dtype="f32")
+    say(f"{kern}> {m_sizes} x {N} x {K}")
+    d = sg.grouped_gemm(case.A.to(dev), case.B.to(dev), case.m_offsets,
+                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert sg.gemm_last_kernel().startswith(kern), sg.gemm_last_kernel()
+    ref, bound = oracle.grouped_gemm(case.m_offsets, case.N, case.K, case.A, case.B, "bf16")
+    check_close(_np(d), ref, bound, "f32", kern)
 
 
 # ------------------------------------------------------ MXFP8 code range
@@ -206,8 +223,12 @@ def _e4m3_all_codes(rng, shape):
 
 
 @pytest.mark.parametrize("M,N,K,kern", [(4100, 4104, 384, "pingpong_mx_kernel<e4m3"),
+                                        (2600, 2600, 384, "pingpong_mx_kernel<e4m3"),
                                         (300, 264, 384, "mx_gemm_kernel<128,e4m3")])
 def test_mxfp8_full_e4m3_range(dev, M, N, K, kern):
+    # 4100 x 4104: 17 x 17 tiles of 256; 2600 x 2600: 11 x 11 tiles of 256
+    # but two rounds of 21 x 21 tiles of 128, so the ping-pong too; 300 x 264:
+    # the 128x128 kernel.
     rng = np.random.default_rng(M + K)
     A = torch.from_numpy(_e4m3_all_codes(rng, (M, K)))
     B = torch.from_numpy(_e4m3_all_codes(rng, (N, K)))
